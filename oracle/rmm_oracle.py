@@ -1,0 +1,215 @@
+"""Plain CPU oracle for Reduced Matrix Multiplication (RMM).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this module: only the tests, the smoke check of the build entry point
+and the benchmark's CPU-baseline leg use it.  It shares no code, header,
+table or helper with the HIP library.
+
+What it computes (everything in float64, from the exact stored input bits;
+bf16 and fp32 values convert to float64 without rounding):
+
+* k rule      -- |I| = ceil(rho * d) for rho in (0, 1].
+                 Source: hackcv.com "Algorithm Deep-Dive: RMM", section
+                 "Core Approach (Formula Level) / Contraction-Dimension TopK
+                 Selection"; gist.science "Reduced Matrix Multiplication",
+                 Technical Summary, "Selection Strategy".
+* scores      -- s_j = ||A[:, j]||_2, the L2 norm of column j of the
+                 activation matrix A (n x d) over all n rows.  Ranking uses
+                 q_j = s_j**2, which orders the columns identically.
+                 Source: hackcv.com, same section ("importance score");
+                 kaelemshawn.blog, section on why fewer multiply-adds can
+                 suffice (the column L2 norm as importance).
+* selection   -- the k indices with the largest scores; among equal scores
+                 the lower index wins; the set is returned in ascending order.
+                 The pages only say the selection is deterministic for a
+                 given input; lowest-index tie-breaking and ascending output
+                 are the readings this oracle fixes.
+* product     -- Y = A[:, I] @ B[I, :]  (hackcv.com, "Core Approach":
+                 RMM_rho(A, B)).  Only the kept rows of B take part.
+* QK^T        -- per query head h: I_h from the column norms of Q[h]
+                 (tokens x head_dim) over its query rows, and
+                 S_h = Q[h][:, I_h] @ K[g(h)][:, I_h]^T, where K/V head
+                 g(h) = h // (hq // hkv) serves query head h (grouped-query
+                 attention: selection on Q, K gathers the same feature
+                 dims).  Source: hackcv.com "Component mapping"; kaelemshawn
+                 .blog section on where RMM cuts inside the Transformer.
+* PV          -- per head h: I_h from the column norms of P[h]
+                 (queries x keys) over its query rows (the token axis is the
+                 contraction axis), and O_h = P[h][:, I_h] @ V[g(h)][I_h, :].
+                 Same sources.
+
+No blocking, fusion or reordering beyond these definitions.  A library
+matmul serves as the product step; a stable argsort serves as the ranking
+step.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "k_rule",
+    "col_energy",
+    "select",
+    "matmul",
+    "dense",
+    "qk",
+    "pv",
+    "kv_head",
+    "error_bound",
+]
+
+
+def k_rule(rho: float, d: int) -> int:
+    """Number of kept contraction indices, ceil(rho * d).
+
+    hackcv.com "Algorithm Deep-Dive: RMM", Core Approach: |I| = ceil(rho d);
+    the retention-ratio knob section: rho lies in (0, 1].
+
+    Reading (the pages are silent on floating-point rounding of rho * d):
+    rho is the decimal the caller wrote, so a product that lands within
+    1e-9 relative of an integer is that integer.  Example: 0.07 * 100 is
+    7.000000000000001 in binary floating point; a bare ceil would keep 8
+    columns where the caller asked for 7.
+    """
+    if isinstance(rho, bool) or not isinstance(rho, (int, float, np.floating)):
+        raise TypeError("rho must be a real number")
+    rho = float(rho)
+    if not math.isfinite(rho) or rho <= 0.0 or rho > 1.0:
+        raise ValueError(f"rho must lie in (0, 1], got {rho!r}")
+    d = int(d)
+    if d < 1:
+        raise ValueError(f"d must be >= 1, got {d}")
+    x = rho * d
+    r = round(x)
+    if abs(x - r) <= 1e-9 * max(1.0, x):
+        k = int(r)
+    else:
+        k = int(math.ceil(x))
+    return min(max(k, 1), d)
+
+
+def col_energy(A) -> np.ndarray:
+    """q_j = sum_i A[i, j]**2 in float64 (the squared column L2 norm)."""
+    A64 = np.asarray(A, dtype=np.float64)
+    if A64.ndim != 2:
+        raise ValueError("A must be 2-D (rows x contraction)")
+    return np.sum(A64 * A64, axis=0)
+
+
+def select(A, rho: float):
+    """Indices of the ceil(rho d) largest column norms of A, ascending.
+
+    Ranking key: descending q_j; equal keys keep ascending index order
+    (stable sort), so the lowest index wins a tie.  Returns (idx, q) with
+    idx int64 of length k, sorted ascending, and q the float64 energies.
+    """
+    A64 = np.asarray(A, dtype=np.float64)
+    d = A64.shape[1]
+    k = k_rule(rho, d)
+    q = col_energy(A64)
+    order = np.argsort(-q, kind="stable")
+    idx = np.sort(order[:k])
+    return idx.astype(np.int64), q
+
+
+def matmul(A, B, rho: float):
+    """RMM_rho(A, B) = A[:, I] @ B[I, :] with I = select(A, rho).
+
+    A: n x d, B: d x m.  Returns (idx, Y) with Y float64 n x m.
+    """
+    A64 = np.asarray(A, dtype=np.float64)
+    B64 = np.asarray(B, dtype=np.float64)
+    if A64.ndim != 2 or B64.ndim != 2 or A64.shape[1] != B64.shape[0]:
+        raise ValueError("need A (n x d) and B (d x m)")
+    idx, _ = select(A64, rho)
+    Y = A64[:, idx] @ B64[idx, :]
+    return idx, Y
+
+
+def dense(A, B) -> np.ndarray:
+    """The unreduced product A @ B in float64."""
+    return np.asarray(A, dtype=np.float64) @ np.asarray(B, dtype=np.float64)
+
+
+def kv_head(h: int, hq: int, hkv: int) -> int:
+    """K/V head serving query head h under grouped-query attention.
+
+    The pages say selection happens on Q per head and K/V gather the
+    matching dims; which K/V head pairs with which Q head is not stated.
+    Reading: contiguous groups of hq // hkv query heads share one K/V head
+    (the Llama convention).
+    """
+    if hq % hkv != 0:
+        raise ValueError("hq must be a multiple of hkv")
+    return h // (hq // hkv)
+
+
+def qk(Q, K, rho: float):
+    """Per-head reduced attention scores.
+
+    Q: (hq, tq, dh), K: (hkv, tk, dh).  For each query head h, I_h is chosen
+    from the column norms of Q[h] (over its tq rows) and
+    S[h] = Q[h][:, I_h] @ K[g(h)][:, I_h]^T.  Raw product: no 1/sqrt(dh)
+    scale and no mask (the pages give neither for the reduced product).
+    Returns (idx (hq, k) int64, S (hq, tq, tk) float64).
+    """
+    Q64 = np.asarray(Q, dtype=np.float64)
+    K64 = np.asarray(K, dtype=np.float64)
+    hq, tq, dh = Q64.shape
+    hkv, tk, dh2 = K64.shape
+    if dh2 != dh:
+        raise ValueError("Q and K head dims differ")
+    k = k_rule(rho, dh)
+    idx = np.empty((hq, k), dtype=np.int64)
+    S = np.empty((hq, tq, tk), dtype=np.float64)
+    for h in range(hq):
+        g = kv_head(h, hq, hkv)
+        I, _ = select(Q64[h], rho)
+        idx[h] = I
+        S[h] = Q64[h][:, I] @ K64[g][:, I].T
+    return idx, S
+
+
+def pv(P, V, rho: float):
+    """Per-head reduced attention output over the key (token) axis.
+
+    P: (h, tq, tk) attention weights, V: (hkv, tk, dv).  For each head h,
+    I_h is chosen from the column norms of P[h] over its tq query rows and
+    O[h] = P[h][:, I_h] @ V[g(h)][I_h, :].
+    Returns (idx (h, k) int64, O (h, tq, dv) float64).
+    """
+    P64 = np.asarray(P, dtype=np.float64)
+    V64 = np.asarray(V, dtype=np.float64)
+    h_, tq, tk = P64.shape
+    hkv, tk2, dv = V64.shape
+    if tk2 != tk:
+        raise ValueError("P key axis and V rows differ")
+    k = k_rule(rho, tk)
+    idx = np.empty((h_, k), dtype=np.int64)
+    O = np.empty((h_, tq, dv), dtype=np.float64)
+    for h in range(h_):
+        g = kv_head(h, h_, hkv)
+        I, _ = select(P64[h], rho)
+        idx[h] = I
+        O[h] = P64[h][:, I] @ V64[g][I, :]
+    return idx, O
+
+
+def error_bound(A, B, idx) -> float:
+    """Right-hand side of the pages' Frobenius error bound.
+
+    hackcv.com "Algorithm Deep-Dive: RMM", Core Approach, Properties:
+    ||AB - A[:, I] B[I, :]||_F <= sum over dropped j of
+    ||A[:, j]||_2 * ||B[j, :]||_2.
+    """
+    A64 = np.asarray(A, dtype=np.float64)
+    B64 = np.asarray(B, dtype=np.float64)
+    keep = np.zeros(A64.shape[1], dtype=bool)
+    keep[np.asarray(idx)] = True
+    drop = ~keep
+    s = np.sqrt(col_energy(A64))
+    b = np.sqrt(np.sum(B64 * B64, axis=1))
+    return float(np.sum(s[drop] * b[drop]))

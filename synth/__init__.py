@@ -1,0 +1,16 @@
+"""Seeded synthetic input generators (no part of the method lives here)."""
+
+from .workloads import (  # noqa: F401
+    FULL,
+    GAP_REQUIRED,
+    Workload,
+    attn_pv,
+    decode_qkv,
+    gqa_qk,
+    mlp_down,
+    mlp_up,
+    stored64,
+    tiny_projection,
+    to_bf16,
+    to_f32,
+)

@@ -1,0 +1,398 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+None of these re-derive the oracle's own formula: they use hand-worked
+values, exact rational arithmetic, pure-Python loops, brute force over all
+subsets, closed forms and invariants.  Each pin is written as a checker that
+takes an oracle-like namespace, so planted mistakes (mutants at the bottom of
+this file) can be shown to fail at least one pin.
+"""
+
+import itertools
+import json
+import math
+import os
+import types
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import rmm_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _loop_matmul(A, B):
+    """Pure-Python triple loop with exactly rounded sums (math.fsum)."""
+    n, d = len(A), len(A[0])
+    m = len(B[0])
+    return [[math.fsum(float(A[i][t]) * float(B[t][j]) for t in range(d)) for j in range(m)]
+            for i in range(n)]
+
+
+# --------------------------------------------------------------------------
+# pin checkers (return None when the pin holds, else a message)
+# --------------------------------------------------------------------------
+
+def pin_k_rule(ns):
+    for c in _load("k_rule.json")["cases"]:
+        k = ns.k_rule(c["rho"], c["d"])
+        if k != c["k"]:
+            return f"k_rule({c['rho']}, {c['d']}) = {k}, hand value {c['k']}"
+    # exact decimal arithmetic on many awkward products
+    for num in range(1, 101):
+        rho_s = f"{num / 100:.2f}"
+        for d in (1, 3, 7, 10, 100, 128, 999, 4096, 14336):
+            want = math.ceil(Fraction(rho_s) * d)
+            want = max(1, min(d, want))
+            got = ns.k_rule(float(rho_s), d)
+            if got != want:
+                return f"k_rule({rho_s}, {d}) = {got}, exact decimal ceil {want}"
+    return None
+
+
+def pin_worked_example(ns):
+    g = _load("worked_example.json")
+    A = np.array(g["A"], dtype=np.float64)
+    B = np.array(g["B"], dtype=np.float64)
+    if not np.array_equal(ns.col_energy(A), np.array(g["col_energy"], dtype=np.float64)):
+        return "column energies differ from the hand values"
+    for c in g["cases"]:
+        idx, Y = ns.matmul(A, B, c["rho"])
+        if list(np.asarray(idx)) != c["idx"]:
+            return f"rho={c['rho']}: idx {list(idx)} != hand {c['idx']}"
+        if not np.array_equal(np.asarray(Y), np.array(c["Y"], dtype=np.float64)):
+            return f"rho={c['rho']}: Y differs from the hand value"
+        err = float(np.linalg.norm(A @ B - Y))
+        if abs(err - c["err_fro"]) > 1e-12 * max(1.0, c["err_fro"]):
+            return f"rho={c['rho']}: error {err} != hand {c['err_fro']}"
+        bnd = ns.error_bound(A, B, idx)
+        if abs(bnd - c["bound"]) > 1e-12 * max(1.0, c["bound"]):
+            return f"rho={c['rho']}: bound {bnd} != hand {c['bound']}"
+    return None
+
+
+def pin_dense_loop(ns):
+    r = np.random.default_rng(7)
+    A = r.standard_normal((5, 7))
+    B = r.standard_normal((7, 3))
+    idx, Y = ns.matmul(A, B, 1.0)
+    if list(np.asarray(idx)) != list(range(7)):
+        return "rho=1 must keep every index"
+    ref = np.array(_loop_matmul(A.tolist(), B.tolist()))
+    if np.max(np.abs(np.asarray(Y) - ref)) > 1e-12 * np.max(np.abs(ref)):
+        return "rho=1 product differs from the triple loop"
+    return None
+
+
+def pin_reduced_loop(ns):
+    """Reduced product equals the triple loop restricted to the kept set,
+    where the kept set is recomputed by brute-force comparison of norms."""
+    r = np.random.default_rng(11)
+    A = r.integers(-4, 5, size=(4, 9)).astype(np.float64)
+    B = r.standard_normal((9, 5))
+    rho = 0.5
+    idx, Y = ns.matmul(A, B, rho)
+    k = 5
+    # brute force: an index is kept iff fewer than k indices beat it, where
+    # "beats" means a larger energy, or an equal energy and a lower index
+    energy = [sum(float(A[i][j]) ** 2 for i in range(4)) for j in range(9)]
+    keep = [j for j in range(9)
+            if sum(1 for t in range(9) if energy[t] > energy[j] or (energy[t] == energy[j] and t < j)) < k]
+    if list(np.asarray(idx)) != keep:
+        return f"kept set {list(idx)} != brute force {keep}"
+    ref = np.array(_loop_matmul(A[:, keep].tolist(), B[keep, :].tolist()))
+    if np.max(np.abs(np.asarray(Y) - ref)) > 1e-12 * np.max(np.abs(ref)):
+        return "reduced product differs from the loop over the kept set"
+    return None
+
+
+def pin_minimax_bruteforce(ns):
+    """TopK by column norm maximises the kept norm (and energy) sum over all
+    k-subsets, i.e. minimises the worst-case error over B with unit rows
+    (the pages' minimax property); ties go to the lexicographically smallest
+    maximiser."""
+    r = np.random.default_rng(3)
+    for trial in range(6):
+        d, n = 12, 5
+        A = r.integers(-3, 4, size=(n, d)).astype(np.float64)
+        if trial % 2 == 1:
+            A[:, 7] = A[:, 2]          # planted exact tie
+            A[:, 9] = -A[:, 4]         # sign-flipped copy: same energy
+        q = [int(sum(int(v) ** 2 for v in A[:, j])) for j in range(d)]
+        for k in (1, 3, 6, 11):
+            rho = k / d
+            idx, _ = ns.matmul(A, np.eye(d), rho)
+            idx = tuple(int(i) for i in np.asarray(idx))
+            best_q = max(sum(q[j] for j in S) for S in itertools.combinations(range(d), k))
+            maximisers = [S for S in itertools.combinations(range(d), k)
+                          if sum(q[j] for j in S) == best_q]
+            if sum(q[j] for j in idx) != best_q:
+                return f"trial {trial} k={k}: kept energy is not maximal"
+            if idx != min(maximisers):
+                return f"trial {trial} k={k}: {idx} is not the lexicographically smallest maximiser"
+            s = [math.sqrt(v) for v in q]
+            best_s = max(math.fsum(s[j] for j in S) for S in itertools.combinations(range(d), k))
+            if math.fsum(s[j] for j in idx) < best_s * (1 - 1e-12):
+                return f"trial {trial} k={k}: kept norm sum is not maximal"
+    return None
+
+
+def pin_error_bound(ns):
+    """||AB - A_I B_I||_F <= sum_{j not in I} ||A_j|| ||B_j|| on generated inputs."""
+    cases = []
+    w = synth.tiny_projection()
+    cases.append((synth.stored64(w.tensors["A"]), synth.stored64(w.tensors["B"]), 0.5))
+    w = synth.mlp_down(n=64, d=512, m=96)
+    for rho in w.rhos:
+        cases.append((synth.stored64(w.tensors["A"]), synth.stored64(w.tensors["B"]), rho))
+    for A, B, rho in cases:
+        idx, Y = ns.matmul(A, B, rho)
+        err = float(np.linalg.norm(A @ B - np.asarray(Y)))
+        bnd = ns.error_bound(A, B, idx)
+        if not err <= bnd * (1 + 1e-12) + 1e-300:
+            return f"error {err} exceeds bound {bnd} at rho={rho}"
+    return None
+
+
+def pin_worst_case(ns):
+    """Orthonormal dropped rows of B attain error sqrt(sum dropped energy)."""
+    r = np.random.default_rng(5)
+    n, d, m = 10, 8, 6
+    A = r.standard_normal((n, d))
+    rho = 0.5
+    idx, _ = ns.matmul(A, np.zeros((d, m)), rho)
+    drop = [j for j in range(d) if j not in set(int(i) for i in np.asarray(idx))]
+    Qm, _ = np.linalg.qr(r.standard_normal((m, m)))
+    B = r.standard_normal((d, m))
+    for t, j in enumerate(drop):
+        B[j] = Qm[t]
+    _, Y = ns.matmul(A, B, rho)
+    err = float(np.linalg.norm(A @ B - np.asarray(Y)))
+    want = math.sqrt(math.fsum(float(A[i, j]) ** 2 for i in range(n) for j in drop))
+    if abs(err - want) > 1e-12 * want:
+        return f"worst-case error {err} != closed form {want}"
+    return None
+
+
+def pin_ties(ns):
+    # all columns identical: the first k are kept
+    A = np.tile(np.array([[1.0], [2.0], [-2.0]]), (1, 10))
+    idx, _ = ns.matmul(A, np.eye(10), 0.3)
+    if list(np.asarray(idx)) != [0, 1, 2]:
+        return f"identical columns: {list(idx)}"
+    # zero columns are kept only when nothing else is left, lowest first
+    A = np.zeros((2, 6))
+    A[:, 4] = [1, 1]
+    idx, _ = ns.matmul(A, np.eye(6), 0.5)
+    if list(np.asarray(idx)) != [0, 1, 4]:
+        return f"zero columns: {list(idx)}"
+    # k = 1 is the first argmax
+    A = np.array([[1.0, 3.0, -3.0, 2.0]])
+    idx, _ = ns.matmul(A, np.eye(4), 0.25)
+    if list(np.asarray(idx)) != [int(np.argmax(np.abs(A[0])))]:
+        return f"k=1: {list(idx)}"
+    return None
+
+
+def pin_invariances(ns):
+    r = np.random.default_rng(9)
+    w = synth.mlp_down(n=32, d=256, m=40)
+    A = synth.stored64(w.tensors["A"])
+    B = synth.stored64(w.tensors["B"])
+    rho = 0.7
+    idx, Y = ns.matmul(A, B, rho)
+    # scaling by a power of two is exact
+    idx2, Y2 = ns.matmul(4.0 * A, B, rho)
+    if not np.array_equal(np.asarray(idx2), np.asarray(idx)) or not np.array_equal(np.asarray(Y2), 4.0 * np.asarray(Y)):
+        return "scaling A changed the selection or did not scale Y"
+    # sign flips of columns (with the matching rows of B) change nothing
+    sg = np.where(r.random(256) < 0.5, -1.0, 1.0)
+    idx3, Y3 = ns.matmul(A * sg, B * sg[:, None], rho)
+    if not np.array_equal(np.asarray(idx3), np.asarray(idx)) or np.max(np.abs(np.asarray(Y3) - np.asarray(Y))) > 1e-12 * np.max(np.abs(Y)):
+        return "sign flips changed the result"
+    # permuting columns of A with rows of B permutes I and keeps Y
+    perm = r.permutation(256)
+    idx4, Y4 = ns.matmul(A[:, perm], B[perm, :], rho)
+    if sorted(int(perm[i]) for i in np.asarray(idx4)) != [int(i) for i in np.asarray(idx)]:
+        return "permutation did not permute the kept set"
+    if np.max(np.abs(np.asarray(Y4) - np.asarray(Y))) > 1e-12 * np.max(np.abs(Y)):
+        return "permutation changed Y"
+    return None
+
+
+def pin_qk(ns):
+    r = np.random.default_rng(13)
+    hq, hkv, tq, tk, dh = 4, 2, 3, 5, 8
+    Q = r.standard_normal((hq, tq, dh))
+    K = r.standard_normal((hkv, tk, dh))
+    idx, S = ns.qk(Q, K, 1.0)
+    Kx = np.repeat(K, hq // hkv, axis=0)   # Llama-style repeat of K/V heads
+    for h in range(hq):
+        ref = np.array(_loop_matmul(Q[h].tolist(), Kx[h].T.tolist()))
+        if np.max(np.abs(np.asarray(S[h]) - ref)) > 1e-12 * np.max(np.abs(ref)):
+            return f"rho=1 QK^T head {h} differs from the triple loop"
+    idx, S = ns.qk(Q, K, 0.5)
+    idx_r, S_r = ns.qk(Q, Kx, 0.5)
+    if not np.array_equal(np.asarray(idx), np.asarray(idx_r)) or np.max(np.abs(np.asarray(S) - np.asarray(S_r))) > 0:
+        return "GQA gather differs from explicitly repeated K heads"
+    for h in range(hq):
+        q = np.sum(Q[h] ** 2, axis=0)
+        kept = set(int(i) for i in np.asarray(idx[h]))
+        if min(q[j] for j in kept) < max(q[j] for j in range(dh) if j not in kept):
+            return f"head {h}: a dropped feature outranks a kept one"
+        ref = np.array(_loop_matmul(Q[h][:, sorted(kept)].tolist(), Kx[h][:, sorted(kept)].T.tolist()))
+        if np.max(np.abs(np.asarray(S[h]) - ref)) > 1e-12 * np.max(np.abs(ref)):
+            return f"head {h}: reduced QK^T differs from the loop over kept features"
+    return None
+
+
+def pin_pv(ns):
+    r = np.random.default_rng(17)
+    h, hkv, tq, tk, dv = 4, 1, 3, 10, 4
+    L = r.standard_normal((h, tq, tk)) * 2
+    P = np.exp(L) / np.exp(L).sum(axis=2, keepdims=True)
+    V = r.standard_normal((hkv, tk, dv))
+    idx, Ov = ns.pv(P, V, 1.0)
+    for hh in range(h):
+        ref = np.array(_loop_matmul(P[hh].tolist(), V[0].tolist()))
+        if np.max(np.abs(np.asarray(Ov[hh]) - ref)) > 1e-12 * np.max(np.abs(ref)):
+            return f"rho=1 PV head {hh} differs from the triple loop"
+    Vx = np.repeat(V, h // hkv, axis=0)
+    idx, Ov = ns.pv(P, V, 0.5)
+    idx_r, O_r = ns.pv(P, Vx, 0.5)
+    if not np.array_equal(np.asarray(idx), np.asarray(idx_r)) or np.max(np.abs(np.asarray(Ov) - np.asarray(O_r))) > 0:
+        return "GQA gather differs from explicitly repeated V heads"
+    for hh in range(h):
+        q = np.sum(P[hh] ** 2, axis=0)
+        kept = sorted(int(i) for i in np.asarray(idx[hh]))
+        if min(q[kept]) < max(q[j] for j in range(tk) if j not in kept):
+            return f"head {hh}: a dropped key outranks a kept one"
+        ref = np.array(_loop_matmul(P[hh][:, kept].tolist(), V[0][kept, :].tolist()))
+        if np.max(np.abs(np.asarray(Ov[hh]) - ref)) > 1e-12 * np.max(np.abs(ref)):
+            return f"head {hh}: reduced PV differs from the loop over kept keys"
+        err = float(np.linalg.norm(P[hh] @ V[0] - np.asarray(Ov[hh])))
+        drop = [j for j in range(tk) if j not in kept]
+        bnd = math.fsum(math.sqrt(q[j]) * float(np.linalg.norm(V[0][j])) for j in drop)
+        if err > bnd * (1 + 1e-12):
+            return f"head {hh}: PV error exceeds the bound"
+    return None
+
+
+PINS = [pin_k_rule, pin_worked_example, pin_dense_loop, pin_reduced_loop, pin_minimax_bruteforce,
+        pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_pv]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    msg = pin(O)
+    assert msg is None, msg
+
+
+def test_k_rule_rejects_bad_rho():
+    for bad in (0.0, -0.1, 1.5, float("nan"), float("inf"), -float("inf")):
+        with pytest.raises(ValueError):
+            O.k_rule(bad, 10)
+    with pytest.raises(ValueError):
+        O.k_rule(0.5, 0)
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each mutant of the oracle must fail at least one pin
+# --------------------------------------------------------------------------
+
+def _mutant(**over):
+    ns = types.SimpleNamespace(**{k: getattr(O, k) for k in O.__all__})
+    for k, v in over.items():
+        setattr(ns, k, v)
+    # rebuild the composite functions so they call the mutated pieces
+    def select(A, rho, _ns=ns):
+        A64 = np.asarray(A, dtype=np.float64)
+        k = _ns.k_rule(rho, A64.shape[1])
+        q = _ns.col_energy(A64)
+        order = _ns._order(q) if hasattr(_ns, "_order") else np.argsort(-q, kind="stable")
+        return np.sort(order[:k]), q
+
+    def matmul(A, B, rho, _ns=ns):
+        A64 = np.asarray(A, dtype=np.float64)
+        B64 = np.asarray(B, dtype=np.float64)
+        idx, _ = _ns.select(A64, rho)
+        return idx, _ns._product(A64, B64, idx)
+
+    def qk(Q, K, rho, _ns=ns):
+        Q64 = np.asarray(Q, dtype=np.float64)
+        K64 = np.asarray(K, dtype=np.float64)
+        hq, tq, dh = Q64.shape
+        hkv, tk, _ = K64.shape
+        out_i, out_s = [], []
+        for h in range(hq):
+            g = _ns.kv_head(h, hq, hkv)
+            I, _ = _ns.select(Q64[h], rho)
+            out_i.append(I)
+            out_s.append(Q64[h][:, I] @ K64[g][:, I].T)
+        return np.array(out_i), np.array(out_s)
+
+    def pv(P, V, rho, _ns=ns):
+        P64 = np.asarray(P, dtype=np.float64)
+        V64 = np.asarray(V, dtype=np.float64)
+        h_, tq, tk = P64.shape
+        hkv = V64.shape[0]
+        out_i, out_o = [], []
+        for h in range(h_):
+            g = _ns.kv_head(h, h_, hkv)
+            I, _ = _ns.select(P64[h], rho)
+            out_i.append(I)
+            out_o.append(P64[h][:, I] @ V64[g][I, :])
+        return np.array(out_i), np.array(out_o)
+
+    if not hasattr(ns, "_product"):
+        ns._product = lambda A, B, idx: A[:, idx] @ B[idx, :]
+    if "select" not in over:
+        ns.select = select
+    ns.matmul = matmul
+    ns.qk = qk
+    ns.pv = pv
+    return ns
+
+
+MUTANTS = {
+    "row_norms_instead_of_column": dict(col_energy=lambda A: np.sum(np.asarray(A, float) ** 2, axis=1)
+                                        if np.asarray(A).shape[0] == np.asarray(A).shape[1]
+                                        else np.resize(np.sum(np.asarray(A, float) ** 2, axis=1), np.asarray(A).shape[1])),
+    "l1_instead_of_l2": dict(col_energy=lambda A: np.sum(np.abs(np.asarray(A, float)), axis=0)),
+    "smallest_instead_of_largest": dict(_order=lambda q: np.argsort(q, kind="stable")),
+    "highest_index_wins_ties": dict(_order=lambda q: (len(q) - 1 - np.argsort(-q[::-1], kind="stable"))),
+    "floor_instead_of_ceil": dict(k_rule=lambda rho, d: max(1, int(math.floor(rho * d)))),
+    "bare_binary_ceil": dict(k_rule=lambda rho, d: min(d, max(1, int(math.ceil(rho * d))))),
+    "drops_kept_rows_of_B": dict(_product=lambda A, B, idx: A[:, idx] @ B[np.sort(np.setdiff1d(np.arange(B.shape[0]), idx))[:len(idx)], :]
+                                 if len(idx) < B.shape[0] else A @ B),
+    "gqa_modulo_mapping": dict(kv_head=lambda h, hq, hkv: h % hkv),
+    "product_sign_flip": dict(_product=lambda A, B, idx: -(A[:, idx] @ B[idx, :])),
+    "dense_instead_of_reduced": dict(_product=lambda A, B, idx: A @ B),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_fails_a_pin(name):
+    ns = _mutant(**MUTANTS[name])
+    failures = []
+    for pin in PINS:
+        try:
+            msg = pin(ns)
+        except Exception as e:  # a crash also counts as caught
+            msg = f"raised {type(e).__name__}"
+        if msg is not None:
+            failures.append(pin.__name__)
+    assert failures, f"mutant {name} passed every pin"
+
+
+def test_unmutated_rebuild_passes_every_pin():
+    ns = _mutant()
+    for pin in PINS:
+        assert pin(ns) is None, pin.__name__
