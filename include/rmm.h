@@ -1,0 +1,162 @@
+/*
+ * rmm.h -- C ABI of librmm, Reduced Matrix Multiplication (RMM) on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (sources are the public pages about the paper "Reduced Matrix
+ * Multiplication: Input-Adaptive Matrix-Product Reduction for LLM
+ * Inference"):
+ *   For Y = A B with A (n x d) activations and B (d x m), score every
+ *   contraction index j by the L2 norm of column j of A over all n rows,
+ *   keep the k = ceil(rho d) largest, and multiply over the kept slice only:
+ *   Y = A[:, I] B[I, :].
+ *   -- "Algorithm Deep-Dive: RMM" (hackcv.com), Core Approach (Formula
+ *      Level): Contraction-Dimension TopK Selection and the importance score;
+ *      gist.science technical summary, Methodology: Selection Strategy.
+ *   The same rule covers linear / MLP projections (contraction over the
+ *   hidden dim), Q K^T (per query head, over the head feature dim, K of the
+ *   shared kv head gathering the same dims) and P V (over key positions).
+ *   -- hackcv.com, Core Approach: Component mapping.
+ *
+ * Readings fixed by this library where the pages are silent:
+ *   - k = ceil(rho d) with rho read as the decimal it was written as: a
+ *     product within 1e-9 relative of an integer is that integer (rmm_k).
+ *   - Ranking key is the fp32 sum of squares of the stored values (same
+ *     order as the norm).  Equal keys: the lower index wins.  The kept set
+ *     is written in ascending index order.
+ *   - One kept set per call over all rows of A; one per head for QK / PV.
+ *   - GQA: query head h reads K/V head h / (hq / hkv).
+ *   - Q K^T is the raw product (no 1/sqrt(dh) scale, no mask).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no state between calls; scratch memory is
+ *     the caller's workspace (size from the matching *_workspace query).
+ *   - Matrices are row-major with unit inner stride; leading dimensions and
+ *     head strides are in ELEMENTS.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream); outputs are valid once the stream reaches that point.  The
+ *     calls never synchronise the host.
+ *   - Every argument is checked before any work is queued: a call that
+ *     returns an argument error (anything but RMM_ERR_HIP) has queued
+ *     nothing and written nothing.  RMM_ERR_HIP means the runtime refused a
+ *     launch; earlier stages of that call may already be queued.
+ *     Overlapping calls on different streams must use different workspaces.
+ *   - Results are bitwise reproducible for identical inputs and shapes
+ *     (fixed reduction order, no floating-point atomics).
+ *   - Floating-point inputs are expected finite; results for NaN / Inf
+ *     inputs are unspecified (but the call completes).
+ *   - Sizes: every dimension in [1, 2^31); per-head operands must stay below
+ *     2 GiB (matrix-core loaders use 32-bit byte offsets).
+ *   - bf16 products run on the matrix cores (bf16 x bf16, fp32 accumulate);
+ *     fp32 products run on the vector ALUs in fp32.
+ */
+#ifndef RMM_H_
+#define RMM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RMM_OK = 0,
+  RMM_ERR_NULL = 1,      /* a required pointer is NULL */
+  RMM_ERR_RHO = 2,       /* rho not finite or outside (0, 1] */
+  RMM_ERR_SHAPE = 3,     /* a dimension < 1, a leading dim too small, hq % hkv != 0, or a size limit */
+  RMM_ERR_DTYPE = 4,     /* unsupported dtype or dtype combination */
+  RMM_ERR_ALIGN = 5,     /* pointer not aligned to its element size */
+  RMM_ERR_WORKSPACE = 6, /* workspace NULL / too small / not 256-byte aligned */
+  RMM_ERR_HIP = 7,       /* the HIP runtime refused a launch */
+  RMM_ERR_ALIAS = 8      /* an output overlaps an input or another output */
+} rmm_status_t;
+
+typedef enum { RMM_FP32 = 0, RMM_BF16 = 1 } rmm_dtype_t;
+
+/* Number of kept indices, ceil(rho * d) under the decimal reading above;
+ * -1 when rho is not finite, rho <= 0, rho > 1 or d < 1.
+ * hackcv.com "Algorithm Deep-Dive: RMM", Core Approach and the
+ * retention-ratio section (rho in (0, 1]). */
+int64_t rmm_k(double rho, int64_t d);
+
+/* Static, human-readable name of a status code. */
+const char* rmm_status_str(int status);
+
+/* ---------------------------------------------------------------------
+ * rmm_select: the kept index set of A alone.
+ *   A       [n x d] (lda >= d), fp32 or bf16.
+ *   idx     [k] int32, written ascending, k = rmm_k(rho, d).
+ *   scores  optional [d] fp32: s_j = sqrt(fp32 sum of squares of column j);
+ *           NULL to skip.
+ * Score and TopK: hackcv.com, Core Approach ("importance score" and TopK).
+ * ------------------------------------------------------------------- */
+size_t rmm_select_workspace(int64_t n, int64_t d, int dtype);
+rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho,
+                        int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * rmm_matmul: Y = A[:, I] B[I, :] with I = rmm_select(A, rho).
+ *   A   [n x d] activations (lda >= d), B [d x m] (ldb >= m); both `dtype`.
+ *   idx [k] int32 ascending (always written; 0..d-1 when rho = 1).
+ *   Y   [n x m] (ldy >= m), y_dtype fp32 or bf16.
+ * rho = 1 computes the dense product with no scoring pass.
+ * n <= 16 with bf16 takes the decode path (GEMV over the kept rows of B).
+ * Source: hackcv.com, Core Approach: RMM_rho(A, B) = A[:, I] B[I, :];
+ * linear / MLP mapping from the Component mapping paragraph.
+ * ------------------------------------------------------------------- */
+size_t rmm_matmul_workspace(int64_t n, int64_t d, int64_t m, int64_t lda, int dtype, double rho);
+rmm_status_t rmm_matmul(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
+                        int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Instrumented rmm_matmul: the same computation, and in addition records
+ * five caller-created HIP events (hipEvent_t, timing enabled) on `stream`
+ * at the stage boundaries: [0] before scoring, [1] before TopK, [2] before
+ * the gather-pack, [3] before the product kernel, [4] after it.  A stage a
+ * path does not run leaves its two events back to back.  For per-kernel
+ * timing by benchmarks; stage_events and its five entries must be non-NULL. */
+rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
+                              int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy,
+                              void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
+
+/* ---------------------------------------------------------------------
+ * rmm_qk: per query head h, S[h] = Q[h][:, I_h] K[g(h)][:, I_h]^T with
+ * I_h the ceil(rho dh) head-feature dims of largest column norm of Q[h]
+ * over its tq rows, g(h) = h / (hq / hkv).
+ *   Q   element (h, t, f) at Q[h*q_hs + t*q_ts + f]; K likewise with k_hs,
+ *       k_ts.  Q and K share `dtype` (fp32 or bf16).
+ *   idx [hq][k] int32, each row ascending, k = rmm_k(rho, dh).
+ *   S   [hq][tq][tk] contiguous, s_dtype fp32 or bf16.
+ * Source: hackcv.com, Component mapping (QK^T over the head feature dim,
+ * selection on Q, K gathers the matching dims under GQA).
+ * ------------------------------------------------------------------- */
+size_t rmm_qk_workspace(int64_t hq, int64_t tq, int64_t tk, int64_t dh, int dtype, double rho);
+rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
+                    int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho,
+                    int32_t* idx, void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * rmm_pv: per head h, O[h] = P[h][:, I_h] V[g(h)][I_h, :] with I_h the
+ * ceil(rho tk) key positions of largest column norm of P[h] over its tq
+ * query rows, g(h) = h / (h_count / hkv).
+ *   P   element (h, q, t) at P[h*p_hs + q*p_ts + t], p_dtype fp32 or bf16.
+ *   V   element (g, t, c) at V[g*v_hs + t*v_ts + c], v_dtype bf16 or fp32.
+ *       bf16 V uses the matrix cores and rounds P to bf16 (nearest even);
+ *       fp32 V requires fp32 P and runs in fp32.
+ *   idx [h][k] int32, each row ascending, k = rmm_k(rho, tk).
+ *   O   [h][tq][dv] contiguous, o_dtype fp32 or bf16.
+ * Source: hackcv.com, Component mapping (PV optionally over token
+ * positions); kaelemshawn.blog, section on where RMM cuts inside the
+ * Transformer (column norm of P over the history positions).
+ * ------------------------------------------------------------------- */
+size_t rmm_pv_workspace(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho);
+rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
+                    int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
+                    int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMM_H_ */

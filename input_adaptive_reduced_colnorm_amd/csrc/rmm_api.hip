@@ -1,0 +1,607 @@
+// C ABI of librmm: argument checks, path planning, workspace carving and
+// kernel dispatch.  Every check runs before the first launch.
+
+#include <math.h>
+#include <string.h>
+
+#include "rmm.h"
+#include "rmm_internal.h"
+
+using namespace rmm;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxOperandBytes = ((int64_t)1 << 31) - 1;
+constexpr int kDecodeRows = 16;
+constexpr int kKTile = 64;
+
+bool rho_ok(double rho) { return isfinite(rho) && rho > 0.0 && rho <= 1.0; }
+
+int64_t k_of(double rho, int64_t d) {
+  if (!rho_ok(rho) || d < 1 || d >= kMaxDim) return -1;
+  const double x = rho * (double)d;
+  const double r = nearbyint(x);
+  int64_t k;
+  if (fabs(x - r) <= 1e-9 * (x > 1.0 ? x : 1.0))
+    k = (int64_t)r;
+  else
+    k = (int64_t)ceil(x);
+  if (k < 1) k = 1;
+  if (k > d) k = d;
+  return k;
+}
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+bool dim_ok(int64_t x) { return x >= 1 && x < kMaxDim; }
+bool dtype_ok(int dt) { return dt == RMM_FP32 || dt == RMM_BF16; }
+size_t elt_size(int dt) { return dt == RMM_BF16 ? 2 : 4; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Byte span [lo, hi) touched by a strided 3-D operand.
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span3(const void* p, int64_t heads, int64_t hs, int64_t rows, int64_t rs, int64_t cols, size_t elt) {
+  const int64_t last = (heads - 1) * hs + (rows - 1) * rs + (cols - 1);
+  Span s;
+  s.lo = (uintptr_t)p;
+  s.hi = (uintptr_t)p + (uintptr_t)((last + 1) * (int64_t)elt);
+  return s;
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Workspace carving: 256-byte aligned regions laid out in call order.
+struct Carve {
+  size_t used = 0;
+  size_t take(size_t bytes) {
+    const size_t off = used;
+    used += (bytes + 255) / 256 * 256;
+    return off;
+  }
+};
+
+hipError_t clear_error() { return hipGetLastError(); }
+
+#define RMM_LAUNCH(expr)                           \
+  do {                                             \
+    if ((expr) != hipSuccess) return RMM_ERR_HIP;  \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// selection plan (shared by select / matmul / qk / pv)
+// ---------------------------------------------------------------------------
+struct SelPlan {
+  int splits = 0;
+  size_t off_partial = 0, off_gkeys = 0;
+  bool gkeys = false;
+};
+
+void plan_select(Carve& cv, SelPlan& sp, int heads, int64_t n, int64_t d, bool bf16) {
+  sp.splits = colnorm_splits(heads, (int)n, (int)d, bf16);
+  sp.off_partial = cv.take((size_t)heads * sp.splits * d * 4);
+  sp.gkeys = d > topk_lds_capacity();
+  if (sp.gkeys) sp.off_gkeys = cv.take((size_t)heads * d * 4);
+}
+
+// Records stage event i when the caller asked for stage timing.
+struct Marks {
+  void* const* ev;
+  hipStream_t s;
+  hipError_t mark(int i) const { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; }
+};
+hipError_t mark_of(const Marks* mk, int i) { return mk->mark(i); }
+
+hipError_t run_select(const SelPlan& sp, char* ws, const void* A, bool bf16, int64_t hs, int64_t lda, int heads,
+                      int64_t n, int64_t d, int64_t k, int32_t* idx, int64_t idx_hs, float* scores, hipStream_t s,
+                      const Marks* mk = nullptr) {
+  float* partial = (float*)(ws + sp.off_partial);
+  hipError_t e = launch_colnorm(A, bf16, hs, lda, heads, (int)n, (int)d, sp.splits, partial, s);
+  if (e != hipSuccess) return e;
+  if (mk && (e = mark_of(mk, 1)) != hipSuccess) return e;
+  return launch_topk(partial, heads, sp.splits, (int)d, (int)k, idx, idx_hs, scores, d,
+                     sp.gkeys ? (uint32_t*)(ws + sp.off_gkeys) : nullptr, s);
+}
+
+// ---------------------------------------------------------------------------
+// matmul plan
+// ---------------------------------------------------------------------------
+enum class MatPath { kSimt, kDecode, kMfmaDirect, kMfmaPacked };
+
+struct MatPlan {
+  MatPath path;
+  int64_t k = 0, k_pad = 0;
+  bool all = false;
+  SelPlan sel;
+  bool use_sel = false;
+  size_t off_pack = 0, off_at = 0, off_gpart = 0, off_cnt = 0, off_dkeys = 0;
+  int gsplits = 0;
+  size_t total = 0;
+};
+
+MatPlan plan_matmul(int64_t n, int64_t d, int64_t m, int64_t lda, int64_t ldb, int dtype, double rho,
+                    bool a_ptr_ok, bool b_ptr_ok) {
+  MatPlan p;
+  Carve cv;
+  p.k = k_of(rho, d);
+  p.all = p.k == d;
+  p.k_pad = round_up(p.k, kKTile);
+  const bool bf16 = dtype == RMM_BF16;
+  const bool b_vec = bf16 && b_ptr_ok && ldb % 8 == 0 && m % 8 == 0;
+  if (!bf16 || !b_vec) {
+    p.path = MatPath::kSimt;
+    if (!p.all) {
+      plan_select(cv, p.sel, 1, n, d, bf16);
+      p.use_sel = true;
+    }
+  } else if (n <= kDecodeRows) {
+    p.path = MatPath::kDecode;
+    if (d > topk_lds_capacity()) p.off_dkeys = cv.take((size_t)d * 4);
+    p.off_at = cv.take((size_t)p.k_pad * 16 * 4);
+    p.gsplits = gemv_splits((int)p.k, (int)n, (int)m);
+    p.off_gpart = cv.take((size_t)p.gsplits * 16 * m * 4);
+    p.off_cnt = cv.take((size_t)((m + 127) / 128) * 4);
+  } else {
+    const bool a_direct = p.all && a_ptr_ok && lda % 8 == 0 && d % 8 == 0;
+    if (a_direct) {
+      p.path = MatPath::kMfmaDirect;
+    } else {
+      p.path = MatPath::kMfmaPacked;
+      if (!p.all) {
+        plan_select(cv, p.sel, 1, n, d, true);
+        p.use_sel = true;
+      }
+      p.off_pack = cv.take((size_t)n * p.k_pad * 2);
+    }
+  }
+  p.total = cv.used;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t rmm_k(double rho, int64_t d) { return k_of(rho, d); }
+
+const char* rmm_status_str(int status) {
+  switch (status) {
+    case RMM_OK: return "RMM_OK";
+    case RMM_ERR_NULL: return "RMM_ERR_NULL: a required pointer is NULL";
+    case RMM_ERR_RHO: return "RMM_ERR_RHO: rho must be finite and in (0, 1]";
+    case RMM_ERR_SHAPE: return "RMM_ERR_SHAPE: invalid dimension, stride or size";
+    case RMM_ERR_DTYPE: return "RMM_ERR_DTYPE: unsupported dtype";
+    case RMM_ERR_ALIGN: return "RMM_ERR_ALIGN: pointer not aligned to its element size";
+    case RMM_ERR_WORKSPACE: return "RMM_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case RMM_ERR_HIP: return "RMM_ERR_HIP: a kernel launch failed";
+    case RMM_ERR_ALIAS: return "RMM_ERR_ALIAS: an output overlaps another argument";
+    default: return "unknown rmm status";
+  }
+}
+
+// ------------------------------- select ------------------------------------
+
+size_t rmm_select_workspace(int64_t n, int64_t d, int dtype) {
+  if (!dim_ok(n) || !dim_ok(d) || !dtype_ok(dtype)) return 0;
+  Carve cv;
+  SelPlan sp;
+  plan_select(cv, sp, 1, n, d, dtype == RMM_BF16);
+  return cv.used;
+}
+
+rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho, int32_t* idx,
+                        float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!A || !idx) return RMM_ERR_NULL;
+  if (!rho_ok(rho)) return RMM_ERR_RHO;
+  if (!dtype_ok(dtype)) return RMM_ERR_DTYPE;
+  if (!dim_ok(n) || !dim_ok(d) || lda < d || lda >= kMaxDim) return RMM_ERR_SHAPE;
+  const size_t elt = elt_size(dtype);
+  if (!aligned(A, elt) || !aligned(idx, 4) || (scores && !aligned(scores, 4))) return RMM_ERR_ALIGN;
+  const int64_t k = k_of(rho, d);
+  const bool all = k == d;
+  Carve cv;
+  SelPlan sp;
+  const bool need_sel = !all || scores != nullptr;
+  if (need_sel) plan_select(cv, sp, 1, n, d, dtype == RMM_BF16);
+  if (cv.used > 0 && (!workspace || workspace_bytes < cv.used || !aligned(workspace, 256))) return RMM_ERR_WORKSPACE;
+  const Span sa = span3(A, 1, 0, n, lda, d, elt);
+  const Span si = span3(idx, 1, 0, 1, k, k, 4);
+  if (overlap(si, sa)) return RMM_ERR_ALIAS;
+  if (scores) {
+    const Span ss = span3(scores, 1, 0, 1, d, d, 4);
+    if (overlap(ss, sa) || overlap(ss, si)) return RMM_ERR_ALIAS;
+  }
+  if (cv.used > 0) {
+    const Span sw = span3(workspace, 1, 0, 1, (int64_t)cv.used, (int64_t)cv.used, 1);
+    if (overlap(sw, sa) || overlap(sw, si) || (scores && overlap(sw, span3(scores, 1, 0, 1, d, d, 4))))
+      return RMM_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  clear_error();
+  if (need_sel) {
+    RMM_LAUNCH(run_select(sp, (char*)workspace, A, dtype == RMM_BF16, 0, lda, 1, n, d, k, idx, k, scores, s));
+  } else {
+    RMM_LAUNCH(launch_iota(idx, k, 1, (int)d, s));
+  }
+  return RMM_OK;
+}
+
+// ------------------------------- matmul ------------------------------------
+
+size_t rmm_matmul_workspace(int64_t n, int64_t d, int64_t m, int64_t lda, int dtype, double rho) {
+  if (!dim_ok(n) || !dim_ok(d) || !dim_ok(m) || lda < d || !dtype_ok(dtype) || !rho_ok(rho)) return 0;
+  // Upper bound over the paths the call may take (B layout is not known here).
+  MatPlan a = plan_matmul(n, d, m, lda, m, dtype, rho, true, true);
+  MatPlan b = plan_matmul(n, d, m, lda, m + 1, dtype, rho, true, false);
+  return a.total > b.total ? a.total : b.total;
+}
+
+namespace {
+
+rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
+                         int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (!A || !B || !idx || !Y) return RMM_ERR_NULL;
+  if (!rho_ok(rho)) return RMM_ERR_RHO;
+  if (!dtype_ok(dtype) || !dtype_ok(y_dtype)) return RMM_ERR_DTYPE;
+  if (!dim_ok(n) || !dim_ok(d) || !dim_ok(m) || lda < d || ldb < m || ldy < m || lda >= kMaxDim ||
+      ldb >= kMaxDim || ldy >= kMaxDim)
+    return RMM_ERR_SHAPE;
+  const size_t elt = elt_size(dtype);
+  if (!aligned(A, elt) || !aligned(B, elt) || !aligned(idx, 4) || !aligned(Y, elt_size(y_dtype)))
+    return RMM_ERR_ALIGN;
+  const MatPlan p = plan_matmul(n, d, m, lda, ldb, dtype, rho, aligned(A, 16), aligned(B, 16));
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
+    return RMM_ERR_WORKSPACE;
+  const Span sa = span3(A, 1, 0, n, lda, d, elt), sb = span3(B, 1, 0, d, ldb, m, elt);
+  const Span si = span3(idx, 1, 0, 1, p.k, p.k, 4), sy = span3(Y, 1, 0, n, ldy, m, elt_size(y_dtype));
+  if (overlap(si, sa) || overlap(si, sb) || overlap(sy, sa) || overlap(sy, sb) || overlap(sy, si))
+    return RMM_ERR_ALIAS;
+  if (p.total > 0) {
+    const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
+    if (overlap(sw, sa) || overlap(sw, sb) || overlap(sw, si) || overlap(sw, sy)) return RMM_ERR_ALIAS;
+  }
+  if (p.path == MatPath::kMfmaDirect || p.path == MatPath::kMfmaPacked) {
+    const int64_t b_bytes = ((d - 1) * ldb + m) * 2;
+    const int64_t a_bytes = p.path == MatPath::kMfmaDirect ? ((n - 1) * lda + d) * 2 : n * p.k_pad * 2;
+    if (b_bytes > kMaxOperandBytes || a_bytes > kMaxOperandBytes) return RMM_ERR_SHAPE;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool bf16 = dtype == RMM_BF16;
+  const Marks mk{stage_events, s};
+  clear_error();
+  RMM_LAUNCH(mk.mark(0));
+  switch (p.path) {
+    case MatPath::kSimt: {
+      if (p.use_sel) {
+        RMM_LAUNCH(run_select(p.sel, ws, A, bf16, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk));
+      } else {
+        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, s));
+        RMM_LAUNCH(mk.mark(1));
+      }
+      RMM_LAUNCH(mk.mark(2));
+      RMM_LAUNCH(mk.mark(3));
+      SimtArgs g{};
+      g.A = A; g.a_bf16 = bf16; g.a_bs = 0; g.a_rs = lda; g.a_cs = 1;
+      g.B = B; g.b_bf16 = bf16; g.b_bs = 0; g.b_ts = ldb; g.b_js = 1; g.b_group = 1;
+      g.idx = p.all ? nullptr : idx; g.idx_bs = 0;
+      g.C = Y; g.c_bf16 = y_dtype == RMM_BF16; g.c_bs = 0; g.ldc = ldy;
+      g.M = (int)n; g.N = (int)m; g.k = (int)p.k; g.batch = 1;
+      RMM_LAUNCH(launch_gemm_simt(g, s));
+      break;
+    }
+    case MatPath::kDecode: {
+      float* at = (float*)(ws + p.off_at);
+      uint32_t* cnt = (uint32_t*)(ws + p.off_cnt);
+      const int strips = (int)((m + 127) / 128);
+      RMM_LAUNCH(launch_decode_select(A, bf16, lda, (int)n, (int)d, (int)p.k, (int)p.k_pad, p.all, idx, nullptr, at,
+                                      d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, cnt, strips,
+                                      s));
+      RMM_LAUNCH(mk.mark(1));
+      RMM_LAUNCH(mk.mark(2));
+      RMM_LAUNCH(mk.mark(3));
+      GemvArgs g{};
+      g.a_t = at; g.B = (const uint16_t*)B; g.ldb = ldb; g.idx = idx;
+      g.k = (int)p.k; g.n = (int)n; g.m = (int)m; g.splits = p.gsplits;
+      g.rows_per_split = (int)((p.k + p.gsplits - 1) / p.gsplits);
+      g.partial = (float*)(ws + p.off_gpart); g.counters = cnt;
+      g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;
+      RMM_LAUNCH(launch_gemv(g, s));
+      break;
+    }
+    case MatPath::kMfmaDirect: {
+      RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, s));
+      RMM_LAUNCH(mk.mark(1));
+      RMM_LAUNCH(mk.mark(2));
+      RMM_LAUNCH(mk.mark(3));
+      GemmArgs g{};
+      g.A = (const uint16_t*)A; g.a_bs = 0; g.lda = lda;
+      g.B = (const uint16_t*)B; g.b_bs = 0; g.ldb = ldb; g.b_group = 1;
+      g.idx = nullptr; g.idx_bs = 0; g.k_valid = (int)d;
+      g.C = Y; g.c_bs = 0; g.ldc = ldy; g.c_bf16 = y_dtype == RMM_BF16;
+      g.M = (int)n; g.N = (int)m; g.K = (int)d; g.batch = 1; g.b_kmajor = true;
+      g.a_bytes = (uint32_t)(((n - 1) * lda + d) * 2);
+      g.b_bytes = (uint32_t)(((d - 1) * ldb + m) * 2);
+      RMM_LAUNCH(launch_gemm_bf16(g, s));
+      break;
+    }
+    case MatPath::kMfmaPacked: {
+      if (p.use_sel) {
+        RMM_LAUNCH(run_select(p.sel, ws, A, true, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk));
+      } else {
+        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, s));
+        RMM_LAUNCH(mk.mark(1));
+      }
+      RMM_LAUNCH(mk.mark(2));
+      uint16_t* pk = (uint16_t*)(ws + p.off_pack);
+      RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, idx, p.k, (int)p.k, (int)p.k_pad, 1, (int)n, pk, 0, s));
+      RMM_LAUNCH(mk.mark(3));
+      GemmArgs g{};
+      g.A = pk; g.a_bs = 0; g.lda = p.k_pad;
+      g.B = (const uint16_t*)B; g.b_bs = 0; g.ldb = ldb; g.b_group = 1;
+      g.idx = idx; g.idx_bs = 0; g.k_valid = (int)p.k;
+      g.C = Y; g.c_bs = 0; g.ldc = ldy; g.c_bf16 = y_dtype == RMM_BF16;
+      g.M = (int)n; g.N = (int)m; g.K = (int)p.k_pad; g.batch = 1; g.b_kmajor = true;
+      g.a_bytes = (uint32_t)(n * p.k_pad * 2);
+      g.b_bytes = (uint32_t)(((d - 1) * ldb + m) * 2);
+      RMM_LAUNCH(launch_gemm_bf16(g, s));
+      break;
+    }
+  }
+  RMM_LAUNCH(mk.mark(4));
+  return RMM_OK;
+}
+
+}  // namespace
+
+rmm_status_t rmm_matmul(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
+                        int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return matmul_impl(A, B, dtype, n, d, m, lda, ldb, rho, idx, Y, y_dtype, ldy, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
+                              int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy,
+                              void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (!stage_events) return RMM_ERR_NULL;
+  for (int i = 0; i < 5; ++i)
+    if (!stage_events[i]) return RMM_ERR_NULL;
+  return matmul_impl(A, B, dtype, n, d, m, lda, ldb, rho, idx, Y, y_dtype, ldy, workspace, workspace_bytes, stream,
+                     stage_events);
+}
+
+// --------------------------------- qk ---------------------------------------
+
+namespace {
+
+struct QkPlan {
+  int64_t k = 0, k_pad = 0;
+  bool all = false, mfma = false, direct = false, use_sel = false;
+  SelPlan sel;
+  size_t off_q = 0, off_k = 0, total = 0;
+};
+
+QkPlan plan_qk(int64_t hq, int64_t tq, int64_t tk, int64_t dh, int dtype, double rho, bool direct_ok) {
+  QkPlan p;
+  Carve cv;
+  p.k = k_of(rho, dh);
+  p.all = p.k == dh;
+  p.k_pad = round_up(p.k, kKTile);
+  p.mfma = dtype == RMM_BF16;
+  if (!p.all) {
+    plan_select(cv, p.sel, (int)hq, tq, dh, dtype == RMM_BF16);
+    p.use_sel = true;
+  }
+  if (p.mfma) {
+    p.direct = p.all && direct_ok;
+    if (!p.direct) {
+      p.off_q = cv.take((size_t)hq * tq * p.k_pad * 2);
+      p.off_k = cv.take((size_t)hq * tk * p.k_pad * 2);
+    }
+  }
+  p.total = cv.used;
+  return p;
+}
+
+}  // namespace
+
+size_t rmm_qk_workspace(int64_t hq, int64_t tq, int64_t tk, int64_t dh, int dtype, double rho) {
+  if (!dim_ok(hq) || !dim_ok(tq) || !dim_ok(tk) || !dim_ok(dh) || !dtype_ok(dtype) || !rho_ok(rho)) return 0;
+  return plan_qk(hq, tq, tk, dh, dtype, rho, false).total;
+}
+
+rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
+                    int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho, int32_t* idx,
+                    void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !idx || !S) return RMM_ERR_NULL;
+  if (!rho_ok(rho)) return RMM_ERR_RHO;
+  if (!dtype_ok(dtype) || !dtype_ok(s_dtype)) return RMM_ERR_DTYPE;
+  if (!dim_ok(hq) || !dim_ok(hkv) || !dim_ok(tq) || !dim_ok(tk) || !dim_ok(dh) || hq % hkv != 0) return RMM_ERR_SHAPE;
+  if (q_ts < dh || k_ts < dh || q_hs < 0 || k_hs < 0 || (hq > 1 && q_hs < 1) || (hkv > 1 && k_hs < 1))
+    return RMM_ERR_SHAPE;
+  if (hq * tq >= kMaxDim || (double)hq * tq * tk >= 9.0e18) return RMM_ERR_SHAPE;
+  const size_t elt = elt_size(dtype);
+  if (!aligned(Q, elt) || !aligned(K, elt) || !aligned(idx, 4) || !aligned(S, elt_size(s_dtype)))
+    return RMM_ERR_ALIGN;
+  const bool direct_ok = dtype == RMM_BF16 && aligned(Q, 16) && aligned(K, 16) && q_ts % 8 == 0 &&
+                         k_ts % 8 == 0 && q_hs % 8 == 0 && k_hs % 8 == 0 && dh % 8 == 0 &&
+                         ((tq - 1) * q_ts + dh) * 2 <= kMaxOperandBytes && ((tk - 1) * k_ts + dh) * 2 <= kMaxOperandBytes;
+  const QkPlan p = plan_qk(hq, tq, tk, dh, dtype, rho, direct_ok);
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
+    return RMM_ERR_WORKSPACE;
+  if (p.mfma && !p.direct && (tq * p.k_pad * 2 > kMaxOperandBytes || tk * p.k_pad * 2 > kMaxOperandBytes))
+    return RMM_ERR_SHAPE;
+  const Span sq = span3(Q, hq, q_hs, tq, q_ts, dh, elt), sk = span3(K, hkv, k_hs, tk, k_ts, dh, elt);
+  const Span si = span3(idx, 1, 0, hq, p.k, p.k, 4);
+  const Span ss = span3(S, hq, tq * tk, tq, tk, tk, elt_size(s_dtype));
+  if (overlap(si, sq) || overlap(si, sk) || overlap(ss, sq) || overlap(ss, sk) || overlap(ss, si))
+    return RMM_ERR_ALIAS;
+  if (p.total > 0) {
+    const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
+    if (overlap(sw, sq) || overlap(sw, sk) || overlap(sw, si) || overlap(sw, ss)) return RMM_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool bf16 = dtype == RMM_BF16;
+  const int group = (int)(hq / hkv);
+  clear_error();
+  if (p.use_sel) {
+    RMM_LAUNCH(run_select(p.sel, ws, Q, bf16, q_hs, q_ts, (int)hq, tq, dh, p.k, idx, p.k, nullptr, s));
+  } else {
+    RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, s));
+  }
+  if (!p.mfma) {
+    SimtArgs g{};
+    g.A = Q; g.a_bf16 = false; g.a_bs = q_hs; g.a_rs = q_ts; g.a_cs = 1;
+    g.B = K; g.b_bf16 = false; g.b_bs = k_hs; g.b_ts = 1; g.b_js = k_ts; g.b_group = group;
+    g.idx = p.all ? nullptr : idx; g.idx_bs = p.k;
+    g.C = S; g.c_bf16 = s_dtype == RMM_BF16; g.c_bs = tq * tk; g.ldc = tk;
+    g.M = (int)tq; g.N = (int)tk; g.k = (int)p.k; g.batch = (int)hq;
+    RMM_LAUNCH(launch_gemm_simt(g, s));
+    return RMM_OK;
+  }
+  GemmArgs g{};
+  if (p.direct) {
+    g.A = (const uint16_t*)Q; g.a_bs = q_hs; g.lda = q_ts;
+    g.B = (const uint16_t*)K; g.b_bs = k_hs; g.ldb = k_ts; g.b_group = group;
+    g.K = (int)dh;
+    g.a_bytes = (uint32_t)(((tq - 1) * q_ts + dh) * 2);
+    g.b_bytes = (uint32_t)(((tk - 1) * k_ts + dh) * 2);
+  } else {
+    uint16_t* qp = (uint16_t*)(ws + p.off_q);
+    uint16_t* kp = (uint16_t*)(ws + p.off_k);
+    RMM_LAUNCH(launch_pack(Q, true, q_hs, q_ts, 1, idx, p.k, (int)p.k, (int)p.k_pad, (int)hq, (int)tq, qp,
+                           tq * p.k_pad, s));
+    RMM_LAUNCH(launch_pack(K, true, k_hs, k_ts, group, idx, p.k, (int)p.k, (int)p.k_pad, (int)hq, (int)tk, kp,
+                           tk * p.k_pad, s));
+    g.A = qp; g.a_bs = tq * p.k_pad; g.lda = p.k_pad;
+    g.B = kp; g.b_bs = tk * p.k_pad; g.ldb = p.k_pad; g.b_group = 1;
+    g.K = (int)p.k_pad;
+    g.a_bytes = (uint32_t)(tq * p.k_pad * 2);
+    g.b_bytes = (uint32_t)(tk * p.k_pad * 2);
+  }
+  g.idx = nullptr; g.idx_bs = 0; g.k_valid = g.K;
+  g.C = S; g.c_bs = tq * tk; g.ldc = tk; g.c_bf16 = s_dtype == RMM_BF16;
+  g.M = (int)tq; g.N = (int)tk; g.batch = (int)hq; g.b_kmajor = false;
+  RMM_LAUNCH(launch_gemm_bf16(g, s));
+  return RMM_OK;
+}
+
+// --------------------------------- pv ---------------------------------------
+
+namespace {
+
+struct PvPlan {
+  int64_t k = 0, k_pad = 0;
+  bool all = false, mfma = false, direct = false, use_sel = false;
+  SelPlan sel;
+  size_t off_p = 0, total = 0;
+};
+
+PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho, bool v_ok,
+               bool direct_ok) {
+  PvPlan p;
+  Carve cv;
+  p.k = k_of(rho, tk);
+  p.all = p.k == tk;
+  p.k_pad = round_up(p.k, kKTile);
+  p.mfma = v_dtype == RMM_BF16 && v_ok;
+  if (!p.all) {
+    plan_select(cv, p.sel, (int)h, tq, tk, p_dtype == RMM_BF16);
+    p.use_sel = true;
+  }
+  if (p.mfma) {
+    p.direct = p.all && direct_ok;
+    if (!p.direct) p.off_p = cv.take((size_t)h * tq * p.k_pad * 2);
+  }
+  p.total = cv.used;
+  return p;
+}
+
+}  // namespace
+
+size_t rmm_pv_workspace(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho) {
+  if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(tk) || !dim_ok(dv) || !dtype_ok(p_dtype) || !dtype_ok(v_dtype) ||
+      !rho_ok(rho))
+    return 0;
+  return plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, true, false).total;
+}
+
+rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
+                    int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
+                    int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!P || !V || !idx || !O) return RMM_ERR_NULL;
+  if (!rho_ok(rho)) return RMM_ERR_RHO;
+  if (!dtype_ok(p_dtype) || !dtype_ok(v_dtype) || !dtype_ok(o_dtype)) return RMM_ERR_DTYPE;
+  if (!dim_ok(h) || !dim_ok(hkv) || !dim_ok(tq) || !dim_ok(tk) || !dim_ok(dv) || h % hkv != 0) return RMM_ERR_SHAPE;
+  if (p_ts < tk || v_ts < dv || p_hs < 0 || v_hs < 0 || (h > 1 && p_hs < 1) || (hkv > 1 && v_hs < 1))
+    return RMM_ERR_SHAPE;
+  if (h * tq >= kMaxDim) return RMM_ERR_SHAPE;
+  const size_t pe = elt_size(p_dtype), ve = elt_size(v_dtype);
+  if (!aligned(P, pe) || !aligned(V, ve) || !aligned(idx, 4) || !aligned(O, elt_size(o_dtype))) return RMM_ERR_ALIGN;
+  const bool v_ok = v_dtype == RMM_BF16 && aligned(V, 16) && v_ts % 8 == 0 && v_hs % 8 == 0 && dv % 8 == 0 &&
+                    ((tk - 1) * v_ts + dv) * 2 <= kMaxOperandBytes;
+  const bool p_f32 = p_dtype == RMM_FP32;
+  const bool direct_ok = aligned(P, 16) && tk % 8 == 0 && p_hs % (p_f32 ? 4 : 8) == 0 && p_ts % (p_f32 ? 4 : 8) == 0 &&
+                         ((tq - 1) * p_ts + tk) * (int64_t)pe <= kMaxOperandBytes;
+  const PvPlan p = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, v_ok, direct_ok);
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
+    return RMM_ERR_WORKSPACE;
+  if (p.mfma && !p.direct && tq * p.k_pad * 2 > kMaxOperandBytes) return RMM_ERR_SHAPE;
+  const Span sp = span3(P, h, p_hs, tq, p_ts, tk, pe), sv = span3(V, hkv, v_hs, tk, v_ts, dv, ve);
+  const Span si = span3(idx, 1, 0, h, p.k, p.k, 4);
+  const Span so = span3(O, h, tq * dv, tq, dv, dv, elt_size(o_dtype));
+  if (overlap(si, sp) || overlap(si, sv) || overlap(so, sp) || overlap(so, sv) || overlap(so, si))
+    return RMM_ERR_ALIAS;
+  if (p.total > 0) {
+    const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
+    if (overlap(sw, sp) || overlap(sw, sv) || overlap(sw, si) || overlap(sw, so)) return RMM_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int group = (int)(h / hkv);
+  clear_error();
+  if (p.use_sel) {
+    RMM_LAUNCH(run_select(p.sel, ws, P, !p_f32, p_hs, p_ts, (int)h, tq, tk, p.k, idx, p.k, nullptr, s));
+  } else {
+    RMM_LAUNCH(launch_iota(idx, p.k, (int)h, (int)tk, s));
+  }
+  if (!p.mfma) {
+    SimtArgs g{};
+    g.A = P; g.a_bf16 = !p_f32; g.a_bs = p_hs; g.a_rs = p_ts; g.a_cs = 1;
+    g.B = V; g.b_bf16 = v_dtype == RMM_BF16; g.b_bs = v_hs; g.b_ts = v_ts; g.b_js = 1; g.b_group = group;
+    g.idx = p.all ? nullptr : idx; g.idx_bs = p.k;
+    g.C = O; g.c_bf16 = o_dtype == RMM_BF16; g.c_bs = tq * dv; g.ldc = dv;
+    g.M = (int)tq; g.N = (int)dv; g.k = (int)p.k; g.batch = (int)h;
+    RMM_LAUNCH(launch_gemm_simt(g, s));
+    return RMM_OK;
+  }
+  GemmArgs g{};
+  g.B = (const uint16_t*)V; g.b_bs = v_hs; g.ldb = v_ts; g.b_group = group;
+  g.b_bytes = (uint32_t)(((tk - 1) * v_ts + dv) * 2);
+  g.C = O; g.c_bs = tq * dv; g.ldc = dv; g.c_bf16 = o_dtype == RMM_BF16;
+  g.M = (int)tq; g.N = (int)dv; g.batch = (int)h; g.b_kmajor = true;
+  if (p.direct) {
+    g.A = (const uint16_t*)P; g.a_bs = p_hs; g.lda = p_ts;
+    g.a_bytes = (uint32_t)(((tq - 1) * p_ts + tk) * pe);
+    g.idx = nullptr; g.idx_bs = 0; g.k_valid = (int)tk; g.K = (int)tk;
+    if (p_f32) {
+      RMM_LAUNCH(launch_gemm_bf16_af32(g, s));
+    } else {
+      RMM_LAUNCH(launch_gemm_bf16(g, s));
+    }
+    return RMM_OK;
+  }
+  uint16_t* pp = (uint16_t*)(ws + p.off_p);
+  RMM_LAUNCH(launch_pack(P, !p_f32, p_hs, p_ts, 1, idx, p.k, (int)p.k, (int)p.k_pad, (int)h, (int)tq, pp,
+                         tq * p.k_pad, s));
+  g.A = pp; g.a_bs = tq * p.k_pad; g.lda = p.k_pad;
+  g.a_bytes = (uint32_t)(tq * p.k_pad * 2);
+  g.idx = idx; g.idx_bs = p.k; g.k_valid = (int)p.k; g.K = (int)p.k_pad;
+  RMM_LAUNCH(launch_gemm_bf16(g, s));
+  return RMM_OK;
+}
+
+}  // extern "C"

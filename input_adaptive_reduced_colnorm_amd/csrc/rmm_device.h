@@ -1,0 +1,51 @@
+// Device-side helpers shared by the RMM kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmm {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+
+// Fourth descriptor word of a raw buffer resource on gfx9-family parts
+// (32-bit data format, no swizzle): loads past num_records return zero.
+constexpr int kBufferFlags = 0x00020000;
+// Byte offset that is always past num_records (num_records < 2^31 is enforced
+// by the host), so a load through it yields zeros.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (inputs are finite on every path that
+// uses this; NaN is kept a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+// XOR swizzle of 16-byte chunks inside a 128-byte LDS row: makes both the
+// row-wise fills and the 32-row MFMA operand reads free of bank conflicts.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return chunk ^ ((row ^ (row >> 3)) & 7);
+}
+
+}  // namespace rmm

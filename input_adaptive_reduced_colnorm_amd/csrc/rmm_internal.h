@@ -1,0 +1,86 @@
+// Host-side launchers shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rmm {
+
+// Column energy sweep: partial[h][s][j] = sum of A[h][r][j]^2 over the rows r
+// of split s.  elt_bf16 selects bf16 (else fp32) input.
+hipError_t launch_colnorm(const void* A, bool elt_bf16, int64_t head_stride, int64_t lda,
+                          int heads, int n, int d, int splits, float* partial, hipStream_t s);
+
+// Picks the number of row splits for the sweep (deterministic in the shape).
+int colnorm_splits(int heads, int n, int d, bool elt_bf16);
+
+// TopK over the summed partials of each head: writes idx[h][0..k) ascending,
+// optional scores[h][j] = sqrt(energy).  gkeys: [heads][d] uint32 scratch,
+// used only when d exceeds the LDS key capacity (may be null otherwise).
+hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k,
+                       int32_t* idx, int64_t idx_hs, float* scores, int64_t scores_hs,
+                       uint32_t* gkeys, hipStream_t s);
+int topk_lds_capacity();
+
+// Writes idx[h][t] = t for t < d (the rho = 1 selection).
+hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, hipStream_t s);
+
+// Gather-pack: out[b][r][t] = t < k ? bf16(src[b / src_group][r][idx[b][t]]) : 0
+// for t < k_pad, rows r < rows.  src_bf16 selects bf16 (else fp32) input.
+hipError_t launch_pack(const void* src, bool src_bf16, int64_t src_hs, int64_t src_rs, int src_group,
+                       const int32_t* idx, int64_t idx_hs, int k, int k_pad,
+                       int batch, int rows, uint16_t* out, int64_t out_hs, hipStream_t s);
+
+// bf16 MFMA GEMM with fp32 accumulation.
+struct GemmArgs {
+  const uint16_t* A;    // [M][K] row-major, K contiguous (bf16 bits)
+  int64_t a_bs, lda;
+  const uint16_t* B;    // b_kmajor: [K][N] rows gathered by idx; else [N][K] K contiguous
+  int64_t b_bs, ldb;
+  int b_group;          // batch b reads B head b / b_group
+  const int32_t* idx;   // row gather for b_kmajor (null: row t is row t)
+  int64_t idx_bs;
+  int k_valid;          // rows t >= k_valid of B read as zero
+  void* C;              // [M][N] fp32 or bf16
+  int64_t c_bs, ldc;
+  bool c_bf16;
+  int M, N, K, batch;
+  bool b_kmajor;
+  uint32_t a_bytes, b_bytes;  // per-batch extents (bytes) for the buffer descriptors
+};
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+// Same product with A given as fp32 (rounded to bf16 while staged), no gather.
+hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s);
+
+// Generic FMA GEMM over strided, optionally gathered operands (fp32 or bf16
+// inputs, any alignment):
+//   C[b][i][j] = sum_{t<k} A(b,i,col(t)) * B(b/group, row(t), j)
+struct SimtArgs {
+  const void* A; bool a_bf16; int64_t a_bs, a_rs, a_cs;
+  const void* B; bool b_bf16; int64_t b_bs, b_ts, b_js; int b_group;
+  const int32_t* idx; int64_t idx_bs;   // null: identity
+  void* C; bool c_bf16; int64_t c_bs, ldc;
+  int M, N, k, batch;
+};
+hipError_t launch_gemm_simt(const SimtArgs& g, hipStream_t s);
+
+// Decode path (n <= 16): fused energy + TopK + transposed gather of A into
+// a_t[t][16] (fp32, zero padded), and zeroing of the GEMV tile counters.
+hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int k_pad,
+                                bool all, int32_t* idx, float* scores, float* a_t, uint32_t* gkeys,
+                                uint32_t* counters, int n_counters, hipStream_t s);
+
+// Split-K GEMV over the kept rows of B, deterministic ordered reduction.
+struct GemvArgs {
+  const float* a_t;     // [k_pad][16]
+  const uint16_t* B; int64_t ldb;
+  const int32_t* idx;   // kept rows (ascending)
+  int k, n, m, splits, rows_per_split;
+  float* partial;       // [splits][16][m]
+  uint32_t* counters;   // [m / 128 rounded up], zero on entry
+  void* Y; bool y_bf16; int64_t ldy;
+};
+hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);
+int gemv_splits(int k, int n, int m);
+
+}  // namespace rmm

@@ -115,17 +115,20 @@ def select(A, rho: float):
     return idx.astype(np.int64), q
 
 
-def matmul(A, B, rho: float):
+def matmul(A, B, rho: float, rows=None):
     """RMM_rho(A, B) = A[:, I] @ B[I, :] with I = select(A, rho).
 
-    A: n x d, B: d x m.  Returns (idx, Y) with Y float64 n x m.
+    A: n x d, B: d x m.  Returns (idx, Y) with Y float64 n x m.  With
+    `rows`, Y holds only those rows of the product; the selection still
+    uses every row of A.
     """
     A64 = np.asarray(A, dtype=np.float64)
     B64 = np.asarray(B, dtype=np.float64)
     if A64.ndim != 2 or B64.ndim != 2 or A64.shape[1] != B64.shape[0]:
         raise ValueError("need A (n x d) and B (d x m)")
     idx, _ = select(A64, rho)
-    Y = A64[:, idx] @ B64[idx, :]
+    Ar = A64 if rows is None else A64[np.asarray(rows)]
+    Y = Ar[:, idx] @ B64[idx, :]
     return idx, Y
 
 
@@ -147,54 +150,62 @@ def kv_head(h: int, hq: int, hkv: int) -> int:
     return h // (hq // hkv)
 
 
-def qk(Q, K, rho: float):
+def qk(Q, K, rho: float, heads=None):
     """Per-head reduced attention scores.
 
     Q: (hq, tq, dh), K: (hkv, tk, dh).  For each query head h, I_h is chosen
     from the column norms of Q[h] (over its tq rows) and
     S[h] = Q[h][:, I_h] @ K[g(h)][:, I_h]^T.  Raw product: no 1/sqrt(dh)
     scale and no mask (the pages give neither for the reduced product).
-    Returns (idx (hq, k) int64, S (hq, tq, tk) float64).
+    Returns (idx (hq, k) int64, S (hq, tq, tk) float64).  With `heads`,
+    idx and S cover only those query heads, in the order given.
     """
-    Q64 = np.asarray(Q, dtype=np.float64)
-    K64 = np.asarray(K, dtype=np.float64)
-    hq, tq, dh = Q64.shape
-    hkv, tk, dh2 = K64.shape
+    Q = np.asarray(Q)
+    K = np.asarray(K)
+    hq, tq, dh = Q.shape
+    hkv, tk, dh2 = K.shape
     if dh2 != dh:
         raise ValueError("Q and K head dims differ")
+    hs = list(range(hq)) if heads is None else [int(h) for h in heads]
     k = k_rule(rho, dh)
-    idx = np.empty((hq, k), dtype=np.int64)
-    S = np.empty((hq, tq, tk), dtype=np.float64)
-    for h in range(hq):
+    idx = np.empty((len(hs), k), dtype=np.int64)
+    S = np.empty((len(hs), tq, tk), dtype=np.float64)
+    for i, h in enumerate(hs):
         g = kv_head(h, hq, hkv)
-        I, _ = select(Q64[h], rho)
-        idx[h] = I
-        S[h] = Q64[h][:, I] @ K64[g][:, I].T
+        Qh = np.asarray(Q[h], dtype=np.float64)
+        Kg = np.asarray(K[g], dtype=np.float64)
+        I, _ = select(Qh, rho)
+        idx[i] = I
+        S[i] = Qh[:, I] @ Kg[:, I].T
     return idx, S
 
 
-def pv(P, V, rho: float):
+def pv(P, V, rho: float, heads=None):
     """Per-head reduced attention output over the key (token) axis.
 
     P: (h, tq, tk) attention weights, V: (hkv, tk, dv).  For each head h,
     I_h is chosen from the column norms of P[h] over its tq query rows and
     O[h] = P[h][:, I_h] @ V[g(h)][I_h, :].
-    Returns (idx (h, k) int64, O (h, tq, dv) float64).
+    Returns (idx (h, k) int64, O (h, tq, dv) float64).  With `heads`, idx
+    and O cover only those heads, in the order given.
     """
-    P64 = np.asarray(P, dtype=np.float64)
-    V64 = np.asarray(V, dtype=np.float64)
-    h_, tq, tk = P64.shape
-    hkv, tk2, dv = V64.shape
+    P = np.asarray(P)
+    V = np.asarray(V)
+    h_, tq, tk = P.shape
+    hkv, tk2, dv = V.shape
     if tk2 != tk:
         raise ValueError("P key axis and V rows differ")
+    hs = list(range(h_)) if heads is None else [int(h) for h in heads]
     k = k_rule(rho, tk)
-    idx = np.empty((h_, k), dtype=np.int64)
-    O = np.empty((h_, tq, dv), dtype=np.float64)
-    for h in range(h_):
+    idx = np.empty((len(hs), k), dtype=np.int64)
+    O = np.empty((len(hs), tq, dv), dtype=np.float64)
+    for i, h in enumerate(hs):
         g = kv_head(h, h_, hkv)
-        I, _ = select(P64[h], rho)
-        idx[h] = I
-        O[h] = P64[h][:, I] @ V64[g][I, :]
+        Ph = np.asarray(P[h], dtype=np.float64)
+        Vg = np.asarray(V[g], dtype=np.float64)
+        I, _ = select(Ph, rho)
+        idx[i] = I
+        O[i] = Ph[:, I] @ Vg[I, :]
     return idx, O
 
 

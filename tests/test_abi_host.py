@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/rmm.h declares, and
+reject bad arguments before it touches the HIP runtime.  Only argument
+errors are exercised here: a call that passes validation would launch work.
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from input_adaptive_reduced_colnorm_amd import rmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmm.h")
+
+OK, NULL, RHO, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS = range(9)
+FP32, BF16 = 0, 1
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rmm_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return rmm.lib()
+
+
+def test_library_exports_every_declared_function(L):
+    names = header_functions()
+    assert {"rmm_k", "rmm_select", "rmm_matmul", "rmm_qk", "rmm_pv"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", rmm._LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(rmm_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    for n in names:
+        assert n in rmm.SIGNATURES, f"binding lacks {n}"
+        getattr(L, n)
+
+
+def test_k_rule_through_the_abi(L):
+    import json
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "k_rule.json")))["cases"]
+    for c in cases:
+        assert L.rmm_k(c["rho"], c["d"]) == c["k"], c
+    for bad in (0.0, -0.5, 1.0000001, math.nan, math.inf):
+        assert L.rmm_k(bad, 10) == -1
+    assert L.rmm_k(0.5, 0) == -1
+
+
+def test_status_strings(L):
+    for s in range(9):
+        assert L.rmm_status_str(s).decode().startswith("RMM_")
+    assert L.rmm_status_str(99) == b"unknown rmm status"
+
+
+def _matmul(L, A=FAKE, B=FAKE + (1 << 30), dt=BF16, n=64, d=128, m=64, lda=128, ldb=64, rho=0.5,
+            idx=FAKE + (2 << 30), Y=FAKE + (3 << 30), ydt=FP32, ldy=64, ws=FAKE + (4 << 30), wsb=1 << 30):
+    return L.rmm_matmul(A, B, dt, n, d, m, lda, ldb, rho, idx, Y, ydt, ldy, ws, wsb, None)
+
+
+def test_matmul_rejects_bad_arguments(L):
+    assert _matmul(L, A=None) == NULL
+    assert _matmul(L, B=None) == NULL
+    assert _matmul(L, idx=None) == NULL
+    assert _matmul(L, Y=None) == NULL
+    for r in (0.0, -0.1, 1.5, math.nan, math.inf):
+        assert _matmul(L, rho=r) == RHO
+    assert _matmul(L, dt=7) == DTYPE
+    assert _matmul(L, ydt=-1) == DTYPE
+    assert _matmul(L, n=0) == SHAPE          # empty input
+    assert _matmul(L, d=0) == SHAPE
+    assert _matmul(L, m=-3) == SHAPE
+    assert _matmul(L, lda=100) == SHAPE      # lda < d
+    assert _matmul(L, ldb=8) == SHAPE
+    assert _matmul(L, ldy=8) == SHAPE
+    assert _matmul(L, A=FAKE + 1) == ALIGN   # bf16 needs 2-byte alignment
+    assert _matmul(L, ws=None) == WS
+    assert _matmul(L, wsb=16) == WS
+    assert _matmul(L, ws=FAKE + (4 << 30) + 8) == WS   # not 256-byte aligned
+    assert _matmul(L, Y=FAKE) == ALIAS       # output on top of A
+    assert _matmul(L, idx=FAKE + (1 << 30)) == ALIAS   # index output on top of B
+    assert _matmul(L, ws=FAKE + (3 << 30)) == ALIAS    # workspace overlaps Y
+
+
+def test_matmul_dense_needs_no_workspace(L):
+    assert L.rmm_matmul_workspace(64, 128, 64, 128, BF16, 1.0) == 0
+    assert L.rmm_matmul_workspace(64, 128, 64, 128, BF16, 0.5) > 0
+    assert L.rmm_matmul_workspace(0, 128, 64, 128, BF16, 0.5) == 0   # invalid shape
+
+
+def test_qk_rejects_bad_arguments(L):
+    base = dict(Q=FAKE, K=FAKE + (1 << 30), dt=BF16, hq=4, hkv=2, tq=16, tk=16, dh=64, qhs=1024, qts=64,
+                khs=1024, kts=64, rho=0.5, idx=FAKE + (2 << 30), S=FAKE + (3 << 30), sdt=FP32,
+                ws=FAKE + (4 << 30), wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.rmm_qk(a["Q"], a["K"], a["dt"], a["hq"], a["hkv"], a["tq"], a["tk"], a["dh"], a["qhs"], a["qts"],
+                        a["khs"], a["kts"], a["rho"], a["idx"], a["S"], a["sdt"], a["ws"], a["wsb"], None)
+
+    assert call(Q=None) == NULL
+    assert call(rho=0.0) == RHO
+    assert call(hkv=3) == SHAPE              # hq % hkv != 0
+    assert call(tq=0) == SHAPE
+    assert call(qts=32) == SHAPE             # row stride shorter than the head dim
+    assert call(dt=5) == DTYPE
+    assert call(wsb=0) == WS
+    assert call(S=FAKE + (1 << 30)) == ALIAS
+
+
+def test_pv_rejects_bad_arguments(L):
+    base = dict(P=FAKE, pdt=FP32, V=FAKE + (1 << 30), vdt=BF16, h=4, hkv=2, tq=8, tk=64, dv=16, phs=512, pts=64,
+                vhs=1024, vts=16, rho=0.5, idx=FAKE + (2 << 30), O=FAKE + (3 << 30), odt=FP32,
+                ws=FAKE + (4 << 30), wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.rmm_pv(a["P"], a["pdt"], a["V"], a["vdt"], a["h"], a["hkv"], a["tq"], a["tk"], a["dv"], a["phs"],
+                        a["pts"], a["vhs"], a["vts"], a["rho"], a["idx"], a["O"], a["odt"], a["ws"], a["wsb"], None)
+
+    assert call(V=None) == NULL
+    assert call(rho=2.0) == RHO
+    assert call(h=6, hkv=4) == SHAPE
+    assert call(pts=32) == SHAPE             # P row shorter than tk
+    assert call(vdt=3) == DTYPE
+    assert call(P=FAKE + 2) == ALIGN         # fp32 needs 4-byte alignment
+    assert call(ws=None) == WS
+    assert call(O=FAKE) == ALIAS
+
+
+def test_select_rejects_bad_arguments(L):
+    def call(A=FAKE, dt=FP32, n=8, d=32, lda=32, rho=0.5, idx=FAKE + (1 << 30), sc=None, ws=FAKE + (2 << 30),
+             wsb=1 << 30):
+        return L.rmm_select(A, dt, n, d, lda, rho, idx, sc, ws, wsb, None)
+
+    assert call(A=None) == NULL
+    assert call(rho=math.nan) == RHO
+    assert call(lda=16) == SHAPE
+    assert call(dt=2) == DTYPE
+    assert call(wsb=4) == WS
+    assert call(idx=FAKE) == ALIAS
+    assert call(sc=FAKE + 4) == ALIAS

@@ -1,0 +1,285 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Index sets must be bit-identical to the oracle's.  Products must match within
+relative Frobenius error 5e-3 for bf16 inputs and 1e-5 for fp32 inputs.
+Small cases span several tiles with ragged tails and are compared in full;
+the full-size workloads are compared on every index and on sampled rows or
+heads of the product (the selection always uses all rows).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from input_adaptive_reduced_colnorm_amd import rmm
+from oracle import rmm_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 5e-3
+TOL_FP32 = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    rmm.lib()
+    return torch.device("cuda:0")
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    """Exact float32 copy of stored bf16 / fp32 values (numpy has no bf16)."""
+    return t.detach().to("cpu").float().numpy()
+
+
+def rel_fro(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def run_matmul(A, B, rho, dev, out_dtype=torch.float32):
+    idx, Y = rmm.matmul(A.to(dev), B.to(dev), rho, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), Y
+
+
+def check_matmul(A, B, rho, dev, tol, out_dtype=torch.float32, rows=None):
+    idx, Y = run_matmul(A, B, rho, dev, out_dtype)
+    idx_o, Y_o = O.matmul(f32(A), f32(B), rho, rows=rows)
+    assert idx.dtype == np.int32
+    np.testing.assert_array_equal(idx, idx_o)
+    Yg = f32(Y) if rows is None else f32(Y[torch.as_tensor(rows, device=Y.device)])
+    err = rel_fro(Yg, Y_o)
+    assert err <= tol, f"rel Frobenius error {err:.3e} > {tol}"
+    return err
+
+
+# ------------------------------- linear ------------------------------------
+
+def test_tiny_projection_fp32(dev):
+    w = synth.tiny_projection()
+    check_matmul(w.tensors["A"], w.tensors["B"], 0.5, dev, TOL_FP32)
+    check_matmul(w.tensors["A"], w.tensors["B"], 1.0, dev, TOL_FP32)
+
+
+@pytest.mark.parametrize("rho", [0.9, 0.7, 0.5, 1.0])
+def test_linear_bf16_ragged(dev, rho):
+    # 300 x 1000 x 264: several 256-tiles in M, a ragged K tail, N tail
+    w = synth.mlp_down(n=300, d=1000, m=264, rhos=(0.9, 0.7, 0.5))
+    check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16)
+
+
+@pytest.mark.parametrize("rho", [0.7, 1.0])
+def test_linear_bf16_output(dev, rho):
+    w = synth.mlp_down(n=300, d=1000, m=264, rhos=(0.7,))
+    check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16, out_dtype=torch.bfloat16)
+
+
+def test_linear_odd_shapes(dev):
+    # odd m rules out the 16-byte loaders: vector-ALU path on bf16 inputs
+    w = synth.mlp_down(n=37, d=101, m=53, rhos=(0.6,))
+    check_matmul(w.tensors["A"], w.tensors["B"], 0.6, dev, TOL_BF16)
+    w = synth.mlp_down(n=33, d=77, m=40, rhos=(0.6,))
+    check_matmul(w.tensors["A"], w.tensors["B"], 0.6, dev, TOL_BF16)
+    check_matmul(w.tensors["A"], w.tensors["B"], 1.0, dev, TOL_BF16)
+
+
+@pytest.mark.parametrize("rho", [0.7, 1.0])
+def test_linear_leading_dims(dev, rho):
+    w = synth.mlp_down(n=96, d=320, m=136, rhos=(0.7,))
+    A, B = w.tensors["A"], w.tensors["B"]
+    Aw = torch.zeros((96, 344), dtype=A.dtype)
+    Aw[:, :320] = A
+    Bw = torch.zeros((320, 160), dtype=B.dtype)
+    Bw[:, :136] = B
+    Ad, Bd = Aw.to(dev)[:, :320], Bw.to(dev)[:, :136]
+    idx, Y = rmm.matmul(Ad, Bd, rho)
+    torch.cuda.synchronize()
+    idx_o, Y_o = O.matmul(f32(A), f32(B), rho)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    assert rel_fro(f32(Y), Y_o) <= TOL_BF16
+
+
+def test_linear_unaligned_lda_dense(dev):
+    # lda not a multiple of 8: rho = 1 goes through the gather-pack panel
+    w = synth.mlp_down(n=64, d=200, m=72, rhos=(0.5,))
+    A, B = w.tensors["A"], w.tensors["B"]
+    Aw = torch.zeros((64, 203), dtype=A.dtype)
+    Aw[:, :200] = A
+    idx, Y = rmm.matmul(Aw.to(dev)[:, :200], B.to(dev), 1.0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), np.arange(200))
+    assert rel_fro(f32(Y), O.dense(f32(A), f32(B))) <= TOL_BF16
+
+
+def test_edge_cases(dev):
+    w = synth.mlp_down(n=40, d=100, m=48, rhos=(0.5,))
+    A, B = w.tensors["A"], w.tensors["B"]
+    check_matmul(A, B, 1e-6, dev, TOL_BF16)      # k = 1
+    check_matmul(A, B, 0.999, dev, TOL_BF16)     # k = d with rho < 1
+    check_matmul(A, B, 0.07, dev, TOL_BF16)      # k = 7 exactly (decimal reading)
+    A1 = torch.randn(50, 1).to(torch.bfloat16)   # d = 1
+    B1 = torch.randn(1, 16).to(torch.bfloat16)
+    check_matmul(A1, B1, 0.5, dev, TOL_BF16)
+
+
+def test_exact_ties_lowest_index(dev):
+    # integer-valued columns with planted equal energies: lowest index wins
+    r = np.random.default_rng(21)
+    base = r.integers(-3, 4, size=(64, 16)).astype(np.float32)
+    A = np.concatenate([base, base[:, ::-1], -base, np.zeros((64, 16), np.float32)], axis=1)
+    B = r.standard_normal((64, 32)).astype(np.float32)
+    for dt in (torch.float32, torch.bfloat16):
+        At, Bt = torch.from_numpy(A).to(dt), torch.from_numpy(B).to(dt)
+        for rho in (0.25, 0.3, 0.5, 0.8, 0.9):
+            idx, _ = run_matmul(At, Bt, rho, dev)
+            idx_o, _ = O.matmul(A, B, rho)
+            np.testing.assert_array_equal(idx, idx_o)
+
+
+@pytest.mark.parametrize("n", [1, 5, 8, 16])
+def test_decode_rows(dev, n):
+    w = synth.decode_qkv(n=n, d=1024, m=776, rho=0.8)
+    check_matmul(w.tensors["A"], w.tensors["B"], 0.8, dev, TOL_BF16)
+    check_matmul(w.tensors["A"], w.tensors["B"], 1.0, dev, TOL_BF16)
+
+
+def test_select_scores(dev):
+    w = synth.mlp_down(n=200, d=700, m=8, rhos=(0.4,))
+    A = w.tensors["A"]
+    idx, s = rmm.select(A.to(dev), 0.4, scores=True)
+    torch.cuda.synchronize()
+    idx_o, q = O.select(f32(A), 0.4)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(s.cpu().numpy(), np.sqrt(q), rtol=1e-5)
+
+
+def test_determinism(dev):
+    w = synth.mlp_down(n=512, d=2048, m=512, rhos=(0.7,))
+    A, B = w.tensors["A"].to(dev), w.tensors["B"].to(dev)
+    i1, y1 = rmm.matmul(A, B, 0.7)
+    i2, y2 = rmm.matmul(A, B, 0.7)
+    w2 = synth.decode_qkv(n=8, d=2048, m=512, rho=0.8)
+    A2, B2 = w2.tensors["A"].to(dev), w2.tensors["B"].to(dev)
+    i3, y3 = rmm.matmul(A2, B2, 0.8)
+    i4, y4 = rmm.matmul(A2, B2, 0.8)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    assert torch.equal(i3, i4) and torch.equal(y3.view(torch.int32), y4.view(torch.int32))
+
+
+# -------------------------------- QK^T --------------------------------------
+
+def check_qk(Q, K, rho, dev, tol, out_dtype=torch.float32):
+    idx, S = rmm.qk(Q.to(dev), K.to(dev), rho, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    idx_o, S_o = O.qk(f32(Q), f32(K), rho)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    err = rel_fro(f32(S), S_o)
+    assert err <= tol, f"rel Frobenius error {err:.3e}"
+
+
+@pytest.mark.parametrize("rho", [0.5, 1.0])
+def test_qk_small(dev, rho):
+    w = synth.gqa_qk(hq=4, hkv=2, t=300, dh=128)
+    check_qk(w.tensors["Q"], w.tensors["K"], rho, dev, TOL_BF16)
+
+
+def test_qk_fp32_and_odd(dev):
+    w = synth.gqa_qk(hq=4, hkv=1, t=70, dh=64)
+    Q, K = w.tensors["Q"].float(), w.tensors["K"].float()
+    check_qk(Q, K, 0.5, dev, TOL_FP32)
+    w = synth.gqa_qk(hq=6, hkv=3, t=45, dh=40)  # dh not a multiple of 64
+    check_qk(w.tensors["Q"], w.tensors["K"], 0.5, dev, TOL_BF16)
+    check_qk(w.tensors["Q"], w.tensors["K"], 0.5, dev, TOL_BF16, out_dtype=torch.bfloat16)
+
+
+# --------------------------------- PV ---------------------------------------
+
+def check_pv(P, V, rho, dev, tol, heads=None):
+    idx, Og = rmm.pv(P.to(dev), V.to(dev), rho)
+    torch.cuda.synchronize()
+    hs = list(range(P.shape[0])) if heads is None else list(heads)
+    idx_o, O_o = O.pv(f32(P), f32(V), rho, heads=hs)
+    gi = idx.cpu().numpy()
+    np.testing.assert_array_equal(gi[hs], idx_o)
+    err = rel_fro(f32(Og[torch.as_tensor(hs, device=Og.device)]), O_o)
+    assert err <= tol, f"rel Frobenius error {err:.3e}"
+    return gi
+
+
+@pytest.mark.parametrize("rho", [0.5, 1.0])
+def test_pv_small(dev, rho):
+    w = synth.attn_pv(h=4, hkv=2, tq=100, tk=1000, dv=128)
+    check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16)
+    check_pv(w.tensors["P"].to(torch.bfloat16), w.tensors["V"], rho, dev, TOL_BF16)
+
+
+def test_pv_fp32(dev):
+    w = synth.attn_pv(h=2, hkv=1, tq=40, tk=300, dv=24)
+    check_pv(w.tensors["P"], w.tensors["V"].float(), 0.5, dev, TOL_FP32)
+
+
+# ----------------------------- full sizes -----------------------------------
+
+def test_full_mlp_down(dev):
+    w = synth.mlp_down()
+    A, B = w.tensors["A"], w.tensors["B"]
+    rows = np.random.default_rng(0).choice(A.shape[0], size=96, replace=False)
+    rows.sort()
+    for rho in (0.9, 0.7, 0.5, 1.0):
+        print(f"mlp_down 4096x14336x4096 rho={rho}", flush=True)
+        check_matmul(A, B, rho, dev, TOL_BF16, rows=rows)
+
+
+def test_full_decode_qkv(dev):
+    w = synth.decode_qkv()
+    for rho in (0.8, 1.0):
+        check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16)
+
+
+def test_full_mlp_up(dev):
+    w = synth.mlp_up()
+    rows = np.random.default_rng(1).choice(2048, size=48, replace=False)
+    rows.sort()
+    for rho in (0.8, 1.0):
+        print(f"mlp_up 2048x8192x28672 rho={rho}", flush=True)
+        check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16, rows=rows)
+
+
+def test_full_gqa_qk(dev):
+    w = synth.gqa_qk()
+    Q, K = w.tensors["Q"], w.tensors["K"]
+    for rho in (0.5, 1.0):
+        print(f"gqa_qk 32x4096x128 rho={rho}", flush=True)
+        idx, S = rmm.qk(Q.to(dev), K.to(dev), rho)
+        torch.cuda.synchronize()
+        gi = idx.cpu().numpy()
+        for h in range(Q.shape[0]):   # every head's index set
+            ih, _ = O.select(f32(Q[h]), rho)
+            np.testing.assert_array_equal(gi[h], ih)
+        hs = [0, 5, 17, 31]
+        _, S_o = O.qk(f32(Q), f32(K), rho, heads=hs)
+        err = rel_fro(f32(S[torch.as_tensor(hs, device=S.device)]), S_o)
+        assert err <= TOL_BF16, err
+        del S
+
+
+def test_full_attn_pv(dev):
+    w = synth.attn_pv()
+    P, V = w.tensors["P"], w.tensors["V"]
+    for rho in (0.5, 1.0):
+        print(f"attn_pv 64x512x8192 rho={rho}", flush=True)
+        idx, Og = rmm.pv(P.to(dev), V.to(dev), rho)
+        torch.cuda.synchronize()
+        gi = idx.cpu().numpy()
+        Pn = f32(P)
+        for h in range(P.shape[0]):
+            ih, _ = O.select(Pn[h], rho)
+            np.testing.assert_array_equal(gi[h], ih)
+        hs = [0, 9, 40, 63]
+        _, O_o = O.pv(Pn, f32(V), rho, heads=hs)
+        err = rel_fro(f32(Og[torch.as_tensor(hs, device=Og.device)]), O_o)
+        assert err <= TOL_BF16, err
