@@ -76,10 +76,11 @@ template <int BM, int BN, bool KMAJOR, bool GATHER, bool A_F32, int NBUF>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_CH = BM * 8 / kThreads;          // 16-byte chunks of A per thread
+  constexpr int A_CH = BM * 8 / kThreads;          // 16-byte chunks of A (bf16) per thread
   constexpr int B_CH = BN * 8 / kThreads;          // (N-contiguous B) chunks per thread
-  constexpr int B_BLK_THREADS = BN;                // (K-major B) threads owning one 8x8 block
   constexpr int STAGE = (BM + BN) * 128;           // bytes per LDS stage
+  constexpr int ES = A_F32 ? 4 : 2;                // A element size
+  static_assert(BN <= kThreads, "one 8x8 B block per thread at most");
   __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
 
   const int tid = threadIdx.x;
@@ -92,69 +93,60 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
   const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
-  const char* Ab = (const char*)g.A + (size_t)b * g.a_bs * (A_F32 ? 4 : 2);
+  const char* Ab = (const char*)g.A + (size_t)b * g.a_bs * ES;
   const char* Bb = (const char*)g.B + (size_t)(b / g.b_group) * g.b_bs * 2;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, g.b_bytes);
   const int32_t* idxb = GATHER ? g.idx + (size_t)b * g.idx_bs : nullptr;
 
-  // ---- per-thread load geometry -------------------------------------------
-  uint32_t a_row_off[A_CH];
-  int a_kc[A_CH];
-  bool a_row_ok[A_CH];
+  // ---- per-thread load geometry (K is a multiple of 64 on every path) -----
+  // A chunk i of this thread: row (tid >> 3) + 32 i, 8 elements at column
+  // (tid & 7) * 8 of the K tile.  Rows past M read through an offset that is
+  // always out of range, so they load zeros without a branch.
+  const int a_kc = (tid & 7) * 8;
+  uint32_t a_off[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int c = i * kThreads + tid;
-    const int row = c >> 3;
-    a_kc[i] = (c & 7) * 8;
-    a_row_ok[i] = (m0 + row) < g.M;
-    a_row_off[i] = (uint32_t)((int64_t)(m0 + row) * g.lda * (A_F32 ? 4 : 2));
+    const int row = m0 + (tid >> 3) + 32 * i;
+    a_off[i] = row < g.M ? (uint32_t)(row * g.lda + a_kc) * ES : kOobOffset;
   }
-  uint32_t b_row_off[KMAJOR ? 1 : B_CH];
-  int b_kc[KMAJOR ? 1 : B_CH];
-  bool b_row_ok[KMAJOR ? 1 : B_CH];
+  uint32_t b_off[KMAJOR ? 1 : B_CH];
   if constexpr (!KMAJOR) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c >> 3;
-      b_kc[i] = (c & 7) * 8;
-      b_row_ok[i] = (n0 + row) < g.N;
-      b_row_off[i] = (uint32_t)((int64_t)(n0 + row) * g.ldb * 2);
+      const int row = n0 + (tid >> 3) + 32 * i;
+      b_off[i] = row < g.N ? (uint32_t)(row * g.ldb + a_kc) * 2u : kOobOffset;
     }
   }
-  const bool kb_owner = KMAJOR && tid < B_BLK_THREADS;
+  // K-major B: this thread owns the 8x8 block of rows kb_kg*8.. and columns
+  // kb_cg*8.. of each K tile.  A row index of -1 (padding past k) makes the
+  // 32-bit offset wrap far past the buffer end, so it also reads zeros.
+  const bool kb_owner = KMAJOR && tid < BN;
   const int kb_cg = tid % (BN / 8), kb_kg = tid / (BN / 8);
-  const bool kb_col_ok = (n0 + kb_cg * 8) < g.N;
+  const uint32_t kb_colmask = (n0 + kb_cg * 8) < g.N ? 0u : kOobOffset;
+  const int kb_col = n0 + kb_cg * 8;
 
   constexpr int A_REGS = A_F32 ? 2 * A_CH : A_CH;
   i32x4 ra_regs[A_REGS];
   i32x4 rb_regs[KMAJOR ? 8 : B_CH];
-  int rows_next[8];  // gathered B rows for the tile being loaded
+  i32x4 idx_lo, idx_hi;   // kept rows for the next tile to load
 
-  auto load_rows = [&](int kt, int (&rows)[8]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = kt * BK + kb_kg * 8 + e;
-      if constexpr (GATHER) {
-        rows[e] = t < g.k_valid ? idxb[t] : -1;
-      } else {
-        rows[e] = t < g.K ? t : -1;
-      }
+  auto load_idx = [&](int kt) {
+    if constexpr (GATHER) {
+      const i32x4* p = (const i32x4*)(idxb + kt * BK + kb_kg * 8);
+      idx_lo = p[0];
+      idx_hi = p[1];
     }
   };
 
-  auto load_tile = [&](int kt, const int (&rows)[8]) {
+  auto load_tile = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      const int gk = kt * BK + a_kc[i];
-      const bool ok = a_row_ok[i] && gk < g.K;
+      const uint32_t off = a_off[i] + (uint32_t)(kt * BK * ES);
       if constexpr (A_F32) {
-        const uint32_t off = ok ? a_row_off[i] + (uint32_t)gk * 4u : kOobOffset;
         ra_regs[2 * i] = buf_load16(ra, off);
-        ra_regs[2 * i + 1] = buf_load16(ra, ok ? off + 16u : kOobOffset);
+        ra_regs[2 * i + 1] = buf_load16(ra, off + 16u);
       } else {
-        const uint32_t off = ok ? a_row_off[i] + (uint32_t)gk * 2u : kOobOffset;
         ra_regs[i] = buf_load16(ra, off);
       }
     }
@@ -162,19 +154,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
       if (kb_owner) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const bool ok = rows[e] >= 0 && kb_col_ok;
-          const uint32_t off =
-              ok ? (uint32_t)((int64_t)rows[e] * g.ldb * 2 + (int64_t)(n0 + kb_cg * 8) * 2) : kOobOffset;
+          int row;
+          if constexpr (GATHER)
+            row = e < 4 ? idx_lo[e] : idx_hi[e - 4];
+          else
+            row = kt * BK + kb_kg * 8 + e;
+          const uint32_t off = ((uint32_t)(row * g.ldb + kb_col) * 2u) | kb_colmask;
           rb_regs[e] = buf_load16(rb, off);
         }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int gk = kt * BK + b_kc[i];
-        const bool ok = b_row_ok[i] && gk < g.K;
-        rb_regs[i] = buf_load16(rb, ok ? b_row_off[i] + (uint32_t)gk * 2u : kOobOffset);
-      }
+      for (int i = 0; i < B_CH; ++i) rb_regs[i] = buf_load16(rb, b_off[i] + (uint32_t)(kt * BK * 2));
     }
   };
 
@@ -183,8 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
     char* Bs = As + BM * 128;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      const int c = i * kThreads + tid;
-      const int row = c >> 3, ch = c & 7;
+      const int row = (tid >> 3) + 32 * i, ch = tid & 7;
       i32x4 v;
       if constexpr (A_F32) {
         const i32x4 lo = ra_regs[2 * i], hi = ra_regs[2 * i + 1];
@@ -210,8 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
     } else {
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
-        const int c = i * kThreads + tid;
-        const int row = c >> 3, ch = c & 7;
+        const int row = (tid >> 3) + 32 * i, ch = tid & 7;
         *(i32x4*)(Bs + row * 128 + swz(row, ch) * 16) = rb_regs[i];
       }
     }
@@ -225,60 +214,71 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  auto compute = [&](int buf) {
+  // LDS byte offsets of this lane's operand rows (before the chunk swizzle)
+  int a_row[TM], b_row[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row[i] = wm * WM + i * 32 + li;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_row[j] = wn * WN + j * 32 + li;
+
+  auto read_frags = [&](int buf, int s, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
     const char* As = smem + buf * STAGE;
     const char* Bs = As + BM * 128;
+    const int ch = 2 * s + lk;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 af[TM], bfr[TN];
-      const int ch = 2 * s + lk;
+    for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8*)(As + a_row[i] * 128 + swz(a_row[i], ch) * 16);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + li;
-        af[i] = *(const bf16x8*)(As + row * 128 + swz(row, ch) * 16);
-      }
+    for (int j = 0; j < TN; ++j) bfr[j] = *(const bf16x8*)(Bs + b_row[j] * 128 + swz(b_row[j], ch) * 16);
+  };
+  auto mfma_all = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfr)[TN]) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int nrow = wn * WN + j * 32 + li;
-        bfr[j] = *(const bf16x8*)(Bs + nrow * 128 + swz(nrow, ch) * 16);
-      }
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
-  const int KT = (g.K + BK - 1) / BK;
-  int rows_cur[8];
-  if constexpr (KMAJOR) load_rows(0, rows_cur);
-  load_tile(0, rows_cur);
-  if constexpr (KMAJOR) {
-    if (KT > 1) load_rows(1, rows_next);
-  }
+  const int KT = g.K / BK;
+  // prologue: tile 0 into LDS, tile 1 in flight in registers
+  load_idx(0);
+  load_tile(0);
   store_tile(0);
+  if (KT > 1) {
+    load_idx(1);
+    load_tile(1);
+  }
+  if (KT > 2) load_idx(2);
   __syncthreads();
 
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = NBUF == 1 ? 0 : (kt & 1);
-    const bool more = kt + 1 < KT;
-    int rows_after[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rows_after[e] = -1;
-    if (more) {
-      load_tile(kt + 1, rows_next);
-      if constexpr (KMAJOR) {
-        if (kt + 2 < KT) load_rows(kt + 2, rows_after);
+    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+    read_frags(cur, 0, a0, b0);
+    read_frags(cur, 1, a1, b1);
+    mfma_all(a0, b0);
+    if constexpr (NBUF == 2) {
+      // the other buffer was released by the barrier that ended kt - 1
+      if (kt + 1 < KT) {
+        store_tile(cur ^ 1);
+        if (kt + 2 < KT) {
+          load_tile(kt + 2);
+          if (kt + 3 < KT) load_idx(kt + 3);
+        }
       }
     }
-    compute(cur);
-    if (more) {
-      if (NBUF == 1) __syncthreads();
-      store_tile(NBUF == 1 ? 0 : (cur ^ 1));
-      if constexpr (KMAJOR) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rows_next[e] = rows_after[e];
+    read_frags(cur, 2, a0, b0);
+    mfma_all(a1, b1);
+    read_frags(cur, 3, a1, b1);
+    mfma_all(a0, b0);
+    mfma_all(a1, b1);
+    if constexpr (NBUF == 1) {
+      if (kt + 1 < KT) {
+        __syncthreads();
+        store_tile(0);
+        if (kt + 2 < KT) {
+          load_tile(kt + 2);
+          if (kt + 3 < KT) load_idx(kt + 3);
+        }
       }
     }
     __syncthreads();
@@ -287,16 +287,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
   // ---- epilogue: lane (li, lk) of accumulator register v holds row
   //      8*(v/4) + 4*lk + v%4 and column li of its 32x32 block.
   char* Cb = (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
+  const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = n0 + wn * WN + j * 32 + li;
-      if (col >= g.N) continue;
+      const int row0 = m0 + wm * WM + i * 32 + 4 * lk;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-        if (row < g.M) {
+        const int row = row0 + 8 * (v >> 2) + (v & 3);
+        if (full || (row < g.M && col < g.N)) {
           const size_t off = (size_t)row * g.ldc + col;
           if (g.c_bf16)
             __builtin_nontemporal_store(f32_to_bf16(acc[i][j][v]), (uint16_t*)Cb + off);

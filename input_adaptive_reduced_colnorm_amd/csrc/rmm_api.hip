@@ -94,12 +94,12 @@ hipError_t mark_of(const Marks* mk, int i) { return mk->mark(i); }
 
 hipError_t run_select(const SelPlan& sp, char* ws, const void* A, bool bf16, int64_t hs, int64_t lda, int heads,
                       int64_t n, int64_t d, int64_t k, int32_t* idx, int64_t idx_hs, float* scores, hipStream_t s,
-                      const Marks* mk = nullptr) {
+                      const Marks* mk = nullptr, int32_t* pad = nullptr, int64_t k_pad = 0) {
   float* partial = (float*)(ws + sp.off_partial);
   hipError_t e = launch_colnorm(A, bf16, hs, lda, heads, (int)n, (int)d, sp.splits, partial, s);
   if (e != hipSuccess) return e;
   if (mk && (e = mark_of(mk, 1)) != hipSuccess) return e;
-  return launch_topk(partial, heads, sp.splits, (int)d, (int)k, idx, idx_hs, scores, d,
+  return launch_topk(partial, heads, sp.splits, (int)d, (int)k, idx, idx_hs, pad, k_pad, (int)k_pad, scores, d,
                      sp.gkeys ? (uint32_t*)(ws + sp.off_gkeys) : nullptr, s);
 }
 
@@ -114,8 +114,7 @@ struct MatPlan {
   bool all = false;
   SelPlan sel;
   bool use_sel = false;
-  size_t off_pack = 0, off_at = 0, off_gpart = 0, off_cnt = 0, off_dkeys = 0;
-  int gsplits = 0;
+  size_t off_pack = 0, off_ipad = 0, off_at = 0, off_dkeys = 0;
   size_t total = 0;
 };
 
@@ -134,15 +133,12 @@ MatPlan plan_matmul(int64_t n, int64_t d, int64_t m, int64_t lda, int64_t ldb, i
       plan_select(cv, p.sel, 1, n, d, bf16);
       p.use_sel = true;
     }
-  } else if (n <= kDecodeRows) {
+  } else if (n <= kDecodeRows && p.k <= gemv_max_kept()) {
     p.path = MatPath::kDecode;
     if (d > topk_lds_capacity()) p.off_dkeys = cv.take((size_t)d * 4);
     p.off_at = cv.take((size_t)p.k_pad * 16 * 4);
-    p.gsplits = gemv_splits((int)p.k, (int)n, (int)m);
-    p.off_gpart = cv.take((size_t)p.gsplits * 16 * m * 4);
-    p.off_cnt = cv.take((size_t)((m + 127) / 128) * 4);
   } else {
-    const bool a_direct = p.all && a_ptr_ok && lda % 8 == 0 && d % 8 == 0;
+    const bool a_direct = p.all && a_ptr_ok && lda % 8 == 0 && d % kKTile == 0;
     if (a_direct) {
       p.path = MatPath::kMfmaDirect;
     } else {
@@ -151,6 +147,7 @@ MatPlan plan_matmul(int64_t n, int64_t d, int64_t m, int64_t lda, int64_t ldb, i
         plan_select(cv, p.sel, 1, n, d, true);
         p.use_sel = true;
       }
+      p.off_ipad = cv.take((size_t)p.k_pad * 4);
       p.off_pack = cv.take((size_t)n * p.k_pad * 2);
     }
   }
@@ -221,7 +218,7 @@ rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t 
   if (need_sel) {
     RMM_LAUNCH(run_select(sp, (char*)workspace, A, dtype == RMM_BF16, 0, lda, 1, n, d, k, idx, k, scores, s));
   } else {
-    RMM_LAUNCH(launch_iota(idx, k, 1, (int)d, s));
+    RMM_LAUNCH(launch_iota(idx, k, 1, (int)d, nullptr, 0, 0, s));
   }
   return RMM_OK;
 }
@@ -277,7 +274,7 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
       if (p.use_sel) {
         RMM_LAUNCH(run_select(p.sel, ws, A, bf16, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk));
       } else {
-        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, s));
+        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
         RMM_LAUNCH(mk.mark(1));
       }
       RMM_LAUNCH(mk.mark(2));
@@ -293,32 +290,27 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
     }
     case MatPath::kDecode: {
       float* at = (float*)(ws + p.off_at);
-      uint32_t* cnt = (uint32_t*)(ws + p.off_cnt);
-      const int strips = (int)((m + 127) / 128);
       RMM_LAUNCH(launch_decode_select(A, bf16, lda, (int)n, (int)d, (int)p.k, (int)p.k_pad, p.all, idx, nullptr, at,
-                                      d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, cnt, strips,
-                                      s));
+                                      d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, s));
       RMM_LAUNCH(mk.mark(1));
       RMM_LAUNCH(mk.mark(2));
       RMM_LAUNCH(mk.mark(3));
       GemvArgs g{};
       g.a_t = at; g.B = (const uint16_t*)B; g.ldb = ldb; g.idx = idx;
-      g.k = (int)p.k; g.n = (int)n; g.m = (int)m; g.splits = p.gsplits;
-      g.rows_per_split = (int)((p.k + p.gsplits - 1) / p.gsplits);
-      g.partial = (float*)(ws + p.off_gpart); g.counters = cnt;
+      g.k = (int)p.k; g.n = (int)n; g.m = (int)m;
       g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;
       RMM_LAUNCH(launch_gemv(g, s));
       break;
     }
     case MatPath::kMfmaDirect: {
-      RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, s));
+      RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
       RMM_LAUNCH(mk.mark(1));
       RMM_LAUNCH(mk.mark(2));
       RMM_LAUNCH(mk.mark(3));
       GemmArgs g{};
       g.A = (const uint16_t*)A; g.a_bs = 0; g.lda = lda;
       g.B = (const uint16_t*)B; g.b_bs = 0; g.ldb = ldb; g.b_group = 1;
-      g.idx = nullptr; g.idx_bs = 0; g.k_valid = (int)d;
+      g.idx = nullptr; g.idx_bs = 0;
       g.C = Y; g.c_bs = 0; g.ldc = ldy; g.c_bf16 = y_dtype == RMM_BF16;
       g.M = (int)n; g.N = (int)m; g.K = (int)d; g.batch = 1; g.b_kmajor = true;
       g.a_bytes = (uint32_t)(((n - 1) * lda + d) * 2);
@@ -327,10 +319,11 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
       break;
     }
     case MatPath::kMfmaPacked: {
+      int32_t* ipad = (int32_t*)(ws + p.off_ipad);
       if (p.use_sel) {
-        RMM_LAUNCH(run_select(p.sel, ws, A, true, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk));
+        RMM_LAUNCH(run_select(p.sel, ws, A, true, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk, ipad, p.k_pad));
       } else {
-        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, s));
+        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, ipad, 0, (int)p.k_pad, s));
         RMM_LAUNCH(mk.mark(1));
       }
       RMM_LAUNCH(mk.mark(2));
@@ -340,7 +333,7 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
       GemmArgs g{};
       g.A = pk; g.a_bs = 0; g.lda = p.k_pad;
       g.B = (const uint16_t*)B; g.b_bs = 0; g.ldb = ldb; g.b_group = 1;
-      g.idx = idx; g.idx_bs = 0; g.k_valid = (int)p.k;
+      g.idx = ipad; g.idx_bs = 0;
       g.C = Y; g.c_bs = 0; g.ldc = ldy; g.c_bf16 = y_dtype == RMM_BF16;
       g.M = (int)n; g.N = (int)m; g.K = (int)p.k_pad; g.batch = 1; g.b_kmajor = true;
       g.a_bytes = (uint32_t)(n * p.k_pad * 2);
@@ -426,7 +419,7 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
   if (!aligned(Q, elt) || !aligned(K, elt) || !aligned(idx, 4) || !aligned(S, elt_size(s_dtype)))
     return RMM_ERR_ALIGN;
   const bool direct_ok = dtype == RMM_BF16 && aligned(Q, 16) && aligned(K, 16) && q_ts % 8 == 0 &&
-                         k_ts % 8 == 0 && q_hs % 8 == 0 && k_hs % 8 == 0 && dh % 8 == 0 &&
+                         k_ts % 8 == 0 && q_hs % 8 == 0 && k_hs % 8 == 0 && dh % kKTile == 0 &&
                          ((tq - 1) * q_ts + dh) * 2 <= kMaxOperandBytes && ((tk - 1) * k_ts + dh) * 2 <= kMaxOperandBytes;
   const QkPlan p = plan_qk(hq, tq, tk, dh, dtype, rho, direct_ok);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
@@ -450,7 +443,7 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
   if (p.use_sel) {
     RMM_LAUNCH(run_select(p.sel, ws, Q, bf16, q_hs, q_ts, (int)hq, tq, dh, p.k, idx, p.k, nullptr, s));
   } else {
-    RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, s));
+    RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, nullptr, 0, 0, s));
   }
   if (!p.mfma) {
     SimtArgs g{};
@@ -482,7 +475,7 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
     g.a_bytes = (uint32_t)(tq * p.k_pad * 2);
     g.b_bytes = (uint32_t)(tk * p.k_pad * 2);
   }
-  g.idx = nullptr; g.idx_bs = 0; g.k_valid = g.K;
+  g.idx = nullptr; g.idx_bs = 0;
   g.C = S; g.c_bs = tq * tk; g.ldc = tk; g.c_bf16 = s_dtype == RMM_BF16;
   g.M = (int)tq; g.N = (int)tk; g.batch = (int)hq; g.b_kmajor = false;
   RMM_LAUNCH(launch_gemm_bf16(g, s));
@@ -497,7 +490,7 @@ struct PvPlan {
   int64_t k = 0, k_pad = 0;
   bool all = false, mfma = false, direct = false, use_sel = false;
   SelPlan sel;
-  size_t off_p = 0, total = 0;
+  size_t off_p = 0, off_ipad = 0, total = 0;
 };
 
 PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho, bool v_ok,
@@ -514,7 +507,10 @@ PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v
   }
   if (p.mfma) {
     p.direct = p.all && direct_ok;
-    if (!p.direct) p.off_p = cv.take((size_t)h * tq * p.k_pad * 2);
+    if (!p.direct) {
+      p.off_ipad = cv.take((size_t)h * p.k_pad * 4);
+      p.off_p = cv.take((size_t)h * tq * p.k_pad * 2);
+    }
   }
   p.total = cv.used;
   return p;
@@ -544,7 +540,7 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
   const bool v_ok = v_dtype == RMM_BF16 && aligned(V, 16) && v_ts % 8 == 0 && v_hs % 8 == 0 && dv % 8 == 0 &&
                     ((tk - 1) * v_ts + dv) * 2 <= kMaxOperandBytes;
   const bool p_f32 = p_dtype == RMM_FP32;
-  const bool direct_ok = aligned(P, 16) && tk % 8 == 0 && p_hs % (p_f32 ? 4 : 8) == 0 && p_ts % (p_f32 ? 4 : 8) == 0 &&
+  const bool direct_ok = aligned(P, 16) && tk % kKTile == 0 && p_hs % (p_f32 ? 4 : 8) == 0 && p_ts % (p_f32 ? 4 : 8) == 0 &&
                          ((tq - 1) * p_ts + tk) * (int64_t)pe <= kMaxOperandBytes;
   const PvPlan p = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, v_ok, direct_ok);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
@@ -563,10 +559,12 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
   char* ws = (char*)workspace;
   const int group = (int)(h / hkv);
   clear_error();
+  int32_t* ipad = p.mfma && !p.direct ? (int32_t*)(ws + p.off_ipad) : nullptr;
   if (p.use_sel) {
-    RMM_LAUNCH(run_select(p.sel, ws, P, !p_f32, p_hs, p_ts, (int)h, tq, tk, p.k, idx, p.k, nullptr, s));
+    RMM_LAUNCH(run_select(p.sel, ws, P, !p_f32, p_hs, p_ts, (int)h, tq, tk, p.k, idx, p.k, nullptr, s, nullptr, ipad,
+                          ipad ? p.k_pad : 0));
   } else {
-    RMM_LAUNCH(launch_iota(idx, p.k, (int)h, (int)tk, s));
+    RMM_LAUNCH(launch_iota(idx, p.k, (int)h, (int)tk, ipad, ipad ? p.k_pad : 0, ipad ? (int)p.k_pad : 0, s));
   }
   if (!p.mfma) {
     SimtArgs g{};
@@ -586,7 +584,7 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
   if (p.direct) {
     g.A = (const uint16_t*)P; g.a_bs = p_hs; g.lda = p_ts;
     g.a_bytes = (uint32_t)(((tq - 1) * p_ts + tk) * pe);
-    g.idx = nullptr; g.idx_bs = 0; g.k_valid = (int)tk; g.K = (int)tk;
+    g.idx = nullptr; g.idx_bs = 0; g.K = (int)tk;
     if (p_f32) {
       RMM_LAUNCH(launch_gemm_bf16_af32(g, s));
     } else {
@@ -599,7 +597,7 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
                          tq * p.k_pad, s));
   g.A = pp; g.a_bs = tq * p.k_pad; g.lda = p.k_pad;
   g.a_bytes = (uint32_t)(tq * p.k_pad * 2);
-  g.idx = idx; g.idx_bs = p.k; g.k_valid = (int)p.k; g.K = (int)p.k_pad;
+  g.idx = ipad; g.idx_bs = p.k_pad; g.K = (int)p.k_pad;
   RMM_LAUNCH(launch_gemm_bf16(g, s));
   return RMM_OK;
 }

@@ -15,15 +15,18 @@ hipError_t launch_colnorm(const void* A, bool elt_bf16, int64_t head_stride, int
 int colnorm_splits(int heads, int n, int d, bool elt_bf16);
 
 // TopK over the summed partials of each head: writes idx[h][0..k) ascending,
+// optionally the same list padded with -1 to k_pad entries (pad[h][...]),
 // optional scores[h][j] = sqrt(energy).  gkeys: [heads][d] uint32 scratch,
 // used only when d exceeds the LDS key capacity (may be null otherwise).
 hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k,
-                       int32_t* idx, int64_t idx_hs, float* scores, int64_t scores_hs,
-                       uint32_t* gkeys, hipStream_t s);
+                       int32_t* idx, int64_t idx_hs, int32_t* pad, int64_t pad_hs, int k_pad,
+                       float* scores, int64_t scores_hs, uint32_t* gkeys, hipStream_t s);
 int topk_lds_capacity();
 
-// Writes idx[h][t] = t for t < d (the rho = 1 selection).
-hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, hipStream_t s);
+// Writes idx[h][t] = t for t < d (the rho = 1 selection), and optionally
+// the padded copy pad[h][t] (t < k_pad, -1 past d).
+hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* pad, int64_t pad_hs, int k_pad,
+                       hipStream_t s);
 
 // Gather-pack: out[b][r][t] = t < k ? bf16(src[b / src_group][r][idx[b][t]]) : 0
 // for t < k_pad, rows r < rows.  src_bf16 selects bf16 (else fp32) input.
@@ -38,13 +41,12 @@ struct GemmArgs {
   const uint16_t* B;    // b_kmajor: [K][N] rows gathered by idx; else [N][K] K contiguous
   int64_t b_bs, ldb;
   int b_group;          // batch b reads B head b / b_group
-  const int32_t* idx;   // row gather for b_kmajor (null: row t is row t)
+  const int32_t* idx;   // row gather for b_kmajor, padded to K with -1 (null: row t is row t)
   int64_t idx_bs;
-  int k_valid;          // rows t >= k_valid of B read as zero
   void* C;              // [M][N] fp32 or bf16
   int64_t c_bs, ldc;
   bool c_bf16;
-  int M, N, K, batch;
+  int M, N, K, batch;   // K: multiple of 64 (A zero padded / B rows -1 padded)
   bool b_kmajor;
   uint32_t a_bytes, b_bytes;  // per-batch extents (bytes) for the buffer descriptors
 };
@@ -65,22 +67,20 @@ struct SimtArgs {
 hipError_t launch_gemm_simt(const SimtArgs& g, hipStream_t s);
 
 // Decode path (n <= 16): fused energy + TopK + transposed gather of A into
-// a_t[t][16] (fp32, zero padded), and zeroing of the GEMV tile counters.
+// a_t[t][16] (fp32, zero padded past n and past k up to k_pad).
 hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int k_pad,
-                                bool all, int32_t* idx, float* scores, float* a_t, uint32_t* gkeys,
-                                uint32_t* counters, int n_counters, hipStream_t s);
+                                bool all, int32_t* idx, float* scores, float* a_t, uint32_t* gkeys, hipStream_t s);
 
-// Split-K GEMV over the kept rows of B, deterministic ordered reduction.
+// GEMV over the kept rows of B (all kept rows per workgroup, fixed-order
+// reduction).  k must not exceed gemv_max_kept().
 struct GemvArgs {
-  const float* a_t;     // [k_pad][16]
+  const float* a_t;     // [k][16]
   const uint16_t* B; int64_t ldb;
   const int32_t* idx;   // kept rows (ascending)
-  int k, n, m, splits, rows_per_split;
-  float* partial;       // [splits][16][m]
-  uint32_t* counters;   // [m / 128 rounded up], zero on entry
+  int k, n, m;
   void* Y; bool y_bf16; int64_t ldy;
 };
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);
-int gemv_splits(int k, int n, int m);
+int gemv_max_kept();
 
 }  // namespace rmm

@@ -122,55 +122,104 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
+constexpr int kHistBins = 2048;  // 11-bit radix digits
+constexpr int kChunk = (kKeyCap + kSelThreads - 1) / kSelThreads;  // keys per thread held in registers
+
 struct SelShared {
-  uint32_t hist[256];
+  uint32_t hist[kHistBins];
   uint32_t misc[4];
   uint32_t wave_tot[kSelWaves][2];
 };
 
+// Block-wide inclusive scan of two counters (1024 threads, fixed order).
+__device__ __forceinline__ void block_incl_scan2(uint32_t& a, uint32_t& b, SelShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_incl_scan(a);
+  b = wave_incl_scan(b);
+  if (lane == 63) {
+    sh.wave_tot[wave][0] = a;
+    sh.wave_tot[wave][1] = b;
+  }
+  __syncthreads();
+  uint32_t pa = 0, pb = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint32_t ta = sh.wave_tot[w][0], tb = sh.wave_tot[w][1];
+    if (w < wave) {
+      pa += ta;
+      pb += tb;
+    }
+  }
+  a += pa;
+  b += pb;
+}
+
+// The keys of one thread: a contiguous index chunk [j0, j0 + cnt), kept in
+// registers across all radix passes and the compaction.
+struct KeyChunk {
+  uint32_t key[kChunk];
+  int j0, cnt;
+};
+
+__device__ __forceinline__ void load_chunk(const uint32_t* keys, int d, KeyChunk& kc) {
+  const int chunk = (d + kSelThreads - 1) / kSelThreads;
+  kc.j0 = min(d, (int)threadIdx.x * chunk);
+  kc.cnt = min(chunk, d - kc.j0);
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) kc.key[i] = i < kc.cnt ? keys[kc.j0 + i] : 0u;
+}
+
 // Finds the k-th largest key: on return *T is its value and *rem the number
 // of keys equal to T that belong to the kept set (the lowest-indexed ones).
-// Four MSB-first 8-bit radix passes with integer LDS histograms.
-__device__ void radix_threshold(const uint32_t* keys, int d, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
+// Three MSB-first radix passes (11, 11, 10 bits) with integer LDS
+// histograms; 11-bit first digits spread the exponents of the fp32 energies
+// over many buckets, and the bucket holding the k-th key is found with a
+// block-wide scan from the top bucket down.
+__device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, mask = 0, rem = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kSelThreads) sh.hist[i] = 0;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t nb = pass == 2 ? 1024u : 2048u;
+    for (int i = tid; i < (int)nb; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < d; j += kSelThreads) {
-      uint32_t key = keys[j];
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const uint32_t key = kc.key[i];
+      if (i < kc.cnt && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane l owns buckets 255-4l .. 252-4l, scanned from the top
-      uint32_t c[4], sum = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = sh.hist[255 - 4 * tid - i];
-        sum += c[i];
-      }
-      const uint32_t incl = wave_incl_scan(sum);
-      const uint32_t excl = incl - sum;
-      if (excl < rem && rem <= incl) {
-        uint32_t cum = excl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (cum + c[i] >= rem) {
-            sh.misc[0] = 255u - 4u * tid - i;
-            sh.misc[1] = rem - cum;
-            break;
-          }
-          cum += c[i];
-        }
+    // thread t owns the buckets nb-1-2t and nb-2-2t (one bucket, nb-1-t,
+    // when nb == 1024), counted from the top
+    uint32_t c0, c1 = 0;
+    int b0, b1 = -1;
+    if (nb == 2048u) {
+      b0 = (int)nb - 1 - 2 * tid;
+      b1 = b0 - 1;
+      c0 = sh.hist[b0];
+      c1 = sh.hist[b1];
+    } else {
+      b0 = (int)nb - 1 - tid;
+      c0 = sh.hist[b0];
+    }
+    uint32_t incl = c0 + c1, dummy = 0;
+    block_incl_scan2(incl, dummy, sh);
+    const uint32_t excl = incl - (c0 + c1);
+    if (excl < rem && rem <= incl) {
+      if (excl + c0 >= rem) {
+        sh.misc[0] = (uint32_t)b0;
+        sh.misc[1] = rem - excl;
+      } else {
+        sh.misc[0] = (uint32_t)b1;
+        sh.misc[1] = rem - excl - c0;
       }
     }
     __syncthreads();
     const uint32_t b = sh.misc[0];
     rem = sh.misc[1];
     prefix |= b << shift;
-    mask |= 255u << shift;
+    mask |= (nb - 1) << shift;
     __syncthreads();
   }
   *T = prefix;
@@ -181,32 +230,98 @@ __device__ void radix_threshold(const uint32_t* keys, int d, int k, SelShared& s
 // scan of (#greater, #equal) fixes each thread's output position, so the kept
 // indices come out ascending.  emit(pos, j) is called once per kept index.
 template <typename Emit>
-__device__ void compact_ascending(const uint32_t* keys, int d, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
+__device__ void compact_ascending(const KeyChunk& kc, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    if (i < kc.cnt) {
+      n_gt += kc.key[i] > T;
+      n_eq += kc.key[i] == T;
+    }
+  }
+  uint32_t i_gt = n_gt, i_eq = n_eq;
+  block_incl_scan2(i_gt, i_eq, sh);
+  uint32_t pos = (i_gt - n_gt) + min(i_eq - n_eq, rem);
+  uint32_t eq_seen = i_eq - n_eq;
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    if (i < kc.cnt) {
+      const uint32_t key = kc.key[i];
+      bool take = key > T;
+      if (key == T) {
+        take = eq_seen < rem;
+        ++eq_seen;
+      }
+      if (take) emit(pos++, kc.j0 + i);
+    }
+  }
+}
+
+// Same selection for key arrays too large for the register chunks (d above
+// the LDS key capacity): keys stay in global scratch and are re-read.
+__device__ void radix_threshold_big(const uint32_t* keys, int d, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t prefix = 0, mask = 0, rem = (uint32_t)k;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t nb = pass == 2 ? 1024u : 2048u;
+    for (int i = tid; i < (int)nb; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int j = tid; j < d; j += kSelThreads) {
+      const uint32_t key = keys[j];
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t c0, c1 = 0;
+    int b0, b1 = -1;
+    if (nb == 2048u) {
+      b0 = (int)nb - 1 - 2 * tid;
+      b1 = b0 - 1;
+      c0 = sh.hist[b0];
+      c1 = sh.hist[b1];
+    } else {
+      b0 = (int)nb - 1 - tid;
+      c0 = sh.hist[b0];
+    }
+    uint32_t incl = c0 + c1, dummy = 0;
+    block_incl_scan2(incl, dummy, sh);
+    const uint32_t excl = incl - (c0 + c1);
+    if (excl < rem && rem <= incl) {
+      if (excl + c0 >= rem) {
+        sh.misc[0] = (uint32_t)b0;
+        sh.misc[1] = rem - excl;
+      } else {
+        sh.misc[0] = (uint32_t)b1;
+        sh.misc[1] = rem - excl - c0;
+      }
+    }
+    __syncthreads();
+    const uint32_t b = sh.misc[0];
+    rem = sh.misc[1];
+    prefix |= b << shift;
+    mask |= (nb - 1) << shift;
+    __syncthreads();
+  }
+  *T = prefix;
+  *rem_out = rem;
+}
+
+template <typename Emit>
+__device__ void compact_ascending_big(const uint32_t* keys, int d, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
   const int chunk = (d + kSelThreads - 1) / kSelThreads;
-  const int j0 = min(d, tid * chunk), j1 = min(d, j0 + chunk);
+  const int j0 = min(d, (int)threadIdx.x * chunk), j1 = min(d, j0 + chunk);
   uint32_t n_gt = 0, n_eq = 0;
   for (int j = j0; j < j1; ++j) {
-    uint32_t key = keys[j];
+    const uint32_t key = keys[j];
     n_gt += key > T;
     n_eq += key == T;
   }
-  const uint32_t i_gt = wave_incl_scan(n_gt), i_eq = wave_incl_scan(n_eq);
-  if (lane == 63) {
-    sh.wave_tot[wave][0] = i_gt;
-    sh.wave_tot[wave][1] = i_eq;
-  }
-  __syncthreads();
-  uint32_t p_gt = i_gt - n_gt, p_eq = i_eq - n_eq;
-  for (int w = 0; w < wave; ++w) {
-    p_gt += sh.wave_tot[w][0];
-    p_eq += sh.wave_tot[w][1];
-  }
-  uint32_t pos = p_gt + min(p_eq, rem);
-  uint32_t eq_seen = p_eq;
+  uint32_t i_gt = n_gt, i_eq = n_eq;
+  block_incl_scan2(i_gt, i_eq, sh);
+  uint32_t pos = (i_gt - n_gt) + min(i_eq - n_eq, rem);
+  uint32_t eq_seen = i_eq - n_eq;
   for (int j = j0; j < j1; ++j) {
-    uint32_t key = keys[j];
+    const uint32_t key = keys[j];
     bool take = key > T;
     if (key == T) {
       take = eq_seen < rem;
@@ -219,6 +334,7 @@ __device__ void compact_ascending(const uint32_t* keys, int d, uint32_t T, uint3
 template <bool LDS_KEYS>
 __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restrict__ partial, int splits, int d, int k,
                                                            int32_t* __restrict__ idx, int64_t idx_hs,
+                                                           int32_t* __restrict__ pad, int64_t pad_hs, int k_pad,
                                                            float* __restrict__ scores, int64_t scores_hs,
                                                            uint32_t* __restrict__ gkeys) {
   __shared__ uint32_t s_keys[LDS_KEYS ? kKeyCap : 1];
@@ -226,23 +342,70 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   const int head = blockIdx.x;
   const float* P = partial + (size_t)head * splits * d;
   uint32_t* keys = LDS_KEYS ? s_keys : gkeys + (size_t)head * d;
-  for (int j = threadIdx.x; j < d; j += kSelThreads) {
-    float q = 0.f;
-    for (int s = 0; s < splits; ++s) q += P[(size_t)s * d + j];
-    keys[j] = __float_as_uint(q);
-    if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q);
+  if constexpr (LDS_KEYS) {
+    // each thread owns columns tid + 1024 c; the loads of four splits are
+    // issued together before they are added (in split order)
+    constexpr int NC = (kKeyCap + kSelThreads - 1) / kSelThreads;
+    float q[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c] = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += 4) {
+      float v[4][NC];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int j = threadIdx.x + c * kSelThreads;
+          v[u][c] = (s0 + u < splits && j < d) ? P[(size_t)(s0 + u) * d + j] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (s0 + u < splits)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) q[c] += v[u][c];
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int j = threadIdx.x + c * kSelThreads;
+      if (j < d) {
+        keys[j] = __float_as_uint(q[c]);
+        if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q[c]);
+      }
+    }
+  } else {
+    for (int j = threadIdx.x; j < d; j += kSelThreads) {
+      float q = 0.f;
+      for (int s = 0; s < splits; ++s) q += P[(size_t)s * d + j];
+      keys[j] = __float_as_uint(q);
+      if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q);
+    }
   }
   if (!LDS_KEYS) __threadfence_block();
   __syncthreads();
-  uint32_t T, rem;
-  radix_threshold(keys, d, k, sh, &T, &rem);
   int32_t* out = idx + (size_t)head * idx_hs;
-  compact_ascending(keys, d, T, rem, sh, [&](uint32_t pos, int j) { out[pos] = j; });
+  int32_t* po = pad ? pad + (size_t)head * pad_hs : nullptr;
+  if (po)
+    for (int t = k + threadIdx.x; t < k_pad; t += kSelThreads) po[t] = -1;
+  auto emit = [&](uint32_t pos, int j) {
+    out[pos] = j;
+    if (po) po[pos] = j;
+  };
+  uint32_t T, rem;
+  if constexpr (LDS_KEYS) {
+    KeyChunk kc;
+    load_chunk(keys, d, kc);
+    radix_threshold(kc, k, sh, &T, &rem);
+    compact_ascending(kc, T, rem, sh, emit);
+  } else {
+    radix_threshold_big(keys, d, k, sh, &T, &rem);
+    compact_ascending_big(keys, d, T, rem, sh, emit);
+  }
 }
 
-__global__ void iota_kernel(int32_t* idx, int64_t idx_hs, int d) {
+__global__ void iota_kernel(int32_t* idx, int64_t idx_hs, int d, int32_t* pad, int64_t pad_hs, int k_pad) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j < d) idx[(size_t)blockIdx.y * idx_hs + j] = j;
+  if (pad && j < k_pad) pad[(size_t)blockIdx.y * pad_hs + j] = j < d ? j : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -254,59 +417,76 @@ template <bool BF16, bool LDS_KEYS>
 __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* __restrict__ A_, int64_t lda, int n, int d,
                                                                     int k, int k_pad, int all, int32_t* __restrict__ idx,
                                                                     float* __restrict__ scores, float* __restrict__ a_t,
-                                                                    uint32_t* __restrict__ gkeys,
-                                                                    uint32_t* __restrict__ counters, int n_counters) {
+                                                                    uint32_t* __restrict__ gkeys) {
   __shared__ uint32_t s_keys[LDS_KEYS ? kKeyCap : 1];
+  __shared__ int32_t s_idx[LDS_KEYS ? kKeyCap : 1];
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   auto load = [&](int r, int j) -> float {
-    size_t off = (size_t)r * lda + j;
+    const size_t off = (size_t)r * lda + j;
     return BF16 ? bf16_to_f32(((const uint16_t*)A_)[off]) : ((const float*)A_)[off];
   };
-  for (int i = tid; i < n_counters; i += kSelThreads) counters[i] = 0;
   uint32_t* keys = LDS_KEYS ? s_keys : gkeys;
   const bool need_keys = !all || scores != nullptr;
   if (need_keys) {
+    // all 16 row loads of a column are issued before they are summed (rows
+    // in ascending order)
+#pragma unroll 2
     for (int j = tid; j < d; j += kSelThreads) {
+      float f[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[r] = r < n ? load(r, j) : 0.f;
       float q = 0.f;
-      for (int r = 0; r < n; ++r) {
-        float f = load(r, j);
-        q = fmaf(f, f, q);
-      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r < n) q = fmaf(f[r], f[r], q);
       keys[j] = __float_as_uint(q);
       if (scores) scores[j] = sqrtf(q);
     }
   }
-  for (int t = k + tid; t < k_pad; t += kSelThreads) {
+  auto fill_row = [&](int t, int j) {
+    // a_t[t][0..15] = A[0..15][j] (rows past n are zero)
+    float f[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) a_t[(size_t)t * 16 + r] = 0.f;
+    for (int r = 0; r < 16; ++r) f[r] = r < n ? load(r, j) : 0.f;
+    f32x4* dst = (f32x4*)(a_t + (size_t)t * 16);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) dst[q4] = f32x4{f[4 * q4], f[4 * q4 + 1], f[4 * q4 + 2], f[4 * q4 + 3]};
+  };
+  for (int t = k + tid; t < k_pad; t += kSelThreads) {
+    f32x4* dst = (f32x4*)(a_t + (size_t)t * 16);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) dst[q4] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if (all) {
+#pragma unroll 2
     for (int t = tid; t < k; t += kSelThreads) {
       idx[t] = t;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) a_t[(size_t)t * 16 + r] = r < n ? load(r, t) : 0.f;
+      fill_row(t, t);
     }
     return;
   }
   if (!LDS_KEYS) __threadfence_block();
   __syncthreads();
   uint32_t T, rem;
-  radix_threshold(keys, d, k, sh, &T, &rem);
-  compact_ascending(keys, d, T, rem, sh, [&](uint32_t pos, int j) {
-    idx[pos] = j;
-    f32x4* dst = (f32x4*)(a_t + (size_t)pos * 16);
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int r = 4 * q4 + e;
-        v[e] = r < n ? load(r, j) : 0.f;
-      }
-      dst[q4] = v;
-    }
-  });
+  if constexpr (LDS_KEYS) {
+    KeyChunk kc;
+    load_chunk(keys, d, kc);
+    radix_threshold(kc, k, sh, &T, &rem);
+    compact_ascending(kc, T, rem, sh, [&](uint32_t pos, int j) {
+      idx[pos] = j;
+      s_idx[pos] = j;
+    });
+    __syncthreads();
+#pragma unroll 2
+    for (int t = tid; t < k; t += kSelThreads) fill_row(t, s_idx[t]);
+  } else {
+    radix_threshold_big(keys, d, k, sh, &T, &rem);
+    compact_ascending_big(keys, d, T, rem, sh, [&](uint32_t pos, int j) {
+      idx[pos] = j;
+      fill_row((int)pos, j);
+    });
+  }
 }
 
 }  // namespace
@@ -346,38 +526,42 @@ hipError_t launch_colnorm(const void* A, bool elt_bf16, int64_t head_stride, int
 int topk_lds_capacity() { return kKeyCap; }
 
 hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k, int32_t* idx, int64_t idx_hs,
-                       float* scores, int64_t scores_hs, uint32_t* gkeys, hipStream_t s) {
+                       int32_t* pad, int64_t pad_hs, int k_pad, float* scores, int64_t scores_hs, uint32_t* gkeys,
+                       hipStream_t s) {
   if (d <= kKeyCap)
-    topk_kernel<true><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, scores, scores_hs, nullptr);
+    topk_kernel<true><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
+                                                     scores_hs, nullptr);
   else
-    topk_kernel<false><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, scores, scores_hs, gkeys);
+    topk_kernel<false><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
+                                                      scores_hs, gkeys);
   return hipGetLastError();
 }
 
-hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, hipStream_t s) {
-  dim3 grid((d + 255) / 256, heads);
-  iota_kernel<<<grid, 256, 0, s>>>(idx, idx_hs, d);
+hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* pad, int64_t pad_hs, int k_pad,
+                       hipStream_t s) {
+  const int span = pad && k_pad > d ? k_pad : d;
+  dim3 grid((span + 255) / 256, heads);
+  iota_kernel<<<grid, 256, 0, s>>>(idx, idx_hs, d, pad, pad_hs, k_pad);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int k_pad, bool all,
-                                int32_t* idx, float* scores, float* a_t, uint32_t* gkeys, uint32_t* counters,
-                                int n_counters, hipStream_t s) {
+                                int32_t* idx, float* scores, float* a_t, uint32_t* gkeys, hipStream_t s) {
   const int all_i = all ? 1 : 0;
   if (d <= kKeyCap) {
     if (a_bf16)
       decode_select_kernel<true, true><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, k_pad, all_i, idx, scores, a_t,
-                                                                  nullptr, counters, n_counters);
+                                                                  nullptr);
     else
       decode_select_kernel<false, true><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, k_pad, all_i, idx, scores, a_t,
-                                                                   nullptr, counters, n_counters);
+                                                                   nullptr);
   } else {
     if (a_bf16)
       decode_select_kernel<true, false><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, k_pad, all_i, idx, scores, a_t,
-                                                                   gkeys, counters, n_counters);
+                                                                   gkeys);
     else
       decode_select_kernel<false, false><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, k_pad, all_i, idx, scores, a_t,
-                                                                    gkeys, counters, n_counters);
+                                                                    gkeys);
   }
   return hipGetLastError();
 }
