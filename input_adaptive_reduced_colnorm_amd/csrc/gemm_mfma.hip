@@ -24,7 +24,6 @@ namespace rmm {
 namespace {
 
 constexpr int BK = 64;
-constexpr int kThreads = 256;
 
 struct TileCoord {
   int tm, tn;
@@ -72,20 +71,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
-template <int BM, int BN, bool KMAJOR, bool GATHER, bool A_F32, int NBUF>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+// WAVES = 4: waves in a 2x2 grid, each (BM/2) x (BN/2).
+// WAVES = 8: waves in a 2x4 grid, each (BM/2) x (BN/4); two waves share a
+// SIMD so one wave's MFMAs cover the other's barrier and LDS latency.
+template <int BM, int BN, bool KMAJOR, bool GATHER, bool A_F32, int NBUF, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs g) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int WGN = WAVES / 2;                   // wave grid: 2 x WGN
+  constexpr int WM = BM / 2, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_CH = BM * 8 / kThreads;          // 16-byte chunks of A (bf16) per thread
-  constexpr int B_CH = BN * 8 / kThreads;          // (N-contiguous B) chunks per thread
+  constexpr int A_CH = BM * 8 / NT;                // 16-byte chunks of A (bf16) per thread
+  constexpr int B_CH = BN * 8 / NT;                // (N-contiguous B) chunks per thread
+  constexpr int ROWS_PER_PASS = NT / 8;            // A rows covered by one chunk index
+  // K-major B: the 64 x BN tile is split into 8x8 blocks; each owner thread
+  // loads BR rows (8 or 4) of one block and transposes them.
+  constexpr int NBLK = BN;                          // (64 / 8) * (BN / 8)
+  constexpr int BR = NT >= 2 * NBLK ? 4 : 8;
+  constexpr int B_OWNERS = NBLK * (8 / BR);
   constexpr int STAGE = (BM + BN) * 128;           // bytes per LDS stage
   constexpr int ES = A_F32 ? 4 : 2;                // A element size
-  static_assert(BN <= kThreads, "one 8x8 B block per thread at most");
+  static_assert(B_OWNERS <= NT, "B blocks exceed the thread count");
   __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int li = lane & 31, lk = lane >> 5;
   const int b = blockIdx.y;
 
@@ -100,42 +110,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
   const int32_t* idxb = GATHER ? g.idx + (size_t)b * g.idx_bs : nullptr;
 
   // ---- per-thread load geometry (K is a multiple of 64 on every path) -----
-  // A chunk i of this thread: row (tid >> 3) + 32 i, 8 elements at column
-  // (tid & 7) * 8 of the K tile.  Rows past M read through an offset that is
-  // always out of range, so they load zeros without a branch.
+  // A chunk i of this thread: row (tid >> 3) + ROWS_PER_PASS * i, 8 elements
+  // at column (tid & 7) * 8 of the K tile.  Rows past M read through an
+  // offset that is always out of range, so they load zeros without a branch.
   const int a_kc = (tid & 7) * 8;
   uint32_t a_off[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int row = m0 + (tid >> 3) + 32 * i;
+    const int row = m0 + (tid >> 3) + ROWS_PER_PASS * i;
     a_off[i] = row < g.M ? (uint32_t)(row * g.lda + a_kc) * ES : kOobOffset;
   }
   uint32_t b_off[KMAJOR ? 1 : B_CH];
   if constexpr (!KMAJOR) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      const int row = n0 + (tid >> 3) + 32 * i;
+      const int row = n0 + (tid >> 3) + ROWS_PER_PASS * i;
       b_off[i] = row < g.N ? (uint32_t)(row * g.ldb + a_kc) * 2u : kOobOffset;
     }
   }
-  // K-major B: this thread owns the 8x8 block of rows kb_kg*8.. and columns
-  // kb_cg*8.. of each K tile.  A row index of -1 (padding past k) makes the
-  // 32-bit offset wrap far past the buffer end, so it also reads zeros.
-  const bool kb_owner = KMAJOR && tid < BN;
-  const int kb_cg = tid % (BN / 8), kb_kg = tid / (BN / 8);
+  // K-major B: this thread owns rows kb_kg*8 + kb_h*BR .. +BR-1 and columns
+  // kb_cg*8 .. +7 of each K tile.  A row index of -1 (padding past k) makes
+  // the 32-bit offset wrap far past the buffer end, so it also reads zeros.
+  const bool kb_owner = KMAJOR && tid < B_OWNERS;
+  const int kb_blk = tid / (8 / BR), kb_h = tid % (8 / BR);
+  const int kb_cg = kb_blk % (BN / 8), kb_kg = kb_blk / (BN / 8);
   const uint32_t kb_colmask = (n0 + kb_cg * 8) < g.N ? 0u : kOobOffset;
   const int kb_col = n0 + kb_cg * 8;
+  const int kb_row0 = kb_kg * 8 + kb_h * BR;
 
   constexpr int A_REGS = A_F32 ? 2 * A_CH : A_CH;
   i32x4 ra_regs[A_REGS];
-  i32x4 rb_regs[KMAJOR ? 8 : B_CH];
+  i32x4 rb_regs[KMAJOR ? BR : B_CH];
   i32x4 idx_lo, idx_hi;   // kept rows for the next tile to load
 
   auto load_idx = [&](int kt) {
     if constexpr (GATHER) {
-      const i32x4* p = (const i32x4*)(idxb + kt * BK + kb_kg * 8);
+      const i32x4* p = (const i32x4*)(idxb + kt * BK + kb_row0);
       idx_lo = p[0];
-      idx_hi = p[1];
+      if constexpr (BR == 8) idx_hi = p[1];
     }
   };
 
@@ -153,12 +165,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
     if constexpr (KMAJOR) {
       if (kb_owner) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < BR; ++e) {
           int row;
           if constexpr (GATHER)
             row = e < 4 ? idx_lo[e] : idx_hi[e - 4];
           else
-            row = kt * BK + kb_kg * 8 + e;
+            row = kt * BK + kb_row0 + e;
           const uint32_t off = ((uint32_t)(row * g.ldb + kb_col) * 2u) | kb_colmask;
           rb_regs[e] = buf_load16(rb, off);
         }
@@ -174,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
     char* Bs = As + BM * 128;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      const int row = (tid >> 3) + 32 * i, ch = tid & 7;
+      const int row = (tid >> 3) + ROWS_PER_PASS * i, ch = tid & 7;
       i32x4 v;
       if constexpr (A_F32) {
         const i32x4 lo = ra_regs[2 * i], hi = ra_regs[2 * i + 1];
@@ -189,18 +201,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
     }
     if constexpr (KMAJOR) {
       if (kb_owner) {
-        i32x4 tr[8];
-        transpose8x8(rb_regs, tr);
+        if constexpr (BR == 8) {
+          i32x4 tr[8];
+          transpose8x8(rb_regs, tr);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int nrow = kb_cg * 8 + c;
-          *(i32x4*)(Bs + nrow * 128 + swz(nrow, kb_kg) * 16) = tr[c];
+          for (int c = 0; c < 8; ++c) {
+            const int nrow = kb_cg * 8 + c;
+            *(i32x4*)(Bs + nrow * 128 + swz(nrow, kb_kg) * 16) = tr[c];
+          }
+        } else {
+          // 4 rows x 8 columns: column c becomes 4 consecutive k (8 bytes)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            i32x2 v;
+            v[0] = (int)__builtin_amdgcn_perm((uint32_t)rb_regs[1][c >> 1], (uint32_t)rb_regs[0][c >> 1], sel);
+            v[1] = (int)__builtin_amdgcn_perm((uint32_t)rb_regs[3][c >> 1], (uint32_t)rb_regs[2][c >> 1], sel);
+            const int nrow = kb_cg * 8 + c;
+            *(i32x2*)(Bs + nrow * 128 + swz(nrow, kb_kg) * 16 + kb_h * 8) = v;
+          }
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
-        const int row = (tid >> 3) + 32 * i, ch = tid & 7;
+        const int row = (tid >> 3) + ROWS_PER_PASS * i, ch = tid & 7;
         *(i32x4*)(Bs + row * 128 + swz(row, ch) * 16) = rb_regs[i];
       }
     }
@@ -214,7 +239,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // LDS byte offsets of this lane's operand rows (before the chunk swizzle)
   int a_row[TM], b_row[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) a_row[i] = wm * WM + i * 32 + li;
@@ -309,18 +333,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const GemmArgs g
   }
 }
 
-template <int BM, int BN, int NBUF>
+template <int BM, int BN, int NBUF, int WAVES>
 hipError_t dispatch(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(tiles, g.batch);
   const bool gather = g.idx != nullptr;
   if (g.b_kmajor) {
     if (gather)
-      gemm_bf16_kernel<BM, BN, true, true, false, NBUF><<<grid, kThreads, 0, s>>>(g);
+      gemm_bf16_kernel<BM, BN, true, true, false, NBUF, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
     else
-      gemm_bf16_kernel<BM, BN, true, false, false, NBUF><<<grid, kThreads, 0, s>>>(g);
+      gemm_bf16_kernel<BM, BN, true, false, false, NBUF, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
   } else {
-    gemm_bf16_kernel<BM, BN, false, false, false, NBUF><<<grid, kThreads, 0, s>>>(g);
+    gemm_bf16_kernel<BM, BN, false, false, false, NBUF, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
   }
   return hipGetLastError();
 }
@@ -333,11 +357,11 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
   const int KT = (g.K + BK - 1) / BK;
   if (t256 >= 192 && g.N >= 256 && g.M >= 256) {
-    if (KT == 1) return dispatch<256, 256, 1>(g, s);
-    return dispatch<256, 256, 2>(g, s);
+    if (KT == 1) return dispatch<256, 256, 1, 4>(g, s);
+    return dispatch<256, 256, 2, 8>(g, s);
   }
-  if (KT == 1) return dispatch<128, 128, 1>(g, s);
-  return dispatch<128, 128, 2>(g, s);
+  if (KT == 1) return dispatch<128, 128, 1, 4>(g, s);
+  return dispatch<128, 128, 2, 4>(g, s);
 }
 
 // Dense fp32-A variant (P of attention in fp32, rho = 1): A is read as fp32
@@ -349,16 +373,16 @@ hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s) {
     const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
     dim3 grid(tiles, g.batch);
     if (g.b_kmajor)
-      gemm_bf16_kernel<256, 256, true, false, true, 2><<<grid, kThreads, 0, s>>>(g);
+      gemm_bf16_kernel<256, 256, true, false, true, 2, 8><<<grid, 512, 0, s>>>(g);
     else
-      gemm_bf16_kernel<256, 256, false, false, true, 2><<<grid, kThreads, 0, s>>>(g);
+      gemm_bf16_kernel<256, 256, false, false, true, 2, 8><<<grid, 512, 0, s>>>(g);
   } else {
     const int tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
     dim3 grid(tiles, g.batch);
     if (g.b_kmajor)
-      gemm_bf16_kernel<128, 128, true, false, true, 2><<<grid, kThreads, 0, s>>>(g);
+      gemm_bf16_kernel<128, 128, true, false, true, 2, 4><<<grid, 256, 0, s>>>(g);
     else
-      gemm_bf16_kernel<128, 128, false, false, true, 2><<<grid, kThreads, 0, s>>>(g);
+      gemm_bf16_kernel<128, 128, false, false, true, 2, 4><<<grid, 256, 0, s>>>(g);
   }
   (void)KT;
   return hipGetLastError();
