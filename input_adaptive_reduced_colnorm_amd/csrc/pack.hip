@@ -3,9 +3,12 @@
 //
 // "Algorithm Deep-Dive: RMM" (hackcv.com), Core Approach (Formula Level):
 // only the kept columns of the activation take part in the product.  Each
-// lane owns one output position t (so a wave reads 64 consecutive kept
-// indices, which lie close together because the index list is ascending)
-// and the 8 rows of a row block reuse the same indices held in registers.
+// lane owns output positions t (so a wave reads 64 consecutive kept
+// indices, which lie close together because the index list is ascending);
+// the 8 rows of a row block reuse the same indices held in registers, all 64
+// gathers of a lane are in flight together, and the values pass through LDS
+// so that the panel is written with 16-byte stores.  k_pad is a multiple of
+// 8, so every 16-byte piece lies inside the padded row.
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
@@ -22,6 +25,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ src,
                                                    int src_group, const int32_t* __restrict__ idx, int64_t idx_hs,
                                                    int k, int k_pad, int rows, uint16_t* __restrict__ out,
                                                    int64_t out_hs) {
+  // the gathered values of all rows go through LDS so that every lane
+  // writes whole 16-byte pieces of an output row
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[kPackRows][kPackT];
   const int b = blockIdx.z;
   const int t0 = blockIdx.x * kPackT;
   const int r0 = blockIdx.y * kPackRows;
@@ -33,23 +39,32 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ src,
     cols[e] = t < k ? ib[t] : -1;
   }
   const size_t sbase = (size_t)(b / src_group) * src_hs;
-  uint16_t* ob = out + (size_t)b * out_hs;
+  uint16_t v[kPackRows][8];
+#pragma unroll
   for (int rr = 0; rr < kPackRows; ++rr) {
-    const int r = r0 + rr;
-    if (r >= rows) break;
-    uint16_t v[8];
+    const int r = min(r0 + rr, rows - 1);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[e] = 0;
+      v[rr][e] = 0;
       if (cols[e] >= 0) {
         const size_t off = sbase + (size_t)r * src_rs + cols[e];
-        v[e] = BF16 ? ((const uint16_t*)src)[off] : f32_to_bf16(((const float*)src)[off]);
+        v[rr][e] = BF16 ? ((const uint16_t*)src)[off] : f32_to_bf16(((const float*)src)[off]);
       }
     }
+  }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = t0 + e * 256 + threadIdx.x;
-      if (t < k_pad) ob[(size_t)r * k_pad + t] = v[e];
+  for (int rr = 0; rr < kPackRows; ++rr)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_out[rr][e * 256 + threadIdx.x] = v[rr][e];
+  __syncthreads();
+  uint16_t* ob = out + (size_t)b * out_hs;
+  const int t = t0 + threadIdx.x * 8;
+  if (t < k_pad) {
+#pragma unroll
+    for (int rr = 0; rr < kPackRows; ++rr) {
+      const int r = r0 + rr;
+      if (r >= rows) break;
+      *(i32x4*)(ob + (size_t)r * k_pad + t) = *(const i32x4*)&s_out[rr][threadIdx.x * 8];
     }
   }
 }

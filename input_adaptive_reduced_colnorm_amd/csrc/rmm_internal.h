@@ -30,6 +30,7 @@ hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* 
 
 // Gather-pack: out[b][r][t] = t < k ? bf16(src[b / src_group][r][idx[b][t]]) : 0
 // for t < k_pad, rows r < rows.  src_bf16 selects bf16 (else fp32) input.
+// k_pad must be a multiple of 8 and out 16-byte aligned (16-byte stores).
 hipError_t launch_pack(const void* src, bool src_bf16, int64_t src_hs, int64_t src_rs, int src_group,
                        const int32_t* idx, int64_t idx_hs, int k, int k_pad,
                        int batch, int rows, uint16_t* out, int64_t out_hs, hipStream_t s);
