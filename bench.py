@@ -6,14 +6,18 @@ A 4096 x 14336 bf16 activations times B 14336 x 4096 bf16 weights, fp32 Y.
 One step = one rmm_matmul call at each retention ratio 0.9, 0.7 and 0.5
 (score, TopK, gather-pack, reduced GEMM) plus the rho = 1 dense product
 that the speedups are measured against.  Inputs are resident in HBM before
-the timed region; four copies of (A, B) are rotated so that consecutive
-calls do not find their operands in the 256 MB Infinity Cache.
+the timed region; several copies of the inputs are rotated so that
+consecutive calls do not find their operands in the 256 MB Infinity Cache.
 
 Per-kernel times come from HIP events that the library records on its own
-stream at the stage boundaries (rmm_matmul_timed).  Prints ONE JSON line.
+stream at the stage boundaries (the *_timed entry points).  Prints ONE JSON
+line.
 
-Other workloads (--workload) print the same kind of line for profiling; the
-driver uses the default.
+Other workloads (--workload) print the same kind of line:
+  mlp_up_70b     A 2048 x 8192 @ B 8192 x 28672 (bf16), rho 0.8
+  decode_qkv_8b  A 8 x 4096 @ B 4096 x 6144 (bf16), rho 0.8 (GEMV path)
+  gqa_qk_8b      S = Q K^T per head, Q (32, 4096, 128), K (8, 4096, 128) bf16, rho 0.5
+  attn_pv_70b    O = P V per head, P (64, 512, 8192) fp32, V (8, 8192, 128) bf16, rho 0.5
 """
 
 from __future__ import annotations
@@ -29,11 +33,12 @@ import time
 METRIC = "RMM op latency & speedup vs own dense (rho=1) at Llama-8B shapes; MFMA/HBM %"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+STAGES = ("score", "topk", "pack", "gemm")
 
 
 def _die_multi_gpu(n):
-    print(json.dumps({"error": f"--gpus {n}: this build measures one GPU only; the path has no multi-GPU "
-                               "collective (see DESIGN.md for how it would shard)"}))
+    print(json.dumps({"error": f"--gpus {n}: this benchmark measures one GPU only; the RMM path has no "
+                               "multi-GPU collective (its sharding is described in the design notes)"}))
     sys.exit(2)
 
 
@@ -75,83 +80,260 @@ class Events:
             self.hip.hipEventDestroy(e)
 
 
-def cpu_baseline_matmul(A_cpu, B_cpu, rhos, sample_rows):
-    """The oracle as it stands, on a bounded sample of the same workload."""
-    import numpy as np
-    from oracle import rmm_oracle as O
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = sum(int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas")
+        return sum(int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas")
     except Exception:  # pragma: no cover - informational only
-        threads = os.cpu_count()
-    A = A_cpu.float().numpy()
-    B = B_cpu.float().numpy()
-    n = A.shape[0]
-    rows = np.arange(sample_rows)
-    est = {}
-    wall = 0.0
-    for rho in rhos:
-        t0 = time.perf_counter()
-        O.select(A, rho)
-        t1 = time.perf_counter()
-        O.matmul(A, B, rho, rows=rows)
-        t2 = time.perf_counter()
-        t_sel = t1 - t0
-        t_prod = max(t2 - t1 - t_sel, 0.0)
-        est[rho] = t_sel + t_prod * n / sample_rows
-        wall += t2 - t0
-    total = sum(est.values())
-    return {
-        "value": len(rhos) / total,
-        "unit": "RMM ops/s",
-        "cores": threads,
-        "host_cpus": os.cpu_count(),
-        "kind": "oracle",
-        "sample": (f"full fp64 scoring + stable-sort TopK on all {n} rows, reduced product on rows 0..{sample_rows - 1} "
-                   f"of {n}, scaled by {n // sample_rows}x; one call per rho in {list(rhos)}; "
-                   f"{wall:.1f} s of CPU work"),
-        "est_op_s": {str(r): round(v, 4) for r, v in est.items()},
-    }
+        return os.cpu_count()
 
 
-def bench_matmul(args, name, A_cpu, B_cpu, rhos, desc):
-    import torch
-    from input_adaptive_reduced_colnorm_amd import rmm
+# ---------------------------------------------------------------------------
+# workloads: each provides the call, its stage work and its oracle sample
+# ---------------------------------------------------------------------------
 
-    dev = torch.device("cuda:0")
-    hip = _hip()
-    L = rmm.lib()
-    n, d = A_cpu.shape
-    m = B_cpu.shape[1]
-    copies = max(1, args.copies)
-    As = [A_cpu.to(dev) for _ in range(copies)]
-    Bs = [B_cpu.to(dev) for _ in range(copies)]
-    Y = torch.empty((n, m), dtype=torch.float32, device=dev)
-    ks = {r: rmm.k(r, d) for r in rhos}
-    idx = {r: torch.empty(ks[r], dtype=torch.int32, device=dev) for r in rhos}
-    ws_bytes = max(int(L.rmm_matmul_workspace(n, d, m, d, rmm.RMM_BF16, r)) for r in rhos)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
-    nops = len(rhos)
-    evs = Events(hip, 5 * args.stage_iters * nops)
+class MatmulOp:
+    """Linear / MLP product Y = A[:, I] B[I, :] (rmm_matmul)."""
 
-    def call_timed(c, rho, slot):
-        st = L.rmm_matmul_timed(As[c].data_ptr(), Bs[c].data_ptr(), rmm.RMM_BF16, n, d, m, d, m, float(rho),
-                                idx[rho].data_ptr(), Y.data_ptr(), rmm.RMM_FP32, m, ws.data_ptr(), ws.numel(), sh,
-                                evs.array(5 * slot))
-        if st != 0:
-            raise RuntimeError(f"rmm_matmul_timed: {rmm.status_str(st)}")
+    def __init__(self, name, A_cpu, B_cpu, rhos, desc, copies):
+        import torch
+        from input_adaptive_reduced_colnorm_amd import rmm
+        self.rmm, self.L = rmm, rmm.lib()
+        dev = torch.device("cuda:0")
+        self.name, self.desc, self.rhos = name, desc, rhos
+        self.A_cpu, self.B_cpu = A_cpu, B_cpu
+        self.n, self.d = A_cpu.shape
+        self.m = B_cpu.shape[1]
+        self.copies = copies
+        self.As = [A_cpu.to(dev) for _ in range(copies)]
+        self.Bs = [B_cpu.to(dev) for _ in range(copies)]
+        self.Y = torch.empty((self.n, self.m), dtype=torch.float32, device=dev)
+        self.ks = {r: rmm.k(r, self.d) for r in rhos}
+        self.idx = {r: torch.empty(self.ks[r], dtype=torch.int32, device=dev) for r in rhos}
+        wsb = max(int(self.L.rmm_matmul_workspace(self.n, self.d, self.m, self.d, rmm.RMM_BF16, r)) for r in rhos)
+        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        self.decode = self.n <= 16
 
-    def call(c, rho):
-        st = L.rmm_matmul(As[c].data_ptr(), Bs[c].data_ptr(), rmm.RMM_BF16, n, d, m, d, m, float(rho),
-                          idx[rho].data_ptr(), Y.data_ptr(), rmm.RMM_FP32, m, ws.data_ptr(), ws.numel(), sh)
+    def call(self, c, rho, sh, events=None):
+        n, d, m, L, rmm = self.n, self.d, self.m, self.L, self.rmm
+        args = [self.As[c].data_ptr(), self.Bs[c].data_ptr(), rmm.RMM_BF16, n, d, m, d, m, float(rho),
+                self.idx[rho].data_ptr(), self.Y.data_ptr(), rmm.RMM_FP32, m, self.ws.data_ptr(), self.ws.numel(), sh]
+        st = L.rmm_matmul(*args) if events is None else L.rmm_matmul_timed(*args, events)
         if st != 0:
             raise RuntimeError(f"rmm_matmul: {rmm.status_str(st)}")
 
+    def stage_work(self, rho):
+        """Algorithmic work per stage: (kind, amount) with kind 'B' bytes or 'F' flops."""
+        n, d, m, k = self.n, self.d, self.m, self.ks[rho]
+        if self.decode:
+            # one workgroup scores and selects; the GEMV streams the kept rows of B
+            return {"score": ("B", n * d * 2), "gemm": ("B", k * m * 2)}
+        w = {"gemm": ("F", 2.0 * n * k * m)}
+        if k < d:
+            w["score"] = ("B", n * d * 2)
+            w["pack"] = ("B", 2 * n * k * 2)
+        return w
+
+    def roofline_stage(self):
+        return "gemm"
+
+    def roofline_kernel(self):
+        if self.decode:
+            return "gemv_kernel (kept rows of B)"
+        return "gemm_bf16_kernel<256,256,kmajor,gather> (reduced GEMM)"
+
+    def shape(self):
+        return {"shape": self.desc}
+
+    def cpu_baseline(self):
+        """The oracle as it stands, on the whole step (every rho, every row)."""
+        import numpy as np
+        from oracle import rmm_oracle as O
+        A = self.A_cpu.float().numpy()
+        B = self.B_cpu.float().numpy()
+        rows = None
+        if self.n * self.d * self.m > 4096 * 14336 * 4096:
+            rows = np.arange(1024)        # bound the sample for larger shapes
+        t0 = time.perf_counter()
+        for rho in self.rhos:
+            O.matmul(A, B, rho, rows=rows)
+        wall = time.perf_counter() - t0
+        scale = 1 if rows is None else self.n / len(rows)
+        ops = len(self.rhos) / (wall * scale)
+        what = "every row" if rows is None else f"rows 0..{len(rows) - 1} of {self.n} (product), scaled by {scale:g}x"
+        return {"value": ops, "unit": "RMM ops/s", "cores": _blas_threads(), "host_cpus": os.cpu_count(),
+                "kind": "oracle",
+                "sample": (f"fp64 oracle (scoring, stable-sort TopK, gather, product) for one call per rho in "
+                           f"{list(self.rhos)} over {what}; {wall:.1f} s of CPU work")}
+
+
+class QkOp:
+    """Per-head attention scores S_h = Q_h[:, I_h] K_g(h)[:, I_h]^T (rmm_qk)."""
+
+    def __init__(self, name, Q_cpu, K_cpu, rhos, desc, copies):
+        import torch
+        from input_adaptive_reduced_colnorm_amd import rmm
+        self.rmm, self.L = rmm, rmm.lib()
+        dev = torch.device("cuda:0")
+        self.name, self.desc, self.rhos, self.copies = name, desc, rhos, copies
+        self.Q_cpu, self.K_cpu = Q_cpu, K_cpu
+        self.hq, self.tq, self.dh = Q_cpu.shape
+        self.hkv, self.tk, _ = K_cpu.shape
+        self.Qs = [Q_cpu.to(dev) for _ in range(copies)]
+        self.Ks = [K_cpu.to(dev) for _ in range(copies)]
+        self.S = torch.empty((self.hq, self.tq, self.tk), dtype=torch.float32, device=dev)
+        self.ks = {r: rmm.k(r, self.dh) for r in rhos}
+        self.idx = {r: torch.empty((self.hq, self.ks[r]), dtype=torch.int32, device=dev) for r in rhos}
+        wsb = max(int(self.L.rmm_qk_workspace(self.hq, self.tq, self.tk, self.dh, rmm.RMM_BF16, r)) for r in rhos)
+        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+    def call(self, c, rho, sh, events=None):
+        hq, tq, tk, dh, L, rmm = self.hq, self.tq, self.tk, self.dh, self.L, self.rmm
+        args = [self.Qs[c].data_ptr(), self.Ks[c].data_ptr(), rmm.RMM_BF16, hq, self.hkv, tq, tk, dh, tq * dh, dh,
+                tk * dh, dh, float(rho), self.idx[rho].data_ptr(), self.S.data_ptr(), rmm.RMM_FP32,
+                self.ws.data_ptr(), self.ws.numel(), sh]
+        st = L.rmm_qk(*args) if events is None else L.rmm_qk_timed(*args, events)
+        if st != 0:
+            raise RuntimeError(f"rmm_qk: {rmm.status_str(st)}")
+
+    def stage_work(self, rho):
+        hq, hkv, tq, tk, dh, k = self.hq, self.hkv, self.tq, self.tk, self.dh, self.ks[rho]
+        s_bytes = hq * tq * tk * 4
+        if k == dh:   # dense: Q and K read in place, S written
+            return {"gemm": ("B", s_bytes + hq * tq * dh * 2 + hkv * tk * dh * 2)}
+        return {"score": ("B", hq * tq * dh * 2),
+                "pack": ("B", 2 * (hq * tq * k + hq * tk * k) * 2),
+                "gemm": ("B", s_bytes + (hq * tq * k + hq * tk * k) * 2)}
+
+    def roofline_stage(self):
+        return "gemm"
+
+    def roofline_kernel(self):
+        return "gemm_bf16_kernel<256,256,nmajor> (batched per-head QK^T, fp32 S store)"
+
+    def shape(self):
+        return {"shape": self.desc}
+
+    def cpu_baseline(self):
+        import numpy as np
+        from oracle import rmm_oracle as O
+        Q = self.Q_cpu.float().numpy()
+        K = self.K_cpu.float().numpy()
+        heads = list(range(0, self.hq, 4))          # 8 of 32 query heads
+        t0 = time.perf_counter()
+        for rho in self.rhos:
+            O.qk(Q, K, rho, heads=heads)
+        wall = time.perf_counter() - t0
+        scale = self.hq / len(heads)
+        return {"value": len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
+                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "sample": (f"fp64 oracle qk for query heads {heads[0]}, {heads[1]}, ... (every 4th, "
+                           f"{len(heads)} of {self.hq}) at each rho in {list(self.rhos)}, scaled by {scale:g}x; "
+                           f"{wall:.1f} s of CPU work")}
+
+
+class PvOp:
+    """Per-head attention output O_h = P_h[:, I_h] V_g(h)[I_h, :] (rmm_pv)."""
+
+    def __init__(self, name, P_cpu, V_cpu, rhos, desc, copies):
+        import torch
+        from input_adaptive_reduced_colnorm_amd import rmm
+        self.rmm, self.L = rmm, rmm.lib()
+        dev = torch.device("cuda:0")
+        self.name, self.desc, self.rhos, self.copies = name, desc, rhos, copies
+        self.P_cpu, self.V_cpu = P_cpu, V_cpu
+        self.h, self.tq, self.tk = P_cpu.shape
+        self.hkv, _, self.dv = V_cpu.shape
+        self.Ps = [P_cpu.to(dev) for _ in range(copies)]
+        self.Vs = [V_cpu.to(dev) for _ in range(copies)]
+        self.O = torch.empty((self.h, self.tq, self.dv), dtype=torch.float32, device=dev)
+        self.ks = {r: rmm.k(r, self.tk) for r in rhos}
+        self.idx = {r: torch.empty((self.h, self.ks[r]), dtype=torch.int32, device=dev) for r in rhos}
+        wsb = max(int(self.L.rmm_pv_workspace(self.h, self.tq, self.tk, self.dv, rmm.RMM_FP32, rmm.RMM_BF16, r))
+                  for r in rhos)
+        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+    def call(self, c, rho, sh, events=None):
+        h, tq, tk, dv, L, rmm = self.h, self.tq, self.tk, self.dv, self.L, self.rmm
+        args = [self.Ps[c].data_ptr(), rmm.RMM_FP32, self.Vs[c].data_ptr(), rmm.RMM_BF16, h, self.hkv, tq, tk, dv,
+                tq * tk, tk, tk * dv, dv, float(rho), self.idx[rho].data_ptr(), self.O.data_ptr(), rmm.RMM_FP32,
+                self.ws.data_ptr(), self.ws.numel(), sh]
+        st = L.rmm_pv(*args) if events is None else L.rmm_pv_timed(*args, events)
+        if st != 0:
+            raise RuntimeError(f"rmm_pv: {rmm.status_str(st)}")
+
+    def masked(self, rho):
+        """The library runs PV over all key positions of P in place (dropped
+        rows of V read as zeros) when at least one key in eight is kept."""
+        return self.ks[rho] * 8 >= self.tk and self.tk % 64 == 0
+
+    def stage_work(self, rho):
+        h, tq, tk, dv, k = self.h, self.tq, self.tk, self.dv, self.ks[rho]
+        o_bytes = h * tq * dv * 4
+        if k == tk:   # dense: fp32 P and V read in place
+            return {"gemm": ("B", h * tq * tk * 4 + self.hkv * tk * dv * 2 + o_bytes)}
+        score = ("B", h * tq * tk * 4)
+        if self.masked(rho):
+            # P read in place once more, kept rows of V, O written
+            return {"score": score, "gemm": ("B", h * tq * tk * 4 + h * k * dv * 2 + o_bytes)}
+        return {"score": score,
+                "pack": ("B", h * tq * k * 4 + h * tq * k * 2),
+                "gemm": ("B", h * tq * k * 2 + h * k * dv * 2 + o_bytes)}
+
+    def roofline_stage(self):
+        return None   # the slowest stage of the reduced op
+
+    def roofline_kernel(self):
+        masked = all(self.masked(r) for r in self.rhos if r < 1.0)
+        gemm = ("gemm_bf16_kernel<128,128,kmajor,gather,fp32 A> (per-head PV over all keys of P, dropped V rows "
+                "masked)" if masked else "gemm_bf16_kernel<128,128,kmajor,gather> (per-head PV on packed P)")
+        return {"score": "colnorm_kernel<fp32> (column energies of P)", "pack": "pack_kernel<fp32> (kept columns of P)",
+                "gemm": gemm}
+
+    def shape(self):
+        return {"shape": self.desc}
+
+    def cpu_baseline(self):
+        import numpy as np
+        from oracle import rmm_oracle as O
+        P = self.P_cpu.numpy()
+        V = self.V_cpu.float().numpy()
+        heads = list(range(0, self.h, 4))           # 16 of 64 heads
+        t0 = time.perf_counter()
+        for rho in self.rhos:
+            O.pv(P, V, rho, heads=heads)
+        wall = time.perf_counter() - t0
+        scale = self.h / len(heads)
+        return {"value": len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
+                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "sample": (f"fp64 oracle pv for heads {heads[0]}, {heads[1]}, ... (every 4th, {len(heads)} of "
+                           f"{self.h}) at each rho in {list(self.rhos)}, scaled by {scale:g}x; "
+                           f"{wall:.1f} s of CPU work")}
+
+
+# ---------------------------------------------------------------------------
+
+def _rate(kind, amount, us):
+    if kind == "F":
+        v = amount / (us * 1e-6) / 1e12
+        return {"tflops": round(v, 1), "mfma_frac": round(v / PEAK_BF16_TFLOPS, 4)}
+    v = amount / (us * 1e-6) / 1e9
+    return {"gbs": round(v, 1), "hbm_frac": round(v / PEAK_HBM_GBS, 4)}
+
+
+def run(args, op):
+    import torch
+
+    hip = _hip()
+    stream = torch.cuda.current_stream(torch.device("cuda:0"))
+    sh = stream.cuda_stream
+    rhos = op.rhos
+    nops = len(rhos)
+    copies = op.copies
+
     for step in range(args.warmup):
         for j, rho in enumerate(rhos):
-            call((step * nops + j) % copies, rho)
+            op.call((step * nops + j) % copies, rho, sh)
     torch.cuda.synchronize()
 
     # timed region: K steps; barrier (single process) + device sync on both sides
@@ -161,11 +343,10 @@ def bench_matmul(args, name, A_cpu, B_cpu, rhos, desc):
     t_start.record(stream)
     for step in range(args.steps):
         for j, rho in enumerate(rhos):
-            call((step * nops + j) % copies, rho)
+            op.call((step * nops + j) % copies, rho, sh)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
-    ms_per_step = ms_total / args.steps
 
     # op latency per rho: back-to-back calls between two events (no events
     # between calls: an event record costs a few microseconds of GPU time)
@@ -174,112 +355,71 @@ def bench_matmul(args, name, A_cpu, B_cpu, rhos, desc):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for it in range(args.steps):
-            call((it + j) % copies, rho)
+            op.call((it + j) % copies, rho, sh)
         e1.record(stream)
         torch.cuda.synchronize()
         op_us[rho] = e0.elapsed_time(e1) / args.steps * 1e3
 
     # per-kernel durations: the same calls with stage events recorded by the
-    # library on its stream (rmm_matmul_timed)
-    stages = {r: {"score": [], "topk": [], "pack": [], "gemm": [], "op": []} for r in rhos}
+    # library on the stream the kernels run on
+    evs = Events(hip, 5 * args.stage_iters * nops)
+    stages = {r: {s: [] for s in STAGES + ("op",)} for r in rhos}
     slot = 0
     for it in range(args.stage_iters):
         for j, rho in enumerate(rhos):
-            call_timed((it * nops + j) % copies, rho, slot)
+            op.call((it * nops + j) % copies, rho, sh, evs.array(5 * slot))
             slot += 1
     torch.cuda.synchronize()
     slot = 0
     for it in range(args.stage_iters):
         for rho in rhos:
             b = 5 * slot
-            st = stages[rho]
-            st["score"].append(evs.ms(b, b + 1))
-            st["topk"].append(evs.ms(b + 1, b + 2))
-            st["pack"].append(evs.ms(b + 2, b + 3))
-            st["gemm"].append(evs.ms(b + 3, b + 4))
-            st["op"].append(evs.ms(b, b + 4))
+            for i, s in enumerate(STAGES):
+                stages[rho][s].append(evs.ms(b + i, b + i + 1))
+            stages[rho]["op"].append(evs.ms(b, b + 4))
             slot += 1
     evs.close()
+    mean = {r: {s: statistics.fmean(v) * 1e3 for s, v in stages[r].items()} for r in rhos}   # us
 
-    med = {r: {k2: statistics.median(v) * 1e3 for k2, v in stages[r].items()} for r in rhos}  # us
-    mean = {r: {k2: statistics.fmean(v) * 1e3 for k2, v in stages[r].items()} for r in rhos}
     dense_r = 1.0 if 1.0 in rhos else None
-    lat = {str(r): round(op_us[r], 2) for r in rhos}
-    speed = {}
-    if dense_r is not None:
-        for r in rhos:
-            if r != dense_r:
-                speed[str(r)] = round(op_us[dense_r] / op_us[r], 4)
-
-    def gemm_flops(r):
-        return 2.0 * n * ks[r] * m
-
+    speed = {str(r): round(op_us[dense_r] / op_us[r], 4) for r in rhos if dense_r is not None and r != dense_r}
     per_kernel = {}
     for r in rhos:
-        e = mean[r]
-        row = {
-            "gemm_us": round(e["gemm"], 2),
-            "gemm_tflops": round(gemm_flops(r) / (e["gemm"] * 1e-6) / 1e12, 1),
-            "gemm_mfma_frac": round(gemm_flops(r) / (e["gemm"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        }
-        if r != dense_r:
-            a_bytes = n * d * 2
-            row["score_us"] = round(e["score"], 2)
-            row["score_gbs"] = round(a_bytes / (e["score"] * 1e-6) / 1e9, 1)
-            row["score_hbm_frac"] = round(a_bytes / (e["score"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
-            row["topk_us"] = round(e["topk"], 2)
-            pk_bytes = 2 * n * ks[r] * 2
-            row["pack_us"] = round(e["pack"], 2)
-            row["pack_gbs"] = round(pk_bytes / (e["pack"] * 1e-6) / 1e9, 1)
-            row["pack_hbm_frac"] = round(pk_bytes / (e["pack"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        row = {}
+        work = op.stage_work(r)
+        for s in STAGES:
+            if s in work or (s == "topk" and "score" in work):
+                row[f"{s}_us"] = round(mean[r][s], 2)
+                if s in work:
+                    for key, v in _rate(*work[s], mean[r][s]).items():
+                        row[f"{s}_{key}"] = v
         per_kernel[str(r)] = row
 
-    # dominant kernel: the reduced product kernel, averaged over its launches (rho < 1)
+    # roofline of the dominant kernel of the reduced op (mean over its launches)
     red = [r for r in rhos if r != dense_r]
-    tot_s = sum(mean[r]["gemm"] * 1e-6 for r in red)
-    if n <= 16:
-        # decode: the GEMV streams the kept rows of B (k x m bf16)
-        for r in rhos:
-            per_kernel[str(r)]["gemv_gbs"] = round(ks[r] * m * 2 / (mean[r]["gemm"] * 1e-6) / 1e9, 1)
-            per_kernel[str(r)]["gemv_hbm_frac"] = round(ks[r] * m * 2 / (mean[r]["gemm"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
-        tot_b = sum(ks[r] * m * 2 for r in red)
-        achieved = tot_b / tot_s / 1e9
-        roofline = {
-            "kernel": "gemv_kernel (kept rows of B, mean over rho in %s)" % red,
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-            "per_launch_bytes": {str(r): ks[r] * m * 2 for r in red},
-            "avg_launch_us": round(tot_s / len(red) * 1e6, 2),
-        }
+    stage = op.roofline_stage()
+    if stage is None:
+        stage = max((s for s in STAGES if s in op.stage_work(red[0])), key=lambda s: sum(mean[r][s] for r in red))
+    kinds = {op.stage_work(r)[stage][0] for r in red}
+    assert len(kinds) == 1
+    kind = kinds.pop()
+    tot_s = sum(mean[r][stage] * 1e-6 for r in red)
+    tot_w = sum(op.stage_work(r)[stage][1] for r in red)
+    kname = op.roofline_kernel()
+    if isinstance(kname, dict):
+        kname = kname[stage]
+    if kind == "F":
+        achieved = tot_w / tot_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "per_launch_flops": {str(r): op.stage_work(r)[stage][1] for r in red}}
     else:
-        tot_flops = sum(gemm_flops(r) for r in red)
-        achieved = tot_flops / tot_s / 1e12
-        roofline = {
-            "kernel": "gemm_bf16_kernel<256,256,kmajor,gather> (reduced GEMM, mean over rho in %s)" % red,
-            "bound": "mfma",
-            "achieved": round(achieved, 1),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
-            "per_launch_flops": {str(r): gemm_flops(r) for r in red},
-            "avg_launch_us": round(tot_s / len(red) * 1e6, 2),
-        }
-
-    # hipBLASLt dense time at the same shape, as context only (bf16 output)
-    ctx = None
-    if not args.no_context:
-        Ad, Bd = As[0], Bs[0]
-        for _ in range(3):
-            torch.matmul(Ad, Bd)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            torch.matmul(Ad, Bd)
-        e1.record()
-        torch.cuda.synchronize()
-        ctx = round(e0.elapsed_time(e1) / 10 * 1e3, 1)
+        achieved = tot_w / tot_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                    "per_launch_bytes": {str(r): op.stage_work(r)[stage][1] for r in red}}
+    roofline = {"kernel": f"{kname}, stage '{stage}', mean over rho in {red}", **roofline,
+                "avg_launch_us": round(tot_s / len(red) * 1e6, 2)}
 
     line = {
         "metric": METRIC,
@@ -288,22 +428,67 @@ def bench_matmul(args, name, A_cpu, B_cpu, rhos, desc):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms_total / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name, "shape": desc, "rhos": list(rhos),
-                   "k": {str(r): ks[r] for r in rhos}, "copies_rotated": copies},
-        "latency_us": lat,
-        "latency_note": "per-op mean of back-to-back rmm_matmul calls; kernel times below come from stage events",
+        "config": {"workload": op.name, **op.shape(), "rhos": list(rhos),
+                   "k": {str(r): op.ks[r] for r in rhos}, "copies_rotated": copies},
+        "latency_us": {str(r): round(op_us[r], 2) for r in rhos},
+        "latency_note": "per-op mean of back-to-back calls; kernel times below come from stage events",
         "speedup_vs_dense": speed,
         "kernels": per_kernel,
         "roofline": roofline,
-        "hipblaslt_dense_bf16out_us_context": ctx,
     }
     return line
+
+
+def hipblaslt_context(op):
+    """hipBLASLt dense time at the same shape (bf16 output), as context only."""
+    import torch
+    if not isinstance(op, MatmulOp):
+        return None
+    Ad, Bd = op.As[0], op.Bs[0]
+    for _ in range(3):
+        torch.matmul(Ad, Bd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(Ad, Bd)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) / 10 * 1e3, 1)
+
+
+WORKLOADS = ("mlp_down_8b", "mlp_up_70b", "decode_qkv_8b", "gqa_qk_8b", "attn_pv_70b")
+
+
+def make_op(name, copies):
+    import synth
+    if name == "mlp_down_8b":
+        w = synth.mlp_down()
+        return MatmulOp(name, w.tensors["A"], w.tensors["B"], (0.9, 0.7, 0.5, 1.0),
+                        "A 4096x14336 bf16 (log-normal channel scale, 1% outlier channels x20) @ "
+                        "B 14336x4096 bf16 -> Y fp32", copies)
+    if name == "mlp_up_70b":
+        w = synth.mlp_up()
+        return MatmulOp(name, w.tensors["A"], w.tensors["B"], (0.8, 1.0),
+                        "A 2048x8192 bf16 @ B 8192x28672 bf16 -> Y fp32", copies)
+    if name == "decode_qkv_8b":
+        w = synth.decode_qkv()
+        return MatmulOp(name, w.tensors["A"], w.tensors["B"], (0.8, 1.0),
+                        "A 8x4096 bf16 @ B 4096x6144 bf16 -> Y fp32 (decode GEMV over kept rows)", copies)
+    if name == "gqa_qk_8b":
+        w = synth.gqa_qk()
+        return QkOp(name, w.tensors["Q"], w.tensors["K"], (0.5, 1.0),
+                    "Q (32,4096,128) bf16, K (8,4096,128) bf16 (GQA group 4) -> S (32,4096,4096) fp32", copies)
+    w = synth.attn_pv()
+    return PvOp(name, w.tensors["P"], w.tensors["V"], (0.5, 1.0),
+                "P (64,512,8192) fp32 row-softmax, V (8,8192,128) bf16 (GQA group 8) -> O (64,512,128) fp32",
+                copies)
 
 
 def main():
@@ -311,8 +496,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mlp_down_8b", choices=["mlp_down_8b", "mlp_up_70b", "decode_qkv_8b"])
-    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--workload", default="mlp_down_8b", choices=WORKLOADS)
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated (default: enough to exceed the "
+                                                          "256 MB Infinity Cache)")
     ap.add_argument("--stage-iters", type=int, default=10, help="calls per rho with stage events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the hipBLASLt context timing")
@@ -322,24 +508,14 @@ def main():
         _die_multi_gpu(max(args.gpus, world))
 
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    import synth
-
-    if args.workload == "mlp_down_8b":
-        w = synth.mlp_down()
-        rhos = (0.9, 0.7, 0.5, 1.0)
-        desc = "A 4096x14336 bf16 (log-normal channel scale, 1% outlier channels x20) @ B 14336x4096 bf16 -> Y fp32"
-    elif args.workload == "mlp_up_70b":
-        w = synth.mlp_up()
-        rhos = (0.8, 1.0)
-        desc = "A 2048x8192 bf16 @ B 8192x28672 bf16 -> Y fp32"
-    else:
-        w = synth.decode_qkv()
-        rhos = (0.8, 1.0)
-        desc = "A 8x4096 bf16 @ B 4096x6144 bf16 -> Y fp32 (decode GEMV over kept rows)"
-    A_cpu, B_cpu = w.tensors["A"], w.tensors["B"]
-    line = bench_matmul(args, args.workload, A_cpu, B_cpu, rhos, desc)
+    copies = args.copies
+    if copies <= 0:
+        copies = {"gqa_qk_8b": 8, "attn_pv_70b": 2}.get(args.workload, 4)
+    op = make_op(args.workload, copies)
+    line = run(args, op)
+    line["hipblaslt_dense_bf16out_us_context"] = None if args.no_context else hipblaslt_context(op)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_matmul(A_cpu, B_cpu, rhos, sample_rows=min(1024, A_cpu.shape[0]))
+        line["cpu_baseline"] = op.cpu_baseline()
     print(json.dumps(line), flush=True)
 
 

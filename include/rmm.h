@@ -136,6 +136,15 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
                     int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho,
                     int32_t* idx, void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* rmm_qk with the five stage events of rmm_matmul_timed recorded on `stream`
+ * ([0] start, [1] after the column energies, [2] after TopK, [3] after the
+ * packs of Q and K, [4] after the batched product).  Same arguments,
+ * results and errors as rmm_qk; stage_events and its entries non-NULL. */
+rmm_status_t rmm_qk_timed(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
+                          int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho,
+                          int32_t* idx, void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* stage_events);
+
 /* ---------------------------------------------------------------------
  * rmm_pv: per head h, O[h] = P[h][:, I_h] V[g(h)][I_h, :] with I_h the
  * ceil(rho tk) key positions of largest column norm of P[h] over its tq
@@ -143,7 +152,12 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
  *   P   element (h, q, t) at P[h*p_hs + q*p_ts + t], p_dtype fp32 or bf16.
  *   V   element (g, t, c) at V[g*v_hs + t*v_ts + c], v_dtype bf16 or fp32.
  *       bf16 V uses the matrix cores and rounds P to bf16 (nearest even);
- *       fp32 V requires fp32 P and runs in fp32.
+ *       fp32 V requires fp32 P and runs in fp32.  With bf16 V, P 16-byte
+ *       aligned, tk a multiple of 64 and at least one key in eight kept,
+ *       the product reads P in place over all tk positions with the
+ *       dropped rows of V read as zeros (the same sum over I_h; P is
+ *       bandwidth-bound either way); otherwise the kept columns of P are
+ *       packed first.
  *   idx [h][k] int32, each row ascending, k = rmm_k(rho, tk).
  *   O   [h][tq][dv] contiguous, o_dtype fp32 or bf16.
  * Source: hackcv.com, Component mapping (PV optionally over token
@@ -154,6 +168,16 @@ size_t rmm_pv_workspace(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dty
 rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
                     int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
                     int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* rmm_pv with the five stage events of rmm_matmul_timed recorded on `stream`
+ * ([0] start, [1] after the column energies of P, [2] after TopK, [3] after
+ * the pack of P when the path packs it, [4] after the batched product).
+ * Same arguments, results and errors as rmm_pv; stage_events and its
+ * entries non-NULL. */
+rmm_status_t rmm_pv_timed(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
+                          int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
+                          int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* stage_events);
 
 #ifdef __cplusplus
 }

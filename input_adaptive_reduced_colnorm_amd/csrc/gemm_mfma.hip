@@ -8,11 +8,14 @@
 // runs over ceil(rho d) indices and nothing else.  The same kernel with the
 // identity index is the rho = 1 dense baseline.
 //
-// Tiling: BM x BN x 64 per workgroup of 4 waves (2 x 2), each wave owning a
-// (BM/2) x (BN/2) block of 32x32 accumulators fed by v_mfma_f32_32x32x16_bf16.
-// Global -> register prefetch of the next K tile overlaps the MFMAs of the
-// current one; LDS is double buffered with one barrier per K tile.  LDS rows
-// are 128 bytes (64 bf16 along K) with an XOR swizzle of the 16-byte chunks.
+// Tiling: BM x BN x 64 per workgroup.  Large products use 256 x 256 tiles
+// over 8 waves (2 x 4, two waves per SIMD so that one wave's MFMAs cover the
+// other's LDS traffic and barrier); small ones 128 x 128 over 4 waves (2 x 2).
+// Each wave owns a block of 32x32 accumulators fed by
+// v_mfma_f32_32x32x16_bf16.  Global -> register prefetch of the next K tile
+// overlaps the MFMAs of the current one; LDS is double buffered with one
+// barrier per K tile.  LDS rows are 128 bytes (64 bf16 along K) with an XOR
+// swizzle of the 16-byte chunks.
 // B tiles that are K-major in memory (weights, V) are transposed in
 // registers in 8x8 blocks (v_perm) before they reach LDS.
 
@@ -74,7 +77,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // WAVES = 4: waves in a 2x2 grid, each (BM/2) x (BN/2).
 // WAVES = 8: waves in a 2x4 grid, each (BM/2) x (BN/4); two waves share a
 // SIMD so one wave's MFMAs cover the other's barrier and LDS latency.
-template <int BM, int BN, bool KMAJOR, bool GATHER, bool A_F32, int NBUF, int WAVES>
+template <int BM, int BN, bool KMAJOR, bool GATHER, bool A_F32, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs g) {
   constexpr int NT = 64 * WAVES;
   constexpr int WGN = WAVES / 2;                   // wave grid: 2 x WGN
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   constexpr int STAGE = (BM + BN) * 128;           // bytes per LDS stage
   constexpr int ES = A_F32 ? 4 : 2;                // A element size
   static_assert(B_OWNERS <= NT, "B blocks exceed the thread count");
-  __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -275,19 +278,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   __syncthreads();
 
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = NBUF == 1 ? 0 : (kt & 1);
+    const int cur = kt & 1;
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
     read_frags(cur, 0, a0, b0);
     read_frags(cur, 1, a1, b1);
     mfma_all(a0, b0);
-    if constexpr (NBUF == 2) {
-      // the other buffer was released by the barrier that ended kt - 1
-      if (kt + 1 < KT) {
-        store_tile(cur ^ 1);
-        if (kt + 2 < KT) {
-          load_tile(kt + 2);
-          if (kt + 3 < KT) load_idx(kt + 3);
-        }
+    // the other buffer was released by the barrier that ended kt - 1
+    if (kt + 1 < KT) {
+      store_tile(cur ^ 1);
+      if (kt + 2 < KT) {
+        load_tile(kt + 2);
+        if (kt + 3 < KT) load_idx(kt + 3);
       }
     }
     read_frags(cur, 2, a0, b0);
@@ -295,16 +296,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     read_frags(cur, 3, a1, b1);
     mfma_all(a0, b0);
     mfma_all(a1, b1);
-    if constexpr (NBUF == 1) {
-      if (kt + 1 < KT) {
-        __syncthreads();
-        store_tile(0);
-        if (kt + 2 < KT) {
-          load_tile(kt + 2);
-          if (kt + 3 < KT) load_idx(kt + 3);
-        }
-      }
-    }
     __syncthreads();
   }
 
@@ -333,18 +324,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   }
 }
 
-template <int BM, int BN, int NBUF, int WAVES>
+template <int BM, int BN, int WAVES>
 hipError_t dispatch(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(tiles, g.batch);
   const bool gather = g.idx != nullptr;
   if (g.b_kmajor) {
     if (gather)
-      gemm_bf16_kernel<BM, BN, true, true, false, NBUF, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
+      gemm_bf16_kernel<BM, BN, true, true, false, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
     else
-      gemm_bf16_kernel<BM, BN, true, false, false, NBUF, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
+      gemm_bf16_kernel<BM, BN, true, false, false, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
   } else {
-    gemm_bf16_kernel<BM, BN, false, false, false, NBUF, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
+    gemm_bf16_kernel<BM, BN, false, false, false, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
   }
   return hipGetLastError();
 }
@@ -355,36 +346,34 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   // Small-N / small-M products (per-head PV) use 128x128 tiles so that the
   // grid still covers the chip; large products use 256x256.
   const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-  const int KT = (g.K + BK - 1) / BK;
-  if (t256 >= 192 && g.N >= 256 && g.M >= 256) {
-    if (KT == 1) return dispatch<256, 256, 1, 4>(g, s);
-    return dispatch<256, 256, 2, 8>(g, s);
-  }
-  if (KT == 1) return dispatch<128, 128, 1, 4>(g, s);
-  return dispatch<128, 128, 2, 4>(g, s);
+  if (t256 >= 192 && g.N >= 256 && g.M >= 256) return dispatch<256, 256, 8>(g, s);
+  return dispatch<128, 128, 4>(g, s);
 }
 
-// Dense fp32-A variant (P of attention in fp32, rho = 1): A is read as fp32
-// and rounded to bf16 on its way into LDS.
-hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s) {
-  const int KT = (g.K + BK - 1) / BK;
-  const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-  if (t256 >= 192 && g.N >= 256 && g.M >= 256) {
-    const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
-    dim3 grid(tiles, g.batch);
-    if (g.b_kmajor)
-      gemm_bf16_kernel<256, 256, true, false, true, 2, 8><<<grid, 512, 0, s>>>(g);
+// fp32-A variant (P of attention in fp32): A is read as fp32 and rounded to
+// bf16 on its way into LDS.  With an index list the K-major B rows are
+// gathered (a -1 entry reads a zero row), which lets PV run over every key
+// position of P with the dropped rows of V masked to zero.
+template <int BM, int BN, int WAVES>
+void dispatch_af32(const GemmArgs& g, hipStream_t s) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  dim3 grid(tiles, g.batch);
+  if (g.b_kmajor) {
+    if (g.idx)
+      gemm_bf16_kernel<BM, BN, true, true, true, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
     else
-      gemm_bf16_kernel<256, 256, false, false, true, 2, 8><<<grid, 512, 0, s>>>(g);
+      gemm_bf16_kernel<BM, BN, true, false, true, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
   } else {
-    const int tiles = ((g.M + 127) / 128) * ((g.N + 127) / 128);
-    dim3 grid(tiles, g.batch);
-    if (g.b_kmajor)
-      gemm_bf16_kernel<128, 128, true, false, true, 2, 4><<<grid, 256, 0, s>>>(g);
-    else
-      gemm_bf16_kernel<128, 128, false, false, true, 2, 4><<<grid, 256, 0, s>>>(g);
+    gemm_bf16_kernel<BM, BN, false, false, true, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
   }
-  (void)KT;
+}
+
+hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s) {
+  const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+  if (t256 >= 192 && g.N >= 256 && g.M >= 256)
+    dispatch_af32<256, 256, 8>(g, s);
+  else
+    dispatch_af32<128, 128, 4>(g, s);
   return hipGetLastError();
 }
 

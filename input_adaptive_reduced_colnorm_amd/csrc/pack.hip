@@ -69,11 +69,66 @@ __global__ __launch_bounds__(256) void pack_kernel(const void* __restrict__ src,
   }
 }
 
+// Narrow rows (k_pad <= 256, e.g. the head features of attention): each lane
+// owns one 16-byte piece (8 kept positions) of an output row, so k_pad / 8
+// lanes cover a row and a workgroup covers 256 / (k_pad / 8) rows per pass.
+constexpr int kNarrowMax = 256;
+constexpr int kNarrowPasses = 8;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void pack_narrow_kernel(const void* __restrict__ src, int64_t src_hs,
+                                                          int64_t src_rs, int src_group,
+                                                          const int32_t* __restrict__ idx, int64_t idx_hs, int k,
+                                                          int k_pad, int rows, uint16_t* __restrict__ out,
+                                                          int64_t out_hs) {
+  const int b = blockIdx.y;
+  const int cpr = k_pad >> 3;                 // pieces per row, at most 32
+  const int rstep = 256 / cpr;                // rows per pass
+  if ((int)threadIdx.x >= rstep * cpr) return;
+  const int piece = threadIdx.x % cpr;
+  const int32_t* ib = idx + (size_t)b * idx_hs;
+  int cols[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = piece * 8 + e;
+    cols[e] = t < k ? ib[t] : -1;
+  }
+  const size_t sbase = (size_t)(b / src_group) * src_hs;
+  uint16_t* ob = out + (size_t)b * out_hs;
+  const int r0 = blockIdx.x * rstep * kNarrowPasses + threadIdx.x / cpr;
+#pragma unroll
+  for (int pass = 0; pass < kNarrowPasses; ++pass) {
+    const int r = r0 + pass * rstep;
+    if (r >= rows) break;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (cols[e] >= 0) {
+        const size_t off = sbase + (size_t)r * src_rs + cols[e];
+        const uint32_t h = BF16 ? ((const uint16_t*)src)[off] : f32_to_bf16(((const float*)src)[off]);
+        w[e >> 1] |= h << (16 * (e & 1));
+      }
+    }
+    *(i32x4*)(ob + (size_t)r * k_pad + piece * 8) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pack(const void* src, bool src_bf16, int64_t src_hs, int64_t src_rs, int src_group,
                        const int32_t* idx, int64_t idx_hs, int k, int k_pad, int batch, int rows, uint16_t* out,
                        int64_t out_hs, hipStream_t s) {
+  if (k_pad <= kNarrowMax) {
+    const int rows_per_wg = 256 / (k_pad / 8) * kNarrowPasses;
+    dim3 grid((rows + rows_per_wg - 1) / rows_per_wg, batch);
+    if (src_bf16)
+      pack_narrow_kernel<true><<<grid, 256, 0, s>>>(src, src_hs, src_rs, src_group, idx, idx_hs, k, k_pad, rows, out,
+                                                    out_hs);
+    else
+      pack_narrow_kernel<false><<<grid, 256, 0, s>>>(src, src_hs, src_rs, src_group, idx, idx_hs, k, k_pad, rows,
+                                                     out, out_hs);
+    return hipGetLastError();
+  }
   dim3 grid((k_pad + kPackT - 1) / kPackT, (rows + kPackRows - 1) / kPackRows, batch);
   if (src_bf16)
     pack_kernel<true><<<grid, 256, 0, s>>>(src, src_hs, src_rs, src_group, idx, idx_hs, k, k_pad, rows, out, out_hs);

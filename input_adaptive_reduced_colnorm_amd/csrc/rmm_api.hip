@@ -1,6 +1,7 @@
 // C ABI of librmm: argument checks, path planning, workspace carving and
 // kernel dispatch.  Every check runs before the first launch.
 
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -114,7 +115,8 @@ struct MatPlan {
   bool all = false;
   SelPlan sel;
   bool use_sel = false;
-  size_t off_pack = 0, off_ipad = 0, off_at = 0, off_dkeys = 0;
+  size_t off_pack = 0, off_ipad = 0, off_part = 0, off_dkeys = 0;
+  int gemv_splits = 1;
   size_t total = 0;
 };
 
@@ -133,10 +135,11 @@ MatPlan plan_matmul(int64_t n, int64_t d, int64_t m, int64_t lda, int64_t ldb, i
       plan_select(cv, p.sel, 1, n, d, bf16);
       p.use_sel = true;
     }
-  } else if (n <= kDecodeRows && p.k <= gemv_max_kept()) {
+  } else if (n <= kDecodeRows) {
     p.path = MatPath::kDecode;
-    if (d > topk_lds_capacity()) p.off_dkeys = cv.take((size_t)d * 4);
-    p.off_at = cv.take((size_t)p.k_pad * 16 * 4);
+    if (!p.all && d > topk_lds_capacity()) p.off_dkeys = cv.take((size_t)d * 4);
+    p.gemv_splits = gemv_splits((int)p.k, (int)m);
+    if (p.gemv_splits > 1) p.off_part = cv.take((size_t)p.gemv_splits * n * m * 4);
   } else {
     const bool a_direct = p.all && a_ptr_ok && lda % 8 == 0 && d % kKTile == 0;
     if (a_direct) {
@@ -289,15 +292,20 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
       break;
     }
     case MatPath::kDecode: {
-      float* at = (float*)(ws + p.off_at);
-      RMM_LAUNCH(launch_decode_select(A, bf16, lda, (int)n, (int)d, (int)p.k, (int)p.k_pad, p.all, idx, nullptr, at,
-                                      d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, s));
+      // rho < 1: one selection kernel; rho = 1: the GEMV runs over all rows
+      // of B and writes the identity index itself
+      if (!p.all)
+        RMM_LAUNCH(launch_decode_select(A, bf16, lda, (int)n, (int)d, (int)p.k, idx, nullptr,
+                                        d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, s));
       RMM_LAUNCH(mk.mark(1));
       RMM_LAUNCH(mk.mark(2));
       RMM_LAUNCH(mk.mark(3));
       GemvArgs g{};
-      g.a_t = at; g.B = (const uint16_t*)B; g.ldb = ldb; g.idx = idx;
+      g.A = A; g.a_bf16 = bf16; g.lda = lda;
+      g.B = (const uint16_t*)B; g.ldb = ldb;
+      g.idx = p.all ? nullptr : idx; g.idx_out = p.all ? idx : nullptr;
       g.k = (int)p.k; g.n = (int)n; g.m = (int)m;
+      g.partial = (float*)(ws + p.off_part); g.splits = p.gemv_splits;
       g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;
       RMM_LAUNCH(launch_gemv(g, s));
       break;
@@ -405,9 +413,12 @@ size_t rmm_qk_workspace(int64_t hq, int64_t tq, int64_t tk, int64_t dh, int dtyp
   return plan_qk(hq, tq, tk, dh, dtype, rho, false).total;
 }
 
-rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
-                    int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho, int32_t* idx,
-                    void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
+                     int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho, int32_t* idx,
+                     void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                     void* const* stage_events) {
   if (!Q || !K || !idx || !S) return RMM_ERR_NULL;
   if (!rho_ok(rho)) return RMM_ERR_RHO;
   if (!dtype_ok(dtype) || !dtype_ok(s_dtype)) return RMM_ERR_DTYPE;
@@ -439,12 +450,16 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
   char* ws = (char*)workspace;
   const bool bf16 = dtype == RMM_BF16;
   const int group = (int)(hq / hkv);
+  const Marks mk{stage_events, s};
   clear_error();
+  RMM_LAUNCH(mk.mark(0));
   if (p.use_sel) {
-    RMM_LAUNCH(run_select(p.sel, ws, Q, bf16, q_hs, q_ts, (int)hq, tq, dh, p.k, idx, p.k, nullptr, s));
+    RMM_LAUNCH(run_select(p.sel, ws, Q, bf16, q_hs, q_ts, (int)hq, tq, dh, p.k, idx, p.k, nullptr, s, &mk));
   } else {
     RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, nullptr, 0, 0, s));
+    RMM_LAUNCH(mk.mark(1));
   }
+  RMM_LAUNCH(mk.mark(2));
   if (!p.mfma) {
     SimtArgs g{};
     g.A = Q; g.a_bf16 = false; g.a_bs = q_hs; g.a_rs = q_ts; g.a_cs = 1;
@@ -452,7 +467,9 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
     g.idx = p.all ? nullptr : idx; g.idx_bs = p.k;
     g.C = S; g.c_bf16 = s_dtype == RMM_BF16; g.c_bs = tq * tk; g.ldc = tk;
     g.M = (int)tq; g.N = (int)tk; g.k = (int)p.k; g.batch = (int)hq;
+    RMM_LAUNCH(mk.mark(3));
     RMM_LAUNCH(launch_gemm_simt(g, s));
+    RMM_LAUNCH(mk.mark(4));
     return RMM_OK;
   }
   GemmArgs g{};
@@ -478,8 +495,35 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
   g.idx = nullptr; g.idx_bs = 0;
   g.C = S; g.c_bs = tq * tk; g.ldc = tk; g.c_bf16 = s_dtype == RMM_BF16;
   g.M = (int)tq; g.N = (int)tk; g.batch = (int)hq; g.b_kmajor = false;
+  RMM_LAUNCH(mk.mark(3));
   RMM_LAUNCH(launch_gemm_bf16(g, s));
+  RMM_LAUNCH(mk.mark(4));
   return RMM_OK;
+}
+
+bool events_ok(void* const* ev) {
+  if (!ev) return false;
+  for (int i = 0; i < 5; ++i)
+    if (!ev[i]) return false;
+  return true;
+}
+
+}  // namespace
+
+rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
+                    int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho, int32_t* idx,
+                    void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return qk_impl(Q, K, dtype, hq, hkv, tq, tk, dh, q_hs, q_ts, k_hs, k_ts, rho, idx, S, s_dtype, workspace,
+                 workspace_bytes, stream, nullptr);
+}
+
+rmm_status_t rmm_qk_timed(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
+                          int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho, int32_t* idx,
+                          void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* stage_events) {
+  if (!events_ok(stage_events)) return RMM_ERR_NULL;
+  return qk_impl(Q, K, dtype, hq, hkv, tq, tk, dh, q_hs, q_ts, k_hs, k_ts, rho, idx, S, s_dtype, workspace,
+                 workspace_bytes, stream, stage_events);
 }
 
 // --------------------------------- pv ---------------------------------------
@@ -488,11 +532,18 @@ namespace {
 
 struct PvPlan {
   int64_t k = 0, k_pad = 0;
-  bool all = false, mfma = false, direct = false, use_sel = false;
+  bool all = false, mfma = false, direct = false, masked = false, use_sel = false;
   SelPlan sel;
-  size_t off_p = 0, off_ipad = 0, total = 0;
+  size_t off_p = 0, off_ipad = 0, off_mask = 0, total = 0;
 };
 
+// PV reads P once for the column energies whatever the path; the product
+// then either packs the kept columns of P (a second read of P that touches
+// every sector anyway once more than about one column in eight is kept) or
+// runs over all key positions of P in place with the dropped rows of V read
+// as zeros.  The second form ("masked") is used when at least one key in
+// eight is kept and P can be read in place; both compute the same sum
+// over the kept positions.
 PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho, bool v_ok,
                bool direct_ok) {
   PvPlan p;
@@ -507,7 +558,10 @@ PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v
   }
   if (p.mfma) {
     p.direct = p.all && direct_ok;
-    if (!p.direct) {
+    p.masked = !p.all && direct_ok && p.k * 8 >= tk;
+    if (p.masked) {
+      p.off_mask = cv.take((size_t)h * tk * 4);
+    } else if (!p.direct) {
       p.off_ipad = cv.take((size_t)h * p.k_pad * 4);
       p.off_p = cv.take((size_t)h * tq * p.k_pad * 2);
     }
@@ -522,12 +576,18 @@ size_t rmm_pv_workspace(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dty
   if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(tk) || !dim_ok(dv) || !dtype_ok(p_dtype) || !dtype_ok(v_dtype) ||
       !rho_ok(rho))
     return 0;
-  return plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, true, false).total;
+  // upper bound over the paths the call may take (alignment is not known here)
+  const size_t a = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, true, false).total;
+  const size_t b = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, true, true).total;
+  return a > b ? a : b;
 }
 
-rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
-                    int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
-                    int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
+                     int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
+                     int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                     void* const* stage_events) {
   if (!P || !V || !idx || !O) return RMM_ERR_NULL;
   if (!rho_ok(rho)) return RMM_ERR_RHO;
   if (!dtype_ok(p_dtype) || !dtype_ok(v_dtype) || !dtype_ok(o_dtype)) return RMM_ERR_DTYPE;
@@ -545,7 +605,7 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
   const PvPlan p = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, v_ok, direct_ok);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
     return RMM_ERR_WORKSPACE;
-  if (p.mfma && !p.direct && tq * p.k_pad * 2 > kMaxOperandBytes) return RMM_ERR_SHAPE;
+  if (p.mfma && !p.direct && !p.masked && tq * p.k_pad * 2 > kMaxOperandBytes) return RMM_ERR_SHAPE;
   const Span sp = span3(P, h, p_hs, tq, p_ts, tk, pe), sv = span3(V, hkv, v_hs, tk, v_ts, dv, ve);
   const Span si = span3(idx, 1, 0, h, p.k, p.k, 4);
   const Span so = span3(O, h, tq * dv, tq, dv, dv, elt_size(o_dtype));
@@ -558,14 +618,28 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int group = (int)(h / hkv);
+  const Marks mk{stage_events, s};
   clear_error();
-  int32_t* ipad = p.mfma && !p.direct ? (int32_t*)(ws + p.off_ipad) : nullptr;
+  RMM_LAUNCH(mk.mark(0));
+  const bool packed = p.mfma && !p.direct && !p.masked;
+  int32_t* ipad = packed ? (int32_t*)(ws + p.off_ipad) : nullptr;
+  int32_t* kmask = p.masked ? (int32_t*)(ws + p.off_mask) : nullptr;
+  uint16_t* pp = packed ? (uint16_t*)(ws + p.off_p) : nullptr;
   if (p.use_sel) {
-    RMM_LAUNCH(run_select(p.sel, ws, P, !p_f32, p_hs, p_ts, (int)h, tq, tk, p.k, idx, p.k, nullptr, s, nullptr, ipad,
-                          ipad ? p.k_pad : 0));
+    float* partial = (float*)(ws + p.sel.off_partial);
+    RMM_LAUNCH(launch_colnorm(P, !p_f32, p_hs, p_ts, (int)h, (int)tq, (int)tk, p.sel.splits, partial, s));
+    RMM_LAUNCH(mk.mark(1));
+    RMM_LAUNCH(launch_topk(partial, (int)h, p.sel.splits, (int)tk, (int)p.k, idx, p.k, ipad, p.k_pad,
+                           ipad ? (int)p.k_pad : 0, nullptr, tk,
+                           p.sel.gkeys ? (uint32_t*)(ws + p.sel.off_gkeys) : nullptr, s, kmask, tk));
   } else {
     RMM_LAUNCH(launch_iota(idx, p.k, (int)h, (int)tk, ipad, ipad ? p.k_pad : 0, ipad ? (int)p.k_pad : 0, s));
+    RMM_LAUNCH(mk.mark(1));
   }
+  RMM_LAUNCH(mk.mark(2));
+  if (pp)
+    RMM_LAUNCH(launch_pack(P, !p_f32, p_hs, p_ts, 1, idx, p.k, (int)p.k, (int)p.k_pad, (int)h, (int)tq, pp,
+                           tq * p.k_pad, s));
   if (!p.mfma) {
     SimtArgs g{};
     g.A = P; g.a_bf16 = !p_f32; g.a_bs = p_hs; g.a_rs = p_ts; g.a_cs = 1;
@@ -573,7 +647,9 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
     g.idx = p.all ? nullptr : idx; g.idx_bs = p.k;
     g.C = O; g.c_bf16 = o_dtype == RMM_BF16; g.c_bs = tq * dv; g.ldc = dv;
     g.M = (int)tq; g.N = (int)dv; g.k = (int)p.k; g.batch = (int)h;
+    RMM_LAUNCH(mk.mark(3));
     RMM_LAUNCH(launch_gemm_simt(g, s));
+    RMM_LAUNCH(mk.mark(4));
     return RMM_OK;
   }
   GemmArgs g{};
@@ -581,25 +657,44 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
   g.b_bytes = (uint32_t)(((tk - 1) * v_ts + dv) * 2);
   g.C = O; g.c_bs = tq * dv; g.ldc = dv; g.c_bf16 = o_dtype == RMM_BF16;
   g.M = (int)tq; g.N = (int)dv; g.batch = (int)h; g.b_kmajor = true;
-  if (p.direct) {
+  if (p.direct || p.masked) {
     g.A = (const uint16_t*)P; g.a_bs = p_hs; g.lda = p_ts;
     g.a_bytes = (uint32_t)(((tq - 1) * p_ts + tk) * pe);
-    g.idx = nullptr; g.idx_bs = 0; g.K = (int)tk;
+    g.idx = kmask; g.idx_bs = p.masked ? tk : 0; g.K = (int)tk;
+    RMM_LAUNCH(mk.mark(3));
     if (p_f32) {
       RMM_LAUNCH(launch_gemm_bf16_af32(g, s));
     } else {
       RMM_LAUNCH(launch_gemm_bf16(g, s));
     }
+    RMM_LAUNCH(mk.mark(4));
     return RMM_OK;
   }
-  uint16_t* pp = (uint16_t*)(ws + p.off_p);
-  RMM_LAUNCH(launch_pack(P, !p_f32, p_hs, p_ts, 1, idx, p.k, (int)p.k, (int)p.k_pad, (int)h, (int)tq, pp,
-                         tq * p.k_pad, s));
   g.A = pp; g.a_bs = tq * p.k_pad; g.lda = p.k_pad;
   g.a_bytes = (uint32_t)(tq * p.k_pad * 2);
   g.idx = ipad; g.idx_bs = p.k_pad; g.K = (int)p.k_pad;
+  RMM_LAUNCH(mk.mark(3));
   RMM_LAUNCH(launch_gemm_bf16(g, s));
+  RMM_LAUNCH(mk.mark(4));
   return RMM_OK;
+}
+
+}  // namespace
+
+rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
+                    int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
+                    int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return pv_impl(P, p_dtype, V, v_dtype, h, hkv, tq, tk, dv, p_hs, p_ts, v_hs, v_ts, rho, idx, O, o_dtype, workspace,
+                 workspace_bytes, stream, nullptr);
+}
+
+rmm_status_t rmm_pv_timed(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
+                          int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
+                          int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                          void* const* stage_events) {
+  if (!events_ok(stage_events)) return RMM_ERR_NULL;
+  return pv_impl(P, p_dtype, V, v_dtype, h, hkv, tq, tk, dv, p_hs, p_ts, v_hs, v_ts, rho, idx, O, o_dtype, workspace,
+                 workspace_bytes, stream, stage_events);
 }
 
 }  // extern "C"

@@ -16,11 +16,14 @@ int colnorm_splits(int heads, int n, int d, bool elt_bf16);
 
 // TopK over the summed partials of each head: writes idx[h][0..k) ascending,
 // optionally the same list padded with -1 to k_pad entries (pad[h][...]),
-// optional scores[h][j] = sqrt(energy).  gkeys: [heads][d] uint32 scratch,
-// used only when d exceeds the LDS key capacity (may be null otherwise).
+// optional scores[h][j] = sqrt(energy), and optionally the keep mask
+// mask[h][j] = j if column j is kept else -1 (all d entries).  gkeys:
+// [heads][d] uint32 scratch, used only when d exceeds the LDS key capacity
+// (may be null otherwise).
 hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k,
                        int32_t* idx, int64_t idx_hs, int32_t* pad, int64_t pad_hs, int k_pad,
-                       float* scores, int64_t scores_hs, uint32_t* gkeys, hipStream_t s);
+                       float* scores, int64_t scores_hs, uint32_t* gkeys, hipStream_t s,
+                       int32_t* mask = nullptr, int64_t mask_hs = 0);
 int topk_lds_capacity();
 
 // Writes idx[h][t] = t for t < d (the rho = 1 selection), and optionally
@@ -52,7 +55,8 @@ struct GemmArgs {
   uint32_t a_bytes, b_bytes;  // per-batch extents (bytes) for the buffer descriptors
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
-// Same product with A given as fp32 (rounded to bf16 while staged), no gather.
+// Same product with A given as fp32 (rounded to bf16 while staged); a gather
+// list (idx) is honoured for K-major B only.
 hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s);
 
 // Generic FMA GEMM over strided, optionally gathered operands (fp32 or bf16
@@ -67,21 +71,26 @@ struct SimtArgs {
 };
 hipError_t launch_gemm_simt(const SimtArgs& g, hipStream_t s);
 
-// Decode path (n <= 16): fused energy + TopK + transposed gather of A into
-// a_t[t][16] (fp32, zero padded past n and past k up to k_pad).
-hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int k_pad,
-                                bool all, int32_t* idx, float* scores, float* a_t, uint32_t* gkeys, hipStream_t s);
+// Decode path (n <= 16): one workgroup computes the column energies over the
+// n rows and selects the k kept columns into idx (ascending).
+hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int32_t* idx,
+                                float* scores, uint32_t* gkeys, hipStream_t s);
 
-// GEMV over the kept rows of B (all kept rows per workgroup, fixed-order
-// reduction).  k must not exceed gemv_max_kept().
+// GEMV over the kept rows of B, split into `splits` slices of kept rows
+// (gemv_splits) whose partial sums partial[splits][n][m] are added in slice
+// order by a second kernel (splits == 1 writes Y directly).  A is read in
+// place (n <= 16 rows).  idx == nullptr means the identity (dense), and then
+// idx_out (if not null) receives 0..k-1.  m must be a multiple of 8.
 struct GemvArgs {
-  const float* a_t;     // [k][16]
+  const void* A; bool a_bf16; int64_t lda;
   const uint16_t* B; int64_t ldb;
-  const int32_t* idx;   // kept rows (ascending)
+  const int32_t* idx;
+  int32_t* idx_out;
   int k, n, m;
+  float* partial; int splits;
   void* Y; bool y_bf16; int64_t ldy;
 };
+int gemv_splits(int k, int m);
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);
-int gemv_max_kept();
 
 }  // namespace rmm

@@ -126,7 +126,7 @@ constexpr int kHistBins = 2048;  // 11-bit radix digits
 constexpr int kChunk = (kKeyCap + kSelThreads - 1) / kSelThreads;  // keys per thread held in registers
 
 struct SelShared {
-  uint32_t hist[kHistBins];
+  uint32_t hist[3 * kHistBins];   // one histogram per radix pass
   uint32_t misc[4];
   uint32_t wave_tot[kSelWaves][2];
 };
@@ -170,39 +170,60 @@ __device__ __forceinline__ void load_chunk(const uint32_t* keys, int d, KeyChunk
 }
 
 // Finds the k-th largest key: on return *T is its value and *rem the number
-// of keys equal to T that belong to the kept set (the lowest-indexed ones).
-// Three MSB-first radix passes (11, 11, 10 bits) with integer LDS
-// histograms; 11-bit first digits spread the exponents of the fp32 energies
-// over many buckets, and the bucket holding the k-th key is found with a
-// block-wide scan from the top bucket down.
+// of keys equal to T that belong to the kept set (the lowest-indexed ones;
+// 0xffffffff means every key equal to T is kept).  MSB-first radix passes
+// with integer LDS histograms of up to 11-bit digits.  The digits start
+// below the leading bits that all keys share (fp32 energies of similar
+// magnitude share sign and upper exponent bits), so the first histogram is
+// spread over many buckets instead of a few contended ones; all histograms
+// are cleared up front, and the passes stop as soon as the bucket holding
+// the k-th key is kept whole.
 __device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0, rem = (uint32_t)k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t k_or = 0u, k_and = 0xffffffffu;
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t nb = pass == 2 ? 1024u : 2048u;
-    for (int i = tid; i < (int)nb; i += kSelThreads) sh.hist[i] = 0;
-    __syncthreads();
+  for (int i = 0; i < kChunk; ++i)
+    if (i < kc.cnt) {
+      k_or |= kc.key[i];
+      k_and &= kc.key[i];
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    k_or |= __shfl_xor(k_or, o, 64);
+    k_and &= __shfl_xor(k_and, o, 64);
+  }
+  for (int i = tid; i < 3 * kHistBins; i += kSelThreads) sh.hist[i] = 0;
+  if (lane == 0) {
+    sh.wave_tot[wave][0] = k_or;
+    sh.wave_tot[wave][1] = k_and;
+  }
+  __syncthreads();
+  k_or = 0u;
+  k_and = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    k_or |= sh.wave_tot[w][0];
+    k_and &= sh.wave_tot[w][1];
+  }
+  const uint32_t diff = k_or ^ k_and;        // bits that differ between some keys
+  int hi = diff ? 32 - __clz(diff) : 0;      // bits below hi still to resolve
+  uint32_t mask = hi == 32 ? 0u : ~((1u << hi) - 1u);
+  uint32_t prefix = k_and & mask;            // shared leading bits
+  uint32_t rem = (uint32_t)k;
+  for (int pass = 0; hi > 0; ++pass) {
+    const int w = hi < 11 ? hi : 11;
+    const int shift = hi - w;
+    const uint32_t nb = 1u << w;
+    uint32_t* hist = sh.hist + pass * kHistBins;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       const uint32_t key = kc.key[i];
-      if (i < kc.cnt && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+      if (i < kc.cnt && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
-    // thread t owns the buckets nb-1-2t and nb-2-2t (one bucket, nb-1-t,
-    // when nb == 1024), counted from the top
-    uint32_t c0, c1 = 0;
-    int b0, b1 = -1;
-    if (nb == 2048u) {
-      b0 = (int)nb - 1 - 2 * tid;
-      b1 = b0 - 1;
-      c0 = sh.hist[b0];
-      c1 = sh.hist[b1];
-    } else {
-      b0 = (int)nb - 1 - tid;
-      c0 = sh.hist[b0];
-    }
+    // thread t owns the buckets nb-1-2t and nb-2-2t, counted from the top
+    const int b0 = (int)nb - 1 - 2 * tid, b1 = b0 - 1;
+    const uint32_t c0 = b0 >= 0 ? hist[b0] : 0u, c1 = b1 >= 0 ? hist[b1] : 0u;
     uint32_t incl = c0 + c1, dummy = 0;
     block_incl_scan2(incl, dummy, sh);
     const uint32_t excl = incl - (c0 + c1);
@@ -210,17 +231,25 @@ __device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32
       if (excl + c0 >= rem) {
         sh.misc[0] = (uint32_t)b0;
         sh.misc[1] = rem - excl;
+        sh.misc[2] = c0;
       } else {
         sh.misc[0] = (uint32_t)b1;
         sh.misc[1] = rem - excl - c0;
+        sh.misc[2] = c1;
       }
     }
     __syncthreads();
-    const uint32_t b = sh.misc[0];
+    const uint32_t b = sh.misc[0], cnt = sh.misc[2];
     rem = sh.misc[1];
     prefix |= b << shift;
     mask |= (nb - 1) << shift;
-    __syncthreads();
+    hi = shift;
+    if (cnt == rem) {
+      // every key of this bucket is kept: keep all keys >= its lowest value
+      *T = prefix;
+      *rem_out = 0xffffffffu;
+      return;
+    }
   }
   *T = prefix;
   *rem_out = rem;
@@ -228,7 +257,8 @@ __device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32
 
 // Ordered compaction: every thread owns a contiguous index chunk; a block
 // scan of (#greater, #equal) fixes each thread's output position, so the kept
-// indices come out ascending.  emit(pos, j) is called once per kept index.
+// indices come out ascending.  emit(take, pos, j) is called once for every
+// index j of the chunk, in order; pos is the output position when take.
 template <typename Emit>
 __device__ void compact_ascending(const KeyChunk& kc, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
   uint32_t n_gt = 0, n_eq = 0;
@@ -252,7 +282,8 @@ __device__ void compact_ascending(const KeyChunk& kc, uint32_t T, uint32_t rem, 
         take = eq_seen < rem;
         ++eq_seen;
       }
-      if (take) emit(pos++, kc.j0 + i);
+      emit(take, pos, kc.j0 + i);
+      pos += take;
     }
   }
 }
@@ -327,7 +358,8 @@ __device__ void compact_ascending_big(const uint32_t* keys, int d, uint32_t T, u
       take = eq_seen < rem;
       ++eq_seen;
     }
-    if (take) emit(pos++, j);
+    emit(take, pos, j);
+    pos += take;
   }
 }
 
@@ -336,8 +368,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
                                                            int32_t* __restrict__ idx, int64_t idx_hs,
                                                            int32_t* __restrict__ pad, int64_t pad_hs, int k_pad,
                                                            float* __restrict__ scores, int64_t scores_hs,
+                                                           int32_t* __restrict__ mask, int64_t mask_hs,
                                                            uint32_t* __restrict__ gkeys) {
   __shared__ uint32_t s_keys[LDS_KEYS ? kKeyCap : 1];
+  __shared__ int32_t s_out[LDS_KEYS ? kKeyCap : 1];
   __shared__ SelShared sh;
   const int head = blockIdx.x;
   const float* P = partial + (size_t)head * splits * d;
@@ -386,20 +420,85 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   int32_t* po = pad ? pad + (size_t)head * pad_hs : nullptr;
   if (po)
     for (int t = k + threadIdx.x; t < k_pad; t += kSelThreads) po[t] = -1;
-  auto emit = [&](uint32_t pos, int j) {
-    out[pos] = j;
-    if (po) po[pos] = j;
+  int32_t* mo = mask ? mask + (size_t)head * mask_hs : nullptr;
+  auto emit = [&](bool take, uint32_t pos, int j) {
+    if (take) {
+      out[pos] = j;
+      if (po) po[pos] = j;
+    }
+    if (mo) mo[j] = take ? j : -1;
   };
   uint32_t T, rem;
   if constexpr (LDS_KEYS) {
+    // the kept list is assembled in LDS and written out coalesced; the keys
+    // now live in registers, so s_keys takes the keep flags
     KeyChunk kc;
     load_chunk(keys, d, kc);
     radix_threshold(kc, k, sh, &T, &rem);
-    compact_ascending(kc, T, rem, sh, emit);
+    compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j) {
+      if (take) s_out[pos] = j;
+      s_keys[j] = take;
+    });
+    __syncthreads();
+    for (int t = threadIdx.x; t < k; t += kSelThreads) {
+      const int j = s_out[t];
+      out[t] = j;
+      if (po) po[t] = j;
+    }
+    if (mo)
+      for (int j = threadIdx.x; j < d; j += kSelThreads) mo[j] = s_keys[j] ? j : -1;
   } else {
     radix_threshold_big(keys, d, k, sh, &T, &rem);
     compact_ascending_big(keys, d, T, rem, sh, emit);
   }
+}
+
+// Small selections (d <= 256, e.g. the head features of attention): one
+// 256-thread workgroup per head; thread j ranks its key against all d keys
+// (higher key first, lower index first among equal keys), keeps it when the
+// rank is below k, and writes it at the count of kept columns before it.
+constexpr int kSmallD = 256;
+
+__global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __restrict__ partial, int splits, int d,
+                                                             int k, int32_t* __restrict__ idx, int64_t idx_hs,
+                                                             int32_t* __restrict__ pad, int64_t pad_hs, int k_pad,
+                                                             float* __restrict__ scores, int64_t scores_hs,
+                                                             int32_t* __restrict__ mask, int64_t mask_hs) {
+  __shared__ uint32_t s_keys[kSmallD];
+  __shared__ int s_wave[kSmallD / 64];
+  const int head = blockIdx.x;
+  const int j = threadIdx.x;
+  const float* P = partial + (size_t)head * splits * d;
+  float q = 0.f;
+  if (j < d) {
+    for (int s = 0; s < splits; ++s) q += P[(size_t)s * d + j];   // split order, as in topk_kernel
+    if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q);
+  }
+  const uint32_t key = __float_as_uint(q);
+  s_keys[j] = key;
+  __syncthreads();
+  int rank = 0;
+  for (int i = 0; i < d; ++i) {
+    const uint32_t v = s_keys[i];
+    rank += (v > key) || (v == key && i < j);
+  }
+  const bool keep = j < d && rank < k;
+  const uint64_t ballot = __ballot(keep);
+  const int lane = j & 63, wave = j >> 6;
+  const int before = __popcll(ballot & ((1ull << lane) - 1ull));
+  if (lane == 0) s_wave[wave] = __popcll(ballot);
+  __syncthreads();
+  int pos = before;
+  for (int w = 0; w < wave; ++w) pos += s_wave[w];
+  int32_t* out = idx + (size_t)head * idx_hs;
+  int32_t* po = pad ? pad + (size_t)head * pad_hs : nullptr;
+  if (keep) {
+    out[pos] = j;
+    if (po) po[pos] = j;
+  }
+  if (mask && j < d) mask[(size_t)head * mask_hs + j] = keep ? j : -1;
+  if (po)
+    for (int t = k + j; t < k_pad; t += kSmallD) po[t] = -1;
 }
 
 __global__ void iota_kernel(int32_t* idx, int64_t idx_hs, int d, int32_t* pad, int64_t pad_hs, int k_pad) {
@@ -409,17 +508,16 @@ __global__ void iota_kernel(int32_t* idx, int64_t idx_hs, int d, int32_t* pad, i
 }
 
 // ---------------------------------------------------------------------------
-// Decode selection (n <= 16 rows): one workgroup computes the energies,
-// selects, and writes a_t[t][r] = A[r][idx[t]] (fp32, rows padded to 16),
-// so the GEMV streams only kept rows of B.
+// Decode selection (n <= 16 rows): one workgroup computes the energies over
+// the n rows and selects into idx; the GEMV then reads A[:, I] itself.
 // ---------------------------------------------------------------------------
 template <bool BF16, bool LDS_KEYS>
-__global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* __restrict__ A_, int64_t lda, int n, int d,
-                                                                    int k, int k_pad, int all, int32_t* __restrict__ idx,
-                                                                    float* __restrict__ scores, float* __restrict__ a_t,
+__global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* __restrict__ A_, int64_t lda, int n,
+                                                                    int d, int k, int32_t* __restrict__ idx,
+                                                                    float* __restrict__ scores,
                                                                     uint32_t* __restrict__ gkeys) {
   __shared__ uint32_t s_keys[LDS_KEYS ? kKeyCap : 1];
-  __shared__ int32_t s_idx[LDS_KEYS ? kKeyCap : 1];
+  __shared__ int32_t s_out[LDS_KEYS ? kKeyCap : 1];
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   auto load = [&](int r, int j) -> float {
@@ -427,44 +525,19 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
     return BF16 ? bf16_to_f32(((const uint16_t*)A_)[off]) : ((const float*)A_)[off];
   };
   uint32_t* keys = LDS_KEYS ? s_keys : gkeys;
-  const bool need_keys = !all || scores != nullptr;
-  if (need_keys) {
-    // all 16 row loads of a column are issued before they are summed (rows
-    // in ascending order)
+  // all 16 row loads of a column are issued before they are summed (rows in
+  // ascending order)
 #pragma unroll 2
-    for (int j = tid; j < d; j += kSelThreads) {
-      float f[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) f[r] = r < n ? load(r, j) : 0.f;
-      float q = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (r < n) q = fmaf(f[r], f[r], q);
-      keys[j] = __float_as_uint(q);
-      if (scores) scores[j] = sqrtf(q);
-    }
-  }
-  auto fill_row = [&](int t, int j) {
-    // a_t[t][0..15] = A[0..15][j] (rows past n are zero)
+  for (int j = tid; j < d; j += kSelThreads) {
     float f[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) f[r] = r < n ? load(r, j) : 0.f;
-    f32x4* dst = (f32x4*)(a_t + (size_t)t * 16);
+    float q = 0.f;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) dst[q4] = f32x4{f[4 * q4], f[4 * q4 + 1], f[4 * q4 + 2], f[4 * q4 + 3]};
-  };
-  for (int t = k + tid; t < k_pad; t += kSelThreads) {
-    f32x4* dst = (f32x4*)(a_t + (size_t)t * 16);
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) dst[q4] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  if (all) {
-#pragma unroll 2
-    for (int t = tid; t < k; t += kSelThreads) {
-      idx[t] = t;
-      fill_row(t, t);
-    }
-    return;
+    for (int r = 0; r < 16; ++r)
+      if (r < n) q = fmaf(f[r], f[r], q);
+    keys[j] = __float_as_uint(q);
+    if (scores) scores[j] = sqrtf(q);
   }
   if (!LDS_KEYS) __threadfence_block();
   __syncthreads();
@@ -473,18 +546,15 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
     KeyChunk kc;
     load_chunk(keys, d, kc);
     radix_threshold(kc, k, sh, &T, &rem);
-    compact_ascending(kc, T, rem, sh, [&](uint32_t pos, int j) {
-      idx[pos] = j;
-      s_idx[pos] = j;
+    compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j) {
+      if (take) s_out[pos] = j;
     });
     __syncthreads();
-#pragma unroll 2
-    for (int t = tid; t < k; t += kSelThreads) fill_row(t, s_idx[t]);
+    for (int t = tid; t < k; t += kSelThreads) idx[t] = s_out[t];
   } else {
     radix_threshold_big(keys, d, k, sh, &T, &rem);
-    compact_ascending_big(keys, d, T, rem, sh, [&](uint32_t pos, int j) {
-      idx[pos] = j;
-      fill_row((int)pos, j);
+    compact_ascending_big(keys, d, T, rem, sh, [&](bool take, uint32_t pos, int j) {
+      if (take) idx[pos] = j;
     });
   }
 }
@@ -527,13 +597,16 @@ int topk_lds_capacity() { return kKeyCap; }
 
 hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k, int32_t* idx, int64_t idx_hs,
                        int32_t* pad, int64_t pad_hs, int k_pad, float* scores, int64_t scores_hs, uint32_t* gkeys,
-                       hipStream_t s) {
-  if (d <= kKeyCap)
+                       hipStream_t s, int32_t* mask, int64_t mask_hs) {
+  if (d <= kSmallD)
+    topk_small_kernel<<<heads, kSmallD, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
+                                                scores_hs, mask, mask_hs);
+  else if (d <= kKeyCap)
     topk_kernel<true><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
-                                                     scores_hs, nullptr);
+                                                     scores_hs, mask, mask_hs, nullptr);
   else
     topk_kernel<false><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
-                                                      scores_hs, gkeys);
+                                                      scores_hs, mask, mask_hs, gkeys);
   return hipGetLastError();
 }
 
@@ -545,23 +618,18 @@ hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int k_pad, bool all,
-                                int32_t* idx, float* scores, float* a_t, uint32_t* gkeys, hipStream_t s) {
-  const int all_i = all ? 1 : 0;
+hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int32_t* idx,
+                                float* scores, uint32_t* gkeys, hipStream_t s) {
   if (d <= kKeyCap) {
     if (a_bf16)
-      decode_select_kernel<true, true><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, k_pad, all_i, idx, scores, a_t,
-                                                                  nullptr);
+      decode_select_kernel<true, true><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, nullptr);
     else
-      decode_select_kernel<false, true><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, k_pad, all_i, idx, scores, a_t,
-                                                                   nullptr);
+      decode_select_kernel<false, true><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, nullptr);
   } else {
     if (a_bf16)
-      decode_select_kernel<true, false><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, k_pad, all_i, idx, scores, a_t,
-                                                                   gkeys);
+      decode_select_kernel<true, false><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, gkeys);
     else
-      decode_select_kernel<false, false><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, k_pad, all_i, idx, scores, a_t,
-                                                                    gkeys);
+      decode_select_kernel<false, false><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, gkeys);
   }
   return hipGetLastError();
 }

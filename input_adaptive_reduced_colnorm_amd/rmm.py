@@ -35,9 +35,13 @@ SIGNATURES = {
     "rmm_qk_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _dbl]),
     "rmm_qk": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int,
                       _vp, _sz, _vp]),
+    "rmm_qk_timed": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp,
+                            _int, _vp, _sz, _vp, _vp]),
     "rmm_pv_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _dbl]),
     "rmm_pv": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp,
                       _int, _vp, _sz, _vp]),
+    "rmm_pv_timed": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp,
+                            _vp, _int, _vp, _sz, _vp, _vp]),
 }
 
 _lib = None

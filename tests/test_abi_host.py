@@ -149,3 +149,32 @@ def test_select_rejects_bad_arguments(L):
     assert call(wsb=4) == WS
     assert call(idx=FAKE) == ALIAS
     assert call(sc=FAKE + 4) == ALIAS
+
+
+def test_timed_variants_check_events_then_arguments(L):
+    """The stage-timed entry points need five event handles, then validate
+    exactly like the plain calls (fake handles are never touched because
+    validation fails before the first event is recorded)."""
+    ev_ok = (ctypes.c_void_p * 5)(*([FAKE + (5 << 30)] * 5))
+    ev_hole = (ctypes.c_void_p * 5)(FAKE, FAKE, None, FAKE, FAKE)
+    mm = [FAKE, FAKE + (1 << 30), BF16, 512, 1024, 256, 1024, 256, 0.5, FAKE + (2 << 30), FAKE + (3 << 30), FP32, 256,
+          FAKE + (4 << 30), 1 << 30, None]
+    assert L.rmm_matmul_timed(*mm, None) == NULL
+    assert L.rmm_matmul_timed(*mm, ev_hole) == NULL
+    bad = list(mm)
+    bad[8] = 0.0
+    assert L.rmm_matmul_timed(*bad, ev_ok) == RHO
+    qk = [FAKE, FAKE + (1 << 30), BF16, 4, 2, 16, 16, 64, 1024, 64, 1024, 64, 0.5, FAKE + (2 << 30),
+          FAKE + (3 << 30), FP32, FAKE + (4 << 30), 1 << 30, None]
+    assert L.rmm_qk_timed(*qk, None) == NULL
+    assert L.rmm_qk_timed(*qk, ev_hole) == NULL
+    bad = list(qk)
+    bad[4] = 3                                # hq % hkv != 0
+    assert L.rmm_qk_timed(*bad, ev_ok) == SHAPE
+    pv = [FAKE, FP32, FAKE + (1 << 30), BF16, 4, 2, 8, 64, 16, 512, 64, 1024, 16, 0.5, FAKE + (2 << 30),
+          FAKE + (3 << 30), FP32, FAKE + (4 << 30), 1 << 30, None]
+    assert L.rmm_pv_timed(*pv, None) == NULL
+    assert L.rmm_pv_timed(*pv, ev_hole) == NULL
+    bad = list(pv)
+    bad[3] = 9                                # unknown V dtype
+    assert L.rmm_pv_timed(*bad, ev_ok) == DTYPE

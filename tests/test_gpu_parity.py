@@ -196,6 +196,20 @@ def test_qk_fp32_and_odd(dev):
     check_qk(w.tensors["Q"], w.tensors["K"], 0.5, dev, TOL_BF16, out_dtype=torch.bfloat16)
 
 
+def test_qk_wide_head(dev):
+    # dh = 256 at rho 0.7: k = 180, padded to 192 (24 packed pieces per row)
+    w = synth.gqa_qk(hq=4, hkv=2, t=130, dh=256)
+    check_qk(w.tensors["Q"], w.tensors["K"], 0.7, dev, TOL_BF16)
+
+
+@pytest.mark.parametrize("d", [255, 256, 257])
+def test_selection_size_boundary(dev, d):
+    # d <= 256 selects with the rank kernel, larger d with the radix kernel
+    w = synth.mlp_down(n=96, d=d, m=72, rhos=(0.5, 0.3))
+    for rho in (0.5, 0.3):
+        check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16)
+
+
 # --------------------------------- PV ---------------------------------------
 
 def check_pv(P, V, rho, dev, tol, heads=None):
@@ -213,6 +227,15 @@ def check_pv(P, V, rho, dev, tol, heads=None):
 @pytest.mark.parametrize("rho", [0.5, 1.0])
 def test_pv_small(dev, rho):
     w = synth.attn_pv(h=4, hkv=2, tq=100, tk=1000, dv=128)
+    check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16)
+    check_pv(w.tensors["P"].to(torch.bfloat16), w.tensors["V"], rho, dev, TOL_BF16)
+
+
+@pytest.mark.parametrize("rho", [0.5, 0.2, 0.1])
+def test_pv_masked_and_packed(dev, rho):
+    # tk = 1024: rho 0.5 and 0.2 keep at least one key in eight (P read in
+    # place, dropped V rows masked); rho 0.1 keeps fewer (kept P packed)
+    w = synth.attn_pv(h=4, hkv=2, tq=96, tk=1024, dv=64, rho=rho)
     check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16)
     check_pv(w.tensors["P"].to(torch.bfloat16), w.tensors["V"], rho, dev, TOL_BF16)
 
