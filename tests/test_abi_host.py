@@ -178,3 +178,12 @@ def test_timed_variants_check_events_then_arguments(L):
     bad = list(pv)
     bad[3] = 9                                # unknown V dtype
     assert L.rmm_pv_timed(*bad, ev_ok) == DTYPE
+
+
+def test_library_resolves_every_kernel_launch():
+    """Each kernel the library launches must have its host launch stub in the
+    library itself (a missing stub would only fail at the first call)."""
+    path = rmm._LIB_PATH
+    out = subprocess.run(["nm", "-u", "-C", path], capture_output=True, text=True, check=True).stdout
+    missing = [l.strip() for l in out.splitlines() if "__device_stub__" in l]
+    assert not missing, missing
