@@ -142,6 +142,9 @@ class MatmulOp:
             return "gemv_kernel (kept rows of B)"
         return "gemm_bf16_kernel<256,256,kmajor,gather> (reduced GEMM)"
 
+    def traffic_ref(self):
+        return None if self.decode else f"gemm_bf16_kernel_{self.name}_traffic.json"
+
     def shape(self):
         return {"shape": self.desc}
 
@@ -210,6 +213,9 @@ class QkOp:
 
     def roofline_kernel(self):
         return "gemm_bf16_kernel<256,256,nmajor> (batched per-head QK^T, fp32 S store)"
+
+    def traffic_ref(self):
+        return None
 
     def shape(self):
         return {"shape": self.desc}
@@ -290,6 +296,9 @@ class PvOp:
         return {"score": "colnorm_kernel<fp32> (column energies of P)", "pack": "pack_kernel<fp32> (kept columns of P)",
                 "gemm": gemm}
 
+    def traffic_ref(self):
+        return None
+
     def shape(self):
         return {"shape": self.desc}
 
@@ -312,6 +321,27 @@ class PvOp:
 
 
 # ---------------------------------------------------------------------------
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def measured_traffic(op):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    runs (profiles/), or None when there are none or the kernel source has
+    changed since they were taken."""
+    ref = op.traffic_ref()
+    if ref is None:
+        return None, None
+    path = os.path.join(ROOT, "profiles", ref)
+    if not os.path.exists(path):
+        return None, None
+    import hashlib
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["kernel_source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
+        return None, "stale: " + ref
+    return rec["hbm_bytes_per_launch"]["total"], ref
+
 
 def _rate(kind, amount, us):
     if kind == "F":
@@ -420,6 +450,9 @@ def run(args, op):
                     "per_launch_bytes": {str(r): op.stage_work(r)[stage][1] for r in red}}
     roofline = {"kernel": f"{kname}, stage '{stage}', mean over rho in {red}", **roofline,
                 "avg_launch_us": round(tot_s / len(red) * 1e6, 2)}
+    traffic, src = measured_traffic(op)
+    roofline["traffic"] = traffic
+    roofline["traffic_source"] = src
 
     line = {
         "metric": METRIC,
