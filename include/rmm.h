@@ -121,6 +121,25 @@ rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n
                               void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
 
 /* ---------------------------------------------------------------------
+ * rmm_matmul_idx: Y = sum over t < k of A[:, idx[t]] B[idx[t], :], the
+ * reduced product over an index set the caller supplies (for instance one
+ * rmm_select on X reused for the Q, K and V projections, or a random set
+ * of the same size as an ablation of the norm-based choice).
+ *   A, B, Y as in rmm_matmul; idx: k int32 device values in any order.
+ *   An entry outside [0, d) contributes nothing; a repeated entry
+ *   contributes once per occurrence.
+ *   Workspace: rmm_matmul_idx_workspace(n, k, m, dtype) bytes, 256-byte
+ *   aligned (always needed: the padded copy of idx lives there).
+ * Source: hackcv.com, Core Approach (Formula Level): RMM_rho(A, B) =
+ * A[:, I] B[I, :] for the kept set I; gist.science, Selection Strategy (the
+ * random-selection comparison uses a set of the same size).
+ * ------------------------------------------------------------------- */
+size_t rmm_matmul_idx_workspace(int64_t n, int64_t k, int64_t m, int dtype);
+rmm_status_t rmm_matmul_idx(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
+                            int64_t ldb, const int32_t* idx, int64_t k, void* Y, int y_dtype, int64_t ldy,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * rmm_qk: per query head h, S[h] = Q[h][:, I_h] K[g(h)][:, I_h]^T with
  * I_h the ceil(rho dh) head-feature dims of largest column norm of Q[h]
  * over its tq rows, g(h) = h / (hq / hkv).

@@ -42,8 +42,8 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(const SimtArgs g) {
       const int t = k0 + kk;
       float v = 0.f;
       if (m0 + i < g.M && t < g.k) {
-        const int64_t col = ib ? ib[t] : t;
-        v = ld(Ab, (size_t)((int64_t)(m0 + i) * g.a_rs + col * g.a_cs), ABF);
+        const int64_t col = ib ? ib[t] : t;   // -1: an index that contributes nothing
+        if (col >= 0) v = ld(Ab, (size_t)((int64_t)(m0 + i) * g.a_rs + col * g.a_cs), ABF);
       }
       As[kk][i] = v;
     }
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(const SimtArgs g) {
       float v = 0.f;
       if (n0 + j < g.N && t < g.k) {
         const int64_t row = ib ? ib[t] : t;
-        v = ld(Bb, (size_t)(row * g.b_ts + (int64_t)(n0 + j) * g.b_js), BBF);
+        if (row >= 0) v = ld(Bb, (size_t)(row * g.b_ts + (int64_t)(n0 + j) * g.b_js), BBF);
       }
       Bs[kk][j] = v;
     }

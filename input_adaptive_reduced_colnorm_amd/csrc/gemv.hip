@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs g) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       av[u][r] = 0.f;
-      if (tid + u * kThreads < L && r < g.n) {
+      if (tid + u * kThreads < L && r < g.n && rows[u] >= 0) {   // -1: contributes nothing
         const size_t off = (size_t)r * g.lda + rows[u];
         av[u][r] = A_BF16 ? bf16_to_f32(((const uint16_t*)g.A)[off]) : ((const float*)g.A)[off];
       }
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs g) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int tl = base + kRowLanes * u;
-      if (tl < L && col_ok)
+      if (tl < L && col_ok && s_rows[tl] >= 0)
         bv[u] = __builtin_nontemporal_load((const i32x4*)(g.B + (size_t)s_rows[tl] * g.ldb + c));
       else
         bv[u] = i32x4{0, 0, 0, 0};

@@ -373,6 +373,115 @@ rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n
                      stage_events);
 }
 
+// ----------------------------- matmul_idx -----------------------------------
+
+namespace {
+
+struct IdxPlan {
+  MatPath path = MatPath::kSimt;
+  int64_t k_pad = 0;
+  int gemv_splits = 1;
+  size_t off_ipad = 0, off_pack = 0, off_part = 0, total = 0;
+};
+
+IdxPlan plan_matmul_idx(int64_t n, int64_t k, int64_t m, int64_t ldb, int dtype, bool b_ptr_ok) {
+  IdxPlan p;
+  Carve cv;
+  p.k_pad = round_up(k, kKTile);
+  p.off_ipad = cv.take((size_t)p.k_pad * 4);
+  const bool bf16 = dtype == RMM_BF16;
+  const bool b_vec = bf16 && b_ptr_ok && ldb % 8 == 0 && m % 8 == 0;
+  if (!b_vec) {
+    p.path = MatPath::kSimt;
+  } else if (n <= kDecodeRows) {
+    p.path = MatPath::kDecode;
+    p.gemv_splits = gemv_splits((int)k, (int)m);
+    if (p.gemv_splits > 1) p.off_part = cv.take((size_t)p.gemv_splits * n * m * 4);
+  } else {
+    p.path = MatPath::kMfmaPacked;
+    p.off_pack = cv.take((size_t)n * p.k_pad * 2);
+  }
+  p.total = cv.used;
+  return p;
+}
+
+}  // namespace
+
+size_t rmm_matmul_idx_workspace(int64_t n, int64_t k, int64_t m, int dtype) {
+  if (!dim_ok(n) || !dim_ok(k) || !dim_ok(m) || !dtype_ok(dtype)) return 0;
+  const size_t a = plan_matmul_idx(n, k, m, m, dtype, true).total;
+  const size_t b = plan_matmul_idx(n, k, m, m, dtype, false).total;
+  return a > b ? a : b;
+}
+
+rmm_status_t rmm_matmul_idx(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
+                            int64_t ldb, const int32_t* idx, int64_t k, void* Y, int y_dtype, int64_t ldy,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!A || !B || !idx || !Y) return RMM_ERR_NULL;
+  if (!dtype_ok(dtype) || !dtype_ok(y_dtype)) return RMM_ERR_DTYPE;
+  if (!dim_ok(n) || !dim_ok(d) || !dim_ok(m) || !dim_ok(k) || lda < d || ldb < m || ldy < m || lda >= kMaxDim ||
+      ldb >= kMaxDim || ldy >= kMaxDim)
+    return RMM_ERR_SHAPE;
+  const size_t elt = elt_size(dtype);
+  if (!aligned(A, elt) || !aligned(B, elt) || !aligned(idx, 4) || !aligned(Y, elt_size(y_dtype)))
+    return RMM_ERR_ALIGN;
+  const IdxPlan p = plan_matmul_idx(n, k, m, ldb, dtype, aligned(B, 16));
+  if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return RMM_ERR_WORKSPACE;
+  const Span sa = span3(A, 1, 0, n, lda, d, elt), sb = span3(B, 1, 0, d, ldb, m, elt);
+  const Span si = span3(idx, 1, 0, 1, k, k, 4), sy = span3(Y, 1, 0, n, ldy, m, elt_size(y_dtype));
+  const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
+  if (overlap(sy, sa) || overlap(sy, sb) || overlap(sy, si) || overlap(sw, sa) || overlap(sw, sb) ||
+      overlap(sw, si) || overlap(sw, sy))
+    return RMM_ERR_ALIAS;
+  if (p.path == MatPath::kMfmaPacked &&
+      (((d - 1) * ldb + m) * 2 > kMaxOperandBytes || n * p.k_pad * 2 > kMaxOperandBytes))
+    return RMM_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool bf16 = dtype == RMM_BF16;
+  int32_t* ipad = (int32_t*)(ws + p.off_ipad);
+  clear_error();
+  RMM_LAUNCH(launch_pad_index(idx, (int)k, (int)d, ipad, (int)p.k_pad, s));
+  switch (p.path) {
+    case MatPath::kSimt: {
+      SimtArgs g{};
+      g.A = A; g.a_bf16 = bf16; g.a_bs = 0; g.a_rs = lda; g.a_cs = 1;
+      g.B = B; g.b_bf16 = bf16; g.b_bs = 0; g.b_ts = ldb; g.b_js = 1; g.b_group = 1;
+      g.idx = ipad; g.idx_bs = 0;
+      g.C = Y; g.c_bf16 = y_dtype == RMM_BF16; g.c_bs = 0; g.ldc = ldy;
+      g.M = (int)n; g.N = (int)m; g.k = (int)k; g.batch = 1;
+      RMM_LAUNCH(launch_gemm_simt(g, s));
+      break;
+    }
+    case MatPath::kDecode: {
+      GemvArgs g{};
+      g.A = A; g.a_bf16 = bf16; g.lda = lda;
+      g.B = (const uint16_t*)B; g.ldb = ldb;
+      g.idx = ipad; g.idx_out = nullptr;
+      g.k = (int)k; g.n = (int)n; g.m = (int)m;
+      g.partial = (float*)(ws + p.off_part); g.splits = p.gemv_splits;
+      g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;
+      RMM_LAUNCH(launch_gemv(g, s));
+      break;
+    }
+    default: {
+      uint16_t* pk = (uint16_t*)(ws + p.off_pack);
+      RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, ipad, 0, (int)p.k_pad, (int)p.k_pad, 1, (int)n, pk, 0, s));
+      GemmArgs g{};
+      g.A = pk; g.a_bs = 0; g.lda = p.k_pad;
+      g.B = (const uint16_t*)B; g.b_bs = 0; g.ldb = ldb; g.b_group = 1;
+      g.idx = ipad; g.idx_bs = 0;
+      g.C = Y; g.c_bs = 0; g.ldc = ldy; g.c_bf16 = y_dtype == RMM_BF16;
+      g.M = (int)n; g.N = (int)m; g.K = (int)p.k_pad; g.batch = 1; g.b_kmajor = true;
+      g.a_bytes = (uint32_t)(n * p.k_pad * 2);
+      g.b_bytes = (uint32_t)(((d - 1) * ldb + m) * 2);
+      RMM_LAUNCH(launch_gemm_bf16(g, s));
+      break;
+    }
+  }
+  return RMM_OK;
+}
+
 // --------------------------------- qk ---------------------------------------
 
 namespace {

@@ -31,7 +31,10 @@ int topk_lds_capacity();
 hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* pad, int64_t pad_hs, int k_pad,
                        hipStream_t s);
 
-// Gather-pack: out[b][r][t] = t < k ? bf16(src[b / src_group][r][idx[b][t]]) : 0
+// pad[t] = idx[t] for t < k when 0 <= idx[t] < d, else -1 (t < k_pad).
+hipError_t launch_pad_index(const int32_t* idx, int k, int d, int32_t* pad, int k_pad, hipStream_t s);
+
+// Gather-pack: out[b][r][t] = t < k && idx[b][t] >= 0 ? bf16(src[b / src_group][r][idx[b][t]]) : 0
 // for t < k_pad, rows r < rows.  src_bf16 selects bf16 (else fp32) input.
 // k_pad must be a multiple of 8 and out 16-byte aligned (16-byte stores).
 hipError_t launch_pack(const void* src, bool src_bf16, int64_t src_hs, int64_t src_rs, int src_group,

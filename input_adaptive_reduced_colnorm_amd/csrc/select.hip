@@ -501,6 +501,20 @@ __global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __rest
     for (int t = k + j; t < k_pad; t += kSmallD) po[t] = -1;
 }
 
+// Caller-supplied index list -> the padded form the loaders read: entries
+// outside [0, d) and the tail past k become -1 (a column / row that
+// contributes nothing).
+__global__ void pad_index_kernel(const int32_t* __restrict__ idx, int k, int d, int32_t* __restrict__ pad, int k_pad) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= k_pad) return;
+  int v = -1;
+  if (t < k) {
+    const int j = idx[t];
+    v = (j >= 0 && j < d) ? j : -1;
+  }
+  pad[t] = v;
+}
+
 __global__ void iota_kernel(int32_t* idx, int64_t idx_hs, int d, int32_t* pad, int64_t pad_hs, int k_pad) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j < d) idx[(size_t)blockIdx.y * idx_hs + j] = j;
@@ -607,6 +621,11 @@ hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k
   else
     topk_kernel<false><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
                                                       scores_hs, mask, mask_hs, gkeys);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_index(const int32_t* idx, int k, int d, int32_t* pad, int k_pad, hipStream_t s) {
+  pad_index_kernel<<<(k_pad + 255) / 256, 256, 0, s>>>(idx, k, d, pad, k_pad);
   return hipGetLastError();
 }
 

@@ -32,6 +32,9 @@ SIGNATURES = {
     "rmm_matmul": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz, _vp]),
     "rmm_matmul_timed": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz,
                                 _vp, _vp]),
+    "rmm_matmul_idx_workspace": (_sz, [_i64, _i64, _i64, _int]),
+    "rmm_matmul_idx": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _int, _i64, _vp, _sz,
+                              _vp]),
     "rmm_qk_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _dbl]),
     "rmm_qk": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int,
                       _vp, _sz, _vp]),
@@ -151,6 +154,34 @@ def matmul(A: torch.Tensor, B: torch.Tensor, rho: float, out_dtype=torch.float32
                       workspace.numel(), _stream(dev))
     _raise(st, "rmm_matmul")
     return idx, out
+
+
+def matmul_idx(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, out_dtype=torch.float32,
+               workspace: torch.Tensor = None, out: torch.Tensor = None) -> torch.Tensor:
+    """Y = sum over t of A[:, idx[t]] B[idx[t], :] for a given int32 index list
+    (entries outside [0, d) contribute nothing).  Returns Y."""
+    dev = _check_dev(A, B)
+    n, d = A.shape
+    d2, m = B.shape
+    if d2 != d:
+        raise ValueError("A and B disagree on the contraction size")
+    if A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A and B need unit inner stride")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must share a dtype")
+    if idx.dtype != torch.int32 or idx.dim() != 1 or not idx.is_contiguous() or idx.device != dev:
+        raise TypeError("idx must be a contiguous 1-D int32 tensor on the same device")
+    L = lib()
+    kk = idx.numel()
+    if out is None:
+        out = torch.empty((n, m), dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = _ws(L.rmm_matmul_idx_workspace(n, kk, m, _dt(A)), dev)
+    st = L.rmm_matmul_idx(A.data_ptr(), B.data_ptr(), _dt(A), n, d, m, A.stride(0), B.stride(0), idx.data_ptr(), kk,
+                          out.data_ptr(), _dt(out), out.stride(0), workspace.data_ptr(), workspace.numel(),
+                          _stream(dev))
+    _raise(st, "rmm_matmul_idx")
+    return out
 
 
 def matmul_workspace(n: int, d: int, m: int, lda: int, dtype, rho: float) -> int:

@@ -33,6 +33,8 @@ bf16 and fp32 values convert to float64 without rounding):
                  attention: selection on Q, K gathers the same feature
                  dims).  Source: hackcv.com "Component mapping"; kaelemshawn
                  .blog section on where RMM cuts inside the Transformer.
+* given I     -- Y = sum over the entries t of a caller-given list of
+                 A[:, t] B[t, :] (entries outside [0, d) ignored).
 * PV          -- per head h: I_h from the column norms of P[h]
                  (queries x keys) over its query rows (the token axis is the
                  contraction axis), and O_h = P[h][:, I_h] @ V[g(h)][I_h, :].
@@ -54,6 +56,7 @@ __all__ = [
     "col_energy",
     "select",
     "matmul",
+    "matmul_given",
     "dense",
     "qk",
     "pv",
@@ -130,6 +133,26 @@ def matmul(A, B, rho: float, rows=None):
     Ar = A64 if rows is None else A64[np.asarray(rows)]
     Y = Ar[:, idx] @ B64[idx, :]
     return idx, Y
+
+
+def matmul_given(A, B, idx) -> np.ndarray:
+    """The reduced product over an index list the caller supplies:
+    Y = sum over the entries t of idx of A[:, t] B[t, :].
+
+    This is RMM_rho(A, B) = A[:, I] B[I, :] (hackcv.com, "Core Approach")
+    with I given instead of selected, as when one selection on X serves
+    several projections or a random set of the same size replaces it
+    (gist.science, Selection Strategy, random-selection comparison).  The
+    list may be in any order; a repeated entry counts once per occurrence;
+    an entry outside [0, d) contributes nothing (the reading the library's
+    interface fixes for invalid entries).  Returns float64 n x m.
+    """
+    A64 = np.asarray(A, dtype=np.float64)
+    B64 = np.asarray(B, dtype=np.float64)
+    d = A64.shape[1]
+    I = np.asarray(idx, dtype=np.int64).ravel()
+    I = I[(I >= 0) & (I < d)]
+    return A64[:, I] @ B64[I, :]
 
 
 def dense(A, B) -> np.ndarray:

@@ -187,3 +187,19 @@ def test_library_resolves_every_kernel_launch():
     out = subprocess.run(["nm", "-u", "-C", path], capture_output=True, text=True, check=True).stdout
     missing = [l.strip() for l in out.splitlines() if "__device_stub__" in l]
     assert not missing, missing
+
+
+def test_matmul_idx_rejects_bad_arguments(L):
+    def call(A=FAKE, B=FAKE + (1 << 30), dt=BF16, n=64, d=128, m=64, lda=128, ldb=64, idx=FAKE + (2 << 30), k=32,
+             Y=FAKE + (3 << 30), ydt=FP32, ldy=64, ws=FAKE + (4 << 30), wsb=1 << 30):
+        return L.rmm_matmul_idx(A, B, dt, n, d, m, lda, ldb, idx, k, Y, ydt, ldy, ws, wsb, None)
+
+    assert call(idx=None) == NULL
+    assert call(dt=4) == DTYPE
+    assert call(k=0) == SHAPE                # empty index list
+    assert call(lda=64) == SHAPE
+    assert call(ws=None) == WS               # the padded list always needs workspace
+    assert call(Y=FAKE + 64) == ALIAS
+    assert call(ws=FAKE + (1 << 30) + 256) == ALIAS
+    assert L.rmm_matmul_idx_workspace(64, 32, 64, BF16) > 0
+    assert L.rmm_matmul_idx_workspace(64, 0, 64, BF16) == 0

@@ -170,6 +170,52 @@ def test_determinism(dev):
     assert torch.equal(i3, i4) and torch.equal(y3.view(torch.int32), y4.view(torch.int32))
 
 
+# ------------------------- given index list ---------------------------------
+
+def _given_idx(d, k, seed):
+    r = np.random.default_rng(seed)
+    idx = r.choice(d, size=k, replace=True)                       # unsorted, with repeats
+    idx[: max(1, k // 50)] = -5                                    # entries outside [0, d) are ignored
+    idx[-1] = d + 7
+    return idx.astype(np.int32)
+
+
+@pytest.mark.parametrize("n", [300, 8])
+def test_matmul_idx_selected_list_equals_reduced_product(dev, n):
+    # the selected list handed back reproduces rmm_matmul bit for bit
+    w = synth.mlp_down(n=n, d=1000, m=264, rhos=(0.7,))
+    A, B = w.tensors["A"].to(dev), w.tensors["B"].to(dev)
+    idx, Y = rmm.matmul(A, B, 0.7)
+    Y2 = rmm.matmul_idx(A, B, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("n,dtype", [(300, torch.bfloat16), (8, torch.bfloat16), (40, torch.float32)])
+def test_matmul_idx_arbitrary_list(dev, n, dtype):
+    w = synth.mlp_down(n=n, d=700, m=136, rhos=(0.5,))
+    A, B = w.tensors["A"].to(dtype), w.tensors["B"].to(dtype)
+    idx = _given_idx(700, 450, seed=n)
+    Y = rmm.matmul_idx(A.to(dev), B.to(dev), torch.from_numpy(idx).to(dev))
+    torch.cuda.synchronize()
+    ref = O.matmul_given(f32(A), f32(B), idx)
+    err = rel_fro(f32(Y), ref)
+    assert err <= (TOL_FP32 if dtype == torch.float32 else TOL_BF16), f"rel Frobenius error {err:.3e}"
+
+
+def test_select_once_reuse_for_qkv(dev):
+    # one selection on X serves three projections; each equals the matching
+    # columns of the reduced product with the concatenated weights
+    w = synth.mlp_down(n=256, d=1024, m=768, rhos=(0.6,))
+    X, W = w.tensors["A"].to(dev), w.tensors["B"].to(dev)
+    idx = rmm.select(X, 0.6)
+    _, Y = rmm.matmul(X, W, 0.6)
+    for lo, hi in ((0, 512), (512, 640), (640, 768)):
+        Yp = rmm.matmul_idx(X, W[:, lo:hi].contiguous(), idx)
+        torch.cuda.synchronize()
+        assert rel_fro(f32(Yp), f32(Y[:, lo:hi])) <= 1e-6
+
+
 # -------------------------------- QK^T --------------------------------------
 
 def check_qk(Q, K, rho, dev, tol, out_dtype=torch.float32):

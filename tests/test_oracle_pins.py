@@ -285,8 +285,30 @@ def pin_pv(ns):
     return None
 
 
+def pin_given_index(ns):
+    """The product over a given list against a pure-Python loop over the
+    list's entries (any order, repeats, entries outside [0, d) skipped), and
+    against the selected-set product when the list is the selection."""
+    r = np.random.default_rng(77)
+    A = r.integers(-4, 5, size=(5, 9)).astype(np.float64)
+    B = r.integers(-3, 4, size=(9, 6)).astype(np.float64)
+    for idx in ([4, 0, 7], [2, 2, 5], [-1, 3, 9, 100, 8], [8, 7, 6, 5, 4, 3, 2, 1, 0], [-3]):
+        got = np.asarray(ns.matmul_given(A, B, np.asarray(idx, dtype=np.int32)))
+        valid = [t for t in idx if 0 <= t < A.shape[1]]
+        ref = [[math.fsum(A[i][t] * B[t][j] for t in valid) for j in range(B.shape[1])] for i in range(A.shape[0])]
+        if got.shape != (5, 6) or np.max(np.abs(got - np.asarray(ref))) > 0:
+            return f"given list {idx}: product differs from the loop over its valid entries"
+    w = synth.mlp_down(n=24, d=40, m=12, rhos=(0.5,))
+    A2, B2 = synth.stored64(w.tensors["A"]), synth.stored64(w.tensors["B"])
+    I, Y = ns.matmul(A2, B2, 0.5)
+    Yg = np.asarray(ns.matmul_given(A2, B2, np.asarray(I)[::-1].copy()))
+    if np.max(np.abs(Yg - np.asarray(Y))) > 1e-12 * np.max(np.abs(Y)):
+        return "the product over the selected list differs from the reduced product"
+    return None
+
+
 PINS = [pin_k_rule, pin_worked_example, pin_dense_loop, pin_reduced_loop, pin_minimax_bruteforce,
-        pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_pv]
+        pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_pv, pin_given_index]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -375,6 +397,11 @@ MUTANTS = {
     "gqa_modulo_mapping": dict(kv_head=lambda h, hq, hkv: h % hkv),
     "product_sign_flip": dict(_product=lambda A, B, idx: -(A[:, idx] @ B[idx, :])),
     "dense_instead_of_reduced": dict(_product=lambda A, B, idx: A @ B),
+    "given_list_repeats_counted_once": dict(matmul_given=lambda A, B, idx: np.asarray(A, float)[:, np.unique(
+        [t for t in np.asarray(idx) if 0 <= t < np.asarray(A).shape[1]]).astype(int)] @ np.asarray(B, float)[np.unique(
+        [t for t in np.asarray(idx) if 0 <= t < np.asarray(A).shape[1]]).astype(int), :]),
+    "given_list_negative_wraps": dict(matmul_given=lambda A, B, idx: np.asarray(A, float)[:, [t for t in np.asarray(idx)
+        if t < np.asarray(A).shape[1]]] @ np.asarray(B, float)[[t for t in np.asarray(idx) if t < np.asarray(A).shape[1]], :]),
 }
 
 
