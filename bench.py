@@ -122,6 +122,20 @@ class MatmulOp:
         if st != 0:
             raise RuntimeError(f"rmm_matmul: {rmm.status_str(st)}")
 
+    def call_idx(self, c, rho, sh):
+        """The product over the index set the last call at this rho selected
+        (rmm_matmul_idx: the reuse of one selection for another projection)."""
+        n, d, m, L, rmm = self.n, self.d, self.m, self.L, self.rmm
+        if not hasattr(self, "ws_idx"):
+            import torch
+            wsb = max(int(L.rmm_matmul_idx_workspace(n, self.ks[r], m, rmm.RMM_BF16)) for r in self.rhos)
+            self.ws_idx = torch.empty(max(wsb, 256), dtype=torch.uint8, device=self.Y.device)
+        st = L.rmm_matmul_idx(self.As[c].data_ptr(), self.Bs[c].data_ptr(), rmm.RMM_BF16, n, d, m, d, m,
+                              self.idx[rho].data_ptr(), self.ks[rho], self.Y.data_ptr(), rmm.RMM_FP32, m,
+                              self.ws_idx.data_ptr(), self.ws_idx.numel(), sh)
+        if st != 0:
+            raise RuntimeError(f"rmm_matmul_idx: {rmm.status_str(st)}")
+
     def stage_work(self, rho):
         """Algorithmic work per stage: (kind, amount) with kind 'B' bytes or 'F' flops."""
         n, d, m, k = self.n, self.d, self.m, self.ks[rho]
@@ -241,13 +255,13 @@ class QkOp:
 class PvOp:
     """Per-head attention output O_h = P_h[:, I_h] V_g(h)[I_h, :] (rmm_pv)."""
 
-    def __init__(self, name, P_cpu, V_cpu, rhos, desc, copies):
+    def __init__(self, name, P_cpu, V_cpu, rhos, desc, copies, L_cpu=None):
         import torch
         from input_adaptive_reduced_colnorm_amd import rmm
         self.rmm, self.L = rmm, rmm.lib()
         dev = torch.device("cuda:0")
         self.name, self.desc, self.rhos, self.copies = name, desc, rhos, copies
-        self.P_cpu, self.V_cpu = P_cpu, V_cpu
+        self.P_cpu, self.V_cpu, self.L_cpu = P_cpu, V_cpu, L_cpu
         self.h, self.tq, self.tk = P_cpu.shape
         self.hkv, _, self.dv = V_cpu.shape
         self.Ps = [P_cpu.to(dev) for _ in range(copies)]
@@ -267,6 +281,63 @@ class PvOp:
         st = L.rmm_pv(*args) if events is None else L.rmm_pv_timed(*args, events)
         if st != 0:
             raise RuntimeError(f"rmm_pv: {rmm.status_str(st)}")
+
+    def extra(self, args, sh):
+        """Producer-side scoring: the softmax pass over the logits writes P and
+        the key energies; PV then runs on the supplied energies (no scoring
+        pass over P).  Times both, back to back, outside the stepped loop."""
+        import torch
+        rmm, L = self.rmm, self.L
+        if self.L_cpu is None:
+            return None
+        dev = self.Ps[0].device
+        Ld = self.L_cpu.to(dev)
+        Pout = torch.empty_like(self.Ps[0])
+        E = torch.empty((self.h, self.tk), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(int(L.rmm_softmax_energy_workspace(self.h, self.tq, self.tk)), 256), dtype=torch.uint8,
+                         device=dev)
+
+        def producer():
+            st = L.rmm_softmax_energy(Ld.data_ptr(), self.h, self.tq, self.tk, self.tq * self.tk, self.tk,
+                                      Pout.data_ptr(), self.tq * self.tk, self.tk, E.data_ptr(), ws.data_ptr(),
+                                      ws.numel(), sh)
+            if st != 0:
+                raise RuntimeError(f"rmm_softmax_energy: {rmm.status_str(st)}")
+
+        rho = min(self.rhos)
+        wsp = torch.empty(max(int(L.rmm_pv_energy_workspace(self.h, self.tq, self.tk, self.dv, rmm.RMM_FP32,
+                                                             rmm.RMM_BF16, rho)), 256), dtype=torch.uint8, device=dev)
+
+        def pv_e(c):
+            st = L.rmm_pv_energy(self.Ps[c].data_ptr(), rmm.RMM_FP32, self.Vs[c].data_ptr(), rmm.RMM_BF16,
+                                 E.data_ptr(), self.h, self.hkv, self.tq, self.tk, self.dv, self.tq * self.tk, self.tk,
+                                 self.tk * self.dv, self.dv, float(rho), self.idx[rho].data_ptr(), self.O.data_ptr(),
+                                 rmm.RMM_FP32, wsp.data_ptr(), wsp.numel(), sh)
+            if st != 0:
+                raise RuntimeError(f"rmm_pv_energy: {rmm.status_str(st)}")
+
+        def timed(fn, n):
+            stream = torch.cuda.current_stream(dev)
+            fn(0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n):
+                fn(i % self.copies)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n * 1e3
+
+        prod_us = timed(lambda c: producer(), args.steps)
+        pv_us = timed(pv_e, args.steps)
+        prod_bytes = 2 * self.h * self.tq * self.tk * 4
+        return {"rho": rho,
+                "softmax_energy_us": round(prod_us, 2),
+                "softmax_energy_gbs": round(prod_bytes / (prod_us * 1e-6) / 1e9, 1),
+                "pv_energy_latency_us": round(pv_us, 2),
+                "note": ("rmm_softmax_energy writes P (fp32) and the key energies from the logits; rmm_pv_energy "
+                         "then selects on those energies and never scores P; compare pv_energy_latency_us with "
+                         "latency_us['1.0']")}
 
     def masked(self, rho):
         """The library runs PV over all key positions of P in place (dropped
@@ -390,6 +461,21 @@ def run(args, op):
         torch.cuda.synchronize()
         op_us[rho] = e0.elapsed_time(e1) / args.steps * 1e3
 
+    # the same products over the index sets just selected (selection reused)
+    reuse_us = {}
+    if hasattr(op, "call_idx"):
+        for j, rho in enumerate(rhos):
+            if rho >= 1.0:
+                continue
+            op.call(j % copies, rho, sh)   # the index set of this rho
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for it in range(args.steps):
+                op.call_idx((it + j) % copies, rho, sh)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reuse_us[str(rho)] = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
+
     # per-kernel durations: the same calls with stage events recorded by the
     # library on the stream the kernels run on
     evs = Events(hip, 5 * args.stage_iters * nops)
@@ -454,6 +540,8 @@ def run(args, op):
     roofline["traffic"] = traffic
     roofline["traffic_source"] = src
 
+    extra = op.extra(args, sh) if hasattr(op, "extra") else None
+
     line = {
         "metric": METRIC,
         "value": round(nops * args.steps / (ms_total * 1e-3), 2),
@@ -472,9 +560,14 @@ def run(args, op):
         "latency_us": {str(r): round(op_us[r], 2) for r in rhos},
         "latency_note": "per-op mean of back-to-back calls; kernel times below come from stage events",
         "speedup_vs_dense": speed,
+        "given_index_latency_us": reuse_us or None,
+        "given_index_note": ("rmm_matmul_idx over the set each rho selected (pack + GEMM, no scoring or TopK): "
+                             "the cost of a projection that reuses another's selection") if reuse_us else None,
         "kernels": per_kernel,
         "roofline": roofline,
     }
+    if extra:
+        line["producer_side_scoring"] = extra
     return line
 
 
@@ -518,10 +611,10 @@ def make_op(name, copies):
         w = synth.gqa_qk()
         return QkOp(name, w.tensors["Q"], w.tensors["K"], (0.5, 1.0),
                     "Q (32,4096,128) bf16, K (8,4096,128) bf16 (GQA group 4) -> S (32,4096,4096) fp32", copies)
-    w = synth.attn_pv()
+    w = synth.attn_pv(with_logits=True)
     return PvOp(name, w.tensors["P"], w.tensors["V"], (0.5, 1.0),
                 "P (64,512,8192) fp32 row-softmax, V (8,8192,128) bf16 (GQA group 8) -> O (64,512,128) fp32",
-                copies)
+                copies, L_cpu=w.tensors["L"])
 
 
 def main():

@@ -188,6 +188,36 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
                     int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
                     int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------
+ * Producer-side scoring for PV: the pass that writes P also emits the
+ * column energies that PV selects on, so PV never reads P twice.
+ * Source: kaelemshawn.blog, section on where RMM cuts inside the
+ * Transformer (PV keys scored by the column norm of P over the history
+ * positions); hackcv.com, Core Approach (scores are column L2 norms).
+ *
+ * rmm_softmax_energy: for every head h and query row i,
+ *   P[h][i][:] = softmax(L[h][i][:]) (max subtracted; fp32), and
+ *   energy[h][j] = sum over i of P[h][i][j]^2 (fixed order).
+ *   L, P: fp32, element (h, i, j) at [h*hs + i*ts + j]; tk <= 16384;
+ *   energy: [h][tk] fp32 contiguous.  Logits must be finite.  L and P may
+ *   not overlap.  Workspace: rmm_softmax_energy_workspace(h, tq, tk) bytes.
+ *
+ * rmm_pv_energy: rmm_pv with the energies supplied (energy[h][tk], e.g. from
+ *   rmm_softmax_energy over the same P) instead of computed from P: I_h is
+ *   the ceil(rho tk) positions of largest energy[h][:], ties to the lowest
+ *   index.  Same arguments, results and errors as rmm_pv otherwise;
+ *   workspace: rmm_pv_energy_workspace(...).
+ * ------------------------------------------------------------------- */
+size_t rmm_softmax_energy_workspace(int64_t h, int64_t tq, int64_t tk);
+rmm_status_t rmm_softmax_energy(const float* L, int64_t h, int64_t tq, int64_t tk, int64_t l_hs, int64_t l_ts,
+                                float* P, int64_t p_hs, int64_t p_ts, float* energy, void* workspace,
+                                size_t workspace_bytes, void* stream);
+size_t rmm_pv_energy_workspace(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho);
+rmm_status_t rmm_pv_energy(const void* P, int p_dtype, const void* V, int v_dtype, const float* energy, int64_t h,
+                           int64_t hkv, int64_t tq, int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs,
+                           int64_t v_ts, double rho, int32_t* idx, void* O, int o_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* rmm_pv with the five stage events of rmm_matmul_timed recorded on `stream`
  * ([0] start, [1] after the column energies of P, [2] after TopK, [3] after
  * the pack of P when the path packs it, [4] after the batched product).

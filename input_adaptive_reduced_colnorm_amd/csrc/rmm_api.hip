@@ -654,7 +654,7 @@ struct PvPlan {
 // eight is kept and P can be read in place; both compute the same sum
 // over the kept positions.
 PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho, bool v_ok,
-               bool direct_ok) {
+               bool direct_ok, bool has_energy = false) {
   PvPlan p;
   Carve cv;
   p.k = k_of(rho, tk);
@@ -662,7 +662,14 @@ PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v
   p.k_pad = round_up(p.k, kKTile);
   p.mfma = v_dtype == RMM_BF16 && v_ok;
   if (!p.all) {
-    plan_select(cv, p.sel, (int)h, tq, tk, p_dtype == RMM_BF16);
+    if (has_energy) {
+      // energies come from the caller: only TopK's key scratch (large tk)
+      p.sel.splits = 1;
+      p.sel.gkeys = tk > topk_lds_capacity();
+      if (p.sel.gkeys) p.sel.off_gkeys = cv.take((size_t)h * tk * 4);
+    } else {
+      plan_select(cv, p.sel, (int)h, tq, tk, p_dtype == RMM_BF16);
+    }
     p.use_sel = true;
   }
   if (p.mfma) {
@@ -696,7 +703,7 @@ namespace {
 rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,
                      int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs, int64_t v_ts, double rho,
                      int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream,
-                     void* const* stage_events) {
+                     void* const* stage_events, const float* energy = nullptr) {
   if (!P || !V || !idx || !O) return RMM_ERR_NULL;
   if (!rho_ok(rho)) return RMM_ERR_RHO;
   if (!dtype_ok(p_dtype) || !dtype_ok(v_dtype) || !dtype_ok(o_dtype)) return RMM_ERR_DTYPE;
@@ -711,7 +718,7 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
   const bool p_f32 = p_dtype == RMM_FP32;
   const bool direct_ok = aligned(P, 16) && tk % kKTile == 0 && p_hs % (p_f32 ? 4 : 8) == 0 && p_ts % (p_f32 ? 4 : 8) == 0 &&
                          ((tq - 1) * p_ts + tk) * (int64_t)pe <= kMaxOperandBytes;
-  const PvPlan p = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, v_ok, direct_ok);
+  const PvPlan p = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, v_ok, direct_ok, energy != nullptr);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
     return RMM_ERR_WORKSPACE;
   if (p.mfma && !p.direct && !p.masked && tq * p.k_pad * 2 > kMaxOperandBytes) return RMM_ERR_SHAPE;
@@ -723,7 +730,10 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
   if (p.total > 0) {
     const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
     if (overlap(sw, sp) || overlap(sw, sv) || overlap(sw, si) || overlap(sw, so)) return RMM_ERR_ALIAS;
+    if (energy && overlap(sw, span3(energy, 1, 0, h, tk, tk, 4))) return RMM_ERR_ALIAS;
   }
+  if (energy && (overlap(span3(energy, 1, 0, h, tk, tk, 4), si) || overlap(span3(energy, 1, 0, h, tk, tk, 4), so)))
+    return RMM_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const int group = (int)(h / hkv);
@@ -735,8 +745,12 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
   int32_t* kmask = p.masked ? (int32_t*)(ws + p.off_mask) : nullptr;
   uint16_t* pp = packed ? (uint16_t*)(ws + p.off_p) : nullptr;
   if (p.use_sel) {
-    float* partial = (float*)(ws + p.sel.off_partial);
-    RMM_LAUNCH(launch_colnorm(P, !p_f32, p_hs, p_ts, (int)h, (int)tq, (int)tk, p.sel.splits, partial, s));
+    const float* partial = energy;
+    if (!energy) {
+      float* part = (float*)(ws + p.sel.off_partial);
+      RMM_LAUNCH(launch_colnorm(P, !p_f32, p_hs, p_ts, (int)h, (int)tq, (int)tk, p.sel.splits, part, s));
+      partial = part;
+    }
     RMM_LAUNCH(mk.mark(1));
     RMM_LAUNCH(launch_topk(partial, (int)h, p.sel.splits, (int)tk, (int)p.k, idx, p.k, ipad, p.k_pad,
                            ipad ? (int)p.k_pad : 0, nullptr, tk,
@@ -795,6 +809,52 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
                     int32_t* idx, void* O, int o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return pv_impl(P, p_dtype, V, v_dtype, h, hkv, tq, tk, dv, p_hs, p_ts, v_hs, v_ts, rho, idx, O, o_dtype, workspace,
                  workspace_bytes, stream, nullptr);
+}
+
+size_t rmm_pv_energy_workspace(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho) {
+  if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(tk) || !dim_ok(dv) || !dtype_ok(p_dtype) || !dtype_ok(v_dtype) ||
+      !rho_ok(rho))
+    return 0;
+  const size_t a = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, true, false, true).total;
+  const size_t b = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, true, true, true).total;
+  return a > b ? a : b;
+}
+
+rmm_status_t rmm_pv_energy(const void* P, int p_dtype, const void* V, int v_dtype, const float* energy, int64_t h,
+                           int64_t hkv, int64_t tq, int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs,
+                           int64_t v_ts, double rho, int32_t* idx, void* O, int o_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!energy) return RMM_ERR_NULL;
+  if (!aligned(energy, 4)) return RMM_ERR_ALIGN;
+  return pv_impl(P, p_dtype, V, v_dtype, h, hkv, tq, tk, dv, p_hs, p_ts, v_hs, v_ts, rho, idx, O, o_dtype, workspace,
+                 workspace_bytes, stream, nullptr, energy);
+}
+
+size_t rmm_softmax_energy_workspace(int64_t h, int64_t tq, int64_t tk) {
+  if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(tk) || tk > softmax_max_keys()) return 0;
+  return (size_t)h * softmax_row_blocks((int)h, (int)tq) * tk * 4;
+}
+
+rmm_status_t rmm_softmax_energy(const float* L, int64_t h, int64_t tq, int64_t tk, int64_t l_hs, int64_t l_ts,
+                                float* P, int64_t p_hs, int64_t p_ts, float* energy, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!L || !P || !energy) return RMM_ERR_NULL;
+  if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(tk) || tk > softmax_max_keys() || l_ts < tk || p_ts < tk || l_hs < 0 ||
+      p_hs < 0 || (h > 1 && (l_hs < 1 || p_hs < 1)) || h * tq >= kMaxDim)
+    return RMM_ERR_SHAPE;
+  if (!aligned(L, 4) || !aligned(P, 4) || !aligned(energy, 4)) return RMM_ERR_ALIGN;
+  const size_t need = rmm_softmax_energy_workspace(h, tq, tk);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return RMM_ERR_WORKSPACE;
+  const Span sl = span3(L, h, l_hs, tq, l_ts, tk, 4), sp = span3(P, h, p_hs, tq, p_ts, tk, 4);
+  const Span se = span3(energy, 1, 0, h, tk, tk, 4);
+  const Span sw = span3(workspace, 1, 0, 1, (int64_t)need, (int64_t)need, 1);
+  if (overlap(sp, sl) || overlap(se, sl) || overlap(se, sp) || overlap(sw, sl) || overlap(sw, sp) || overlap(sw, se))
+    return RMM_ERR_ALIAS;
+  clear_error();
+  RMM_LAUNCH(launch_softmax_energy(L, l_hs, l_ts, P, p_hs, p_ts, (int)h, (int)tq, (int)tk,
+                                   softmax_row_blocks((int)h, (int)tq), (float*)workspace, energy,
+                                   (hipStream_t)stream));
+  return RMM_OK;
 }
 
 rmm_status_t rmm_pv_timed(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,

@@ -43,6 +43,11 @@ SIGNATURES = {
     "rmm_pv_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _dbl]),
     "rmm_pv": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp,
                       _int, _vp, _sz, _vp]),
+    "rmm_softmax_energy_workspace": (_sz, [_i64, _i64, _i64]),
+    "rmm_softmax_energy": (_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "rmm_pv_energy_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _dbl]),
+    "rmm_pv_energy": (_int, [_vp, _int, _vp, _int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl,
+                             _vp, _vp, _int, _vp, _sz, _vp]),
     "rmm_pv_timed": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp,
                             _vp, _int, _vp, _sz, _vp, _vp]),
 }
@@ -239,6 +244,51 @@ def pv(P: torch.Tensor, V: torch.Tensor, rho: float, out_dtype=torch.float32, wo
                   V.stride(0), V.stride(1), float(rho), idx.data_ptr(), out.data_ptr(), _dt(out),
                   workspace.data_ptr(), workspace.numel(), _stream(dev))
     _raise(st, "rmm_pv")
+    return idx, out
+
+
+def softmax_energy(L_: torch.Tensor, P: torch.Tensor = None, energy: torch.Tensor = None):
+    """Row softmax of fp32 logits (h, tq, tk) into P, with the column energies
+    energy[h][j] = sum over rows of P^2.  Returns (P, energy)."""
+    dev = _check_dev(L_)
+    if L_.dtype != torch.float32 or L_.dim() != 3 or L_.stride(2) != 1:
+        raise TypeError("logits must be fp32 (h, tq, tk) with unit inner stride")
+    h, tq, tk = L_.shape
+    if P is None:
+        P = torch.empty((h, tq, tk), dtype=torch.float32, device=dev)
+    if energy is None:
+        energy = torch.empty((h, tk), dtype=torch.float32, device=dev)
+    L = lib()
+    ws = _ws(L.rmm_softmax_energy_workspace(h, tq, tk), dev)
+    st = L.rmm_softmax_energy(L_.data_ptr(), h, tq, tk, L_.stride(0), L_.stride(1), P.data_ptr(), P.stride(0),
+                              P.stride(1), energy.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    _raise(st, "rmm_softmax_energy")
+    return P, energy
+
+
+def pv_energy(P: torch.Tensor, V: torch.Tensor, energy: torch.Tensor, rho: float, out_dtype=torch.float32,
+              workspace: torch.Tensor = None, out: torch.Tensor = None, idx: torch.Tensor = None):
+    """Per-head reduced P V with the key energies supplied (h, tk) fp32.
+    Returns (idx (h, k), O (h, tq, dv))."""
+    dev = _check_dev(P, V, energy)
+    h, tq, tk = P.shape
+    hkv, tk2, dv = V.shape
+    if tk2 != tk or P.stride(2) != 1 or V.stride(2) != 1:
+        raise ValueError("P key axis must match V rows; unit inner strides")
+    if energy.dtype != torch.float32 or tuple(energy.shape) != (h, tk) or not energy.is_contiguous():
+        raise TypeError("energy must be a contiguous fp32 (h, tk) tensor")
+    L = lib()
+    kk = k(rho, tk)
+    if idx is None:
+        idx = torch.empty((h, kk), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((h, tq, dv), dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = _ws(L.rmm_pv_energy_workspace(h, tq, tk, dv, _dt(P), _dt(V), float(rho)), dev)
+    st = L.rmm_pv_energy(P.data_ptr(), _dt(P), V.data_ptr(), _dt(V), energy.data_ptr(), h, hkv, tq, tk, dv,
+                         P.stride(0), P.stride(1), V.stride(0), V.stride(1), float(rho), idx.data_ptr(),
+                         out.data_ptr(), _dt(out), workspace.data_ptr(), workspace.numel(), _stream(dev))
+    _raise(st, "rmm_pv_energy")
     return idx, out
 
 

@@ -33,6 +33,9 @@ bf16 and fp32 values convert to float64 without rounding):
                  attention: selection on Q, K gathers the same feature
                  dims).  Source: hackcv.com "Component mapping"; kaelemshawn
                  .blog section on where RMM cuts inside the Transformer.
+* producer    -- P = row softmax of logits (float64) and, per head, the
+                 column energies of P: the PV scores emitted by the pass
+                 that writes P; pv_given_energy selects on supplied scores.
 * given I     -- Y = sum over the entries t of a caller-given list of
                  A[:, t] B[t, :] (entries outside [0, d) ignored).
 * PV          -- per head h: I_h from the column norms of P[h]
@@ -60,6 +63,8 @@ __all__ = [
     "dense",
     "qk",
     "pv",
+    "softmax_rows",
+    "pv_given_energy",
     "kv_head",
     "error_bound",
 ]
@@ -247,3 +252,42 @@ def error_bound(A, B, idx) -> float:
     s = np.sqrt(col_energy(A64))
     b = np.sqrt(np.sum(B64 * B64, axis=1))
     return float(np.sum(s[drop] * b[drop]))
+
+
+def softmax_rows(L) -> np.ndarray:
+    """Row softmax in float64 over the last axis: exp(x - max x) / sum exp(x - max x).
+
+    P, the attention weights that the PV product contracts over key
+    positions (kaelemshawn.blog, section on where RMM cuts inside the
+    Transformer), is this softmax of the logits row by row; the pass that
+    writes it can also emit col_energy(P) per head, the PV scores.
+    """
+    L64 = np.asarray(L, dtype=np.float64)
+    m = np.max(L64, axis=-1, keepdims=True)
+    e = np.exp(L64 - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def pv_given_energy(P, V, energy, rho: float, heads=None):
+    """PV with the key scores supplied: for each head h, I_h holds the
+    ceil(rho tk) key positions of largest energy[h] (ties to the lower
+    index, ascending) and O_h = P[h][:, I_h] @ V[g(h)][I_h, :].  With
+    energy = column energies of P this is pv(P, V, rho).  Returns
+    (idx (h, k) int64, O (h, tq, dv) float64); `heads` as in pv.
+    """
+    P = np.asarray(P)
+    V = np.asarray(V)
+    E = np.asarray(energy, dtype=np.float64)
+    h_, tq, tk = P.shape
+    hkv, _, dv = V.shape
+    hs = list(range(h_)) if heads is None else [int(h) for h in heads]
+    k = k_rule(rho, tk)
+    idx = np.empty((len(hs), k), dtype=np.int64)
+    O = np.empty((len(hs), tq, dv), dtype=np.float64)
+    for i, h in enumerate(hs):
+        g = kv_head(h, h_, hkv)
+        order = np.argsort(-E[h], kind="stable")
+        I = np.sort(order[:k])
+        idx[i] = I
+        O[i] = np.asarray(P[h], dtype=np.float64)[:, I] @ np.asarray(V[g], dtype=np.float64)[I, :]
+    return idx, O

@@ -216,15 +216,17 @@ def _softmax_rows(L: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=1, keepdims=True)
 
 
-def attn_pv(h=64, hkv=8, tq=512, tk=8192, dv=128, rho=0.5) -> Workload:
+def attn_pv(h=64, hkv=8, tq=512, tk=8192, dv=128, rho=0.5, with_logits=False) -> Workload:
     """PV: P (h, tq, tk) fp32 = row softmax of N(0, std 2) logits; V (hkv, tk, dv).
 
     The boundary gap of each head is widened by lowering the logits of the
-    key positions ranked below the boundary (rows stay stochastic).
+    key positions ranked below the boundary (rows stay stochastic).  With
+    `with_logits` the shifted logits L (fp32) whose softmax P is are kept too.
     """
     g = rng(4, part=1)
     k = ceil_keep(rho, tk)
     P = torch.empty((h, tq, tk), dtype=torch.float32)
+    Ls = torch.empty((h, tq, tk), dtype=torch.float32) if with_logits else None
     gaps = []
     for hh in range(h):
         L = 2.0 * g.standard_normal((tq, tk))
@@ -243,9 +245,14 @@ def attn_pv(h=64, hkv=8, tq=512, tk=8192, dv=128, rho=0.5) -> Workload:
         else:
             raise RuntimeError("could not space the PV boundary")
         P[hh] = Ph
+        if with_logits:
+            Ls[hh] = to_f32(L + shift[None, :])
         gaps.append(gap)
     V = to_bf16(g.standard_normal((hkv, tk, dv), dtype=np.float32))
-    return Workload("attn_pv_70b", {"P": P, "V": V}, (rho,),
+    tensors = {"P": P, "V": V}
+    if with_logits:
+        tensors["L"] = Ls
+    return Workload("attn_pv_70b", tensors, (rho,),
                     {"h": h, "hkv": hkv, "tq": tq, "tk": tk, "dv": dv,
                      "dtype": "fp32/bf16", "min_gap": float(min(gaps))})
 

@@ -203,3 +203,26 @@ def test_matmul_idx_rejects_bad_arguments(L):
     assert call(ws=FAKE + (1 << 30) + 256) == ALIAS
     assert L.rmm_matmul_idx_workspace(64, 32, 64, BF16) > 0
     assert L.rmm_matmul_idx_workspace(64, 0, 64, BF16) == 0
+
+
+def test_softmax_energy_and_pv_energy_reject_bad_arguments(L):
+    def sm(Lp=FAKE, h=4, tq=16, tk=512, lhs=8192, lts=512, P=FAKE + (1 << 30), phs=8192, pts=512,
+           E=FAKE + (2 << 30), ws=FAKE + (3 << 30), wsb=1 << 30):
+        return L.rmm_softmax_energy(Lp, h, tq, tk, lhs, lts, P, phs, pts, E, ws, wsb, None)
+
+    assert sm(E=None) == NULL
+    assert sm(tk=20000) == SHAPE             # more keys than one row of registers holds
+    assert sm(lts=100) == SHAPE
+    assert sm(P=FAKE + 2) == ALIGN
+    assert sm(wsb=4) == WS
+    assert sm(P=FAKE + 4096) == ALIAS        # P on top of the logits
+    assert L.rmm_softmax_energy_workspace(4, 16, 512) > 0
+
+    def pe(E=FAKE + (5 << 30), rho=0.5, h=4, hkv=2):
+        return L.rmm_pv_energy(FAKE, FP32, FAKE + (1 << 30), BF16, E, h, hkv, 8, 64, 16, 512, 64, 1024, 16, rho,
+                               FAKE + (2 << 30), FAKE + (3 << 30), FP32, FAKE + (4 << 30), 1 << 30, None)
+
+    assert pe(E=None) == NULL
+    assert pe(rho=0.0) == RHO
+    assert pe(h=6, hkv=4) == SHAPE
+    assert pe(E=FAKE + (2 << 30)) == ALIAS   # energies on top of the index output

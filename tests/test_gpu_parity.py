@@ -286,6 +286,48 @@ def test_pv_masked_and_packed(dev, rho):
     check_pv(w.tensors["P"].to(torch.bfloat16), w.tensors["V"], rho, dev, TOL_BF16)
 
 
+# ------------------- producer-side PV scoring (softmax) ----------------------
+
+def check_softmax_energy(L, dev, heads=None):
+    P, E = rmm.softmax_energy(L.to(dev))
+    torch.cuda.synchronize()
+    hs = list(range(L.shape[0])) if heads is None else list(heads)
+    Pg = f32(P[torch.as_tensor(hs, device=P.device)])
+    Po = O.softmax_rows(f32(L[hs]))
+    err = rel_fro(Pg, Po)
+    assert err <= 1e-6, f"softmax rel Frobenius error {err:.3e}"
+    assert np.max(np.abs(Pg - Po)) <= 1e-6 * np.max(Po)
+    # the energies are those of the P the kernel wrote
+    Eo = np.stack([O.col_energy(Pg[i]) for i in range(len(hs))])
+    e_err = rel_fro(f32(E[torch.as_tensor(hs, device=E.device)]), Eo)
+    assert e_err <= 1e-5, f"energy rel error {e_err:.3e}"
+    return P, E
+
+
+@pytest.mark.parametrize("rho", [0.5, 0.2])
+def test_softmax_energy_then_pv(dev, rho):
+    w = synth.attn_pv(h=4, hkv=2, tq=96, tk=1024, dv=64, rho=rho, with_logits=True)
+    P, E = check_softmax_energy(w.tensors["L"], dev)
+    V = w.tensors["V"].to(dev)
+    idx, Og = rmm.pv_energy(P, V, E, rho)
+    torch.cuda.synchronize()
+    Pc = f32(P)
+    idx_o, O_o = O.pv_given_energy(Pc, f32(w.tensors["V"]), f32(E), rho)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    assert rel_fro(f32(Og), O_o) <= TOL_BF16
+    # the same keys and product as PV scoring P itself
+    idx2, O2 = rmm.pv(P, V, rho)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(Og.view(torch.int32), O2.view(torch.int32))
+
+
+def test_softmax_energy_odd_sizes(dev):
+    r = np.random.default_rng(3)
+    for h, tq, tk in ((3, 5, 77), (2, 33, 300), (1, 7, 2500)):
+        L = torch.from_numpy(r.normal(0.0, 2.0, size=(h, tq, tk)).astype(np.float32))
+        check_softmax_energy(L, dev)
+
+
 def test_pv_fp32(dev):
     w = synth.attn_pv(h=2, hkv=1, tq=40, tk=300, dv=24)
     check_pv(w.tensors["P"], w.tensors["V"].float(), 0.5, dev, TOL_FP32)
@@ -334,6 +376,24 @@ def test_full_gqa_qk(dev):
         err = rel_fro(f32(S[torch.as_tensor(hs, device=S.device)]), S_o)
         assert err <= TOL_BF16, err
         del S
+
+
+def test_full_attn_pv_with_producer(dev):
+    w = synth.attn_pv(with_logits=True)
+    heads = [0, 9, 37, 63]
+    P, E = check_softmax_energy(w.tensors["L"], dev, heads=heads)
+    idx, Og = rmm.pv_energy(P, w.tensors["V"].to(dev), E, 0.5)
+    torch.cuda.synchronize()
+    hi = torch.as_tensor(heads)
+    Pc = f32(P[hi.to(P.device)])
+    Eo = np.stack([O.col_energy(Pc[i]) for i in range(len(heads))])
+    order = [np.sort(np.argsort(-Eo[i], kind="stable")[:O.k_rule(0.5, Pc.shape[2])]) for i in range(len(heads))]
+    np.testing.assert_array_equal(idx.cpu().numpy()[heads], np.stack(order))
+    Vc = f32(w.tensors["V"])
+    for i, h in enumerate(heads):
+        g = O.kv_head(h, 64, 8)
+        ref = Pc[i][:, order[i]].astype(np.float64) @ Vc[g][order[i], :].astype(np.float64)
+        assert rel_fro(f32(Og[h]), ref) <= TOL_BF16
 
 
 def test_full_attn_pv(dev):

@@ -307,8 +307,45 @@ def pin_given_index(ns):
     return None
 
 
+def pin_softmax_energy(ns):
+    """Row softmax against math.exp / fsum loops, shift invariance, and PV on
+    supplied energies against PV scoring P itself."""
+    r = np.random.default_rng(5)
+    L = r.normal(0.0, 2.0, size=(2, 3, 7))
+    P = np.asarray(ns.softmax_rows(L))
+    for h in range(2):
+        for i in range(3):
+            row = [float(x) for x in L[h, i]]
+            mx = max(row)
+            ex = [math.exp(x - mx) for x in row]
+            s = math.fsum(ex)
+            if max(abs(P[h, i, j] - ex[j] / s) for j in range(7)) > 1e-15:
+                return "softmax differs from the exp / fsum loop"
+    if np.max(np.abs(np.asarray(ns.softmax_rows(L + 3.5)) - P)) > 1e-12:
+        return "softmax changes when a row is shifted"
+    w = synth.attn_pv(h=2, hkv=1, tq=12, tk=40, dv=8)
+    P2, V2 = synth.stored64(w.tensors["P"]), synth.stored64(w.tensors["V"])
+    E = np.stack([np.asarray(ns.col_energy(P2[h])) for h in range(2)])
+    i1, o1 = ns.pv(P2, V2, 0.5)
+    i2, o2 = ns.pv_given_energy(P2, V2, E, 0.5)
+    if not np.array_equal(np.asarray(i1), np.asarray(i2)) or np.max(np.abs(np.asarray(o1) - np.asarray(o2))) > 0:
+        return "PV on the column energies of P differs from PV scoring P"
+    # other energies: the kept keys are exactly those of largest supplied energy
+    E2 = -E
+    i3, o3 = ns.pv_given_energy(P2, V2, E2, 0.5)
+    for h in range(2):
+        kept = set(int(j) for j in np.asarray(i3)[h])
+        if min(E2[h][j] for j in kept) < max(E2[h][j] for j in range(40) if j not in kept):
+            return "a dropped key has a larger supplied energy than a kept one"
+        ref = np.array(_loop_matmul(P2[h][:, sorted(kept)].tolist(), V2[0][sorted(kept), :].tolist()))
+        if np.max(np.abs(np.asarray(o3)[h] - ref)) > 1e-12 * np.max(np.abs(ref)):
+            return "PV on supplied energies differs from the loop over its kept keys"
+    return None
+
+
 PINS = [pin_k_rule, pin_worked_example, pin_dense_loop, pin_reduced_loop, pin_minimax_bruteforce,
-        pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_pv, pin_given_index]
+        pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_pv, pin_given_index,
+        pin_softmax_energy]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -400,6 +437,9 @@ MUTANTS = {
     "given_list_repeats_counted_once": dict(matmul_given=lambda A, B, idx: np.asarray(A, float)[:, np.unique(
         [t for t in np.asarray(idx) if 0 <= t < np.asarray(A).shape[1]]).astype(int)] @ np.asarray(B, float)[np.unique(
         [t for t in np.asarray(idx) if 0 <= t < np.asarray(A).shape[1]]).astype(int), :]),
+    "softmax_without_max_shift_and_sign": dict(softmax_rows=lambda L: np.exp(-np.asarray(L, float)) / np.sum(
+        np.exp(-np.asarray(L, float)), axis=-1, keepdims=True)),
+    "pv_energy_smallest_kept": dict(pv_given_energy=lambda P, V, E, rho, heads=None: O.pv_given_energy(P, V, -np.asarray(E), rho, heads)),
     "given_list_negative_wraps": dict(matmul_given=lambda A, B, idx: np.asarray(A, float)[:, [t for t in np.asarray(idx)
         if t < np.asarray(A).shape[1]]] @ np.asarray(B, float)[[t for t in np.asarray(idx) if t < np.asarray(A).shape[1]], :]),
 }
