@@ -95,6 +95,18 @@ size_t rmm_select_workspace(int64_t n, int64_t d, int dtype);
 rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho,
                         int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
 
+/* rmm_select plus the retained fraction of the activation energy,
+ * *retained = (sum over kept j of q_j) / (sum over all j of q_j) in [0, 1]
+ * (fp64 sums of the fp32 energies, fixed order; 1 when all are kept).
+ * retained: one float in device memory.  Source: hackcv.com, "Attention
+ * vs MLP: structural asymmetry" (the supplementary figures quote the
+ * retained activation energy of each reduced component); kaelemshawn.blog,
+ * the compute-normalized component analysis (same figures).
+ * Workspace: rmm_select_workspace(n, d, dtype) bytes. */
+rmm_status_t rmm_select_retained(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho,
+                                 int32_t* idx, float* scores, float* retained, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------
  * rmm_matmul: Y = A[:, I] B[I, :] with I = rmm_select(A, rho).
  *   A   [n x d] activations (lda >= d), B [d x m] (ldb >= m); both `dtype`.

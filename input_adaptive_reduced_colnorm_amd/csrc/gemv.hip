@@ -33,10 +33,19 @@ constexpr int kBatch = 8;                     // kept rows in flight per lane
 constexpr int kTargetGroups = 640;            // workgroups aimed for (256 CUs)
 
 template <int NR, bool A_BF16>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs g) {
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   __shared__ __attribute__((aligned(16))) float s_a[kMaxSlice][NR];
   __shared__ int32_t s_rows[kMaxSlice];
   __shared__ float red[kThreads / 64][NR][kCols];
+  {
+    // batch member (attention head): shift every operand to its slice
+    const int bz = blockIdx.z;
+    g.A = (const char*)g.A + (size_t)bz * g.a_bs * (A_BF16 ? 2 : 4);
+    g.B += (size_t)(bz / g.b_group) * g.b_bs;
+    if (g.idx) g.idx += (size_t)bz * g.idx_bs;
+    g.Y = (char*)g.Y + (size_t)bz * g.y_bs * (g.y_bf16 ? 2 : 4);
+    g.partial += (size_t)bz * g.splits * g.n * g.m;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int cl = tid % kLanesPerRow, rl = tid / kLanesPerRow;
@@ -182,10 +191,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs g) {
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const GemvArgs g) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= g.n * g.m) return;
+  const int bz = blockIdx.y;
   const int r = i / g.m, col = i % g.m;
+  const float* part = g.partial + (size_t)bz * g.splits * g.n * g.m;
   float v = 0.f;
-  for (int s = 0; s < g.splits; ++s) v += g.partial[(size_t)s * g.n * g.m + i];
-  const size_t off = (size_t)r * g.ldy + col;
+  for (int s = 0; s < g.splits; ++s) v += part[(size_t)s * g.n * g.m + i];
+  const size_t off = (size_t)bz * g.y_bs + (size_t)r * g.ldy + col;
   if (g.y_bf16)
     ((uint16_t*)g.Y)[off] = f32_to_bf16(v);
   else
@@ -202,9 +213,9 @@ void launch_nr(const GemvArgs& g, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-int gemv_splits(int k, int m) {
+int gemv_splits(int k, int m, int batch) {
   const int strips = (m + kCols - 1) / kCols;
-  int splits = (kTargetGroups + strips - 1) / strips;
+  int splits = (kTargetGroups + strips * batch - 1) / (strips * batch);
   const int min_splits = (k + kMaxSlice - 1) / kMaxSlice;
   if (splits < min_splits) splits = min_splits;
   // at least 64 kept rows per slice
@@ -214,7 +225,7 @@ int gemv_splits(int k, int m) {
 }
 
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s) {
-  dim3 grid((g.m + kCols - 1) / kCols, g.splits);
+  dim3 grid((g.m + kCols - 1) / kCols, g.splits, g.batch);
   if (g.n <= 4)
     launch_nr<4>(g, grid, s);
   else if (g.n <= 8)
@@ -223,7 +234,7 @@ hipError_t launch_gemv(const GemvArgs& g, hipStream_t s) {
     launch_nr<16>(g, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.splits == 1) return e;
-  gemv_reduce_kernel<<<(g.n * g.m + 255) / 256, 256, 0, s>>>(g);
+  gemv_reduce_kernel<<<dim3((g.n * g.m + 255) / 256, g.batch), 256, 0, s>>>(g);
   return hipGetLastError();
 }
 

@@ -189,19 +189,22 @@ size_t rmm_select_workspace(int64_t n, int64_t d, int dtype) {
   return cv.used;
 }
 
-rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho, int32_t* idx,
-                        float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+rmm_status_t select_impl(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho, int32_t* idx,
+                         float* scores, float* retained, void* workspace, size_t workspace_bytes, void* stream) {
   if (!A || !idx) return RMM_ERR_NULL;
   if (!rho_ok(rho)) return RMM_ERR_RHO;
   if (!dtype_ok(dtype)) return RMM_ERR_DTYPE;
   if (!dim_ok(n) || !dim_ok(d) || lda < d || lda >= kMaxDim) return RMM_ERR_SHAPE;
   const size_t elt = elt_size(dtype);
   if (!aligned(A, elt) || !aligned(idx, 4) || (scores && !aligned(scores, 4))) return RMM_ERR_ALIGN;
+  if (retained && !aligned(retained, 4)) return RMM_ERR_ALIGN;
   const int64_t k = k_of(rho, d);
   const bool all = k == d;
   Carve cv;
   SelPlan sp;
-  const bool need_sel = !all || scores != nullptr;
+  const bool need_sel = !all || scores != nullptr || retained != nullptr;
   if (need_sel) plan_select(cv, sp, 1, n, d, dtype == RMM_BF16);
   if (cv.used > 0 && (!workspace || workspace_bytes < cv.used || !aligned(workspace, 256))) return RMM_ERR_WORKSPACE;
   const Span sa = span3(A, 1, 0, n, lda, d, elt);
@@ -211,6 +214,11 @@ rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t 
     const Span ss = span3(scores, 1, 0, 1, d, d, 4);
     if (overlap(ss, sa) || overlap(ss, si)) return RMM_ERR_ALIAS;
   }
+  if (retained) {
+    const Span sr = span3(retained, 1, 0, 1, 1, 1, 4);
+    if (overlap(sr, sa) || overlap(sr, si) || (scores && overlap(sr, span3(scores, 1, 0, 1, d, d, 4))))
+      return RMM_ERR_ALIAS;
+  }
   if (cv.used > 0) {
     const Span sw = span3(workspace, 1, 0, 1, (int64_t)cv.used, (int64_t)cv.used, 1);
     if (overlap(sw, sa) || overlap(sw, si) || (scores && overlap(sw, span3(scores, 1, 0, 1, d, d, 4))))
@@ -219,11 +227,29 @@ rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t 
   hipStream_t s = (hipStream_t)stream;
   clear_error();
   if (need_sel) {
-    RMM_LAUNCH(run_select(sp, (char*)workspace, A, dtype == RMM_BF16, 0, lda, 1, n, d, k, idx, k, scores, s));
+    float* partial = (float*)((char*)workspace + sp.off_partial);
+    RMM_LAUNCH(launch_colnorm(A, dtype == RMM_BF16, 0, lda, 1, (int)n, (int)d, sp.splits, partial, s));
+    RMM_LAUNCH(launch_topk(partial, 1, sp.splits, (int)d, (int)k, idx, k, nullptr, 0, 0, scores, d,
+                           sp.gkeys ? (uint32_t*)((char*)workspace + sp.off_gkeys) : nullptr, s, nullptr, 0,
+                           retained));
   } else {
     RMM_LAUNCH(launch_iota(idx, k, 1, (int)d, nullptr, 0, 0, s));
   }
   return RMM_OK;
+}
+
+}  // namespace
+
+rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho, int32_t* idx,
+                        float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  return select_impl(A, dtype, n, d, lda, rho, idx, scores, nullptr, workspace, workspace_bytes, stream);
+}
+
+rmm_status_t rmm_select_retained(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho,
+                                 int32_t* idx, float* scores, float* retained, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!retained) return RMM_ERR_NULL;
+  return select_impl(A, dtype, n, d, lda, rho, idx, scores, retained, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------- matmul ------------------------------------
@@ -569,6 +595,20 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
     RMM_LAUNCH(mk.mark(1));
   }
   RMM_LAUNCH(mk.mark(2));
+  if (p.mfma && tq <= kDecodeRows && qk_decode_fits(group, (int)tq, (int)dh) && aligned(K, 16) && k_ts % 8 == 0 &&
+      k_hs % 8 == 0) {
+    // decode-shaped: one streaming pass over the key cache
+    QkDecodeArgs a{};
+    a.Q = Q; a.q_bf16 = true; a.q_hs = q_hs; a.q_ts = q_ts;
+    a.K = (const uint16_t*)K; a.k_hs = k_hs; a.k_ts = k_ts;
+    a.idx = p.all ? nullptr : idx; a.k = (int)p.k;
+    a.hq = (int)hq; a.hkv = (int)hkv; a.tq = (int)tq; a.tk = (int)tk; a.dh = (int)dh;
+    a.S = S; a.s_bf16 = s_dtype == RMM_BF16;
+    RMM_LAUNCH(mk.mark(3));
+    RMM_LAUNCH(launch_qk_decode(a, s));
+    RMM_LAUNCH(mk.mark(4));
+    return RMM_OK;
+  }
   if (!p.mfma) {
     SimtArgs g{};
     g.A = Q; g.a_bf16 = false; g.a_bs = q_hs; g.a_rs = q_ts; g.a_cs = 1;
@@ -642,8 +682,10 @@ namespace {
 struct PvPlan {
   int64_t k = 0, k_pad = 0;
   bool all = false, mfma = false, direct = false, masked = false, use_sel = false;
+  bool decode = false;   // tq <= 16: per-head GEMV over the kept rows of V
+  int gemv_splits = 1;
   SelPlan sel;
-  size_t off_p = 0, off_ipad = 0, off_mask = 0, total = 0;
+  size_t off_p = 0, off_ipad = 0, off_mask = 0, off_gpart = 0, total = 0;
 };
 
 // PV reads P once for the column energies whatever the path; the product
@@ -672,7 +714,12 @@ PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v
     }
     p.use_sel = true;
   }
-  if (p.mfma) {
+  if (p.mfma && tq <= kDecodeRows) {
+    // decode-shaped: a GEMV per head that reads only the kept rows of V
+    p.decode = true;
+    p.gemv_splits = gemv_splits((int)p.k, (int)dv, (int)h);
+    if (p.gemv_splits > 1) p.off_gpart = cv.take((size_t)p.gemv_splits * h * tq * dv * 4);
+  } else if (p.mfma) {
     p.direct = p.all && direct_ok;
     p.masked = !p.all && direct_ok && p.k * 8 >= tk;
     if (p.masked) {
@@ -721,7 +768,7 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
   const PvPlan p = plan_pv(h, tq, tk, dv, p_dtype, v_dtype, rho, v_ok, direct_ok, energy != nullptr);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
     return RMM_ERR_WORKSPACE;
-  if (p.mfma && !p.direct && !p.masked && tq * p.k_pad * 2 > kMaxOperandBytes) return RMM_ERR_SHAPE;
+  if (p.mfma && !p.decode && !p.direct && !p.masked && tq * p.k_pad * 2 > kMaxOperandBytes) return RMM_ERR_SHAPE;
   const Span sp = span3(P, h, p_hs, tq, p_ts, tk, pe), sv = span3(V, hkv, v_hs, tk, v_ts, dv, ve);
   const Span si = span3(idx, 1, 0, h, p.k, p.k, 4);
   const Span so = span3(O, h, tq * dv, tq, dv, dv, elt_size(o_dtype));
@@ -740,7 +787,7 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
   const Marks mk{stage_events, s};
   clear_error();
   RMM_LAUNCH(mk.mark(0));
-  const bool packed = p.mfma && !p.direct && !p.masked;
+  const bool packed = p.mfma && !p.decode && !p.direct && !p.masked;
   int32_t* ipad = packed ? (int32_t*)(ws + p.off_ipad) : nullptr;
   int32_t* kmask = p.masked ? (int32_t*)(ws + p.off_mask) : nullptr;
   uint16_t* pp = packed ? (uint16_t*)(ws + p.off_p) : nullptr;
@@ -772,6 +819,20 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
     g.M = (int)tq; g.N = (int)dv; g.k = (int)p.k; g.batch = (int)h;
     RMM_LAUNCH(mk.mark(3));
     RMM_LAUNCH(launch_gemm_simt(g, s));
+    RMM_LAUNCH(mk.mark(4));
+    return RMM_OK;
+  }
+  if (p.decode) {
+    GemvArgs g{};
+    g.A = P; g.a_bf16 = !p_f32; g.lda = p_ts; g.a_bs = p_hs;
+    g.B = (const uint16_t*)V; g.ldb = v_ts; g.b_bs = v_hs; g.b_group = group;
+    g.idx = p.all ? nullptr : idx; g.idx_bs = p.k; g.idx_out = nullptr;
+    g.k = (int)p.k; g.n = (int)tq; g.m = (int)dv;
+    g.partial = (float*)(ws + p.off_gpart); g.splits = p.gemv_splits;
+    g.Y = O; g.y_bf16 = o_dtype == RMM_BF16; g.ldy = dv; g.y_bs = tq * dv;
+    g.batch = (int)h;
+    RMM_LAUNCH(mk.mark(3));
+    RMM_LAUNCH(launch_gemv(g, s));
     RMM_LAUNCH(mk.mark(4));
     return RMM_OK;
   }

@@ -17,13 +17,14 @@ int colnorm_splits(int heads, int n, int d, bool elt_bf16);
 // TopK over the summed partials of each head: writes idx[h][0..k) ascending,
 // optionally the same list padded with -1 to k_pad entries (pad[h][...]),
 // optional scores[h][j] = sqrt(energy), and optionally the keep mask
-// mask[h][j] = j if column j is kept else -1 (all d entries).  gkeys:
+// mask[h][j] = j if column j is kept else -1 (all d entries), and optionally
+// retained[h] = (sum of kept energies) / (sum of all energies).  gkeys:
 // [heads][d] uint32 scratch, used only when d exceeds the LDS key capacity
 // (may be null otherwise).
 hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k,
                        int32_t* idx, int64_t idx_hs, int32_t* pad, int64_t pad_hs, int k_pad,
                        float* scores, int64_t scores_hs, uint32_t* gkeys, hipStream_t s,
-                       int32_t* mask = nullptr, int64_t mask_hs = 0);
+                       int32_t* mask = nullptr, int64_t mask_hs = 0, float* retained = nullptr);
 int topk_lds_capacity();
 
 // Writes idx[h][t] = t for t < d (the rho = 1 selection), and optionally
@@ -84,6 +85,8 @@ hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, 
 // order by a second kernel (splits == 1 writes Y directly).  A is read in
 // place (n <= 16 rows).  idx == nullptr means the identity (dense), and then
 // idx_out (if not null) receives 0..k-1.  m must be a multiple of 8.
+// Batched (per attention head b < batch): A + b*a_bs, B + (b / b_group)*b_bs,
+// idx + b*idx_bs, Y + b*y_bs (element strides; batch 1 needs none).
 struct GemvArgs {
   const void* A; bool a_bf16; int64_t lda;
   const uint16_t* B; int64_t ldb;
@@ -92,9 +95,24 @@ struct GemvArgs {
   int k, n, m;
   float* partial; int splits;
   void* Y; bool y_bf16; int64_t ldy;
+  int batch = 1; int64_t a_bs = 0, b_bs = 0, idx_bs = 0, y_bs = 0; int b_group = 1;
 };
-int gemv_splits(int k, int m);
+int gemv_splits(int k, int m, int batch = 1);
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);
+
+// Decode-shaped QK^T (tq <= 16, group * tq <= 8, dh <= 256 and a multiple
+// of 8, bf16 K with 16-byte aligned rows): S[h][r][t] = sum over the k
+// features idx[h][0..k) (all dh when idx is null) of Q[h][r][f] K[g(h)][t][f].
+struct QkDecodeArgs {
+  const void* Q; bool q_bf16; int64_t q_hs, q_ts;
+  const uint16_t* K; int64_t k_hs, k_ts;
+  const int32_t* idx; int k;
+  int hq, hkv, tq, tk, dh;
+  void* S; bool s_bf16;
+  int tok_per_block;
+};
+bool qk_decode_fits(int group, int tq, int dh);
+hipError_t launch_qk_decode(QkDecodeArgs a, hipStream_t s);
 
 // Row softmax of fp32 logits L[h][q][:] (tk <= softmax_max_keys()) into P,
 // with the column energies q[h][j] = sum over rows of P^2 (row blocks summed

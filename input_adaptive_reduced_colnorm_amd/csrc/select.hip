@@ -129,7 +129,34 @@ struct SelShared {
   uint32_t hist[3 * kHistBins];   // one histogram per radix pass
   uint32_t misc[4];
   uint32_t wave_tot[kSelWaves][2];
+  double energy[kSelWaves][2];
 };
+
+// Retained fraction of the energy: sum of the kept keys over the sum of all
+// keys (each thread's keys in index order, then a butterfly inside each
+// wave, then the waves in order; fp64 sums of the fp32 keys).
+__device__ void write_retained(double kept, double total, SelShared& sh, float* out) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kept += __shfl_xor(kept, o, 64);
+    total += __shfl_xor(total, o, 64);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    sh.energy[wave][0] = kept;
+    sh.energy[wave][1] = total;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double k = 0.0, t = 0.0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      k += sh.energy[w][0];
+      t += sh.energy[w][1];
+    }
+    *out = t > 0.0 ? (float)(k / t) : 1.0f;
+  }
+}
 
 // Block-wide inclusive scan of two counters (1024 threads, fixed order).
 __device__ __forceinline__ void block_incl_scan2(uint32_t& a, uint32_t& b, SelShared& sh) {
@@ -257,8 +284,8 @@ __device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32
 
 // Ordered compaction: every thread owns a contiguous index chunk; a block
 // scan of (#greater, #equal) fixes each thread's output position, so the kept
-// indices come out ascending.  emit(take, pos, j) is called once for every
-// index j of the chunk, in order; pos is the output position when take.
+// indices come out ascending.  emit(take, pos, j, key) is called once for
+// every index j of the chunk, in order; pos is the output position when take.
 template <typename Emit>
 __device__ void compact_ascending(const KeyChunk& kc, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
   uint32_t n_gt = 0, n_eq = 0;
@@ -282,7 +309,7 @@ __device__ void compact_ascending(const KeyChunk& kc, uint32_t T, uint32_t rem, 
         take = eq_seen < rem;
         ++eq_seen;
       }
-      emit(take, pos, kc.j0 + i);
+      emit(take, pos, kc.j0 + i, key);
       pos += take;
     }
   }
@@ -358,7 +385,7 @@ __device__ void compact_ascending_big(const uint32_t* keys, int d, uint32_t T, u
       take = eq_seen < rem;
       ++eq_seen;
     }
-    emit(take, pos, j);
+    emit(take, pos, j, key);
     pos += take;
   }
 }
@@ -369,6 +396,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
                                                            int32_t* __restrict__ pad, int64_t pad_hs, int k_pad,
                                                            float* __restrict__ scores, int64_t scores_hs,
                                                            int32_t* __restrict__ mask, int64_t mask_hs,
+                                                           float* __restrict__ retained,
                                                            uint32_t* __restrict__ gkeys) {
   __shared__ uint32_t s_keys[LDS_KEYS ? kKeyCap : 1];
   __shared__ int32_t s_out[LDS_KEYS ? kKeyCap : 1];
@@ -421,12 +449,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   if (po)
     for (int t = k + threadIdx.x; t < k_pad; t += kSelThreads) po[t] = -1;
   int32_t* mo = mask ? mask + (size_t)head * mask_hs : nullptr;
-  auto emit = [&](bool take, uint32_t pos, int j) {
+  double e_kept = 0.0, e_all = 0.0;
+  auto emit = [&](bool take, uint32_t pos, int j, uint32_t key) {
     if (take) {
       out[pos] = j;
       if (po) po[pos] = j;
     }
     if (mo) mo[j] = take ? j : -1;
+    const double q = (double)__uint_as_float(key);
+    e_all += q;
+    if (take) e_kept += q;
   };
   uint32_t T, rem;
   if constexpr (LDS_KEYS) {
@@ -435,9 +467,12 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
     KeyChunk kc;
     load_chunk(keys, d, kc);
     radix_threshold(kc, k, sh, &T, &rem);
-    compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j) {
+    compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t key) {
       if (take) s_out[pos] = j;
       s_keys[j] = take;
+      const double q = (double)__uint_as_float(key);
+      e_all += q;
+      if (take) e_kept += q;
     });
     __syncthreads();
     for (int t = threadIdx.x; t < k; t += kSelThreads) {
@@ -451,6 +486,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
     radix_threshold_big(keys, d, k, sh, &T, &rem);
     compact_ascending_big(keys, d, T, rem, sh, emit);
   }
+  if (retained) write_retained(e_kept, e_all, sh, retained + head);
 }
 
 // Small selections (d <= 256, e.g. the head features of attention): one
@@ -463,9 +499,11 @@ __global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __rest
                                                              int k, int32_t* __restrict__ idx, int64_t idx_hs,
                                                              int32_t* __restrict__ pad, int64_t pad_hs, int k_pad,
                                                              float* __restrict__ scores, int64_t scores_hs,
-                                                             int32_t* __restrict__ mask, int64_t mask_hs) {
+                                                             int32_t* __restrict__ mask, int64_t mask_hs,
+                                                             float* __restrict__ retained) {
   __shared__ uint32_t s_keys[kSmallD];
   __shared__ int s_wave[kSmallD / 64];
+  __shared__ double s_energy[kSmallD / 64][2];
   const int head = blockIdx.x;
   const int j = threadIdx.x;
   const float* P = partial + (size_t)head * splits * d;
@@ -499,6 +537,28 @@ __global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __rest
   if (mask && j < d) mask[(size_t)head * mask_hs + j] = keep ? j : -1;
   if (po)
     for (int t = k + j; t < k_pad; t += kSmallD) po[t] = -1;
+  if (retained) {
+    // kept and total energy: butterfly inside each wave, then the waves in order
+    double kept = keep ? (double)q : 0.0, total = j < d ? (double)q : 0.0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      kept += __shfl_xor(kept, o, 64);
+      total += __shfl_xor(total, o, 64);
+    }
+    if (lane == 0) {
+      s_energy[wave][0] = kept;
+      s_energy[wave][1] = total;
+    }
+    __syncthreads();
+    if (j == 0) {
+      double k2 = 0.0, t2 = 0.0;
+      for (int w = 0; w < kSmallD / 64; ++w) {
+        k2 += s_energy[w][0];
+        t2 += s_energy[w][1];
+      }
+      retained[head] = t2 > 0.0 ? (float)(k2 / t2) : 1.0f;
+    }
+  }
 }
 
 // Caller-supplied index list -> the padded form the loaders read: entries
@@ -560,14 +620,14 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
     KeyChunk kc;
     load_chunk(keys, d, kc);
     radix_threshold(kc, k, sh, &T, &rem);
-    compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j) {
+    compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
       if (take) s_out[pos] = j;
     });
     __syncthreads();
     for (int t = tid; t < k; t += kSelThreads) idx[t] = s_out[t];
   } else {
     radix_threshold_big(keys, d, k, sh, &T, &rem);
-    compact_ascending_big(keys, d, T, rem, sh, [&](bool take, uint32_t pos, int j) {
+    compact_ascending_big(keys, d, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
       if (take) idx[pos] = j;
     });
   }
@@ -611,16 +671,16 @@ int topk_lds_capacity() { return kKeyCap; }
 
 hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k, int32_t* idx, int64_t idx_hs,
                        int32_t* pad, int64_t pad_hs, int k_pad, float* scores, int64_t scores_hs, uint32_t* gkeys,
-                       hipStream_t s, int32_t* mask, int64_t mask_hs) {
+                       hipStream_t s, int32_t* mask, int64_t mask_hs, float* retained) {
   if (d <= kSmallD)
     topk_small_kernel<<<heads, kSmallD, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
-                                                scores_hs, mask, mask_hs);
+                                                scores_hs, mask, mask_hs, retained);
   else if (d <= kKeyCap)
     topk_kernel<true><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
-                                                     scores_hs, mask, mask_hs, nullptr);
+                                                     scores_hs, mask, mask_hs, retained, nullptr);
   else
     topk_kernel<false><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
-                                                      scores_hs, mask, mask_hs, gkeys);
+                                                      scores_hs, mask, mask_hs, retained, gkeys);
   return hipGetLastError();
 }
 

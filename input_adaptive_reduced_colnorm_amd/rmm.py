@@ -28,6 +28,7 @@ SIGNATURES = {
     "rmm_status_str": (_c.c_char_p, [_int]),
     "rmm_select_workspace": (_sz, [_i64, _i64, _int]),
     "rmm_select": (_int, [_vp, _int, _i64, _i64, _i64, _dbl, _vp, _vp, _vp, _sz, _vp]),
+    "rmm_select_retained": (_int, [_vp, _int, _i64, _i64, _i64, _dbl, _vp, _vp, _vp, _vp, _sz, _vp]),
     "rmm_matmul_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _dbl]),
     "rmm_matmul": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz, _vp]),
     "rmm_matmul_timed": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz,
@@ -132,6 +133,24 @@ def select(A: torch.Tensor, rho: float, scores: bool = False):
                       sc.data_ptr() if sc is not None else None, ws.data_ptr(), ws.numel(), _stream(dev))
     _raise(st, "rmm_select")
     return (idx, sc) if scores else idx
+
+
+def select_retained(A: torch.Tensor, rho: float):
+    """Kept index set of A and the retained energy fraction (a 1-element fp32
+    device tensor).  Returns (idx, retained)."""
+    dev = _check_dev(A)
+    n, d = A.shape
+    if A.stride(1) != 1:
+        raise ValueError("A needs unit inner stride")
+    L = lib()
+    kk = k(rho, d)
+    idx = torch.empty(max(kk, 1), dtype=torch.int32, device=dev)
+    ret = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = _ws(L.rmm_select_workspace(n, d, _dt(A)), dev)
+    st = L.rmm_select_retained(A.data_ptr(), _dt(A), n, d, A.stride(0), float(rho), idx.data_ptr(), None,
+                               ret.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    _raise(st, "rmm_select_retained")
+    return idx, ret
 
 
 def matmul(A: torch.Tensor, B: torch.Tensor, rho: float, out_dtype=torch.float32, workspace: torch.Tensor = None,

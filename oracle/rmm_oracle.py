@@ -33,6 +33,7 @@ bf16 and fp32 values convert to float64 without rounding):
                  attention: selection on Q, K gathers the same feature
                  dims).  Source: hackcv.com "Component mapping"; kaelemshawn
                  .blog section on where RMM cuts inside the Transformer.
+* retained    -- sum of the kept energies over the sum of all energies.
 * producer    -- P = row softmax of logits (float64) and, per head, the
                  column energies of P: the PV scores emitted by the pass
                  that writes P; pv_given_energy selects on supplied scores.
@@ -67,6 +68,7 @@ __all__ = [
     "pv_given_energy",
     "kv_head",
     "error_bound",
+    "retained_energy",
 ]
 
 
@@ -291,3 +293,15 @@ def pv_given_energy(P, V, energy, rho: float, heads=None):
         idx[i] = I
         O[i] = np.asarray(P[h], dtype=np.float64)[:, I] @ np.asarray(V[g], dtype=np.float64)[I, :]
     return idx, O
+
+
+def retained_energy(A, rho: float) -> float:
+    """Fraction of the activation energy the selection keeps:
+    sum over kept j of q_j / sum over all j of q_j (1.0 when every column is
+    kept).  hackcv.com, "Attention vs MLP: structural asymmetry" (the
+    supplementary figures quote it per reduced component); kaelemshawn.blog,
+    the compute-normalized component analysis.
+    """
+    idx, q = select(A, rho)
+    tot = float(np.sum(q))
+    return 1.0 if tot == 0.0 else float(np.sum(q[idx])) / tot

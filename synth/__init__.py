@@ -5,6 +5,7 @@ from .workloads import (  # noqa: F401
     GAP_REQUIRED,
     Workload,
     attn_pv,
+    decode_attn_qk,
     decode_qkv,
     gqa_qk,
     mlp_down,

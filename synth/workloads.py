@@ -210,6 +210,26 @@ def gqa_qk(hq=32, hkv=8, t=4096, dh=128, rho=0.5) -> Workload:
                      "min_gap": float(min(gaps))})
 
 
+def decode_attn_qk(hq=32, hkv=8, tq=1, tk=8192, dh=128, rho=0.5) -> Workload:
+    """Decode QK^T: Q (hq, tq, dh) with literal separation of each head's
+    feature norms over its tq rows; a key cache K (hkv, tk, dh); bf16."""
+    g = rng(6)
+    Qs = []
+    gaps = []
+    for _ in range(hq):
+        z = g.standard_normal((tq, dh), dtype=np.float32)
+        c = np.exp(g.standard_normal(dh))
+        q, gap = _space_columns(z, c, to_bf16, (), literal=True)
+        Qs.append(q)
+        gaps.append(gap)
+    Q = torch.stack(Qs, 0)
+    zk = g.standard_normal((hkv, tk, dh), dtype=np.float32)
+    ck = np.exp(g.standard_normal((hkv, 1, dh))).astype(np.float32)
+    K = to_bf16(zk * ck)
+    return Workload("decode_attn_qk", {"Q": Q, "K": K}, (rho,),
+                    {"hq": hq, "hkv": hkv, "tq": tq, "tk": tk, "dh": dh, "min_gap": float(min(gaps))})
+
+
 def _softmax_rows(L: np.ndarray) -> np.ndarray:
     m = L.max(axis=1, keepdims=True)
     e = np.exp(L - m)

@@ -156,6 +156,23 @@ def test_select_scores(dev):
     np.testing.assert_allclose(s.cpu().numpy(), np.sqrt(q), rtol=1e-5)
 
 
+@pytest.mark.parametrize("n,d", [(64, 200), (512, 3000), (40, 16000)])
+def test_select_retained_energy(dev, n, d):
+    # the three TopK paths: rank count (d <= 256), radix in LDS, radix in scratch
+    w = synth.mlp_down(n=n, d=d, m=8, rhos=(0.7, 0.3))
+    A = w.tensors["A"]
+    for rho in (0.7, 0.3, 1.0):
+        idx, ret = rmm.select_retained(A.to(dev), rho)
+        torch.cuda.synchronize()
+        idx_o, _ = O.select(f32(A), rho)
+        np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+        want = O.retained_energy(f32(A), rho)
+        got = float(ret.cpu()[0])
+        if rho == 1.0:
+            assert got == 1.0
+        assert abs(got - want) <= 1e-6 * want, (rho, got, want)
+
+
 def test_determinism(dev):
     w = synth.mlp_down(n=512, d=2048, m=512, rhos=(0.7,))
     A, B = w.tensors["A"].to(dev), w.tensors["B"].to(dev)
@@ -331,6 +348,39 @@ def test_softmax_energy_odd_sizes(dev):
 def test_pv_fp32(dev):
     w = synth.attn_pv(h=2, hkv=1, tq=40, tk=300, dv=24)
     check_pv(w.tensors["P"], w.tensors["V"].float(), 0.5, dev, TOL_FP32)
+
+
+# ------------------------- decode attention ----------------------------------
+
+@pytest.mark.parametrize("tq,dh,rho", [(1, 128, 0.5), (1, 128, 1.0), (2, 64, 0.5), (1, 256, 0.7), (1, 40, 0.5)])
+def test_qk_decode(dev, tq, dh, rho):
+    # streaming pass over the key cache (tq <= 16 and group * tq <= 8), and
+    # the pack + GEMM path for a head dim the streaming pass does not take
+    w = synth.decode_attn_qk(hq=8, hkv=2, tq=tq, tk=1000, dh=dh)
+    check_qk(w.tensors["Q"], w.tensors["K"], rho, dev, TOL_BF16)
+
+
+@pytest.mark.parametrize("tq,rho", [(1, 0.5), (1, 1.0), (4, 0.3)])
+def test_pv_decode(dev, tq, rho):
+    # a GEMV per head over the kept rows of V
+    w = synth.attn_pv(h=8, hkv=2, tq=tq, tk=1000, dv=128, rho=rho, with_logits=True)
+    check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16)
+    check_pv(w.tensors["P"].to(torch.bfloat16), w.tensors["V"], rho, dev, TOL_BF16)
+    # with the energies from the softmax pass
+    P, E = check_softmax_energy(w.tensors["L"], dev)
+    idx, Og = rmm.pv_energy(P, w.tensors["V"].to(dev), E, rho)
+    torch.cuda.synchronize()
+    idx_o, O_o = O.pv_given_energy(f32(P), f32(w.tensors["V"]), f32(E), rho)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    assert rel_fro(f32(Og), O_o) <= TOL_BF16
+
+
+def test_full_decode_attention(dev):
+    # Llama-3.1-8B decode step: 32 query heads, 8 kv heads, 8192 cached tokens
+    wq = synth.decode_attn_qk(hq=32, hkv=8, tq=1, tk=8192, dh=128)
+    check_qk(wq.tensors["Q"], wq.tensors["K"], 0.5, dev, TOL_BF16)
+    wp = synth.attn_pv(h=32, hkv=8, tq=1, tk=8192, dv=128, rho=0.5)
+    check_pv(wp.tensors["P"], wp.tensors["V"], 0.5, dev, TOL_BF16)
 
 
 # ----------------------------- full sizes -----------------------------------

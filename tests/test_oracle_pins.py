@@ -343,7 +343,26 @@ def pin_softmax_energy(ns):
     return None
 
 
-PINS = [pin_k_rule, pin_worked_example, pin_dense_loop, pin_reduced_loop, pin_minimax_bruteforce,
+def pin_retained_energy(ns):
+    """Brute force: the retained fraction equals the largest energy fraction
+    any k-subset of columns keeps (TopK maximises the kept energy); ρ=1 keeps
+    everything; integer columns make every sum exact."""
+    r = np.random.default_rng(9)
+    A = r.integers(-4, 5, size=(6, 10)).astype(np.float64)
+    q = [math.fsum(float(A[i, j]) ** 2 for i in range(6)) for j in range(10)]
+    tot = math.fsum(q)
+    for rho in (0.1, 0.3, 0.5, 0.75, 0.95):
+        k = ns.k_rule(rho, 10)
+        best = max(math.fsum(q[j] for j in S) for S in itertools.combinations(range(10), k)) / tot
+        got = ns.retained_energy(A, rho)
+        if abs(got - best) > 1e-15:
+            return f"rho {rho}: retained {got} but the best {k}-subset keeps {best}"
+    if ns.retained_energy(A, 1.0) != 1.0:
+        return "rho = 1 does not keep all the energy"
+    return None
+
+
+PINS = [pin_retained_energy, pin_k_rule, pin_worked_example, pin_dense_loop, pin_reduced_loop, pin_minimax_bruteforce,
         pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_pv, pin_given_index,
         pin_softmax_energy]
 
@@ -440,6 +459,8 @@ MUTANTS = {
     "softmax_without_max_shift_and_sign": dict(softmax_rows=lambda L: np.exp(-np.asarray(L, float)) / np.sum(
         np.exp(-np.asarray(L, float)), axis=-1, keepdims=True)),
     "pv_energy_smallest_kept": dict(pv_given_energy=lambda P, V, E, rho, heads=None: O.pv_given_energy(P, V, -np.asarray(E), rho, heads)),
+    "retained_over_dropped": dict(retained_energy=lambda A, rho: (lambda i_q: float(np.sum(i_q[1]) - np.sum(i_q[1][i_q[0]]))
+                                   / max(float(np.sum(i_q[1])), 1e-300))(O.select(A, rho))),
     "given_list_negative_wraps": dict(matmul_given=lambda A, B, idx: np.asarray(A, float)[:, [t for t in np.asarray(idx)
         if t < np.asarray(A).shape[1]]] @ np.asarray(B, float)[[t for t in np.asarray(idx) if t < np.asarray(A).shape[1]], :]),
 }
