@@ -18,6 +18,8 @@ Other workloads (--workload) print the same kind of line:
   decode_qkv_8b  A 8 x 4096 @ B 4096 x 6144 (bf16), rho 0.8 (GEMV path)
   gqa_qk_8b      S = Q K^T per head, Q (32, 4096, 128), K (8, 4096, 128) bf16, rho 0.5
   attn_pv_70b    O = P V per head, P (64, 512, 8192) fp32, V (8, 8192, 128) bf16, rho 0.5
+  decode_attn_8b one decode step of attention: QK^T, softmax with key energies, PV;
+                 32 query heads, 8 kv heads, 8192 cached tokens, rho 0.5
 """
 
 from __future__ import annotations
@@ -49,6 +51,7 @@ def _hip():
     h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return h
 
 
@@ -298,7 +301,7 @@ class PvOp:
                          device=dev)
 
         def producer():
-            st = L.rmm_softmax_energy(Ld.data_ptr(), self.h, self.tq, self.tk, self.tq * self.tk, self.tk,
+            st = L.rmm_softmax_energy(Ld.data_ptr(), 1.0, self.h, self.tq, self.tk, self.tq * self.tk, self.tk,
                                       Pout.data_ptr(), self.tq * self.tk, self.tk, E.data_ptr(), ws.data_ptr(),
                                       ws.numel(), sh)
             if st != 0:
@@ -479,7 +482,8 @@ def run(args, op):
     # per-kernel durations: the same calls with stage events recorded by the
     # library on the stream the kernels run on
     evs = Events(hip, 5 * args.stage_iters * nops)
-    stages = {r: {s: [] for s in STAGES + ("op",)} for r in rhos}
+    names = getattr(op, "stage_names", STAGES)
+    stages = {r: {s: [] for s in names + ("op",)} for r in rhos}
     slot = 0
     for it in range(args.stage_iters):
         for j, rho in enumerate(rhos):
@@ -490,7 +494,7 @@ def run(args, op):
     for it in range(args.stage_iters):
         for rho in rhos:
             b = 5 * slot
-            for i, s in enumerate(STAGES):
+            for i, s in enumerate(names):
                 stages[rho][s].append(evs.ms(b + i, b + i + 1))
             stages[rho]["op"].append(evs.ms(b, b + 4))
             slot += 1
@@ -503,7 +507,7 @@ def run(args, op):
     for r in rhos:
         row = {}
         work = op.stage_work(r)
-        for s in STAGES:
+        for s in names:
             if s in work or (s == "topk" and "score" in work):
                 row[f"{s}_us"] = round(mean[r][s], 2)
                 if s in work:
@@ -515,7 +519,7 @@ def run(args, op):
     red = [r for r in rhos if r != dense_r]
     stage = op.roofline_stage()
     if stage is None:
-        stage = max((s for s in STAGES if s in op.stage_work(red[0])), key=lambda s: sum(mean[r][s] for r in red))
+        stage = max((s for s in names if s in op.stage_work(red[0])), key=lambda s: sum(mean[r][s] for r in red))
     kinds = {op.stage_work(r)[stage][0] for r in red}
     assert len(kinds) == 1
     kind = kinds.pop()
@@ -589,7 +593,114 @@ def hipblaslt_context(op):
     return round(e0.elapsed_time(e1) / 10 * 1e3, 1)
 
 
-WORKLOADS = ("mlp_down_8b", "mlp_up_70b", "decode_qkv_8b", "gqa_qk_8b", "attn_pv_70b")
+class DecodeAttnOp:
+    """One decode step of attention per layer (one query per head over a KV
+    cache): rmm_qk (features of q kept, streaming pass over K), the softmax
+    of the scores scaled by 1/sqrt(head dim) that emits the key energies
+    (rmm_softmax_energy), and rmm_pv_energy
+    (keys kept by energy; a GEMV per head over the kept V rows)."""
+
+    stage_names = ("qk", "softmax", "none", "pv")
+
+    def __init__(self, name, Q_cpu, K_cpu, V_cpu, rhos, desc, copies, hip):
+        import torch
+        from input_adaptive_reduced_colnorm_amd import rmm
+        self.rmm, self.L, self.hip = rmm, rmm.lib(), hip
+        dev = torch.device("cuda:0")
+        self.name, self.desc, self.rhos, self.copies = name, desc, rhos, copies
+        self.hq, self.tq, self.dh = Q_cpu.shape
+        self.hkv, self.tk, _ = K_cpu.shape
+        self.dv = V_cpu.shape[2]
+        self.Qs = [Q_cpu.to(dev) for _ in range(copies)]
+        self.Ks = [K_cpu.to(dev) for _ in range(copies)]
+        self.Vs = [V_cpu.to(dev) for _ in range(copies)]
+        self.S = torch.empty((self.hq, self.tq, self.tk), dtype=torch.float32, device=dev)
+        self.P = torch.empty_like(self.S)
+        self.E = torch.empty((self.hq, self.tk), dtype=torch.float32, device=dev)
+        self.O = torch.empty((self.hq, self.tq, self.dv), dtype=torch.float32, device=dev)
+        self.ks = {r: rmm.k(r, self.tk) for r in rhos}       # kept keys (PV)
+        self.kf = {r: rmm.k(r, self.dh) for r in rhos}       # kept features (QK)
+        self.iq = {r: torch.empty((self.hq, self.kf[r]), dtype=torch.int32, device=dev) for r in rhos}
+        self.ip = {r: torch.empty((self.hq, self.ks[r]), dtype=torch.int32, device=dev) for r in rhos}
+        L = self.L
+        wq = max(int(L.rmm_qk_workspace(self.hq, self.tq, self.tk, self.dh, rmm.RMM_BF16, r)) for r in rhos)
+        ws = max(int(L.rmm_softmax_energy_workspace(self.hq, self.tq, self.tk)), 1)
+        wp = max(int(L.rmm_pv_energy_workspace(self.hq, self.tq, self.tk, self.dv, rmm.RMM_FP32, rmm.RMM_BF16, r))
+                 for r in rhos)
+        self.wsq = torch.empty(max(wq, 256), dtype=torch.uint8, device=dev)
+        self.wss = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.wsp = torch.empty(max(wp, 256), dtype=torch.uint8, device=dev)
+
+    def call(self, c, rho, sh, events=None):
+        rmm, L = self.rmm, self.L
+        hq, hkv, tq, tk, dh, dv = self.hq, self.hkv, self.tq, self.tk, self.dh, self.dv
+        rec = (lambda i: self.hip.hipEventRecord(events[i], sh)) if events is not None else (lambda i: 0)
+        rec(0)
+        st = L.rmm_qk(self.Qs[c].data_ptr(), self.Ks[c].data_ptr(), rmm.RMM_BF16, hq, hkv, tq, tk, dh, tq * dh, dh,
+                      tk * dh, dh, float(rho), self.iq[rho].data_ptr(), self.S.data_ptr(), rmm.RMM_FP32,
+                      self.wsq.data_ptr(), self.wsq.numel(), sh)
+        if st != 0:
+            raise RuntimeError(f"rmm_qk: {rmm.status_str(st)}")
+        rec(1)
+        st = L.rmm_softmax_energy(self.S.data_ptr(), float(dh) ** -0.5, hq, tq, tk, tq * tk, tk, self.P.data_ptr(),
+                                  tq * tk, tk,
+                                  self.E.data_ptr(), self.wss.data_ptr(), self.wss.numel(), sh)
+        if st != 0:
+            raise RuntimeError(f"rmm_softmax_energy: {rmm.status_str(st)}")
+        rec(2)
+        rec(3)
+        st = L.rmm_pv_energy(self.P.data_ptr(), rmm.RMM_FP32, self.Vs[c].data_ptr(), rmm.RMM_BF16, self.E.data_ptr(),
+                             hq, hkv, tq, tk, dv, tq * tk, tk, tk * dv, dv, float(rho), self.ip[rho].data_ptr(),
+                             self.O.data_ptr(), rmm.RMM_FP32, self.wsp.data_ptr(), self.wsp.numel(), sh)
+        if st != 0:
+            raise RuntimeError(f"rmm_pv_energy: {rmm.status_str(st)}")
+        rec(4)
+
+    def stage_work(self, rho):
+        hq, hkv, tq, tk, dh, dv = self.hq, self.hkv, self.tq, self.tk, self.dh, self.dv
+        s_bytes = hq * tq * tk * 4
+        return {"qk": ("B", hkv * tk * dh * 2 + s_bytes),           # the key cache once per kv head, S
+                "softmax": ("B", 2 * s_bytes),
+                "pv": ("B", hq * self.ks[rho] * dv * 2 + s_bytes)}   # kept V rows per head, P
+
+    def roofline_stage(self):
+        return None
+
+    def roofline_kernel(self):
+        return {"qk": "qk_decode_kernel (streaming pass over the key cache)",
+                "softmax": "softmax_energy_kernel", "pv": "gemv_kernel batched over heads (kept V rows)"}
+
+    def traffic_ref(self):
+        return None
+
+    def shape(self):
+        return {"shape": self.desc}
+
+    def cpu_baseline(self):
+        import numpy as np
+        from oracle import rmm_oracle as O
+        Q = self.Qs[0].float().cpu().numpy()
+        K = self.Ks[0].float().cpu().numpy()
+        V = self.Vs[0].float().cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            for rho in self.rhos:
+                _, S = O.qk(Q, K, rho)
+                P = O.softmax_rows(S, self.dh ** -0.5)
+                E = np.stack([O.col_energy(P[h]) for h in range(self.hq)])
+                O.pv_given_energy(P, V, E, rho)
+            reps += 1
+            if time.perf_counter() - t0 > 5.0:
+                break
+        wall = time.perf_counter() - t0
+        return {"value": reps * len(self.rhos) / wall, "unit": "decode attention steps/s", "cores": _blas_threads(),
+                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "sample": (f"fp64 oracle qk, row softmax, energies and pv on the whole step at each rho in "
+                           f"{list(self.rhos)}, {reps} repetitions; {wall:.1f} s of CPU work")}
+
+
+WORKLOADS = ("mlp_down_8b", "mlp_up_70b", "decode_qkv_8b", "gqa_qk_8b", "attn_pv_70b", "decode_attn_8b")
 
 
 def make_op(name, copies):
@@ -611,6 +722,12 @@ def make_op(name, copies):
         w = synth.gqa_qk()
         return QkOp(name, w.tensors["Q"], w.tensors["K"], (0.5, 1.0),
                     "Q (32,4096,128) bf16, K (8,4096,128) bf16 (GQA group 4) -> S (32,4096,4096) fp32", copies)
+    if name == "decode_attn_8b":
+        wq = synth.decode_attn_qk(hq=32, hkv=8, tq=1, tk=8192, dh=128)
+        wp = synth.attn_pv(h=32, hkv=8, tq=1, tk=8192, dv=128)
+        return DecodeAttnOp(name, wq.tensors["Q"], wq.tensors["K"], wp.tensors["V"], (0.5, 1.0),
+                            "one query per head, Q (32,1,128) bf16, K and V caches (8,8192,128) bf16 (GQA group 4); "
+                            "rho keeps features in QK^T and keys in PV", copies, _hip())
     w = synth.attn_pv(with_logits=True)
     return PvOp(name, w.tensors["P"], w.tensors["V"], (0.5, 1.0),
                 "P (64,512,8192) fp32 row-softmax, V (8,8192,128) bf16 (GQA group 8) -> O (64,512,128) fp32",
@@ -636,7 +753,7 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     copies = args.copies
     if copies <= 0:
-        copies = {"gqa_qk_8b": 8, "attn_pv_70b": 2}.get(args.workload, 4)
+        copies = {"gqa_qk_8b": 8, "attn_pv_70b": 2, "decode_attn_8b": 8}.get(args.workload, 4)
     op = make_op(args.workload, copies)
     line = run(args, op)
     line["hipblaslt_dense_bf16out_us_context"] = None if args.no_context else hipblaslt_context(op)

@@ -208,7 +208,8 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
  * positions); hackcv.com, Core Approach (scores are column L2 norms).
  *
  * rmm_softmax_energy: for every head h and query row i,
- *   P[h][i][:] = softmax(L[h][i][:]) (max subtracted; fp32), and
+ *   P[h][i][:] = softmax(scale * L[h][i][:]) (max subtracted; fp32; scale
+ *   finite and > 0, e.g. 1/sqrt(head dim) for raw QK^T scores), and
  *   energy[h][j] = sum over i of P[h][i][j]^2 (fixed order).
  *   L, P: fp32, element (h, i, j) at [h*hs + i*ts + j]; tk <= 16384;
  *   energy: [h][tk] fp32 contiguous.  Logits must be finite.  L and P may
@@ -221,8 +222,8 @@ rmm_status_t rmm_pv(const void* P, int p_dtype, const void* V, int v_dtype, int6
  *   workspace: rmm_pv_energy_workspace(...).
  * ------------------------------------------------------------------- */
 size_t rmm_softmax_energy_workspace(int64_t h, int64_t tq, int64_t tk);
-rmm_status_t rmm_softmax_energy(const float* L, int64_t h, int64_t tq, int64_t tk, int64_t l_hs, int64_t l_ts,
-                                float* P, int64_t p_hs, int64_t p_ts, float* energy, void* workspace,
+rmm_status_t rmm_softmax_energy(const float* L, float scale, int64_t h, int64_t tq, int64_t tk, int64_t l_hs,
+                                int64_t l_ts, float* P, int64_t p_hs, int64_t p_ts, float* energy, void* workspace,
                                 size_t workspace_bytes, void* stream);
 size_t rmm_pv_energy_workspace(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v_dtype, double rho);
 rmm_status_t rmm_pv_energy(const void* P, int p_dtype, const void* V, int v_dtype, const float* energy, int64_t h,

@@ -896,10 +896,11 @@ size_t rmm_softmax_energy_workspace(int64_t h, int64_t tq, int64_t tk) {
   return (size_t)h * softmax_row_blocks((int)h, (int)tq) * tk * 4;
 }
 
-rmm_status_t rmm_softmax_energy(const float* L, int64_t h, int64_t tq, int64_t tk, int64_t l_hs, int64_t l_ts,
-                                float* P, int64_t p_hs, int64_t p_ts, float* energy, void* workspace,
+rmm_status_t rmm_softmax_energy(const float* L, float scale, int64_t h, int64_t tq, int64_t tk, int64_t l_hs,
+                                int64_t l_ts, float* P, int64_t p_hs, int64_t p_ts, float* energy, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (!L || !P || !energy) return RMM_ERR_NULL;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return RMM_ERR_SHAPE;
   if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(tk) || tk > softmax_max_keys() || l_ts < tk || p_ts < tk || l_hs < 0 ||
       p_hs < 0 || (h > 1 && (l_hs < 1 || p_hs < 1)) || h * tq >= kMaxDim)
     return RMM_ERR_SHAPE;
@@ -913,7 +914,7 @@ rmm_status_t rmm_softmax_energy(const float* L, int64_t h, int64_t tq, int64_t t
     return RMM_ERR_ALIAS;
   clear_error();
   RMM_LAUNCH(launch_softmax_energy(L, l_hs, l_ts, P, p_hs, p_ts, (int)h, (int)tq, (int)tk,
-                                   softmax_row_blocks((int)h, (int)tq), (float*)workspace, energy,
+                                   softmax_row_blocks((int)h, (int)tq), scale, (float*)workspace, energy,
                                    (hipStream_t)stream));
   return RMM_OK;
 }

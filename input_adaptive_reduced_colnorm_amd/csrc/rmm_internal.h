@@ -114,12 +114,13 @@ struct QkDecodeArgs {
 bool qk_decode_fits(int group, int tq, int dh);
 hipError_t launch_qk_decode(QkDecodeArgs a, hipStream_t s);
 
-// Row softmax of fp32 logits L[h][q][:] (tk <= softmax_max_keys()) into P,
+// Row softmax of scale * L[h][q][:] (fp32, tk <= softmax_max_keys()) into P,
 // with the column energies q[h][j] = sum over rows of P^2 (row blocks summed
 // in order through partial[h][blocks][tk]).  blocks = softmax_row_blocks().
 int softmax_max_keys();
 int softmax_row_blocks(int heads, int tq);
 hipError_t launch_softmax_energy(const float* L, int64_t l_hs, int64_t l_ts, float* P, int64_t p_hs, int64_t p_ts,
-                                 int heads, int tq, int tk, int blocks, float* partial, float* q, hipStream_t s);
+                                 int heads, int tq, int tk, int blocks, float scale, float* partial, float* q,
+                                 hipStream_t s);
 
 }  // namespace rmm

@@ -196,6 +196,19 @@ __device__ __forceinline__ void load_chunk(const uint32_t* keys, int d, KeyChunk
   for (int i = 0; i < kChunk; ++i) kc.key[i] = i < kc.cnt ? keys[kc.j0 + i] : 0u;
 }
 
+// Histogram increment with the lanes of a wave that share the first active
+// lane's digit folded into one atomic (ties and underflowed energies put
+// thousands of keys in one bin; one LDS atomic per lane would serialize).
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool m, uint32_t dig) {
+  const uint64_t act = __ballot(m);
+  if (act == 0) return;
+  const int first = __ffsll((unsigned long long)act) - 1;
+  const uint32_t d0 = __shfl(dig, first, 64);
+  const uint64_t same = __ballot(m && dig == d0);
+  if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+  if (m && dig != d0) atomicAdd(&hist[dig], 1u);
+}
+
 // Finds the k-th largest key: on return *T is its value and *rem the number
 // of keys equal to T that belong to the kept set (the lowest-indexed ones;
 // 0xffffffff means every key equal to T is kept).  MSB-first radix passes
@@ -245,7 +258,7 @@ __device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       const uint32_t key = kc.key[i];
-      if (i < kc.cnt && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+      hist_add(hist, i < kc.cnt && (key & mask) == prefix, (key >> shift) & (nb - 1));
     }
     __syncthreads();
     // thread t owns the buckets nb-1-2t and nb-2-2t, counted from the top
@@ -325,9 +338,10 @@ __device__ void radix_threshold_big(const uint32_t* keys, int d, int k, SelShare
     const uint32_t nb = pass == 2 ? 1024u : 2048u;
     for (int i = tid; i < (int)nb; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < d; j += kSelThreads) {
-      const uint32_t key = keys[j];
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+    for (int j0 = 0; j0 < d; j0 += kSelThreads) {
+      const int j = j0 + tid;
+      const uint32_t key = j < d ? keys[j] : 0u;
+      hist_add(sh.hist, j < d && (key & mask) == prefix, (key >> shift) & (nb - 1));
     }
     __syncthreads();
     uint32_t c0, c1 = 0;

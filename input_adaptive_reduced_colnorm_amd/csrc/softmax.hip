@@ -1,4 +1,4 @@
-// Row softmax of attention logits that also emits the column energies of
+// Row softmax of (scaled) attention logits that also emits the column energies of
 // the probabilities it writes, so that the PV product can select key
 // positions without reading P a second time.
 //
@@ -47,7 +47,7 @@ template <int C>
 __global__ __launch_bounds__(kThreads) void softmax_energy_kernel(const float* __restrict__ L, int64_t l_hs,
                                                                   int64_t l_ts, float* __restrict__ P, int64_t p_hs,
                                                                   int64_t p_ts, int tq, int tk, int rows_per_block,
-                                                                  float* __restrict__ partial) {
+                                                                  float scale, float* __restrict__ partial) {
   __shared__ float red[kThreads / 64];
   const int head = blockIdx.y;
   const int r0 = blockIdx.x * rows_per_block;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void softmax_energy_kernel(const float* _
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int j = threadIdx.x + kThreads * c;
-      x[c] = j < tk ? lr[j] : -INFINITY;
+      x[c] = j < tk ? scale * lr[j] : -INFINITY;
       mx = fmaxf(mx, x[c]);
     }
     mx = block_max(mx, red);
@@ -120,16 +120,17 @@ int softmax_row_blocks(int heads, int tq) {
 }
 
 hipError_t launch_softmax_energy(const float* L, int64_t l_hs, int64_t l_ts, float* P, int64_t p_hs, int64_t p_ts,
-                                 int heads, int tq, int tk, int blocks, float* partial, float* q, hipStream_t s) {
+                                 int heads, int tq, int tk, int blocks, float scale, float* partial, float* q,
+                                 hipStream_t s) {
   const int rpb = (tq + blocks - 1) / blocks;
   dim3 grid(blocks, heads);
   const int C = (tk + kThreads - 1) / kThreads;
   if (C <= 8)
-    softmax_energy_kernel<8><<<grid, kThreads, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, rpb, partial);
+    softmax_energy_kernel<8><<<grid, kThreads, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, rpb, scale, partial);
   else if (C <= 32)
-    softmax_energy_kernel<32><<<grid, kThreads, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, rpb, partial);
+    softmax_energy_kernel<32><<<grid, kThreads, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, rpb, scale, partial);
   else
-    softmax_energy_kernel<64><<<grid, kThreads, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, rpb, partial);
+    softmax_energy_kernel<64><<<grid, kThreads, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, rpb, scale, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2((tk + 255) / 256, heads);

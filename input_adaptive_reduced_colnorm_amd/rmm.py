@@ -45,7 +45,7 @@ SIGNATURES = {
     "rmm_pv": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp,
                       _int, _vp, _sz, _vp]),
     "rmm_softmax_energy_workspace": (_sz, [_i64, _i64, _i64]),
-    "rmm_softmax_energy": (_int, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "rmm_softmax_energy": (_int, [_vp, _c.c_float, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "rmm_pv_energy_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _dbl]),
     "rmm_pv_energy": (_int, [_vp, _int, _vp, _int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl,
                              _vp, _vp, _int, _vp, _sz, _vp]),
@@ -266,9 +266,9 @@ def pv(P: torch.Tensor, V: torch.Tensor, rho: float, out_dtype=torch.float32, wo
     return idx, out
 
 
-def softmax_energy(L_: torch.Tensor, P: torch.Tensor = None, energy: torch.Tensor = None):
-    """Row softmax of fp32 logits (h, tq, tk) into P, with the column energies
-    energy[h][j] = sum over rows of P^2.  Returns (P, energy)."""
+def softmax_energy(L_: torch.Tensor, scale: float = 1.0, P: torch.Tensor = None, energy: torch.Tensor = None):
+    """Row softmax of scale * logits (fp32, (h, tq, tk)) into P, with the
+    column energies energy[h][j] = sum over rows of P^2.  Returns (P, energy)."""
     dev = _check_dev(L_)
     if L_.dtype != torch.float32 or L_.dim() != 3 or L_.stride(2) != 1:
         raise TypeError("logits must be fp32 (h, tq, tk) with unit inner stride")
@@ -279,7 +279,7 @@ def softmax_energy(L_: torch.Tensor, P: torch.Tensor = None, energy: torch.Tenso
         energy = torch.empty((h, tk), dtype=torch.float32, device=dev)
     L = lib()
     ws = _ws(L.rmm_softmax_energy_workspace(h, tq, tk), dev)
-    st = L.rmm_softmax_energy(L_.data_ptr(), h, tq, tk, L_.stride(0), L_.stride(1), P.data_ptr(), P.stride(0),
+    st = L.rmm_softmax_energy(L_.data_ptr(), float(scale), h, tq, tk, L_.stride(0), L_.stride(1), P.data_ptr(), P.stride(0),
                               P.stride(1), energy.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _raise(st, "rmm_softmax_energy")
     return P, energy

@@ -256,15 +256,17 @@ def error_bound(A, B, idx) -> float:
     return float(np.sum(s[drop] * b[drop]))
 
 
-def softmax_rows(L) -> np.ndarray:
-    """Row softmax in float64 over the last axis: exp(x - max x) / sum exp(x - max x).
+def softmax_rows(L, scale: float = 1.0) -> np.ndarray:
+    """Row softmax in float64 over the last axis of x = scale * L:
+    exp(x - max x) / sum exp(x - max x) (scale = 1/sqrt(head dim) for raw
+    QK^T scores).
 
     P, the attention weights that the PV product contracts over key
     positions (kaelemshawn.blog, section on where RMM cuts inside the
     Transformer), is this softmax of the logits row by row; the pass that
     writes it can also emit col_energy(P) per head, the PV scores.
     """
-    L64 = np.asarray(L, dtype=np.float64)
+    L64 = float(scale) * np.asarray(L, dtype=np.float64)
     m = np.max(L64, axis=-1, keepdims=True)
     e = np.exp(L64 - m)
     return e / np.sum(e, axis=-1, keepdims=True)

@@ -206,11 +206,13 @@ def test_matmul_idx_rejects_bad_arguments(L):
 
 
 def test_softmax_energy_and_pv_energy_reject_bad_arguments(L):
-    def sm(Lp=FAKE, h=4, tq=16, tk=512, lhs=8192, lts=512, P=FAKE + (1 << 30), phs=8192, pts=512,
+    def sm(Lp=FAKE, scale=1.0, h=4, tq=16, tk=512, lhs=8192, lts=512, P=FAKE + (1 << 30), phs=8192, pts=512,
            E=FAKE + (2 << 30), ws=FAKE + (3 << 30), wsb=1 << 30):
-        return L.rmm_softmax_energy(Lp, h, tq, tk, lhs, lts, P, phs, pts, E, ws, wsb, None)
+        return L.rmm_softmax_energy(Lp, scale, h, tq, tk, lhs, lts, P, phs, pts, E, ws, wsb, None)
 
     assert sm(E=None) == NULL
+    assert sm(scale=0.0) == SHAPE
+    assert sm(scale=math.inf) == SHAPE
     assert sm(tk=20000) == SHAPE             # more keys than one row of registers holds
     assert sm(lts=100) == SHAPE
     assert sm(P=FAKE + 2) == ALIGN

@@ -305,12 +305,12 @@ def test_pv_masked_and_packed(dev, rho):
 
 # ------------------- producer-side PV scoring (softmax) ----------------------
 
-def check_softmax_energy(L, dev, heads=None):
-    P, E = rmm.softmax_energy(L.to(dev))
+def check_softmax_energy(L, dev, heads=None, scale=1.0):
+    P, E = rmm.softmax_energy(L.to(dev), scale)
     torch.cuda.synchronize()
     hs = list(range(L.shape[0])) if heads is None else list(heads)
     Pg = f32(P[torch.as_tensor(hs, device=P.device)])
-    Po = O.softmax_rows(f32(L[hs]))
+    Po = O.softmax_rows(f32(L[hs]), scale)
     err = rel_fro(Pg, Po)
     assert err <= 1e-6, f"softmax rel Frobenius error {err:.3e}"
     assert np.max(np.abs(Pg - Po)) <= 1e-6 * np.max(Po)
@@ -343,6 +343,7 @@ def test_softmax_energy_odd_sizes(dev):
     for h, tq, tk in ((3, 5, 77), (2, 33, 300), (1, 7, 2500)):
         L = torch.from_numpy(r.normal(0.0, 2.0, size=(h, tq, tk)).astype(np.float32))
         check_softmax_energy(L, dev)
+        check_softmax_energy(L, dev, scale=0.125)
 
 
 def test_pv_fp32(dev):

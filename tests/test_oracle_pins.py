@@ -323,6 +323,8 @@ def pin_softmax_energy(ns):
                 return "softmax differs from the exp / fsum loop"
     if np.max(np.abs(np.asarray(ns.softmax_rows(L + 3.5)) - P)) > 1e-12:
         return "softmax changes when a row is shifted"
+    if np.max(np.abs(np.asarray(ns.softmax_rows(L, 0.5)) - np.asarray(ns.softmax_rows(0.5 * L)))) > 1e-15:
+        return "softmax of scaled logits differs from the softmax of the scaled values"
     w = synth.attn_pv(h=2, hkv=1, tq=12, tk=40, dv=8)
     P2, V2 = synth.stored64(w.tensors["P"]), synth.stored64(w.tensors["V"])
     E = np.stack([np.asarray(ns.col_energy(P2[h])) for h in range(2)])
@@ -456,8 +458,9 @@ MUTANTS = {
     "given_list_repeats_counted_once": dict(matmul_given=lambda A, B, idx: np.asarray(A, float)[:, np.unique(
         [t for t in np.asarray(idx) if 0 <= t < np.asarray(A).shape[1]]).astype(int)] @ np.asarray(B, float)[np.unique(
         [t for t in np.asarray(idx) if 0 <= t < np.asarray(A).shape[1]]).astype(int), :]),
-    "softmax_without_max_shift_and_sign": dict(softmax_rows=lambda L: np.exp(-np.asarray(L, float)) / np.sum(
+    "softmax_without_max_shift_and_sign": dict(softmax_rows=lambda L, scale=1.0: np.exp(-np.asarray(L, float)) / np.sum(
         np.exp(-np.asarray(L, float)), axis=-1, keepdims=True)),
+    "softmax_ignores_scale": dict(softmax_rows=lambda L, scale=1.0: O.softmax_rows(L)),
     "pv_energy_smallest_kept": dict(pv_given_energy=lambda P, V, E, rho, heads=None: O.pv_given_energy(P, V, -np.asarray(E), rho, heads)),
     "retained_over_dropped": dict(retained_energy=lambda A, rho: (lambda i_q: float(np.sum(i_q[1]) - np.sum(i_q[1][i_q[0]]))
                                    / max(float(np.sum(i_q[1])), 1e-300))(O.select(A, rho))),
