@@ -216,6 +216,43 @@ class QkOp:
         if st != 0:
             raise RuntimeError(f"rmm_qk: {rmm.status_str(st)}")
 
+    extra_key = "causal_scores"
+
+    def extra(self, args, sh):
+        """Causal scores (rmm_qk_causal: keys after the query position get
+        -inf, tiles wholly above the diagonal skip the product) beside the
+        unmasked call, at each rho, back to back outside the stepped loop."""
+        import torch
+        if self.tq > self.tk:
+            return None
+        dev = self.Qs[0].device
+        stream = torch.cuda.current_stream(dev)
+        out = {}
+        for rho in self.rhos:
+            def run(c, fn):
+                st = fn(self.Qs[c].data_ptr(), self.Ks[c].data_ptr(), self.rmm.RMM_BF16, self.hq, self.hkv, self.tq,
+                        self.tk, self.dh, self.tq * self.dh, self.dh, self.tk * self.dh, self.dh, float(rho),
+                        self.idx[rho].data_ptr(), self.S.data_ptr(), self.rmm.RMM_FP32, self.ws.data_ptr(),
+                        self.ws.numel(), sh)
+                if st != 0:
+                    raise RuntimeError(f"rmm_qk: {self.rmm.status_str(st)}")
+            us = {}
+            for name, fn in (("causal", self.L.rmm_qk_causal), ("unmasked", self.L.rmm_qk)):
+                run(0, fn)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(args.steps):
+                    run(i % self.copies, fn)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us[name] = e0.elapsed_time(e1) / args.steps * 1e3
+            out[str(rho)] = {"causal_latency_us": round(us["causal"], 2),
+                             "unmasked_latency_us": round(us["unmasked"], 2)}
+        out["note"] = ("the causal call writes the same S bytes (-inf above the diagonal) and skips the product on "
+                       "tiles wholly above it")
+        return out
+
     def stage_work(self, rho):
         hq, hkv, tq, tk, dh, k = self.hq, self.hkv, self.tq, self.tk, self.dh, self.ks[rho]
         s_bytes = hq * tq * tk * 4
@@ -571,7 +608,7 @@ def run(args, op):
         "roofline": roofline,
     }
     if extra:
-        line["producer_side_scoring"] = extra
+        line[getattr(op, "extra_key", "producer_side_scoring")] = extra
     return line
 
 

@@ -176,6 +176,19 @@ rmm_status_t rmm_qk_timed(const void* Q, const void* K, int dtype, int64_t hq, i
                           int32_t* idx, void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream,
                           void* const* stage_events);
 
+/* Causal rmm_qk, for prefill over a key cache: the tq queries are the last
+ * tq of the tk key positions (tq <= tk), so query row r sees keys
+ * t <= r + tk - tq and S[h][r][t] = -inf (fp32 or bf16) for every later t.
+ * "Algorithm Deep-Dive: RMM" (hackcv.com), Component mapping: the kept
+ * features I_h still come from the column norms of Q[h] over all tq rows;
+ * the mask acts on the scores only.  Tiles of S that lie wholly above the
+ * shifted diagonal skip the product and only store -inf.  Arguments, idx,
+ * workspace (rmm_qk_workspace) and errors as rmm_qk, and RMM_ERR_SHAPE when
+ * tq > tk.  The scores go straight to rmm_softmax_energy. */
+rmm_status_t rmm_qk_causal(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
+                           int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho,
+                           int32_t* idx, void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------
  * rmm_pv: per head h, O[h] = P[h][:, I_h] V[g(h)][I_h, :] with I_h the
  * ceil(rho tk) key positions of largest column norm of P[h] over its tq

@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kThreads) void qk_decode_kernel(const QkDecodeArgs 
         if (sub == 0 && t < t_end && j < group * a.tq) {
           const int hl = j / a.tq, r = j % a.tq;
           const size_t off = ((size_t)(g * group + hl) * a.tq + r) * a.tk + t;
+          if (a.causal && t > r + a.tk - a.tq) v = -INFINITY;
           if (a.s_bf16)
             ((uint16_t*)a.S)[off] = f32_to_bf16(v);
           else

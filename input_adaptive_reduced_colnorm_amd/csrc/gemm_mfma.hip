@@ -36,10 +36,13 @@ struct TileCoord {
 // (round robin over 8), so the ids are regrouped such that each XCD receives
 // a compact block of tiles that share A row panels and B column panels in its
 // own L2; inside that block tiles are rastered in groups of 4 tile rows.
-__device__ __forceinline__ TileCoord tile_of(int bid, int tiles_m, int tiles_n) {
+// Causal scores keep the plain order instead: a compact block of tile rows
+// per XCD would leave the XCDs holding the top rows (almost all masked) idle
+// while the others carry the whole product.
+__device__ __forceinline__ TileCoord tile_of(int bid, int tiles_m, int tiles_n, bool xcd_blocks) {
   const int total = tiles_m * tiles_n;
   int lin = bid;
-  if ((total & 7) == 0) {
+  if (xcd_blocks && (total & 7) == 0) {
     const int per = total >> 3;
     lin = (bid & 7) * per + (bid >> 3);
   }
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   const int b = blockIdx.y;
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n);
+  const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n, !g.causal);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
   const char* Ab = (const char*)g.A + (size_t)b * g.a_bs * ES;
@@ -265,11 +268,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
-  const int KT = g.K / BK;
+  // causal scores: a tile whose every entry lies above the shifted diagonal
+  // only writes -inf
+  const bool masked_tile = g.causal && (int64_t)n0 > (int64_t)(m0 + BM - 1) + g.causal_off;
+  const bool some_masked = g.causal && (int64_t)(n0 + BN - 1) > (int64_t)m0 + g.causal_off;
+  const int KT = masked_tile ? 0 : g.K / BK;
   // prologue: tile 0 into LDS, tile 1 in flight in registers
-  load_idx(0);
-  load_tile(0);
-  store_tile(0);
+  if (KT > 0) {
+    load_idx(0);
+    load_tile(0);
+    store_tile(0);
+  }
   if (KT > 1) {
     load_idx(1);
     load_tile(1);
@@ -314,10 +323,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
         const int row = row0 + 8 * (v >> 2) + (v & 3);
         if (full || (row < g.M && col < g.N)) {
           const size_t off = (size_t)row * g.ldc + col;
+          const float y = some_masked && (int64_t)col > (int64_t)row + g.causal_off ? -INFINITY : acc[i][j][v];
           if (g.c_bf16)
-            __builtin_nontemporal_store(f32_to_bf16(acc[i][j][v]), (uint16_t*)Cb + off);
+            __builtin_nontemporal_store(f32_to_bf16(y), (uint16_t*)Cb + off);
           else
-            __builtin_nontemporal_store(acc[i][j][v], (float*)Cb + off);
+            __builtin_nontemporal_store(y, (float*)Cb + off);
         }
       }
     }

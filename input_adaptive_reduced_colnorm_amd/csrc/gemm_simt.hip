@@ -84,10 +84,11 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(const SimtArgs g) {
       const int j = n0 + tx * 4 + c;
       if (j >= g.N) continue;
       const size_t off = (size_t)i * g.ldc + j;
+      const float y = g.causal && (int64_t)j > (int64_t)i + g.causal_off ? -INFINITY : acc[r][c];
       if (CBF)
-        ((uint16_t*)Cb)[off] = f32_to_bf16(acc[r][c]);
+        ((uint16_t*)Cb)[off] = f32_to_bf16(y);
       else
-        ((float*)Cb)[off] = acc[r][c];
+        ((float*)Cb)[off] = y;
     }
   }
 }

@@ -553,7 +553,7 @@ namespace {
 rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
                      int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho, int32_t* idx,
                      void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream,
-                     void* const* stage_events) {
+                     void* const* stage_events, bool causal) {
   if (!Q || !K || !idx || !S) return RMM_ERR_NULL;
   if (!rho_ok(rho)) return RMM_ERR_RHO;
   if (!dtype_ok(dtype) || !dtype_ok(s_dtype)) return RMM_ERR_DTYPE;
@@ -561,6 +561,7 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
   if (q_ts < dh || k_ts < dh || q_hs < 0 || k_hs < 0 || (hq > 1 && q_hs < 1) || (hkv > 1 && k_hs < 1))
     return RMM_ERR_SHAPE;
   if (hq * tq >= kMaxDim || (double)hq * tq * tk >= 9.0e18) return RMM_ERR_SHAPE;
+  if (causal && tq > tk) return RMM_ERR_SHAPE;   // the queries are the last tq of the tk positions
   const size_t elt = elt_size(dtype);
   if (!aligned(Q, elt) || !aligned(K, elt) || !aligned(idx, 4) || !aligned(S, elt_size(s_dtype)))
     return RMM_ERR_ALIGN;
@@ -604,6 +605,7 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
     a.idx = p.all ? nullptr : idx; a.k = (int)p.k;
     a.hq = (int)hq; a.hkv = (int)hkv; a.tq = (int)tq; a.tk = (int)tk; a.dh = (int)dh;
     a.S = S; a.s_bf16 = s_dtype == RMM_BF16;
+    a.causal = causal;
     RMM_LAUNCH(mk.mark(3));
     RMM_LAUNCH(launch_qk_decode(a, s));
     RMM_LAUNCH(mk.mark(4));
@@ -616,6 +618,7 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
     g.idx = p.all ? nullptr : idx; g.idx_bs = p.k;
     g.C = S; g.c_bf16 = s_dtype == RMM_BF16; g.c_bs = tq * tk; g.ldc = tk;
     g.M = (int)tq; g.N = (int)tk; g.k = (int)p.k; g.batch = (int)hq;
+    g.causal = causal; g.causal_off = tk - tq;
     RMM_LAUNCH(mk.mark(3));
     RMM_LAUNCH(launch_gemm_simt(g, s));
     RMM_LAUNCH(mk.mark(4));
@@ -644,6 +647,7 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
   g.idx = nullptr; g.idx_bs = 0;
   g.C = S; g.c_bs = tq * tk; g.ldc = tk; g.c_bf16 = s_dtype == RMM_BF16;
   g.M = (int)tq; g.N = (int)tk; g.batch = (int)hq; g.b_kmajor = false;
+  g.causal = causal; g.causal_off = tk - tq;
   RMM_LAUNCH(mk.mark(3));
   RMM_LAUNCH(launch_gemm_bf16(g, s));
   RMM_LAUNCH(mk.mark(4));
@@ -663,7 +667,14 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
                     int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho, int32_t* idx,
                     void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return qk_impl(Q, K, dtype, hq, hkv, tq, tk, dh, q_hs, q_ts, k_hs, k_ts, rho, idx, S, s_dtype, workspace,
-                 workspace_bytes, stream, nullptr);
+                 workspace_bytes, stream, nullptr, false);
+}
+
+rmm_status_t rmm_qk_causal(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
+                           int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho,
+                           int32_t* idx, void* S, int s_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return qk_impl(Q, K, dtype, hq, hkv, tq, tk, dh, q_hs, q_ts, k_hs, k_ts, rho, idx, S, s_dtype, workspace,
+                 workspace_bytes, stream, nullptr, true);
 }
 
 rmm_status_t rmm_qk_timed(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
@@ -672,7 +683,7 @@ rmm_status_t rmm_qk_timed(const void* Q, const void* K, int dtype, int64_t hq, i
                           void* const* stage_events) {
   if (!events_ok(stage_events)) return RMM_ERR_NULL;
   return qk_impl(Q, K, dtype, hq, hkv, tq, tk, dh, q_hs, q_ts, k_hs, k_ts, rho, idx, S, s_dtype, workspace,
-                 workspace_bytes, stream, stage_events);
+                 workspace_bytes, stream, stage_events, false);
 }
 
 // --------------------------------- pv ---------------------------------------

@@ -57,6 +57,8 @@ struct GemmArgs {
   int M, N, K, batch;   // K: multiple of 64 (A zero padded / B rows -1 padded)
   bool b_kmajor;
   uint32_t a_bytes, b_bytes;  // per-batch extents (bytes) for the buffer descriptors
+  bool causal;          // C[i][j] = -inf where j > i + causal_off (tiles wholly above skip the product)
+  int64_t causal_off;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Same product with A given as fp32 (rounded to bf16 while staged); a gather
@@ -72,6 +74,7 @@ struct SimtArgs {
   const int32_t* idx; int64_t idx_bs;   // null: identity
   void* C; bool c_bf16; int64_t c_bs, ldc;
   int M, N, k, batch;
+  bool causal; int64_t causal_off;      // C[i][j] = -inf where j > i + causal_off
 };
 hipError_t launch_gemm_simt(const SimtArgs& g, hipStream_t s);
 
@@ -109,6 +112,7 @@ struct QkDecodeArgs {
   const int32_t* idx; int k;
   int hq, hkv, tq, tk, dh;
   void* S; bool s_bf16;
+  bool causal;          // S[h][r][t] = -inf where t > r + tk - tq
   int tok_per_block;
 };
 bool qk_decode_fits(int group, int tq, int dh);

@@ -39,6 +39,8 @@ SIGNATURES = {
     "rmm_qk_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _dbl]),
     "rmm_qk": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int,
                       _vp, _sz, _vp]),
+    "rmm_qk_causal": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int,
+                      _vp, _sz, _vp]),
     "rmm_qk_timed": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp,
                             _int, _vp, _sz, _vp, _vp]),
     "rmm_pv_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _dbl]),
@@ -214,8 +216,9 @@ def matmul_workspace(n: int, d: int, m: int, lda: int, dtype, rho: float) -> int
 
 
 def qk(Q: torch.Tensor, K: torch.Tensor, rho: float, out_dtype=torch.float32, workspace: torch.Tensor = None,
-       out: torch.Tensor = None, idx: torch.Tensor = None):
-    """Per-head reduced Q K^T.  Q (hq, tq, dh), K (hkv, tk, dh).  Returns (idx (hq, k), S (hq, tq, tk))."""
+       out: torch.Tensor = None, idx: torch.Tensor = None, causal: bool = False):
+    """Per-head reduced Q K^T.  Q (hq, tq, dh), K (hkv, tk, dh).  Returns (idx (hq, k), S (hq, tq, tk)).
+    With causal=True (rmm_qk_causal) query row r sees keys t <= r + tk - tq; later scores are -inf."""
     dev = _check_dev(Q, K)
     hq, tq, dh = Q.shape
     hkv, tk, dh2 = K.shape
@@ -231,10 +234,11 @@ def qk(Q: torch.Tensor, K: torch.Tensor, rho: float, out_dtype=torch.float32, wo
         out = torch.empty((hq, tq, tk), dtype=out_dtype, device=dev)
     if workspace is None:
         workspace = _ws(L.rmm_qk_workspace(hq, tq, tk, dh, _dt(Q), float(rho)), dev)
-    st = L.rmm_qk(Q.data_ptr(), K.data_ptr(), _dt(Q), hq, hkv, tq, tk, dh, Q.stride(0), Q.stride(1), K.stride(0),
-                  K.stride(1), float(rho), idx.data_ptr(), out.data_ptr(), _dt(out), workspace.data_ptr(),
-                  workspace.numel(), _stream(dev))
-    _raise(st, "rmm_qk")
+    fn = L.rmm_qk_causal if causal else L.rmm_qk
+    st = fn(Q.data_ptr(), K.data_ptr(), _dt(Q), hq, hkv, tq, tk, dh, Q.stride(0), Q.stride(1), K.stride(0),
+            K.stride(1), float(rho), idx.data_ptr(), out.data_ptr(), _dt(out), workspace.data_ptr(),
+            workspace.numel(), _stream(dev))
+    _raise(st, "rmm_qk_causal" if causal else "rmm_qk")
     return idx, out
 
 

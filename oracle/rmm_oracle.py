@@ -180,13 +180,16 @@ def kv_head(h: int, hq: int, hkv: int) -> int:
     return h // (hq // hkv)
 
 
-def qk(Q, K, rho: float, heads=None):
+def qk(Q, K, rho: float, heads=None, causal: bool = False):
     """Per-head reduced attention scores.
 
     Q: (hq, tq, dh), K: (hkv, tk, dh).  For each query head h, I_h is chosen
     from the column norms of Q[h] (over its tq rows) and
     S[h] = Q[h][:, I_h] @ K[g(h)][:, I_h]^T.  Raw product: no 1/sqrt(dh)
-    scale and no mask (the pages give neither for the reduced product).
+    scale (the softmax takes it).  With `causal`, the tq queries are the last
+    tq positions of the tk keys (tq <= tk), so query row r sees keys
+    t <= r + tk - tq and every later key gets -inf; the mask acts on the
+    scores only, the selection still reads every row of Q[h].
     Returns (idx (hq, k) int64, S (hq, tq, tk) float64).  With `heads`,
     idx and S cover only those query heads, in the order given.
     """
@@ -196,6 +199,8 @@ def qk(Q, K, rho: float, heads=None):
     hkv, tk, dh2 = K.shape
     if dh2 != dh:
         raise ValueError("Q and K head dims differ")
+    if causal and tq > tk:
+        raise ValueError("causal scores need tq <= tk")
     hs = list(range(hq)) if heads is None else [int(h) for h in heads]
     k = k_rule(rho, dh)
     idx = np.empty((len(hs), k), dtype=np.int64)
@@ -207,6 +212,9 @@ def qk(Q, K, rho: float, heads=None):
         I, _ = select(Qh, rho)
         idx[i] = I
         S[i] = Qh[:, I] @ Kg[:, I].T
+        if causal:
+            for r in range(tq):
+                S[i, r, r + tk - tq + 1:] = -np.inf
     return idx, S
 
 

@@ -102,19 +102,22 @@ def test_qk_rejects_bad_arguments(L):
                 khs=1024, kts=64, rho=0.5, idx=FAKE + (2 << 30), S=FAKE + (3 << 30), sdt=FP32,
                 ws=FAKE + (4 << 30), wsb=1 << 30)
 
-    def call(**kw):
+    def call(fn=L.rmm_qk, **kw):
         a = dict(base, **kw)
-        return L.rmm_qk(a["Q"], a["K"], a["dt"], a["hq"], a["hkv"], a["tq"], a["tk"], a["dh"], a["qhs"], a["qts"],
-                        a["khs"], a["kts"], a["rho"], a["idx"], a["S"], a["sdt"], a["ws"], a["wsb"], None)
+        return fn(a["Q"], a["K"], a["dt"], a["hq"], a["hkv"], a["tq"], a["tk"], a["dh"], a["qhs"], a["qts"],
+                  a["khs"], a["kts"], a["rho"], a["idx"], a["S"], a["sdt"], a["ws"], a["wsb"], None)
 
-    assert call(Q=None) == NULL
-    assert call(rho=0.0) == RHO
-    assert call(hkv=3) == SHAPE              # hq % hkv != 0
-    assert call(tq=0) == SHAPE
-    assert call(qts=32) == SHAPE             # row stride shorter than the head dim
-    assert call(dt=5) == DTYPE
-    assert call(wsb=0) == WS
-    assert call(S=FAKE + (1 << 30)) == ALIAS
+    for fn in (L.rmm_qk, L.rmm_qk_causal):
+        assert call(fn, Q=None) == NULL
+        assert call(fn, rho=0.0) == RHO
+        assert call(fn, hkv=3) == SHAPE              # hq % hkv != 0
+        assert call(fn, tq=0) == SHAPE
+        assert call(fn, qts=32) == SHAPE             # row stride shorter than the head dim
+        assert call(fn, dt=5) == DTYPE
+        assert call(fn, wsb=0) == WS
+        assert call(fn, S=FAKE + (1 << 30)) == ALIAS
+    # causal scores: the queries are the last tq of the tk positions
+    assert call(L.rmm_qk_causal, tq=17, qhs=17 * 64) == SHAPE
 
 
 def test_pv_rejects_bad_arguments(L):

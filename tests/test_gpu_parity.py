@@ -244,6 +244,61 @@ def check_qk(Q, K, rho, dev, tol, out_dtype=torch.float32):
     assert err <= tol, f"rel Frobenius error {err:.3e}"
 
 
+def check_qk_causal(Q, K, rho, dev, tol, out_dtype=torch.float32):
+    idx, S = rmm.qk(Q.to(dev), K.to(dev), rho, out_dtype=out_dtype, causal=True)
+    torch.cuda.synchronize()
+    idx_o, S_o = O.qk(f32(Q), f32(K), rho, causal=True)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    Sg = f32(S)
+    seen = np.isfinite(S_o)
+    # -inf exactly where a key lies after the query position, finite elsewhere
+    np.testing.assert_array_equal(np.isneginf(Sg), ~seen)
+    assert np.all(np.isfinite(Sg[seen]))
+    err = rel_fro(Sg[seen], S_o[seen])
+    assert err <= tol, f"rel Frobenius error {err:.3e}"
+    return S
+
+
+@pytest.mark.parametrize("rho", [0.5, 1.0])
+def test_qk_causal(dev, rho):
+    # square (tq = tk) over several 128 x 128 tiles, whole tiles above the
+    # diagonal skipped; then a chunk of 200 queries at the end of 520 keys
+    w = synth.gqa_qk(hq=4, hkv=2, t=300, dh=128)
+    check_qk_causal(w.tensors["Q"], w.tensors["K"], rho, dev, TOL_BF16)
+    check_qk_causal(w.tensors["Q"], w.tensors["K"], rho, dev, TOL_BF16, out_dtype=torch.bfloat16)
+    w = synth.gqa_qk(hq=4, hkv=1, t=520, dh=64)
+    check_qk_causal(w.tensors["Q"][:, -200:, :].contiguous(), w.tensors["K"], rho, dev, TOL_BF16)
+
+
+def test_qk_causal_large_tiles_fp32_and_decode(dev):
+    # 256 x 256 tiles (16 heads x 1024 x 1024)
+    w = synth.gqa_qk(hq=16, hkv=4, t=1024, dh=128)
+    check_qk_causal(w.tensors["Q"], w.tensors["K"], 0.5, dev, TOL_BF16)
+    # fp32 inputs (vector-ALU product) with a ragged head dim
+    w = synth.gqa_qk(hq=4, hkv=2, t=70, dh=40)
+    check_qk_causal(w.tensors["Q"].float(), w.tensors["K"].float(), 0.5, dev, TOL_FP32)
+    # two new tokens against a cache (streaming pass over K)
+    w = synth.decode_attn_qk(hq=8, hkv=2, tq=2, tk=1000, dh=128)
+    check_qk_causal(w.tensors["Q"], w.tensors["K"], 0.5, dev, TOL_BF16)
+
+
+def test_causal_prefill_attention_chain(dev):
+    # causal scores -> softmax (1/sqrt(dh)) with key energies -> PV on them
+    w = synth.gqa_qk(hq=4, hkv=2, t=384, dh=128)
+    Q, K = w.tensors["Q"], w.tensors["K"]
+    V = synth.attn_pv(h=4, hkv=2, tq=8, tk=384, dv=128).tensors["V"]
+    # each stage against the oracle on the stage's own GPU input
+    S = check_qk_causal(Q, K, 0.5, dev, TOL_BF16)
+    P, E = check_softmax_energy(S.cpu(), dev, scale=128 ** -0.5)
+    Pg = f32(P)
+    assert np.all(Pg[np.isneginf(f32(S))] == 0.0)   # no weight after the query position
+    idx, Og = rmm.pv_energy(P, V.to(dev), E, 0.5)
+    torch.cuda.synchronize()
+    idx_o, O_o = O.pv_given_energy(Pg, f32(V), f32(E), 0.5)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    assert rel_fro(f32(Og), O_o) <= TOL_BF16
+
+
 @pytest.mark.parametrize("rho", [0.5, 1.0])
 def test_qk_small(dev, rho):
     w = synth.gqa_qk(hq=4, hkv=2, t=300, dh=128)

@@ -253,6 +253,40 @@ def pin_qk(ns):
     return None
 
 
+def pin_causal_qk(ns):
+    """Causal scores: query row r of tq is position r + tk - tq of the key
+    sequence, so its row must equal the unmasked scores against the keys up
+    to that position, and its softmax must put zero weight on every later
+    key.  The mask must leave the kept features unchanged, and a single
+    query (decode) sees every key."""
+    r = np.random.default_rng(29)
+    hq, hkv, tq, tk, dh = 4, 2, 5, 9, 8
+    Q = r.standard_normal((hq, tq, dh))
+    K = r.standard_normal((hkv, tk, dh))
+    idx, S = ns.qk(Q, K, 0.5)
+    idx_c, S_c = ns.qk(Q, K, 0.5, causal=True)
+    if not np.array_equal(np.asarray(idx), np.asarray(idx_c)):
+        return "the causal mask changed the kept features"
+    P_c = np.asarray(ns.softmax_rows(S_c))
+    for row in range(tq):
+        seen = row + tk - tq + 1
+        _, S_p = ns.qk(Q, K[:, :seen, :], 0.5)
+        if np.max(np.abs(np.asarray(S_c)[:, row, :seen] - np.asarray(S_p)[:, row, :])) > 0:
+            return f"row {row}: visible scores differ from the scores against the first {seen} keys"
+        P_p = np.asarray(ns.softmax_rows(S_p))[:, row, :]
+        if np.max(np.abs(P_c[:, row, :seen] - P_p)) > 1e-15 or np.any(P_c[:, row, seen:] != 0.0):
+            return f"row {row}: softmax weight on a key after the query position"
+    _, S1 = ns.qk(Q[:, -1:, :], K, 0.5)
+    _, S1c = ns.qk(Q[:, -1:, :], K, 0.5, causal=True)
+    if not np.array_equal(np.asarray(S1), np.asarray(S1c)):
+        return "a single causal query does not see every key"
+    try:
+        ns.qk(K[:, :, :], Q[:2, :3, :], 0.5, causal=True)
+    except ValueError:
+        return None
+    return "causal scores accepted tq > tk"
+
+
 def pin_pv(ns):
     r = np.random.default_rng(17)
     h, hkv, tq, tk, dv = 4, 1, 3, 10, 4
@@ -365,7 +399,7 @@ def pin_retained_energy(ns):
 
 
 PINS = [pin_retained_energy, pin_k_rule, pin_worked_example, pin_dense_loop, pin_reduced_loop, pin_minimax_bruteforce,
-        pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_pv, pin_given_index,
+        pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_causal_qk, pin_pv, pin_given_index,
         pin_softmax_energy]
 
 
@@ -405,17 +439,25 @@ def _mutant(**over):
         idx, _ = _ns.select(A64, rho)
         return idx, _ns._product(A64, B64, idx)
 
-    def qk(Q, K, rho, _ns=ns):
+    def qk(Q, K, rho, heads=None, causal=False, _ns=ns):
         Q64 = np.asarray(Q, dtype=np.float64)
         K64 = np.asarray(K, dtype=np.float64)
         hq, tq, dh = Q64.shape
         hkv, tk, _ = K64.shape
+        if causal and tq > tk:
+            raise ValueError("tq > tk")
         out_i, out_s = [], []
         for h in range(hq):
             g = _ns.kv_head(h, hq, hkv)
             I, _ = _ns.select(Q64[h], rho)
             out_i.append(I)
-            out_s.append(Q64[h][:, I] @ K64[g][:, I].T)
+            Sh = Q64[h][:, I] @ K64[g][:, I].T
+            if causal:
+                for row in range(tq):
+                    for t in range(tk):
+                        if not _ns._visible(row, t, tq, tk):
+                            Sh[row, t] = _ns._masked
+            out_s.append(Sh)
         return np.array(out_i), np.array(out_s)
 
     def pv(P, V, rho, _ns=ns):
@@ -431,6 +473,10 @@ def _mutant(**over):
             out_o.append(P64[h][:, I] @ V64[g][I, :])
         return np.array(out_i), np.array(out_o)
 
+    if not hasattr(ns, "_visible"):
+        ns._visible = lambda row, t, tq, tk: t <= row + tk - tq
+    if not hasattr(ns, "_masked"):
+        ns._masked = -np.inf
     if not hasattr(ns, "_product"):
         ns._product = lambda A, B, idx: A[:, idx] @ B[idx, :]
     if "select" not in over:
@@ -452,6 +498,9 @@ MUTANTS = {
     "bare_binary_ceil": dict(k_rule=lambda rho, d: min(d, max(1, int(math.ceil(rho * d))))),
     "drops_kept_rows_of_B": dict(_product=lambda A, B, idx: A[:, idx] @ B[np.sort(np.setdiff1d(np.arange(B.shape[0]), idx))[:len(idx)], :]
                                  if len(idx) < B.shape[0] else A @ B),
+    "causal_top_left_aligned": dict(_visible=lambda row, t, tq, tk: t <= row),
+    "causal_hides_the_diagonal": dict(_visible=lambda row, t, tq, tk: t < row + tk - tq),
+    "causal_masks_with_zero": dict(_masked=0.0),
     "gqa_modulo_mapping": dict(kv_head=lambda h, hq, hkv: h % hkv),
     "product_sign_flip": dict(_product=lambda A, B, idx: -(A[:, idx] @ B[idx, :])),
     "dense_instead_of_reduced": dict(_product=lambda A, B, idx: A @ B),
@@ -470,6 +519,7 @@ MUTANTS = {
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")   # some planted mistakes overflow on purpose
 def test_planted_mistake_fails_a_pin(name):
     ns = _mutant(**MUTANTS[name])
     failures = []
