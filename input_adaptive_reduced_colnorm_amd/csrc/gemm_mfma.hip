@@ -58,21 +58,6 @@ __device__ __forceinline__ TileCoord tile_of(int bid, int tiles_m, int tiles_n, 
   return c;
 }
 
-// 8x8 transpose of bf16 held as 8 rows x 4 dwords: out[c] holds column c
-// (8 values along the former rows) as 4 dwords.
-__device__ __forceinline__ void transpose8x8(const i32x4 (&in)[8], i32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t lo = (uint32_t)in[2 * p][c >> 1];
-      uint32_t hi = (uint32_t)in[2 * p + 1][c >> 1];
-      out[c][p] = (int)__builtin_amdgcn_perm(hi, lo, sel);
-    }
-  }
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }

@@ -6,16 +6,24 @@
 // cost is reading B, so reading ceil(rho d) of its d rows is the saving.
 // Engineering Notes on the same page: prefill and decode are tuned apart.
 //
-// Layout: the kept rows are split into `splits` slices and the columns into
-// 64-column strips (128 bytes of every kept row); one 256-thread workgroup
-// owns a (slice, strip) pair, so several hundred workgroups keep every CU's
-// memory pipeline busy.  8 lanes span a strip with 16-byte loads and 32 row
-// lanes stride the slice, each with a batch of 8 kept rows in flight while
-// it multiplies the previous batch.  The slice's kept-row list and its
-// activations A[:, I] (fp32) are staged in LDS first, straight from A.
-// Each workgroup folds its 32 row lanes in a fixed order and writes a
-// partial sum per slice; a second kernel adds the slices in slice order, so
-// the result is bitwise reproducible and no workgroup waits on another.
+// The multiply-adds run on the matrix cores: with fp32 FMAs on the vector
+// ALUs every 16 bytes of B cost n x 8 FMAs, which at n = 8 is as long as
+// streaming B itself and does not overlap with it.  Here one wave covers a
+// 128-column strip: lane l loads 8 consecutive kept rows (8 (l / 16) ..)
+// of the 8 columns 8 (l % 16) .. with 16-byte loads, transposes the 8x8
+// block in registers, and feeds eight v_mfma_f32_16x16x32_bf16 (MFMA j
+// takes the columns 8 c + j of the strip, c = l % 16, over 32 kept rows);
+// the activations A[:, I] of the slice (n <= 16 rows, zero padded to 16)
+// sit in LDS as bf16 and are the other operand.  Roofline: HBM; the matrix
+// cores only take the arithmetic off the vector ALUs.
+//
+// Work split: the kept rows are cut into `splits` slices of at most 512
+// (a multiple of 32) and the columns into 128-column strips; a 256-thread
+// workgroup owns a (strip, slice) pair and its 4 waves take the slice's
+// 32-row chunks round robin, every B load of a wave issued before its
+// first MFMA.  The waves are added in a fixed order in LDS; several slices
+// write partial sums that a second kernel adds in slice order, so the
+// result is bitwise reproducible.
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
@@ -25,18 +33,21 @@ namespace rmm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCols = 64;                     // output columns per workgroup
-constexpr int kLanesPerRow = kCols / 8;       // 16-byte lanes per row segment
-constexpr int kRowLanes = kThreads / kLanesPerRow;
-constexpr int kMaxSlice = 512;                // kept rows per workgroup (LDS staged)
-constexpr int kBatch = 8;                     // kept rows in flight per lane
-constexpr int kTargetGroups = 640;            // workgroups aimed for (256 CUs)
+constexpr int kWaves = kThreads / 64;
+constexpr int kCols = 128;                    // output columns per workgroup (one wave's strip)
+constexpr int kChunk = 32;                    // kept rows per MFMA step
+constexpr int kChunksPerWave = 4;
+constexpr int kMaxSlice = kWaves * kChunksPerWave * kChunk;   // 512 kept rows per workgroup
+constexpr int kTargetGroups = 384;            // workgroups aimed for (256 CUs, two resident per CU)
 
-template <int NR, bool A_BF16>
+__device__ __forceinline__ int slice_rows(int k, int splits) {
+  return ((k + splits - 1) / splits + kChunk - 1) / kChunk * kChunk;
+}
+
+template <bool A_BF16>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
-  __shared__ __attribute__((aligned(16))) float s_a[kMaxSlice][NR];
-  __shared__ int32_t s_rows[kMaxSlice];
-  __shared__ float red[kThreads / 64][NR][kCols];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kMaxSlice + 8];   // bf16 activations, row r, kept row t
+  __shared__ float red[kWaves][16][kCols];
   {
     // batch member (attention head): shift every operand to its slice
     const int bz = blockIdx.z;
@@ -48,122 +59,75 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int cl = tid % kLanesPerRow, rl = tid / kLanesPerRow;
-  const int slice = (g.k + g.splits - 1) / g.splits;
+  const int slice = slice_rows(g.k, g.splits);
   const int t0 = blockIdx.y * slice;
   const int L = max(0, min(g.k, t0 + slice) - t0);
+  const int rb = lane >> 4, cg = lane & 15;
+  const int c = blockIdx.x * kCols + cg * 8;
+  const bool col_ok = c < g.m;   // m is a multiple of 8
 
-  // ---- stage the slice: kept rows and the matching activations.  Each
-  //      lane owns up to two kept rows; all their index and activation loads
-  //      are issued before any is used ----
-  constexpr int PER = kMaxSlice / kThreads;
-  int rows[PER];
+  // ---- every B load of this wave first: chunk q covers the slice rows
+  //      (wave + 4 q) * 32 .., the lane its 8 rows 8 rb .. (a row index of
+  //      -1, or a row past the slice, reads as zero) ----
+  i32x4 bv[kChunksPerWave][8];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int i = tid + u * kThreads;
-    rows[u] = i < L ? (g.idx ? g.idx[t0 + i] : t0 + i) : 0;
-  }
-  float av[PER][NR];
+  for (int q = 0; q < kChunksPerWave; ++q) {
+    const int tb = (wave + kWaves * q) * kChunk + 8 * rb;
+    int row[8];
 #pragma unroll
-  for (int u = 0; u < PER; ++u)
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      av[u][r] = 0.f;
-      if (tid + u * kThreads < L && r < g.n && rows[u] >= 0) {   // -1: contributes nothing
-        const size_t off = (size_t)r * g.lda + rows[u];
-        av[u][r] = A_BF16 ? bf16_to_f32(((const uint16_t*)g.A)[off]) : ((const float*)g.A)[off];
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int t = tb + e;
+      row[e] = t < L ? (g.idx ? g.idx[t0 + t] : t0 + t) : -1;
     }
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int i = tid + u * kThreads;
-    if (i < L) {
-      s_rows[i] = rows[u];
-      if (!g.idx && g.idx_out && blockIdx.x == 0) g.idx_out[t0 + i] = t0 + i;
+    for (int e = 0; e < 8; ++e)
+      bv[q][e] = (row[e] >= 0 && col_ok)
+                     ? __builtin_nontemporal_load((const i32x4*)(g.B + (size_t)row[e] * g.ldb + c))
+                     : i32x4{0, 0, 0, 0};
+  }
+
+  // ---- stage A[:, I] of the slice as bf16 (rows past n and kept rows past
+  //      the slice are zero) while the B rows are in flight ----
+  const int L32 = (L + kChunk - 1) / kChunk * kChunk;
+  for (int i = tid; i < L32; i += kThreads) {
+    const int row = i < L ? (g.idx ? g.idx[t0 + i] : t0 + i) : -1;
 #pragma unroll
-      for (int q = 0; q < NR / 4; ++q)
-        *(f32x4*)&s_a[i][4 * q] = f32x4{av[u][4 * q], av[u][4 * q + 1], av[u][4 * q + 2], av[u][4 * q + 3]};
+    for (int r = 0; r < 16; ++r) {
+      uint16_t v = 0;
+      if (r < g.n && row >= 0) {
+        const size_t off = (size_t)r * g.lda + row;
+        v = A_BF16 ? ((const uint16_t*)g.A)[off] : f32_to_bf16(((const float*)g.A)[off]);
+      }
+      s_a[r][i] = v;
     }
   }
   __syncthreads();
 
-  const int c = blockIdx.x * kCols + cl * 8;
-  const bool col_ok = c < g.m;   // m is a multiple of 8
-  float acc[NR][8];
+  f32x4 acc[8];
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
-
-  auto load_batch = [&](int base, i32x4 (&bv)[kBatch]) {
+  for (int q = 0; q < kChunksPerWave; ++q) {
+    const int tb = (wave + kWaves * q) * kChunk;
+    if (tb >= L) break;   // uniform across the wave
+    // A operand: row l % 16 of A, kept rows tb + 8 (l / 16) ..
+    const bf16x8 af = *(const bf16x8*)&s_a[cg][tb + 8 * rb];
+    i32x4 tr[8];
+    transpose8x8(bv[q], tr);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int tl = base + kRowLanes * u;
-      if (tl < L && col_ok && s_rows[tl] >= 0)
-        bv[u] = __builtin_nontemporal_load((const i32x4*)(g.B + (size_t)s_rows[tl] * g.ldb + c));
-      else
-        bv[u] = i32x4{0, 0, 0, 0};
-    }
-  };
-  auto fma_batch = [&](int base, const i32x4 (&bv)[kBatch]) {
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int tl = base + kRowLanes * u;
-      if (tl >= L) break;
-      float a[NR];
-#pragma unroll
-      for (int q = 0; q < NR / 4; ++q) {
-        const f32x4 v = *(const f32x4*)&s_a[tl][4 * q];
-        a[4 * q] = v[0];
-        a[4 * q + 1] = v[1];
-        a[4 * q + 2] = v[2];
-        a[4 * q + 3] = v[3];
-      }
-      float bf[8];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t bits = (uint32_t)bv[u][w];
-        bf[2 * w] = __uint_as_float(bits << 16);
-        bf[2 * w + 1] = __uint_as_float(bits & 0xffff0000u);
-      }
-#pragma unroll
-      for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(a[r], bf[e], acc[r][e]);
-    }
-  };
-
-  constexpr int STEP = kRowLanes * kBatch;
-  i32x4 b0[kBatch], b1[kBatch];
-  int base = rl;
-  if (base < L) load_batch(base, b0);
-  while (base < L) {
-    const int next = base + STEP;
-    if (next < L) load_batch(next, b1);
-    fma_batch(base, b0);
-    if (next >= L) break;
-    const int next2 = next + STEP;
-    if (next2 < L) load_batch(next2, b0);
-    fma_batch(next, b1);
-    base = next2;
+    for (int j = 0; j < 8; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, tr[j]), acc[j], 0, 0, 0);
   }
 
-  // fold the 8 row lanes of each wave (lane bits 3..5), then the 4 waves
+  // ---- lane l, register v of acc[j]: row 4 (l / 16) + v, column
+  //      8 (l % 16) + j of the strip.  Waves are added in order ----
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
+  for (int v = 0; v < 4; ++v) {
+    const int r = 4 * rb + v;
+    if (r < g.n) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[r][e];
-      v += __shfl_xor(v, 8, 64);
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      acc[r][e] = v;
+      for (int j = 0; j < 8; ++j) red[wave][r][cg * 8 + j] = acc[j][v];
     }
-  if (lane < kLanesPerRow) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[wave][r][cl * 8 + e] = acc[r][e];
   }
   __syncthreads();
   const bool direct = g.splits == 1;
@@ -174,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
     if (col >= g.m) continue;
     float v = red[0][r][cc];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) v += red[w][r][cc];
+    for (int w = 1; w < kWaves; ++w) v += red[w][r][cc];
     if (direct) {
       const size_t off = (size_t)r * g.ldy + col;
       if (g.y_bf16)
@@ -203,14 +167,6 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const GemvArgs g) {
     ((float*)g.Y)[off] = v;
 }
 
-template <int NR>
-void launch_nr(const GemvArgs& g, dim3 grid, hipStream_t s) {
-  if (g.a_bf16)
-    gemv_kernel<NR, true><<<grid, kThreads, 0, s>>>(g);
-  else
-    gemv_kernel<NR, false><<<grid, kThreads, 0, s>>>(g);
-}
-
 }  // namespace
 
 int gemv_splits(int k, int m, int batch) {
@@ -218,20 +174,22 @@ int gemv_splits(int k, int m, int batch) {
   int splits = (kTargetGroups + strips * batch - 1) / (strips * batch);
   const int min_splits = (k + kMaxSlice - 1) / kMaxSlice;
   if (splits < min_splits) splits = min_splits;
-  // at least 64 kept rows per slice
-  const int max_splits = (k + 63) / 64;
+  // at least one 32-row chunk per wave
+  const int max_splits = (k + kWaves * kChunk - 1) / (kWaves * kChunk);
   if (splits > max_splits) splits = max_splits > min_splits ? max_splits : min_splits;
-  return splits < 1 ? 1 : splits;
+  if (splits < 1) splits = 1;
+  // slices are whole chunks: drop splits that would be empty
+  const int slice = ((k + splits - 1) / splits + kChunk - 1) / kChunk * kChunk;
+  return (k + slice - 1) / slice;
 }
 
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s) {
+  if (g.n > 16) return hipErrorInvalidValue;
   dim3 grid((g.m + kCols - 1) / kCols, g.splits, g.batch);
-  if (g.n <= 4)
-    launch_nr<4>(g, grid, s);
-  else if (g.n <= 8)
-    launch_nr<8>(g, grid, s);
+  if (g.a_bf16)
+    gemv_kernel<true><<<grid, kThreads, 0, s>>>(g);
   else
-    launch_nr<16>(g, grid, s);
+    gemv_kernel<false><<<grid, kThreads, 0, s>>>(g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.splits == 1) return e;
   gemv_reduce_kernel<<<dim3((g.n * g.m + 255) / 256, g.batch), 256, 0, s>>>(g);

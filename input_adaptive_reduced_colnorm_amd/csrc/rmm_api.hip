@@ -318,18 +318,19 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
       break;
     }
     case MatPath::kDecode: {
-      // rho < 1: one selection kernel; rho = 1: the GEMV runs over all rows
-      // of B and writes the identity index itself
+      // rho < 1: one selection kernel; rho = 1: the identity index
       if (!p.all)
         RMM_LAUNCH(launch_decode_select(A, bf16, lda, (int)n, (int)d, (int)p.k, idx, nullptr,
                                         d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, s));
+      else
+        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
       RMM_LAUNCH(mk.mark(1));
       RMM_LAUNCH(mk.mark(2));
       RMM_LAUNCH(mk.mark(3));
       GemvArgs g{};
       g.A = A; g.a_bf16 = bf16; g.lda = lda;
       g.B = (const uint16_t*)B; g.ldb = ldb;
-      g.idx = p.all ? nullptr : idx; g.idx_out = p.all ? idx : nullptr;
+      g.idx = p.all ? nullptr : idx;
       g.k = (int)p.k; g.n = (int)n; g.m = (int)m;
       g.partial = (float*)(ws + p.off_part); g.splits = p.gemv_splits;
       g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;
@@ -483,7 +484,7 @@ rmm_status_t rmm_matmul_idx(const void* A, const void* B, int dtype, int64_t n, 
       GemvArgs g{};
       g.A = A; g.a_bf16 = bf16; g.lda = lda;
       g.B = (const uint16_t*)B; g.ldb = ldb;
-      g.idx = ipad; g.idx_out = nullptr;
+      g.idx = ipad;
       g.k = (int)k; g.n = (int)n; g.m = (int)m;
       g.partial = (float*)(ws + p.off_part); g.splits = p.gemv_splits;
       g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;
@@ -837,7 +838,7 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
     GemvArgs g{};
     g.A = P; g.a_bf16 = !p_f32; g.lda = p_ts; g.a_bs = p_hs;
     g.B = (const uint16_t*)V; g.ldb = v_ts; g.b_bs = v_hs; g.b_group = group;
-    g.idx = p.all ? nullptr : idx; g.idx_bs = p.k; g.idx_out = nullptr;
+    g.idx = p.all ? nullptr : idx; g.idx_bs = p.k;
     g.k = (int)p.k; g.n = (int)tq; g.m = (int)dv;
     g.partial = (float*)(ws + p.off_gpart); g.splits = p.gemv_splits;
     g.Y = O; g.y_bf16 = o_dtype == RMM_BF16; g.ldy = dv; g.y_bs = tq * dv;

@@ -48,4 +48,20 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return chunk ^ ((row ^ (row >> 3)) & 7);
 }
 
+// 8x8 transpose of bf16 held as 8 rows x 4 dwords: out[c] holds column c
+// (the 8 values along the former rows) as 4 dwords, i.e. the 8-deep K run
+// of one column that a matrix-core operand lane takes.
+__device__ __forceinline__ void transpose8x8(const i32x4 (&in)[8], i32x4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = (uint32_t)in[2 * p][c >> 1];
+      const uint32_t hi = (uint32_t)in[2 * p + 1][c >> 1];
+      out[c][p] = (int)__builtin_amdgcn_perm(hi, lo, sel);
+    }
+  }
+}
+
 }  // namespace rmm

@@ -83,18 +83,18 @@ hipError_t launch_gemm_simt(const SimtArgs& g, hipStream_t s);
 hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int32_t* idx,
                                 float* scores, uint32_t* gkeys, hipStream_t s);
 
-// GEMV over the kept rows of B, split into `splits` slices of kept rows
-// (gemv_splits) whose partial sums partial[splits][n][m] are added in slice
-// order by a second kernel (splits == 1 writes Y directly).  A is read in
-// place (n <= 16 rows).  idx == nullptr means the identity (dense), and then
-// idx_out (if not null) receives 0..k-1.  m must be a multiple of 8.
-// Batched (per attention head b < batch): A + b*a_bs, B + (b / b_group)*b_bs,
+// GEMV over the kept rows of B on the matrix cores (n <= 16 rows of A, read
+// in place and rounded to bf16: exact for bf16 A), split into `splits`
+// slices of kept rows (gemv_splits) whose partial sums
+// partial[splits][n][m] are added in slice order by a second kernel
+// (splits == 1 writes Y directly).  idx == nullptr means the identity
+// (dense).  m must be a multiple of 8, B rows 16-byte aligned.  Batched (per
+// attention head b < batch): A + b*a_bs, B + (b / b_group)*b_bs,
 // idx + b*idx_bs, Y + b*y_bs (element strides; batch 1 needs none).
 struct GemvArgs {
   const void* A; bool a_bf16; int64_t lda;
   const uint16_t* B; int64_t ldb;
   const int32_t* idx;
-  int32_t* idx_out;
   int k, n, m;
   float* partial; int splits;
   void* Y; bool y_bf16; int64_t ldy;
