@@ -133,6 +133,38 @@ rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n
                               void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
 
 /* ---------------------------------------------------------------------
+ * rmm_matmul_w8: the reduced product with int8 weights,
+ *   Y[i][c] = scale[c] * sum over t < k of A[i][I_t] Bq[I_t][c],
+ * i.e. A[:, I] (Bq[I, :] diag(scale)) with I selected from A exactly as in
+ * rmm_matmul.  The weights are symmetric per-output-channel int8 (one fp32
+ * scale per column of B): hackcv.com, "Compatibility & generalization"
+ * (RMM stacks with INT8), and gist.science, Experimental Results
+ * ("Compatibility": INT8 weight quantisation); neither page gives the
+ * quantisation scheme, so this per-channel form is the one fixed here.
+ *   A      bf16 (a_dtype must be RMM_BF16), row-major, lda >= d.
+ *   Bq     int8 [d][ldb] row-major, ldb >= m, Bq 8-byte aligned, and m and
+ *          ldb multiples of 8.  Values in [-128, 127], widened to bf16
+ *          exactly on the device.
+ *   scale  fp32 [m], device.
+ *   idx, Y, y_dtype, ldy, rho as in rmm_matmul (n <= 16 runs the GEMV that
+ *   reads only the kept rows of Bq: half the bytes of bf16 weights).
+ *   Workspace: rmm_matmul_w8_workspace(n, d, m, lda, rho) bytes, 256-byte
+ *   aligned (0 means none needed).
+ * Errors as rmm_matmul; RMM_ERR_DTYPE for an A that is not bf16,
+ * RMM_ERR_SHAPE for m or ldb not a multiple of 8, RMM_ERR_ALIGN for a
+ * misaligned Bq, scale, idx or Y.
+ * ------------------------------------------------------------------- */
+size_t rmm_matmul_w8_workspace(int64_t n, int64_t d, int64_t m, int64_t lda, double rho);
+rmm_status_t rmm_matmul_w8(const void* A, int a_dtype, const int8_t* Bq, const float* scale, int64_t n, int64_t d,
+                           int64_t m, int64_t lda, int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype,
+                           int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+/* rmm_matmul_w8 with the five stage events of rmm_matmul_timed. */
+rmm_status_t rmm_matmul_w8_timed(const void* A, int a_dtype, const int8_t* Bq, const float* scale, int64_t n,
+                                 int64_t d, int64_t m, int64_t lda, int64_t ldb, double rho, int32_t* idx, void* Y,
+                                 int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* stage_events);
+
+/* ---------------------------------------------------------------------
  * rmm_matmul_idx: Y = sum over t < k of A[:, idx[t]] B[idx[t], :], the
  * reduced product over an index set the caller supplies (for instance one
  * rmm_select on X reused for the Q, K and V projections, or a random set

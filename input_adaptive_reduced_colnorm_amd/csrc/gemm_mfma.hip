@@ -17,7 +17,9 @@
 // barrier per K tile.  LDS rows are 128 bytes (64 bf16 along K) with an XOR
 // swizzle of the 16-byte chunks.
 // B tiles that are K-major in memory (weights, V) are transposed in
-// registers in 8x8 blocks (v_perm) before they reach LDS.
+// registers in 8x8 blocks (v_perm) before they reach LDS; int8 weights are
+// loaded 8 bytes at a time and widened to bf16 just before that transpose,
+// their per-column scale applied in the epilogue.
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
@@ -65,8 +67,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // WAVES = 4: waves in a 2x2 grid, each (BM/2) x (BN/2).
 // WAVES = 8: waves in a 2x4 grid, each (BM/2) x (BN/4); two waves share a
 // SIMD so one wave's MFMAs cover the other's barrier and LDS latency.
-template <int BM, int BN, bool KMAJOR, bool GATHER, bool A_F32, int WAVES>
+template <int BM, int BN, bool KMAJOR, bool GATHER, bool A_F32, int WAVES, bool B_I8 = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs g) {
+  static_assert(KMAJOR || !B_I8, "int8 weights come K-major");
+  constexpr uint32_t BE = B_I8 ? 1u : 2u;         // bytes per B element
   constexpr int NT = 64 * WAVES;
   constexpr int WGN = WAVES / 2;                   // wave grid: 2 x WGN
   constexpr int WM = BM / 2, WN = BN / WGN;
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
   const char* Ab = (const char*)g.A + (size_t)b * g.a_bs * ES;
-  const char* Bb = (const char*)g.B + (size_t)(b / g.b_group) * g.b_bs * 2;
+  const char* Bb = (const char*)g.B + (size_t)(b / g.b_group) * g.b_bs * BE;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, g.a_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, g.b_bytes);
   const int32_t* idxb = GATHER ? g.idx + (size_t)b * g.idx_bs : nullptr;
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
 
   constexpr int A_REGS = A_F32 ? 2 * A_CH : A_CH;
   i32x4 ra_regs[A_REGS];
-  i32x4 rb_regs[KMAJOR ? BR : B_CH];
+  typename RowPiece<B_I8>::type rb_regs[KMAJOR ? BR : B_CH];
   i32x4 idx_lo, idx_hi;   // kept rows for the next tile to load
 
   auto load_idx = [&](int kt) {
@@ -162,8 +166,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
             row = e < 4 ? idx_lo[e] : idx_hi[e - 4];
           else
             row = kt * BK + kb_row0 + e;
-          const uint32_t off = ((uint32_t)(row * g.ldb + kb_col) * 2u) | kb_colmask;
-          rb_regs[e] = buf_load16(rb, off);
+          const uint32_t off = ((uint32_t)(row * g.ldb + kb_col) * BE) | kb_colmask;
+          if constexpr (B_I8)
+            rb_regs[e] = buf_load8(rb, off);
+          else
+            rb_regs[e] = buf_load16(rb, off);
         }
       }
     } else {
@@ -192,9 +199,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     }
     if constexpr (KMAJOR) {
       if (kb_owner) {
+        // int8 weights are widened to bf16 (exactly) here, once in flight
+        i32x4 rows[BR];
+#pragma unroll
+        for (int e = 0; e < BR; ++e) {
+          if constexpr (B_I8)
+            rows[e] = i8x8_to_bf16x8(rb_regs[e]);
+          else
+            rows[e] = rb_regs[e];
+        }
         if constexpr (BR == 8) {
           i32x4 tr[8];
-          transpose8x8(rb_regs, tr);
+          transpose8x8(rows, tr);
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             const int nrow = kb_cg * 8 + c;
@@ -206,8 +222,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
           for (int c = 0; c < 8; ++c) {
             const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
             i32x2 v;
-            v[0] = (int)__builtin_amdgcn_perm((uint32_t)rb_regs[1][c >> 1], (uint32_t)rb_regs[0][c >> 1], sel);
-            v[1] = (int)__builtin_amdgcn_perm((uint32_t)rb_regs[3][c >> 1], (uint32_t)rb_regs[2][c >> 1], sel);
+            v[0] = (int)__builtin_amdgcn_perm((uint32_t)rows[1][c >> 1], (uint32_t)rows[0][c >> 1], sel);
+            v[1] = (int)__builtin_amdgcn_perm((uint32_t)rows[3][c >> 1], (uint32_t)rows[2][c >> 1], sel);
             const int nrow = kb_cg * 8 + c;
             *(i32x2*)(Bs + nrow * 128 + swz(nrow, kb_kg) * 16 + kb_h * 8) = v;
           }
@@ -303,12 +319,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     for (int j = 0; j < TN; ++j) {
       const int col = n0 + wn * WN + j * 32 + li;
       const int row0 = m0 + wm * WM + i * 32 + 4 * lk;
+      const float cs = g.col_scale && col < g.N ? g.col_scale[col] : 1.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = row0 + 8 * (v >> 2) + (v & 3);
         if (full || (row < g.M && col < g.N)) {
           const size_t off = (size_t)row * g.ldc + col;
-          const float y = some_masked && (int64_t)col > (int64_t)row + g.causal_off ? -INFINITY : acc[i][j][v];
+          const float a = g.col_scale ? acc[i][j][v] * cs : acc[i][j][v];
+          const float y = some_masked && (int64_t)col > (int64_t)row + g.causal_off ? -INFINITY : a;
           if (g.c_bf16)
             __builtin_nontemporal_store(f32_to_bf16(y), (uint16_t*)Cb + off);
           else
@@ -361,6 +379,28 @@ void dispatch_af32(const GemmArgs& g, hipStream_t s) {
   } else {
     gemm_bf16_kernel<BM, BN, false, false, true, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
   }
+}
+
+// int8 K-major B (weights with a scale per output column in g.col_scale),
+// rows gathered by idx or read in order.
+template <int BM, int BN, int WAVES>
+void dispatch_w8(const GemmArgs& g, hipStream_t s) {
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  dim3 grid(tiles, g.batch);
+  if (g.idx)
+    gemm_bf16_kernel<BM, BN, true, true, false, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(g);
+  else
+    gemm_bf16_kernel<BM, BN, true, false, false, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(g);
+}
+
+hipError_t launch_gemm_w8(const GemmArgs& g, hipStream_t s) {
+  if (!g.b_kmajor || !g.b_i8) return hipErrorInvalidValue;
+  const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+  if (t256 >= 192 && g.N >= 256 && g.M >= 256)
+    dispatch_w8<256, 256, 8>(g, s);
+  else
+    dispatch_w8<128, 128, 4>(g, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s) {

@@ -23,7 +23,9 @@
 // 32-row chunks round robin, every B load of a wave issued before its
 // first MFMA.  The waves are added in a fixed order in LDS; several slices
 // write partial sums that a second kernel adds in slice order, so the
-// result is bitwise reproducible.
+// result is bitwise reproducible.  int8 weights (a scale per output column,
+// applied to the finished sum) are read with 8-byte loads and widened to
+// bf16 in registers before the same transpose.
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
@@ -44,15 +46,16 @@ __device__ __forceinline__ int slice_rows(int k, int splits) {
   return ((k + splits - 1) / splits + kChunk - 1) / kChunk * kChunk;
 }
 
-template <bool A_BF16>
+template <bool A_BF16, bool B_I8>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
+  constexpr int BE = B_I8 ? 1 : 2;   // bytes per B element
   __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kMaxSlice + 8];   // bf16 activations, row r, kept row t
   __shared__ float red[kWaves][16][kCols];
   {
     // batch member (attention head): shift every operand to its slice
     const int bz = blockIdx.z;
     g.A = (const char*)g.A + (size_t)bz * g.a_bs * (A_BF16 ? 2 : 4);
-    g.B += (size_t)(bz / g.b_group) * g.b_bs;
+    g.B = (const char*)g.B + (size_t)(bz / g.b_group) * g.b_bs * BE;
     if (g.idx) g.idx += (size_t)bz * g.idx_bs;
     g.Y = (char*)g.Y + (size_t)bz * g.y_bs * (g.y_bf16 ? 2 : 4);
     g.partial += (size_t)bz * g.splits * g.n * g.m;
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   // ---- every B load of this wave first: chunk q covers the slice rows
   //      (wave + 4 q) * 32 .., the lane its 8 rows 8 rb .. (a row index of
   //      -1, or a row past the slice, reads as zero) ----
-  i32x4 bv[kChunksPerWave][8];
+  typename RowPiece<B_I8>::type bv[kChunksPerWave][8];
 #pragma unroll
   for (int q = 0; q < kChunksPerWave; ++q) {
     const int tb = (wave + kWaves * q) * kChunk + 8 * rb;
@@ -80,10 +83,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
       row[e] = t < L ? (g.idx ? g.idx[t0 + t] : t0 + t) : -1;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      bv[q][e] = (row[e] >= 0 && col_ok)
-                     ? __builtin_nontemporal_load((const i32x4*)(g.B + (size_t)row[e] * g.ldb + c))
-                     : i32x4{0, 0, 0, 0};
+    for (int e = 0; e < 8; ++e) {
+      typedef typename RowPiece<B_I8>::type R;
+      const char* src = (const char*)g.B + ((size_t)row[e] * g.ldb + c) * BE;
+      bv[q][e] = (row[e] >= 0 && col_ok) ? __builtin_nontemporal_load((const R*)src) : R{};
+    }
   }
 
   // ---- stage A[:, I] of the slice as bf16 (rows past n and kept rows past
@@ -112,8 +116,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
     if (tb >= L) break;   // uniform across the wave
     // A operand: row l % 16 of A, kept rows tb + 8 (l / 16) ..
     const bf16x8 af = *(const bf16x8*)&s_a[cg][tb + 8 * rb];
-    i32x4 tr[8];
-    transpose8x8(bv[q], tr);
+    i32x4 rows8[8], tr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (B_I8)
+        rows8[e] = i8x8_to_bf16x8(bv[q][e]);
+      else
+        rows8[e] = bv[q][e];
+    }
+    transpose8x8(rows8, tr);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, tr[j]), acc[j], 0, 0, 0);
@@ -141,6 +152,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
     for (int w = 1; w < kWaves; ++w) v += red[w][r][cc];
     if (direct) {
       const size_t off = (size_t)r * g.ldy + col;
+      if (g.col_scale) v *= g.col_scale[col];
       if (g.y_bf16)
         ((uint16_t*)g.Y)[off] = f32_to_bf16(v);
       else
@@ -160,6 +172,7 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const GemvArgs g) {
   const float* part = g.partial + (size_t)bz * g.splits * g.n * g.m;
   float v = 0.f;
   for (int s = 0; s < g.splits; ++s) v += part[(size_t)s * g.n * g.m + i];
+  if (g.col_scale) v *= g.col_scale[col];
   const size_t off = (size_t)bz * g.y_bs + (size_t)r * g.ldy + col;
   if (g.y_bf16)
     ((uint16_t*)g.Y)[off] = f32_to_bf16(v);
@@ -184,12 +197,14 @@ int gemv_splits(int k, int m, int batch) {
 }
 
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s) {
-  if (g.n > 16) return hipErrorInvalidValue;
+  if (g.n > 16 || (g.b_i8 && !g.a_bf16)) return hipErrorInvalidValue;
   dim3 grid((g.m + kCols - 1) / kCols, g.splits, g.batch);
-  if (g.a_bf16)
-    gemv_kernel<true><<<grid, kThreads, 0, s>>>(g);
+  if (g.b_i8)
+    gemv_kernel<true, true><<<grid, kThreads, 0, s>>>(g);   // int8 weights take bf16 activations
+  else if (g.a_bf16)
+    gemv_kernel<true, false><<<grid, kThreads, 0, s>>>(g);
   else
-    gemv_kernel<false><<<grid, kThreads, 0, s>>>(g);
+    gemv_kernel<false, false><<<grid, kThreads, 0, s>>>(g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.splits == 1) return e;
   gemv_reduce_kernel<<<dim3((g.n * g.m + 255) / 256, g.batch), 256, 0, s>>>(g);

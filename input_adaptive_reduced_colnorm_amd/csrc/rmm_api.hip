@@ -400,6 +400,133 @@ rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n
                      stage_events);
 }
 
+// ------------------------------ matmul_w8 -----------------------------------
+
+size_t rmm_matmul_w8_workspace(int64_t n, int64_t d, int64_t m, int64_t lda, double rho) {
+  if (!dim_ok(n) || !dim_ok(d) || !dim_ok(m) || lda < d || !rho_ok(rho)) return 0;
+  // the A side decides the path; B is always vector-loadable here
+  MatPlan a = plan_matmul(n, d, m, lda, m, RMM_BF16, rho, true, true);
+  MatPlan b = plan_matmul(n, d, m, lda, m, RMM_BF16, rho, false, true);
+  return a.total > b.total ? a.total : b.total;
+}
+
+namespace {
+
+rmm_status_t matmul_w8_impl(const void* A, int a_dtype, const int8_t* Bq, const float* scale, int64_t n, int64_t d,
+                            int64_t m, int64_t lda, int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype,
+                            int64_t ldy, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* stage_events) {
+  if (!A || !Bq || !scale || !idx || !Y) return RMM_ERR_NULL;
+  if (!rho_ok(rho)) return RMM_ERR_RHO;
+  if (a_dtype != RMM_BF16 || !dtype_ok(y_dtype)) return RMM_ERR_DTYPE;
+  if (!dim_ok(n) || !dim_ok(d) || !dim_ok(m) || lda < d || ldb < m || ldy < m || lda >= kMaxDim ||
+      ldb >= kMaxDim || ldy >= kMaxDim || m % 8 != 0 || ldb % 8 != 0)
+    return RMM_ERR_SHAPE;
+  if (!aligned(A, 2) || !aligned(Bq, 8) || !aligned(scale, 4) || !aligned(idx, 4) ||
+      !aligned(Y, elt_size(y_dtype)))
+    return RMM_ERR_ALIGN;
+  const MatPlan p = plan_matmul(n, d, m, lda, ldb, RMM_BF16, rho, aligned(A, 16), true);
+  if (p.path == MatPath::kSimt) return RMM_ERR_SHAPE;   // not reachable: B is vector-loadable
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
+    return RMM_ERR_WORKSPACE;
+  const Span sa = span3(A, 1, 0, n, lda, d, 2), sb = span3(Bq, 1, 0, d, ldb, m, 1);
+  const Span sc = span3(scale, 1, 0, 1, m, m, 4);
+  const Span si = span3(idx, 1, 0, 1, p.k, p.k, 4), sy = span3(Y, 1, 0, n, ldy, m, elt_size(y_dtype));
+  if (overlap(si, sa) || overlap(si, sb) || overlap(si, sc) || overlap(sy, sa) || overlap(sy, sb) ||
+      overlap(sy, sc) || overlap(sy, si))
+    return RMM_ERR_ALIAS;
+  if (p.total > 0) {
+    const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
+    if (overlap(sw, sa) || overlap(sw, sb) || overlap(sw, sc) || overlap(sw, si) || overlap(sw, sy))
+      return RMM_ERR_ALIAS;
+  }
+  const int64_t b_bytes = (d - 1) * ldb + m;
+  if (p.path != MatPath::kDecode) {
+    const int64_t a_bytes = p.path == MatPath::kMfmaDirect ? ((n - 1) * lda + d) * 2 : n * p.k_pad * 2;
+    if (b_bytes > kMaxOperandBytes || a_bytes > kMaxOperandBytes) return RMM_ERR_SHAPE;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const Marks mk{stage_events, s};
+  clear_error();
+  RMM_LAUNCH(mk.mark(0));
+  if (p.path == MatPath::kDecode) {
+    if (!p.all)
+      RMM_LAUNCH(launch_decode_select(A, true, lda, (int)n, (int)d, (int)p.k, idx, nullptr,
+                                      d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, s));
+    else
+      RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
+    RMM_LAUNCH(mk.mark(1));
+    RMM_LAUNCH(mk.mark(2));
+    RMM_LAUNCH(mk.mark(3));
+    GemvArgs g{};
+    g.A = A; g.a_bf16 = true; g.lda = lda;
+    g.B = Bq; g.ldb = ldb; g.b_i8 = true; g.col_scale = scale;
+    g.idx = p.all ? nullptr : idx;
+    g.k = (int)p.k; g.n = (int)n; g.m = (int)m;
+    g.partial = (float*)(ws + p.off_part); g.splits = p.gemv_splits;
+    g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;
+    RMM_LAUNCH(launch_gemv(g, s));
+    RMM_LAUNCH(mk.mark(4));
+    return RMM_OK;
+  }
+  GemmArgs g{};
+  g.B = (const uint16_t*)(const void*)Bq; g.b_bs = 0; g.ldb = ldb; g.b_group = 1; g.b_i8 = true;
+  g.b_bytes = (uint32_t)b_bytes;
+  g.col_scale = scale;
+  g.C = Y; g.c_bs = 0; g.ldc = ldy; g.c_bf16 = y_dtype == RMM_BF16;
+  g.M = (int)n; g.N = (int)m; g.batch = 1; g.b_kmajor = true;
+  if (p.path == MatPath::kMfmaDirect) {
+    RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
+    RMM_LAUNCH(mk.mark(1));
+    RMM_LAUNCH(mk.mark(2));
+    RMM_LAUNCH(mk.mark(3));
+    g.A = (const uint16_t*)A; g.a_bs = 0; g.lda = lda;
+    g.idx = nullptr; g.idx_bs = 0;
+    g.K = (int)d;
+    g.a_bytes = (uint32_t)(((n - 1) * lda + d) * 2);
+  } else {
+    int32_t* ipad = (int32_t*)(ws + p.off_ipad);
+    if (p.use_sel) {
+      RMM_LAUNCH(run_select(p.sel, ws, A, true, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk, ipad, p.k_pad));
+    } else {
+      RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, ipad, 0, (int)p.k_pad, s));
+      RMM_LAUNCH(mk.mark(1));
+    }
+    RMM_LAUNCH(mk.mark(2));
+    uint16_t* pk = (uint16_t*)(ws + p.off_pack);
+    RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, idx, p.k, (int)p.k, (int)p.k_pad, 1, (int)n, pk, 0, s));
+    RMM_LAUNCH(mk.mark(3));
+    g.A = pk; g.a_bs = 0; g.lda = p.k_pad;
+    g.idx = ipad; g.idx_bs = 0;
+    g.K = (int)p.k_pad;
+    g.a_bytes = (uint32_t)(n * p.k_pad * 2);
+  }
+  RMM_LAUNCH(launch_gemm_w8(g, s));
+  RMM_LAUNCH(mk.mark(4));
+  return RMM_OK;
+}
+
+}  // namespace
+
+rmm_status_t rmm_matmul_w8(const void* A, int a_dtype, const int8_t* Bq, const float* scale, int64_t n, int64_t d,
+                           int64_t m, int64_t lda, int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype,
+                           int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  return matmul_w8_impl(A, a_dtype, Bq, scale, n, d, m, lda, ldb, rho, idx, Y, y_dtype, ldy, workspace,
+                        workspace_bytes, stream, nullptr);
+}
+
+rmm_status_t rmm_matmul_w8_timed(const void* A, int a_dtype, const int8_t* Bq, const float* scale, int64_t n,
+                                 int64_t d, int64_t m, int64_t lda, int64_t ldb, double rho, int32_t* idx, void* Y,
+                                 int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* stage_events) {
+  if (!stage_events) return RMM_ERR_NULL;
+  for (int i = 0; i < 5; ++i)
+    if (!stage_events[i]) return RMM_ERR_NULL;
+  return matmul_w8_impl(A, a_dtype, Bq, scale, n, d, m, lda, ldb, rho, idx, Y, y_dtype, ldy, workspace,
+                        workspace_bytes, stream, stage_events);
+}
+
 // ----------------------------- matmul_idx -----------------------------------
 
 namespace {

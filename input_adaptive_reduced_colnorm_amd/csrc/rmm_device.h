@@ -28,6 +28,15 @@ __device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+__device__ __forceinline__ i32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// A row piece of 8 B-matrix elements while in flight: 8 bf16 (16 bytes) or
+// 8 int8 weights (8 bytes).
+template <bool I8> struct RowPiece { typedef i32x4 type; };
+template <> struct RowPiece<true> { typedef i32x2 type; };
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
@@ -46,6 +55,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // row-wise fills and the 32-row MFMA operand reads free of bank conflicts.
 __device__ __forceinline__ int swz(int row, int chunk) {
   return chunk ^ ((row ^ (row >> 3)) & 7);
+}
+
+// 8 int8 values (two dwords, byte i = value i) -> 8 bf16 (four dwords, value
+// 2w in the low half of dword w).  Exact: an int8 needs at most 8
+// significant bits, which bf16 holds.  No integer-to-float conversion is
+// used (the compiler folds a byte extract plus a signed conversion into an
+// unsigned one that turns negative bytes into 2^32 - |q|): each byte b is
+// offset to u = b ^ 0x80 in [0, 255] and placed under the exponent of
+// 2^23, so the float is 2^23 + u exactly, and subtracting 2^23 + 128 gives
+// the signed value q = u - 128 exactly.
+__device__ __forceinline__ i32x4 i8x8_to_bf16x8(i32x2 v) {
+  i32x4 o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t u = (uint32_t)v[h] ^ 0x80808080u;
+    float f[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      // bytes (low to high): u.byte b, 0x00, 0x00, 0x4B  ->  2^23 + u_b
+      const uint32_t bits = __builtin_amdgcn_perm(0x4B000000u, u, 0x070c0c00u | (uint32_t)b);
+      f[b] = __uint_as_float(bits) - 8388736.0f;
+    }
+    o[2 * h] = (int)__builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    o[2 * h + 1] = (int)__builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
+  }
+  return o;
 }
 
 // 8x8 transpose of bf16 held as 8 rows x 4 dwords: out[c] holds column c

@@ -57,6 +57,8 @@ struct GemmArgs {
   int M, N, K, batch;   // K: multiple of 64 (A zero padded / B rows -1 padded)
   bool b_kmajor;
   uint32_t a_bytes, b_bytes;  // per-batch extents (bytes) for the buffer descriptors
+  bool b_i8;                  // K-major B holds int8 weights (widened to bf16 exactly)
+  const float* col_scale;     // if not null: C[i][j] *= col_scale[j]
   bool causal;          // C[i][j] = -inf where j > i + causal_off (tiles wholly above skip the product)
   int64_t causal_off;
 };
@@ -64,6 +66,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Same product with A given as fp32 (rounded to bf16 while staged); a gather
 // list (idx) is honoured for K-major B only.
 hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s);
+// Same product with int8 K-major B (b_i8, rows 8-byte aligned) and the
+// per-column scale col_scale; a gather list (idx) is honoured.
+hipError_t launch_gemm_w8(const GemmArgs& g, hipStream_t s);
 
 // Generic FMA GEMM over strided, optionally gathered operands (fp32 or bf16
 // inputs, any alignment):
@@ -83,22 +88,26 @@ hipError_t launch_gemm_simt(const SimtArgs& g, hipStream_t s);
 hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int32_t* idx,
                                 float* scores, uint32_t* gkeys, hipStream_t s);
 
-// GEMV over the kept rows of B on the matrix cores (n <= 16 rows of A, read
-// in place and rounded to bf16: exact for bf16 A), split into `splits`
+// GEMV over the kept rows of B (bf16, or int8) on the matrix cores (n <= 16
+// rows of A, read in place and rounded to bf16: exact for bf16 A), split into `splits`
 // slices of kept rows (gemv_splits) whose partial sums
 // partial[splits][n][m] are added in slice order by a second kernel
 // (splits == 1 writes Y directly).  idx == nullptr means the identity
 // (dense).  m must be a multiple of 8, B rows 16-byte aligned.  Batched (per
 // attention head b < batch): A + b*a_bs, B + (b / b_group)*b_bs,
 // idx + b*idx_bs, Y + b*y_bs (element strides; batch 1 needs none).
+// b_i8: B holds int8 weights (rows 8-byte aligned), widened to bf16 exactly;
+// col_scale (if not null) multiplies output column c by col_scale[c] once
+// the sum over the kept rows is complete.
 struct GemvArgs {
   const void* A; bool a_bf16; int64_t lda;
-  const uint16_t* B; int64_t ldb;
+  const void* B; int64_t ldb;
   const int32_t* idx;
   int k, n, m;
   float* partial; int splits;
   void* Y; bool y_bf16; int64_t ldy;
   int batch = 1; int64_t a_bs = 0, b_bs = 0, idx_bs = 0, y_bs = 0; int b_group = 1;
+  bool b_i8 = false; const float* col_scale = nullptr;
 };
 int gemv_splits(int k, int m, int batch = 1);
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);

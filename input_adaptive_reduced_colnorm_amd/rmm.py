@@ -33,6 +33,11 @@ SIGNATURES = {
     "rmm_matmul": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz, _vp]),
     "rmm_matmul_timed": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz,
                                 _vp, _vp]),
+    "rmm_matmul_w8_workspace": (_sz, [_i64, _i64, _i64, _i64, _dbl]),
+    "rmm_matmul_w8": (_int, [_vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz,
+                             _vp]),
+    "rmm_matmul_w8_timed": (_int, [_vp, _int, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp,
+                                   _sz, _vp, _vp]),
     "rmm_matmul_idx_workspace": (_sz, [_i64, _i64, _i64, _int]),
     "rmm_matmul_idx": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _int, _i64, _vp, _sz,
                               _vp]),
@@ -208,6 +213,34 @@ def matmul_idx(A: torch.Tensor, B: torch.Tensor, idx: torch.Tensor, out_dtype=to
                           _stream(dev))
     _raise(st, "rmm_matmul_idx")
     return out
+
+
+def matmul_w8(A: torch.Tensor, Bq: torch.Tensor, scale: torch.Tensor, rho: float, out_dtype=torch.float32,
+              workspace: torch.Tensor = None, out: torch.Tensor = None, idx: torch.Tensor = None):
+    """Reduced product with int8 weights: Y = A[:, I] (Bq[I, :] * scale) with A bf16 (n, d), Bq int8 (d, m)
+    and scale fp32 (m,).  Returns (idx, Y)."""
+    dev = _check_dev(A, Bq)
+    n, d = A.shape
+    d2, m = Bq.shape
+    if d2 != d:
+        raise ValueError("A and Bq disagree on the contraction size")
+    if A.dtype != torch.bfloat16 or Bq.dtype != torch.int8 or scale.dtype != torch.float32:
+        raise TypeError("A bf16, Bq int8 and scale fp32 expected")
+    if A.stride(1) != 1 or Bq.stride(1) != 1 or not scale.is_contiguous() or scale.numel() != m:
+        raise ValueError("unit inner strides and one scale per column of Bq expected")
+    L = lib()
+    kk = k(rho, d)
+    if idx is None:
+        idx = torch.empty(kk, dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((n, m), dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = _ws(L.rmm_matmul_w8_workspace(n, d, m, A.stride(0), float(rho)), dev)
+    st = L.rmm_matmul_w8(A.data_ptr(), RMM_BF16, Bq.data_ptr(), scale.data_ptr(), n, d, m, A.stride(0), Bq.stride(0),
+                         float(rho), idx.data_ptr(), out.data_ptr(), _dt(out), out.stride(0), workspace.data_ptr(),
+                         workspace.numel(), _stream(dev))
+    _raise(st, "rmm_matmul_w8")
+    return idx, out
 
 
 def matmul_workspace(n: int, d: int, m: int, lda: int, dtype, rho: float) -> int:

@@ -39,6 +39,13 @@ bf16 and fp32 values convert to float64 without rounding):
                  that writes P; pv_given_energy selects on supplied scores.
 * given I     -- Y = sum over the entries t of a caller-given list of
                  A[:, t] B[t, :] (entries outside [0, d) ignored).
+* int8 B      -- Y = A[:, I] @ (Bq[I, :] * s[None, :]): weights stored as
+                 int8 with one scale per output column (symmetric per-channel
+                 quantisation; the pages say RMM stacks with INT8 weight
+                 quantisation but give no scheme, so this plainest reading
+                 is the one fixed here).  Selection is unchanged: it reads A.
+                 Source: hackcv.com, "Compatibility & generalization";
+                 gist.science, Experimental Results ("Compatibility").
 * PV          -- per head h: I_h from the column norms of P[h]
                  (queries x keys) over its query rows (the token axis is the
                  contraction axis), and O_h = P[h][:, I_h] @ V[g(h)][I_h, :].
@@ -61,6 +68,7 @@ __all__ = [
     "select",
     "matmul",
     "matmul_given",
+    "matmul_w8",
     "dense",
     "qk",
     "pv",
@@ -160,6 +168,26 @@ def matmul_given(A, B, idx) -> np.ndarray:
     I = np.asarray(idx, dtype=np.int64).ravel()
     I = I[(I >= 0) & (I < d)]
     return A64[:, I] @ B64[I, :]
+
+
+def matmul_w8(A, Bq, scale, rho: float, rows=None):
+    """Reduced product with int8 weights and a float scale per output column.
+
+    The weights are B[j, c] = Bq[j, c] * scale[c] (symmetric per-output-
+    channel int8, the reading of "INT8 weight quantisation" fixed here), so
+    Y = A[:, I] @ (Bq[I, :] * scale) with I the TopK of A's column norms,
+    exactly as for float weights.  Bq holds integers in [-128, 127].
+    Returns (idx, Y) with Y float64 n x m (only `rows` of it if given; the
+    selection still uses every row of A).
+    """
+    A64 = np.asarray(A, dtype=np.float64)
+    s64 = np.asarray(scale, dtype=np.float64).ravel()
+    if np.asarray(Bq).shape[1] != s64.shape[0]:
+        raise ValueError("one scale per column of Bq")
+    idx, _ = select(A64, rho)
+    Ar = A64 if rows is None else A64[np.asarray(rows)]
+    Bk = np.asarray(Bq)[idx, :].astype(np.float64)
+    return idx, Ar[:, idx] @ (Bk * s64[None, :])
 
 
 def dense(A, B) -> np.ndarray:

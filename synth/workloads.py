@@ -187,6 +187,33 @@ def decode_qkv(n=8, d=4096, m=6144, rho=0.8) -> Workload:
                     {"n": n, "d": d, "m": m, "dtype": "bf16", "min_gap": gap})
 
 
+def int8_weights(g: np.random.Generator, d: int, m: int):
+    """Weights N(0, 1/sqrt(d)) stored as symmetric per-output-column int8:
+    scale[c] = max_j |B[j, c]| / 127 and Bq = round(B / scale) in [-127, 127].
+    Returns (Bq int8 tensor, scale fp32 tensor)."""
+    Bq = np.empty((d, m), dtype=np.int8)
+    scale = np.empty(m, dtype=np.float32)
+    step = max(1, (1 << 24) // max(1, d))
+    for c0 in range(0, m, step):
+        blk = g.standard_normal((d, min(step, m - c0)), dtype=np.float32) / np.float32(math.sqrt(d))
+        sc = np.maximum(np.max(np.abs(blk), axis=0), np.float32(1e-30)) / np.float32(127.0)
+        Bq[:, c0:c0 + blk.shape[1]] = np.clip(np.rint(blk / sc), -127, 127).astype(np.int8)
+        scale[c0:c0 + blk.shape[1]] = sc
+    return torch.from_numpy(Bq), torch.from_numpy(scale)
+
+
+def w8_projection(n=8, d=4096, m=6144, rho=0.8, workload=5, name="decode_qkv_8b_w8") -> Workload:
+    """A n x d bf16 (MLP-down activation recipe, boundary separation at rho)
+    with int8 weights of d x m (int8_weights)."""
+    g = rng(workload)
+    z, c = _activation(g, n, d, 0.01 if n > 64 else 0.0)
+    A, gap = _space_columns(z, c, to_bf16, (ceil_keep(rho, d),) if rho < 1.0 else (), literal=False)
+    del z
+    Bq, scale = int8_weights(g, d, m)
+    return Workload(name, {"A": A, "Bq": Bq, "scale": scale}, (rho,),
+                    {"n": n, "d": d, "m": m, "dtype": "bf16 x int8", "min_gap": gap})
+
+
 def gqa_qk(hq=32, hkv=8, t=4096, dh=128, rho=0.5) -> Workload:
     """QK^T prefill: Q (hq, t, dh), K (hkv, t, dh) bf16, per-feature scales.
 

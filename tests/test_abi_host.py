@@ -192,6 +192,30 @@ def test_library_resolves_every_kernel_launch():
     assert not missing, missing
 
 
+def test_matmul_w8_rejects_bad_arguments(L):
+    def call(A=FAKE, adt=BF16, Bq=FAKE + (1 << 30), sc=FAKE + (5 << 30), n=64, d=128, m=64, lda=128, ldb=64, rho=0.5,
+             idx=FAKE + (2 << 30), Y=FAKE + (3 << 30), ydt=FP32, ldy=64, ws=FAKE + (4 << 30), wsb=1 << 30):
+        return L.rmm_matmul_w8(A, adt, Bq, sc, n, d, m, lda, ldb, rho, idx, Y, ydt, ldy, ws, wsb, None)
+
+    assert call(Bq=None) == NULL
+    assert call(sc=None) == NULL
+    assert call(rho=0.0) == RHO
+    assert call(adt=FP32) == DTYPE           # int8 weights take bf16 activations
+    assert call(m=60, ldb=64, ldy=64) == SHAPE   # columns not a multiple of 8
+    assert call(ldb=68) == SHAPE             # row stride not a multiple of 8
+    assert call(ldb=32) == SHAPE             # ldb < m
+    assert call(Bq=FAKE + (1 << 30) + 4) == ALIGN   # 8-byte loads
+    assert call(sc=FAKE + (5 << 30) + 2) == ALIGN
+    assert call(ws=None) == WS
+    assert call(Y=FAKE + (1 << 30)) == ALIAS     # output on top of the weights
+    assert call(idx=FAKE + (5 << 30)) == ALIAS   # index output on top of the scales
+    assert L.rmm_matmul_w8_workspace(64, 128, 64, 128, 1.0) >= 0
+    assert L.rmm_matmul_w8_workspace(64, 128, 64, 128, 0.5) > 0
+    assert L.rmm_matmul_w8_workspace(64, 128, 64, 100, 0.5) == 0   # lda < d
+    assert L.rmm_matmul_w8_timed(FAKE, BF16, FAKE + (1 << 30), FAKE + (5 << 30), 64, 128, 64, 128, 64, 0.5,
+                                 FAKE + (2 << 30), FAKE + (3 << 30), FP32, 64, None, 0, None, None) == NULL
+
+
 def test_matmul_idx_rejects_bad_arguments(L):
     def call(A=FAKE, B=FAKE + (1 << 30), dt=BF16, n=64, d=128, m=64, lda=128, ldb=64, idx=FAKE + (2 << 30), k=32,
              Y=FAKE + (3 << 30), ydt=FP32, ldy=64, ws=FAKE + (4 << 30), wsb=1 << 30):

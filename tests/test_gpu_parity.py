@@ -56,6 +56,18 @@ def check_matmul(A, B, rho, dev, tol, out_dtype=torch.float32, rows=None):
     return err
 
 
+def check_matmul_w8(w, rho, dev, tol, out_dtype=torch.float32, rows=None):
+    A, Bq, sc = w.tensors["A"], w.tensors["Bq"], w.tensors["scale"]
+    print(f"matmul_w8 {tuple(A.shape)} x {tuple(Bq.shape)} rho={rho}", flush=True)
+    idx, Y = rmm.matmul_w8(A.to(dev), Bq.to(dev), sc.to(dev), rho, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    idx_o, Y_o = O.matmul_w8(f32(A), Bq.numpy(), sc.numpy(), rho, rows=rows)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    Yg = f32(Y) if rows is None else f32(Y[torch.as_tensor(rows, device=Y.device)])
+    err = rel_fro(Yg, Y_o)
+    assert err <= tol, f"rel Frobenius error {err:.3e} > {tol}"
+
+
 # ------------------------------- linear ------------------------------------
 
 def test_tiny_projection_fp32(dev):
@@ -231,6 +243,40 @@ def test_select_once_reuse_for_qkv(dev):
         Yp = rmm.matmul_idx(X, W[:, lo:hi].contiguous(), idx)
         torch.cuda.synchronize()
         assert rel_fro(f32(Yp), f32(Y[:, lo:hi])) <= 1e-6
+
+
+# --------------------------- int8 weights ----------------------------------
+
+@pytest.mark.parametrize("rho", [0.8, 0.5, 1.0])
+def test_matmul_w8_decode(dev, rho):
+    # GEMV over the kept int8 rows: 3 and 16 activation rows, ragged strips
+    w = synth.w8_projection(n=3, d=1000, m=264, rho=rho)
+    check_matmul_w8(w, rho, dev, TOL_BF16)
+    w = synth.w8_projection(n=16, d=2048, m=392, rho=rho)
+    check_matmul_w8(w, rho, dev, TOL_BF16, out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("rho", [0.7, 1.0])
+def test_matmul_w8_prefill(dev, rho):
+    # gathered int8 rows in the matrix-core GEMM: ragged M, K and N
+    w = synth.w8_projection(n=300, d=700, m=520, rho=rho, name="w8_ragged")
+    check_matmul_w8(w, rho, dev, TOL_BF16)
+    # dense path with A read in place (d a multiple of 64), 256 x 256 tiles
+    w = synth.w8_projection(n=1024, d=1024, m=768, rho=rho, name="w8_tiles")
+    check_matmul_w8(w, rho, dev, TOL_BF16)
+
+
+def test_full_mlp_down_w8(dev):
+    # Llama-3.1-8B MLP down projection with int8 weights (256 x 256 tiles)
+    w = synth.w8_projection(n=4096, d=14336, m=4096, rho=0.7, workload=1, name="mlp_down_8b_w8")
+    rows = np.sort(np.random.default_rng(0).choice(4096, size=64, replace=False))
+    check_matmul_w8(w, 0.7, dev, TOL_BF16, rows=rows)
+
+
+def test_full_decode_qkv_w8(dev):
+    w = synth.w8_projection()
+    for rho in (0.8, 1.0):
+        check_matmul_w8(w, rho, dev, TOL_BF16)
 
 
 # -------------------------------- QK^T --------------------------------------

@@ -341,6 +341,31 @@ def pin_given_index(ns):
     return None
 
 
+def pin_matmul_w8(ns):
+    """int8 weights: with integer activations and power-of-two column scales
+    every product and sum is exact, so the result must equal a pure-Python
+    loop over the kept rows that multiplies each column by its own scale;
+    negative weights near -128 catch a weight read as unsigned; the kept set
+    is the float selection's."""
+    r = np.random.default_rng(41)
+    n, d, m = 6, 20, 7
+    A = r.integers(-5, 6, size=(n, d)).astype(np.float64)
+    A[:, 3] *= 9          # a clear top column
+    Bq = r.integers(-128, 128, size=(d, m)).astype(np.int8)
+    Bq[:, 0] = -128
+    Bq[1, :] = -127
+    scale = np.array([2.0 ** e for e in (-3, 1, 0, -7, 4, -1, 2)])
+    for rho in (1.0, 0.55, 0.2):
+        idx, Y = ns.matmul_w8(A, Bq, scale, rho)
+        I, _ = ns.select(A, rho)
+        if not np.array_equal(np.asarray(idx), np.asarray(I)):
+            return f"rho {rho}: kept set differs from the float selection"
+        ref = [[math.fsum(A[i][t] * int(Bq[t][c]) for t in I) * scale[c] for c in range(m)] for i in range(n)]
+        if np.max(np.abs(np.asarray(Y) - np.asarray(ref))) > 0:
+            return f"rho {rho}: int8 product differs from the per-column scaled loop"
+    return None
+
+
 def pin_softmax_energy(ns):
     """Row softmax against math.exp / fsum loops, shift invariance, and PV on
     supplied energies against PV scoring P itself."""
@@ -400,7 +425,7 @@ def pin_retained_energy(ns):
 
 PINS = [pin_retained_energy, pin_k_rule, pin_worked_example, pin_dense_loop, pin_reduced_loop, pin_minimax_bruteforce,
         pin_error_bound, pin_worst_case, pin_ties, pin_invariances, pin_qk, pin_causal_qk, pin_pv, pin_given_index,
-        pin_softmax_energy]
+        pin_matmul_w8, pin_softmax_energy]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -498,6 +523,11 @@ MUTANTS = {
     "bare_binary_ceil": dict(k_rule=lambda rho, d: min(d, max(1, int(math.ceil(rho * d))))),
     "drops_kept_rows_of_B": dict(_product=lambda A, B, idx: A[:, idx] @ B[np.sort(np.setdiff1d(np.arange(B.shape[0]), idx))[:len(idx)], :]
                                  if len(idx) < B.shape[0] else A @ B),
+    "w8_scale_per_row": dict(matmul_w8=lambda A, Bq, s, rho: (lambda I: (I, np.asarray(A, float)[:, I] @ (
+        np.asarray(Bq, float)[I, :] * np.resize(np.asarray(s, float), len(I))[:, None])))(O.select(A, rho)[0])),
+    "w8_read_unsigned": dict(matmul_w8=lambda A, Bq, s, rho: O.matmul_w8(A, np.asarray(Bq).view(np.uint8), s, rho)),
+    "w8_scale_dropped": dict(matmul_w8=lambda A, Bq, s, rho: O.matmul_w8(A, Bq, np.ones_like(np.asarray(s, float)),
+                                                                         rho)),
     "causal_top_left_aligned": dict(_visible=lambda row, t, tq, tk: t <= row),
     "causal_hides_the_diagonal": dict(_visible=lambda row, t, tq, tk: t < row + tk - tq),
     "causal_masks_with_zero": dict(_masked=0.0),
