@@ -187,6 +187,111 @@ class MatmulOp:
                            f"{list(self.rhos)} over {what}; {wall:.1f} s of CPU work")}
 
 
+class MatmulW8Op(MatmulOp):
+    """Linear product with int8 weights and a scale per output column,
+    Y = A[:, I] (Bq[I, :] diag(scale)) (rmm_matmul_w8)."""
+
+    def __init__(self, name, A_cpu, Bq_cpu, scale_cpu, rhos, desc, copies):
+        import torch
+        from input_adaptive_reduced_colnorm_amd import rmm
+        self.rmm, self.L = rmm, rmm.lib()
+        dev = torch.device("cuda:0")
+        self.name, self.desc, self.rhos = name, desc, rhos
+        self.A_cpu, self.Bq_cpu, self.scale_cpu = A_cpu, Bq_cpu, scale_cpu
+        self.n, self.d = A_cpu.shape
+        self.m = Bq_cpu.shape[1]
+        self.copies = copies
+        self.As = [A_cpu.to(dev) for _ in range(copies)]
+        self.Bqs = [Bq_cpu.to(dev) for _ in range(copies)]
+        self.scale = scale_cpu.to(dev)
+        self.Y = torch.empty((self.n, self.m), dtype=torch.float32, device=dev)
+        self.ks = {r: rmm.k(r, self.d) for r in rhos}
+        self.idx = {r: torch.empty(self.ks[r], dtype=torch.int32, device=dev) for r in rhos}
+        wsb = max(int(self.L.rmm_matmul_w8_workspace(self.n, self.d, self.m, self.d, r)) for r in rhos)
+        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        self.decode = self.n <= 16
+
+    call_idx = None   # no int8 variant of the given-index product
+
+    def call(self, c, rho, sh, events=None):
+        n, d, m, L, rmm = self.n, self.d, self.m, self.L, self.rmm
+        args = [self.As[c].data_ptr(), rmm.RMM_BF16, self.Bqs[c].data_ptr(), self.scale.data_ptr(), n, d, m, d, m,
+                float(rho), self.idx[rho].data_ptr(), self.Y.data_ptr(), rmm.RMM_FP32, m, self.ws.data_ptr(),
+                self.ws.numel(), sh]
+        st = L.rmm_matmul_w8(*args) if events is None else L.rmm_matmul_w8_timed(*args, events)
+        if st != 0:
+            raise RuntimeError(f"rmm_matmul_w8: {rmm.status_str(st)}")
+
+    def stage_work(self, rho):
+        n, d, m, k = self.n, self.d, self.m, self.ks[rho]
+        if self.decode:
+            return {"score": ("B", n * d * 2), "gemm": ("B", k * m * 1)}
+        w = {"gemm": ("F", 2.0 * n * k * m)}
+        if k < d:
+            w["score"] = ("B", n * d * 2)
+            w["pack"] = ("B", 2 * n * k * 2)
+        return w
+
+    def roofline_kernel(self):
+        if self.decode:
+            return "gemv_kernel<bf16 A, int8 B> (kept int8 rows of B)"
+        return "gemm_bf16_kernel<256,256,kmajor,gather,int8 B> (reduced GEMM)"
+
+    def traffic_ref(self):
+        return None
+
+    extra_key = "bf16_weights_context"
+
+    def extra(self, args, sh):
+        """The same call with the weights dequantised to bf16 (rmm_matmul), at
+        each rho, for the int8-over-bf16 comparison."""
+        import torch
+        rmm, L = self.rmm, self.L
+        dev = self.Y.device
+        Bb = [(self.Bqs[c].float() * self.scale[None, :]).to(torch.bfloat16) for c in range(self.copies)]
+        wsb = max(int(L.rmm_matmul_workspace(self.n, self.d, self.m, self.d, rmm.RMM_BF16, r)) for r in self.rhos)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        out = {}
+        for rho in self.rhos:
+            def one(c):
+                st = L.rmm_matmul(self.As[c].data_ptr(), Bb[c].data_ptr(), rmm.RMM_BF16, self.n, self.d, self.m,
+                                  self.d, self.m, float(rho), self.idx[rho].data_ptr(), self.Y.data_ptr(),
+                                  rmm.RMM_FP32, self.m, ws.data_ptr(), ws.numel(), sh)
+                if st != 0:
+                    raise RuntimeError(f"rmm_matmul: {rmm.status_str(st)}")
+            one(0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                one(i % self.copies)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[str(rho)] = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
+        del Bb
+        return {"bf16_weights_latency_us": out,
+                "note": "rmm_matmul on the same weights dequantised to bf16 (twice the weight bytes)"}
+
+    def cpu_baseline(self):
+        import numpy as np
+        from oracle import rmm_oracle as O
+        A = self.A_cpu.float().numpy()
+        Bq = self.Bq_cpu.numpy()
+        sc = self.scale_cpu.numpy()
+        rows = None if self.n <= 1024 else np.arange(1024)
+        t0 = time.perf_counter()
+        for rho in self.rhos:
+            O.matmul_w8(A, Bq, sc, rho, rows=rows)
+        wall = time.perf_counter() - t0
+        scale = 1 if rows is None else self.n / len(rows)
+        what = "every row" if rows is None else f"rows 0..{len(rows) - 1} of {self.n} (product), scaled by {scale:g}x"
+        return {"value": len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
+                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "sample": (f"fp64 oracle with int8 weights for one call per rho in {list(self.rhos)} over {what}; "
+                           f"{wall:.1f} s of CPU work")}
+
+
 class QkOp:
     """Per-head attention scores S_h = Q_h[:, I_h] K_g(h)[:, I_h]^T (rmm_qk)."""
 
@@ -503,7 +608,7 @@ def run(args, op):
 
     # the same products over the index sets just selected (selection reused)
     reuse_us = {}
-    if hasattr(op, "call_idx"):
+    if getattr(op, "call_idx", None):
         for j, rho in enumerate(rhos):
             if rho >= 1.0:
                 continue
@@ -615,7 +720,7 @@ def run(args, op):
 def hipblaslt_context(op):
     """hipBLASLt dense time at the same shape (bf16 output), as context only."""
     import torch
-    if not isinstance(op, MatmulOp):
+    if not isinstance(op, MatmulOp) or not hasattr(op, "Bs"):
         return None
     Ad, Bd = op.As[0], op.Bs[0]
     for _ in range(3):
@@ -737,7 +842,8 @@ class DecodeAttnOp:
                            f"{list(self.rhos)}, {reps} repetitions; {wall:.1f} s of CPU work")}
 
 
-WORKLOADS = ("mlp_down_8b", "mlp_up_70b", "decode_qkv_8b", "gqa_qk_8b", "attn_pv_70b", "decode_attn_8b")
+WORKLOADS = ("mlp_down_8b", "mlp_up_70b", "decode_qkv_8b", "gqa_qk_8b", "attn_pv_70b", "decode_attn_8b",
+             "decode_qkv_8b_w8", "mlp_down_8b_w8")
 
 
 def make_op(name, copies):
@@ -755,6 +861,15 @@ def make_op(name, copies):
         w = synth.decode_qkv()
         return MatmulOp(name, w.tensors["A"], w.tensors["B"], (0.8, 1.0),
                         "A 8x4096 bf16 @ B 4096x6144 bf16 -> Y fp32 (decode GEMV over kept rows)", copies)
+    if name == "decode_qkv_8b_w8":
+        w = synth.w8_projection()
+        return MatmulW8Op(name, w.tensors["A"], w.tensors["Bq"], w.tensors["scale"], (0.8, 1.0),
+                          "A 8x4096 bf16 @ Bq 4096x6144 int8 (fp32 scale per column) -> Y fp32 "
+                          "(decode GEMV over kept int8 rows)", copies)
+    if name == "mlp_down_8b_w8":
+        w = synth.w8_projection(n=4096, d=14336, m=4096, rho=0.7, workload=1, name=name)
+        return MatmulW8Op(name, w.tensors["A"], w.tensors["Bq"], w.tensors["scale"], (0.7, 1.0),
+                          "A 4096x14336 bf16 @ Bq 14336x4096 int8 (fp32 scale per column) -> Y fp32", copies)
     if name == "gqa_qk_8b":
         w = synth.gqa_qk()
         return QkOp(name, w.tensors["Q"], w.tensors["K"], (0.5, 1.0),
