@@ -20,12 +20,16 @@
 // Work split: the kept rows are cut into `splits` slices of at most 512
 // (a multiple of 32) and the columns into 128-column strips; a 256-thread
 // workgroup owns a (strip, slice) pair and its 4 waves take the slice's
-// 32-row chunks round robin, every B load of a wave issued before its
-// first MFMA.  The waves are added in a fixed order in LDS; several slices
+// 32-row chunks round robin.  Vector loads retire in order, so a wave first
+// loads every kept-row index it needs, then the activations it stages, and
+// only then all of its B rows: no wait for an index or an activation also
+// waits for B.  The waves are added in a fixed order in LDS; several slices
 // write partial sums that a second kernel adds in slice order, so the
 // result is bitwise reproducible.  int8 weights (a scale per output column,
 // applied to the finished sum) are read with 8-byte loads and widened to
 // bf16 in registers before the same transpose.
+
+#include <type_traits>
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
@@ -46,7 +50,7 @@ __device__ __forceinline__ int slice_rows(int k, int splits) {
   return ((k + splits - 1) / splits + kChunk - 1) / kChunk * kChunk;
 }
 
-template <bool A_BF16, bool B_I8>
+template <int NR, bool A_BF16, bool B_I8>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   constexpr int BE = B_I8 ? 1 : 2;   // bytes per B element
   __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kMaxSlice + 8];   // bf16 activations, row r, kept row t
@@ -69,40 +73,66 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   const int c = blockIdx.x * kCols + cg * 8;
   const bool col_ok = c < g.m;   // m is a multiple of 8
 
-  // ---- every B load of this wave first: chunk q covers the slice rows
-  //      (wave + 4 q) * 32 .., the lane its 8 rows 8 rb .. (a row index of
-  //      -1, or a row past the slice, reads as zero) ----
-  typename RowPiece<B_I8>::type bv[kChunksPerWave][8];
+  // ---- load order matters: vector loads retire in order, so a wait for a
+  //      load also waits for every load issued before it.  First every
+  //      kept-row index this thread needs: its B rows (chunk q covers slice
+  //      rows (wave + 4 q) * 32 .., the lane its 8 rows 8 rb ..) and the up
+  //      to two rows it stages.  A row of -1, or past the slice, is invalid ----
+  int row[kChunksPerWave][8];
 #pragma unroll
-  for (int q = 0; q < kChunksPerWave; ++q) {
-    const int tb = (wave + kWaves * q) * kChunk + 8 * rb;
-    int row[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = tb + e;
-      row[e] = t < L ? (g.idx ? g.idx[t0 + t] : t0 + t) : -1;
-    }
+  for (int q = 0; q < kChunksPerWave; ++q)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      typedef typename RowPiece<B_I8>::type R;
-      const char* src = (const char*)g.B + ((size_t)row[e] * g.ldb + c) * BE;
-      bv[q][e] = (row[e] >= 0 && col_ok) ? __builtin_nontemporal_load((const R*)src) : R{};
+      const int t = (wave + kWaves * q) * kChunk + 8 * rb + e;
+      row[q][e] = t < L ? (g.idx ? g.idx[t0 + t] : t0 + t) : -1;
     }
-  }
-
-  // ---- stage A[:, I] of the slice as bf16 (rows past n and kept rows past
-  //      the slice are zero) while the B rows are in flight ----
+  constexpr int PER = kMaxSlice / kThreads;
   const int L32 = (L + kChunk - 1) / kChunk * kChunk;
-  for (int i = tid; i < L32; i += kThreads) {
-    const int row = i < L ? (g.idx ? g.idx[t0 + i] : t0 + i) : -1;
+  int srow[PER];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      uint16_t v = 0;
-      if (r < g.n && row >= 0) {
-        const size_t off = (size_t)r * g.lda + row;
-        v = A_BF16 ? ((const uint16_t*)g.A)[off] : f32_to_bf16(((const float*)g.A)[off]);
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * kThreads;
+    srow[u] = i < L ? (g.idx ? g.idx[t0 + i] : t0 + i) : -1;
+  }
+  // ---- then the activations to stage and every B row, all unconditional
+  //      (an invalid row reads row 0 and is zeroed where it is used), so the
+  //      staging below waits for its own loads only ----
+  using Act = typename std::conditional<A_BF16, uint16_t, float>::type;
+  Act av[PER][NR];
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int rr = r < g.n ? r : 0;
+      const int col = srow[u] >= 0 ? srow[u] : 0;
+      av[u][r] = ((const Act*)g.A)[(size_t)rr * g.lda + col];
+    }
+  __builtin_amdgcn_sched_barrier(0);   // keep every activation load ahead of the B loads
+  typedef typename RowPiece<B_I8>::type R;
+  R bv[kChunksPerWave][8];
+  const int cc0 = col_ok ? c : 0;
+#pragma unroll
+  for (int q = 0; q < kChunksPerWave; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int rw = row[q][e] >= 0 ? row[q][e] : 0;
+      bv[q][e] = __builtin_nontemporal_load((const R*)((const char*)g.B + ((size_t)rw * g.ldb + cc0) * BE));
+    }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * kThreads;
+    if (i < L32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        uint16_t v = 0;
+        if (r < NR && r < g.n && srow[u] >= 0) {
+          if constexpr (A_BF16)
+            v = av[u][r < NR ? r : 0];
+          else
+            v = f32_to_bf16(av[u][r < NR ? r : 0]);
+        }
+        s_a[r][i] = v;
       }
-      s_a[r][i] = v;
     }
   }
   __syncthreads();
@@ -119,7 +149,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
     i32x4 rows8[8], tr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if constexpr (B_I8)
+      if (row[q][e] < 0 || !col_ok)
+        rows8[e] = i32x4{0, 0, 0, 0};
+      else if constexpr (B_I8)
         rows8[e] = i8x8_to_bf16x8(bv[q][e]);
       else
         rows8[e] = bv[q][e];
@@ -196,15 +228,25 @@ int gemv_splits(int k, int m, int batch) {
   return (k + slice - 1) / slice;
 }
 
+template <int NR>
+void launch_nr(const GemvArgs& g, dim3 grid, hipStream_t s) {
+  if (g.b_i8)
+    gemv_kernel<NR, true, true><<<grid, kThreads, 0, s>>>(g);   // int8 weights take bf16 activations
+  else if (g.a_bf16)
+    gemv_kernel<NR, true, false><<<grid, kThreads, 0, s>>>(g);
+  else
+    gemv_kernel<NR, false, false><<<grid, kThreads, 0, s>>>(g);
+}
+
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s) {
   if (g.n > 16 || (g.b_i8 && !g.a_bf16)) return hipErrorInvalidValue;
   dim3 grid((g.m + kCols - 1) / kCols, g.splits, g.batch);
-  if (g.b_i8)
-    gemv_kernel<true, true><<<grid, kThreads, 0, s>>>(g);   // int8 weights take bf16 activations
-  else if (g.a_bf16)
-    gemv_kernel<true, false><<<grid, kThreads, 0, s>>>(g);
+  if (g.n <= 4)
+    launch_nr<4>(g, grid, s);
+  else if (g.n <= 8)
+    launch_nr<8>(g, grid, s);
   else
-    gemv_kernel<false, false><<<grid, kThreads, 0, s>>>(g);
+    launch_nr<16>(g, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.splits == 1) return e;
   gemv_reduce_kernel<<<dim3((g.n * g.m + 255) / 256, g.batch), 256, 0, s>>>(g);
