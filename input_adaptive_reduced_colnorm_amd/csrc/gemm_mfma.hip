@@ -404,11 +404,9 @@ hipError_t launch_gemm_w8(const GemmArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s) {
-  const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-  if (t256 >= 192 && g.N >= 256 && g.M >= 256)
-    dispatch_af32<256, 256, 8>(g, s);
-  else
-    dispatch_af32<128, 128, 4>(g, s);
+  // 128 x 128 tiles only: with fp32 A staged in registers the 256 x 256
+  // tile needs more than the 256 registers two waves per SIMD allow
+  dispatch_af32<128, 128, 4>(g, s);
   return hipGetLastError();
 }
 

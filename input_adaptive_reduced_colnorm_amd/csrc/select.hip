@@ -9,6 +9,8 @@
 // fixed order and the only atomics are integer LDS histogram counts, so the
 // result is bitwise reproducible.
 
+#include <type_traits>
+
 #include "rmm_device.h"
 #include "rmm_internal.h"
 
@@ -112,18 +114,32 @@ __global__ __launch_bounds__(256) void colnorm_kernel(const void* __restrict__ A
 // ---------------------------------------------------------------------------
 // Block-wide helpers for 1024-thread selection workgroups.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+// Wave-wide inclusive scans on the DPP cross-lane paths (no LDS round
+// trip): shifts by 1, 2, 4 and 8 lanes inside each row of 16, then the
+// totals of rows 0 and 2 broadcast into rows 1 and 3 (row_bcast:15) and the
+// total of rows 0-1 into rows 2-3 (row_bcast:31).  Lanes whose source is
+// outside the pattern take `id`, the identity of the operation.
+template <typename F>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t x, uint32_t id, F op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));   // row_shr:1
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));   // row_shr:2
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));   // row_shr:4
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));   // row_shr:8
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));   // row_bcast:15
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));   // row_bcast:31
   return x;
 }
 
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  return wave_scan_dpp(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
 constexpr int kHistBins = 2048;  // 11-bit radix digits
-constexpr int kChunk = (kKeyCap + kSelThreads - 1) / kSelThreads;  // keys per thread held in registers
+constexpr int kChunk = (kKeyCap + kSelThreads - 1) / kSelThreads;  // most keys per thread held in registers
+
+// Keys per thread for a key count d held in LDS: the radix passes run one
+// unrolled histogram step per register slot, so the slot count follows d.
+__host__ __device__ constexpr int chunk_for(int d) { return d <= 4096 ? 4 : (d <= 8192 ? 8 : kChunk); }
 
 struct SelShared {
   uint32_t hist[3 * kHistBins];   // one histogram per radix pass
@@ -183,17 +199,19 @@ __device__ __forceinline__ void block_incl_scan2(uint32_t& a, uint32_t& b, SelSh
 
 // The keys of one thread: a contiguous index chunk [j0, j0 + cnt), kept in
 // registers across all radix passes and the compaction.
+template <int CH>
 struct KeyChunk {
-  uint32_t key[kChunk];
+  uint32_t key[CH];
   int j0, cnt;
 };
 
-__device__ __forceinline__ void load_chunk(const uint32_t* keys, int d, KeyChunk& kc) {
-  const int chunk = (d + kSelThreads - 1) / kSelThreads;
+template <int CH>
+__device__ __forceinline__ void load_chunk(const uint32_t* keys, int d, KeyChunk<CH>& kc) {
+  const int chunk = (d + kSelThreads - 1) / kSelThreads;   // <= CH
   kc.j0 = min(d, (int)threadIdx.x * chunk);
   kc.cnt = min(chunk, d - kc.j0);
 #pragma unroll
-  for (int i = 0; i < kChunk; ++i) kc.key[i] = i < kc.cnt ? keys[kc.j0 + i] : 0u;
+  for (int i = 0; i < CH; ++i) kc.key[i] = i < kc.cnt ? keys[kc.j0 + i] : 0u;
 }
 
 // Histogram increment with the lanes of a wave that share the first active
@@ -203,7 +221,7 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool m, uint32_t dig) {
   const uint64_t act = __ballot(m);
   if (act == 0) return;
   const int first = __ffsll((unsigned long long)act) - 1;
-  const uint32_t d0 = __shfl(dig, first, 64);
+  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dig, first);
   const uint64_t same = __ballot(m && dig == d0);
   if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
   if (m && dig != d0) atomicAdd(&hist[dig], 1u);
@@ -218,20 +236,20 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool m, uint32_t dig) {
 // spread over many buckets instead of a few contended ones; all histograms
 // are cleared up front, and the passes stop as soon as the bucket holding
 // the k-th key is kept whole.
-__device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
+template <int CH>
+__device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t k_or = 0u, k_and = 0xffffffffu;
 #pragma unroll
-  for (int i = 0; i < kChunk; ++i)
+  for (int i = 0; i < CH; ++i)
     if (i < kc.cnt) {
       k_or |= kc.key[i];
       k_and &= kc.key[i];
     }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    k_or |= __shfl_xor(k_or, o, 64);
-    k_and &= __shfl_xor(k_and, o, 64);
-  }
+  k_or = (uint32_t)__builtin_amdgcn_readlane(
+      (int)wave_scan_dpp(k_or, 0u, [](uint32_t a, uint32_t b) { return a | b; }), 63);
+  k_and = (uint32_t)__builtin_amdgcn_readlane(
+      (int)wave_scan_dpp(k_and, ~0u, [](uint32_t a, uint32_t b) { return a & b; }), 63);
   for (int i = tid; i < 3 * kHistBins; i += kSelThreads) sh.hist[i] = 0;
   if (lane == 0) {
     sh.wave_tot[wave][0] = k_or;
@@ -256,7 +274,7 @@ __device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32
     const uint32_t nb = 1u << w;
     uint32_t* hist = sh.hist + pass * kHistBins;
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
+    for (int i = 0; i < CH; ++i) {
       const uint32_t key = kc.key[i];
       hist_add(hist, i < kc.cnt && (key & mask) == prefix, (key >> shift) & (nb - 1));
     }
@@ -299,11 +317,11 @@ __device__ void radix_threshold(const KeyChunk& kc, int k, SelShared& sh, uint32
 // scan of (#greater, #equal) fixes each thread's output position, so the kept
 // indices come out ascending.  emit(take, pos, j, key) is called once for
 // every index j of the chunk, in order; pos is the output position when take.
-template <typename Emit>
-__device__ void compact_ascending(const KeyChunk& kc, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
+template <int CH, typename Emit>
+__device__ __forceinline__ void compact_ascending(const KeyChunk<CH>& kc, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
-  for (int i = 0; i < kChunk; ++i) {
+  for (int i = 0; i < CH; ++i) {
     if (i < kc.cnt) {
       n_gt += kc.key[i] > T;
       n_eq += kc.key[i] == T;
@@ -314,7 +332,7 @@ __device__ void compact_ascending(const KeyChunk& kc, uint32_t T, uint32_t rem, 
   uint32_t pos = (i_gt - n_gt) + min(i_eq - n_eq, rem);
   uint32_t eq_seen = i_eq - n_eq;
 #pragma unroll
-  for (int i = 0; i < kChunk; ++i) {
+  for (int i = 0; i < CH; ++i) {
     if (i < kc.cnt) {
       const uint32_t key = kc.key[i];
       bool take = key > T;
@@ -330,7 +348,7 @@ __device__ void compact_ascending(const KeyChunk& kc, uint32_t T, uint32_t rem, 
 
 // Same selection for key arrays too large for the register chunks (d above
 // the LDS key capacity): keys stay in global scratch and are re-read.
-__device__ void radix_threshold_big(const uint32_t* keys, int d, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
+__device__ __forceinline__ void radix_threshold_big(const uint32_t* keys, int d, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, mask = 0, rem = (uint32_t)k;
   for (int pass = 0; pass < 3; ++pass) {
@@ -379,7 +397,7 @@ __device__ void radix_threshold_big(const uint32_t* keys, int d, int k, SelShare
 }
 
 template <typename Emit>
-__device__ void compact_ascending_big(const uint32_t* keys, int d, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
+__device__ __forceinline__ void compact_ascending_big(const uint32_t* keys, int d, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
   const int chunk = (d + kSelThreads - 1) / kSelThreads;
   const int j0 = min(d, (int)threadIdx.x * chunk), j1 = min(d, j0 + chunk);
   uint32_t n_gt = 0, n_eq = 0;
@@ -404,7 +422,9 @@ __device__ void compact_ascending_big(const uint32_t* keys, int d, uint32_t T, u
   }
 }
 
-template <bool LDS_KEYS>
+// CH: keys per thread in registers (chunk_for(d)), or 0 for keys in global
+// scratch (d above the LDS key capacity).
+template <int CH>
 __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restrict__ partial, int splits, int d, int k,
                                                            int32_t* __restrict__ idx, int64_t idx_hs,
                                                            int32_t* __restrict__ pad, int64_t pad_hs, int k_pad,
@@ -412,6 +432,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
                                                            int32_t* __restrict__ mask, int64_t mask_hs,
                                                            float* __restrict__ retained,
                                                            uint32_t* __restrict__ gkeys) {
+  constexpr bool LDS_KEYS = CH > 0;
   __shared__ uint32_t s_keys[LDS_KEYS ? kKeyCap : 1];
   __shared__ int32_t s_out[LDS_KEYS ? kKeyCap : 1];
   __shared__ SelShared sh;
@@ -419,33 +440,62 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   const float* P = partial + (size_t)head * splits * d;
   uint32_t* keys = LDS_KEYS ? s_keys : gkeys + (size_t)head * d;
   if constexpr (LDS_KEYS) {
-    // each thread owns columns tid + 1024 c; the loads of four splits are
-    // issued together before they are added (in split order)
-    constexpr int NC = (kKeyCap + kSelThreads - 1) / kSelThreads;
-    float q[NC];
+    if (d % 4 == 0) {
+      // 4 columns per 16-byte load; the loads of up to 8 splits are issued
+      // together, then added in split order
+      const int d4 = d / 4;
+      const f32x4* P4 = (const f32x4*)P;
+      for (int j4 = threadIdx.x; j4 < d4; j4 += kSelThreads) {
+        f32x4 q = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < splits; s0 += 8) {
+          f32x4 v[8];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) q[c] = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += 4) {
-      float v[4][NC];
+          for (int u = 0; u < 8; ++u)
+            v[u] = s0 + u < splits ? P4[(size_t)(s0 + u) * d4 + j4] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int j = threadIdx.x + c * kSelThreads;
-          v[u][c] = (s0 + u < splits && j < d) ? P[(size_t)(s0 + u) * d + j] : 0.f;
+          for (int u = 0; u < 8; ++u)
+            if (s0 + u < splits) {
+              q[0] += v[u][0];
+              q[1] += v[u][1];
+              q[2] += v[u][2];
+              q[3] += v[u][3];
+            }
         }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (s0 + u < splits)
+        for (int e = 0; e < 4; ++e) {
+          keys[4 * j4 + e] = __float_as_uint(q[e]);
+          if (scores) scores[(size_t)head * scores_hs + 4 * j4 + e] = sqrtf(q[e]);
+        }
+      }
+    } else {
+      // each thread owns columns tid + 1024 c; the loads of four splits are
+      // issued together before they are added (in split order)
+      constexpr int NC = CH > 0 ? CH : 1;
+      float q[NC];
 #pragma unroll
-          for (int c = 0; c < NC; ++c) q[c] += v[u][c];
-    }
+      for (int c = 0; c < NC; ++c) q[c] = 0.f;
+      for (int s0 = 0; s0 < splits; s0 += 4) {
+        float v[4][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int j = threadIdx.x + c * kSelThreads;
-      if (j < d) {
-        keys[j] = __float_as_uint(q[c]);
-        if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q[c]);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int j = threadIdx.x + c * kSelThreads;
+            v[u][c] = (s0 + u < splits && j < d) ? P[(size_t)(s0 + u) * d + j] : 0.f;
+          }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (s0 + u < splits)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) q[c] += v[u][c];
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int j = threadIdx.x + c * kSelThreads;
+        if (j < d) {
+          keys[j] = __float_as_uint(q[c]);
+          if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q[c]);
+        }
       }
     }
   } else {
@@ -472,13 +522,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
     if (mo) mo[j] = take ? j : -1;
     const double q = (double)__uint_as_float(key);
     e_all += q;
-    if (take) e_kept += q;
+    e_kept += take ? q : 0.0;   // no branch: both sums stay in registers
   };
   uint32_t T, rem;
   if constexpr (LDS_KEYS) {
     // the kept list is assembled in LDS and written out coalesced; the keys
     // now live in registers, so s_keys takes the keep flags
-    KeyChunk kc;
+    KeyChunk<CH> kc;
     load_chunk(keys, d, kc);
     radix_threshold(kc, k, sh, &T, &rem);
     compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t key) {
@@ -486,7 +536,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
       s_keys[j] = take;
       const double q = (double)__uint_as_float(key);
       e_all += q;
-      if (take) e_kept += q;
+      e_kept += take ? q : 0.0;
     });
     __syncthreads();
     for (int t = threadIdx.x; t < k; t += kSelThreads) {
@@ -599,39 +649,72 @@ __global__ void iota_kernel(int32_t* idx, int64_t idx_hs, int d, int32_t* pad, i
 // Decode selection (n <= 16 rows): one workgroup computes the energies over
 // the n rows and selects into idx; the GEMV then reads A[:, I] itself.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool LDS_KEYS>
+template <bool BF16, int CH>
 __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* __restrict__ A_, int64_t lda, int n,
                                                                     int d, int k, int32_t* __restrict__ idx,
                                                                     float* __restrict__ scores,
                                                                     uint32_t* __restrict__ gkeys) {
+  constexpr bool LDS_KEYS = CH > 0;
   __shared__ uint32_t s_keys[LDS_KEYS ? kKeyCap : 1];
   __shared__ int32_t s_out[LDS_KEYS ? kKeyCap : 1];
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
-  auto load = [&](int r, int j) -> float {
-    const size_t off = (size_t)r * lda + j;
-    return BF16 ? bf16_to_f32(((const uint16_t*)A_)[off]) : ((const float*)A_)[off];
-  };
   uint32_t* keys = LDS_KEYS ? s_keys : gkeys;
-  // all 16 row loads of a column are issued before they are summed (rows in
-  // ascending order)
+  constexpr int VPT = BF16 ? 8 : 4;   // columns per 16-byte load
+  const bool vec = ((uintptr_t)A_ % 16 == 0) && (lda % VPT == 0) && (d % VPT == 0);
+  if (vec) {
+    // a thread takes VPT adjacent columns and issues the 16-byte loads of
+    // all n rows before summing them (rows in ascending order)
+    for (int c = tid; c < d / VPT; c += kSelThreads) {
+      i32x4 x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        x[r] = r < n ? *(const i32x4*)((const char*)A_ + ((size_t)r * lda + (size_t)c * VPT) * (BF16 ? 2 : 4))
+                     : i32x4{0, 0, 0, 0};
+      float q[VPT];
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) q[e] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r < n) {
+#pragma unroll
+          for (int e = 0; e < VPT; ++e) {
+            const uint32_t w = (uint32_t)x[r][BF16 ? e >> 1 : e];
+            const float f = BF16 ? __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)) : __uint_as_float(w);
+            q[e] = fmaf(f, f, q[e]);
+          }
+        }
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) {
+        keys[c * VPT + e] = __float_as_uint(q[e]);
+        if (scores) scores[c * VPT + e] = sqrtf(q[e]);
+      }
+    }
+  } else {
+    // all 16 row loads of a column are issued before they are summed (rows
+    // in ascending order)
+    auto load = [&](int r, int j) -> float {
+      const size_t off = (size_t)r * lda + j;
+      return BF16 ? bf16_to_f32(((const uint16_t*)A_)[off]) : ((const float*)A_)[off];
+    };
 #pragma unroll 2
-  for (int j = tid; j < d; j += kSelThreads) {
-    float f[16];
+    for (int j = tid; j < d; j += kSelThreads) {
+      float f[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) f[r] = r < n ? load(r, j) : 0.f;
-    float q = 0.f;
+      for (int r = 0; r < 16; ++r) f[r] = r < n ? load(r, j) : 0.f;
+      float q = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r < n) q = fmaf(f[r], f[r], q);
-    keys[j] = __float_as_uint(q);
-    if (scores) scores[j] = sqrtf(q);
+      for (int r = 0; r < 16; ++r)
+        if (r < n) q = fmaf(f[r], f[r], q);
+      keys[j] = __float_as_uint(q);
+      if (scores) scores[j] = sqrtf(q);
+    }
   }
   if (!LDS_KEYS) __threadfence_block();
   __syncthreads();
   uint32_t T, rem;
   if constexpr (LDS_KEYS) {
-    KeyChunk kc;
+    KeyChunk<CH> kc;
     load_chunk(keys, d, kc);
     radix_threshold(kc, k, sh, &T, &rem);
     compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
@@ -689,12 +772,18 @@ hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k
   if (d <= kSmallD)
     topk_small_kernel<<<heads, kSmallD, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
                                                 scores_hs, mask, mask_hs, retained);
+  else if (d <= 4096)
+    topk_kernel<chunk_for(4096)><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad,
+                                                               scores, scores_hs, mask, mask_hs, retained, nullptr);
+  else if (d <= 8192)
+    topk_kernel<chunk_for(8192)><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad,
+                                                               scores, scores_hs, mask, mask_hs, retained, nullptr);
   else if (d <= kKeyCap)
-    topk_kernel<true><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
-                                                     scores_hs, mask, mask_hs, retained, nullptr);
+    topk_kernel<kChunk><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
+                                                      scores_hs, mask, mask_hs, retained, nullptr);
   else
-    topk_kernel<false><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
-                                                      scores_hs, mask, mask_hs, retained, gkeys);
+    topk_kernel<0><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
+                                                 scores_hs, mask, mask_hs, retained, gkeys);
   return hipGetLastError();
 }
 
@@ -713,16 +802,27 @@ hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* 
 
 hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, int d, int k, int32_t* idx,
                                 float* scores, uint32_t* gkeys, hipStream_t s) {
-  if (d <= kKeyCap) {
-    if (a_bf16)
-      decode_select_kernel<true, true><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, nullptr);
-    else
-      decode_select_kernel<false, true><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, nullptr);
+  const int ch = d <= kKeyCap ? chunk_for(d) : 0;
+  auto go = [&](auto bf, auto chv) {
+    decode_select_kernel<decltype(bf)::value, decltype(chv)::value>
+        <<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, decltype(chv)::value > 0 ? nullptr : gkeys);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using C4 = std::integral_constant<int, chunk_for(4096)>;
+  using C8 = std::integral_constant<int, chunk_for(8192)>;
+  using CM = std::integral_constant<int, kChunk>;
+  using C0 = std::integral_constant<int, 0>;
+  if (a_bf16) {
+    if (ch == chunk_for(4096)) go(T_{}, C4{});
+    else if (ch == chunk_for(8192)) go(T_{}, C8{});
+    else if (ch == kChunk) go(T_{}, CM{});
+    else go(T_{}, C0{});
   } else {
-    if (a_bf16)
-      decode_select_kernel<true, false><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, gkeys);
-    else
-      decode_select_kernel<false, false><<<1, kSelThreads, 0, s>>>(A, lda, n, d, k, idx, scores, gkeys);
+    if (ch == chunk_for(4096)) go(F_{}, C4{});
+    else if (ch == chunk_for(8192)) go(F_{}, C8{});
+    else if (ch == kChunk) go(F_{}, CM{});
+    else go(F_{}, C0{});
   }
   return hipGetLastError();
 }
