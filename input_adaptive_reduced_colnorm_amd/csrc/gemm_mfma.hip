@@ -274,6 +274,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   const bool masked_tile = g.causal && (int64_t)n0 > (int64_t)(m0 + BM - 1) + g.causal_off;
   const bool some_masked = g.causal && (int64_t)(n0 + BN - 1) > (int64_t)m0 + g.causal_off;
   const int KT = masked_tile ? 0 : g.K / BK;
+  // per-column scales of int8 weights, loaded before the main loop: on this
+  // chip the vector memory counter covers stores too, so a load among the
+  // epilogue's stores would make its wait drain every store issued so far
+  // (the other variants load nothing here)
+  float cs[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    cs[j] = 1.f;
+    if constexpr (B_I8) {
+      const int col = n0 + wn * WN + j * 32 + li;
+      cs[j] = g.col_scale[col < g.N ? col : 0];
+    }
+  }
   // prologue: tile 0 into LDS, tile 1 in flight in registers
   if (KT > 0) {
     load_idx(0);
@@ -313,19 +326,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   //      8*(v/4) + 4*lk + v%4 and column li of its 32x32 block.
   char* Cb = (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
   const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
+
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = n0 + wn * WN + j * 32 + li;
       const int row0 = m0 + wm * WM + i * 32 + 4 * lk;
-      const float cs = g.col_scale && col < g.N ? g.col_scale[col] : 1.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = row0 + 8 * (v >> 2) + (v & 3);
         if (full || (row < g.M && col < g.N)) {
           const size_t off = (size_t)row * g.ldc + col;
-          const float a = g.col_scale ? acc[i][j][v] * cs : acc[i][j][v];
+          const float a = B_I8 ? acc[i][j][v] * cs[j] : acc[i][j][v];
           const float y = some_masked && (int64_t)col > (int64_t)row + g.causal_off ? -INFINITY : a;
           if (g.c_bf16)
             __builtin_nontemporal_store(f32_to_bf16(y), (uint16_t*)Cb + off);
@@ -394,7 +407,7 @@ void dispatch_w8(const GemmArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_gemm_w8(const GemmArgs& g, hipStream_t s) {
-  if (!g.b_kmajor || !g.b_i8) return hipErrorInvalidValue;
+  if (!g.b_kmajor || !g.b_i8 || !g.col_scale) return hipErrorInvalidValue;
   const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
   if (t256 >= 192 && g.N >= 256 && g.M >= 256)
     dispatch_w8<256, 256, 8>(g, s);

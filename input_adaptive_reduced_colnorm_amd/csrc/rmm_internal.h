@@ -58,7 +58,7 @@ struct GemmArgs {
   bool b_kmajor;
   uint32_t a_bytes, b_bytes;  // per-batch extents (bytes) for the buffer descriptors
   bool b_i8;                  // K-major B holds int8 weights (widened to bf16 exactly)
-  const float* col_scale;     // if not null: C[i][j] *= col_scale[j]
+  const float* col_scale;     // int8 B only (required there): C[i][j] *= col_scale[j]
   bool causal;          // C[i][j] = -inf where j > i + causal_off (tiles wholly above skip the product)
   int64_t causal_off;
 };
