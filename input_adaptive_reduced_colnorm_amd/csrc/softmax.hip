@@ -61,10 +61,16 @@ __global__ __launch_bounds__(kThreads) void softmax_energy_kernel(const float* _
     const float* lr = Lh + (size_t)r * l_ts;
     float x[C];
     float mx = -INFINITY;
+    // every load of the row is issued before any is used (a use inside the
+    // guarded load would wait for each load in turn); -inf stays -inf
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int j = threadIdx.x + kThreads * c;
-      x[c] = j < tk ? scale * lr[j] : -INFINITY;
+      x[c] = j < tk ? lr[j] : -INFINITY;
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      x[c] *= scale;
       mx = fmaxf(mx, x[c]);
     }
     mx = block_max(mx, red);
