@@ -89,7 +89,7 @@ const char* rmm_status_str(int status);
  *   idx     [k] int32, written ascending, k = rmm_k(rho, d).
  *   scores  optional [d] fp32: s_j = sqrt(fp32 sum of squares of column j);
  *           NULL to skip.
- * Score and TopK: hackcv.com, Core Approach ("importance score" and TopK).
+ * Score and TopK: hackcv.com, Core Approach (the importance score and TopK).
  * ------------------------------------------------------------------- */
 size_t rmm_select_workspace(int64_t n, int64_t d, int dtype);
 rmm_status_t rmm_select(const void* A, int dtype, int64_t n, int64_t d, int64_t lda, double rho,
@@ -138,8 +138,8 @@ rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n
  * i.e. A[:, I] (Bq[I, :] diag(scale)) with I selected from A exactly as in
  * rmm_matmul.  The weights are symmetric per-output-channel int8 (one fp32
  * scale per column of B): hackcv.com, "Compatibility & generalization"
- * (RMM stacks with INT8), and gist.science, Experimental Results
- * ("Compatibility": INT8 weight quantisation); neither page gives the
+ * (RMM combines with INT8 weights), and gist.science, Experimental Results
+ * (the compatibility item on INT8 weight quantisation); neither page gives the
  * quantisation scheme, so this per-channel form is the one fixed here.
  *   A      bf16 (a_dtype must be RMM_BF16), row-major, lda >= d.
  *   Bq     int8 [d][ldb] row-major, ldb >= m, Bq 8-byte aligned, and m and

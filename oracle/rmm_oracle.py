@@ -41,11 +41,11 @@ bf16 and fp32 values convert to float64 without rounding):
                  A[:, t] B[t, :] (entries outside [0, d) ignored).
 * int8 B      -- Y = A[:, I] @ (Bq[I, :] * s[None, :]): weights stored as
                  int8 with one scale per output column (symmetric per-channel
-                 quantisation; the pages say RMM stacks with INT8 weight
+                 quantisation; the pages say RMM combines with INT8 weight
                  quantisation but give no scheme, so this plainest reading
                  is the one fixed here).  Selection is unchanged: it reads A.
                  Source: hackcv.com, "Compatibility & generalization";
-                 gist.science, Experimental Results ("Compatibility").
+                 gist.science, Experimental Results (the compatibility item).
 * PV          -- per head h: I_h from the column norms of P[h]
                  (queries x keys) over its query rows (the token axis is the
                  contraction axis), and O_h = P[h][:, I_h] @ V[g(h)][I_h, :].
