@@ -1,5 +1,6 @@
 // Decode-shaped reduced QK^T: a few query rows per head (tq <= 16) against
-// a key cache, S[h][r][t] = sum over f in I_h of Q[h][r][f] K[g(h)][t][f].
+// a key cache, S[h][r][t] = sum over f in I_h of Q[h][r][f] K[g(h)][t][f],
+// with the selection of I_h done in the same kernel.
 //
 // hackcv.com, Component mapping: QK^T contracts over the head feature
 // dimension, selection runs on Q per head and K gathers the same feature
@@ -10,7 +11,10 @@
 // holds, for its 8 consecutive features, the query values of every (head,
 // row) of the group with the unselected features set to zero, and every K
 // row is read once with 16-byte loads.  The partial dot products of the
-// lanes that span a row are folded with a fixed butterfly.
+// lanes that span a row are folded with a fixed butterfly.  The kept
+// features of a head (at most 256, from at most 8 query rows) are ranked by
+// every workgroup in its prologue, so the decode step needs no separate
+// scoring and TopK launches.
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
@@ -27,21 +31,69 @@ __global__ __launch_bounds__(kThreads) void qk_decode_kernel(const QkDecodeArgs 
   constexpr int TPW = 64 / LPT;                 // tokens per wave step
   constexpr int TPB = TPW * (kThreads / 64);    // tokens per workgroup step
   __shared__ float qm[G][256];
+  __shared__ __attribute__((aligned(16))) uint64_t s_ck[kThreads];
+  __shared__ int s_cnt[kThreads / 64];
   const int g = blockIdx.y;
   const int group = a.hq / a.hkv;
   const int tid = threadIdx.x;
-  // ---- masked queries of the group: qm[(h - g*group)*tq + r][f] ----
-  for (int i = tid; i < G * 256; i += kThreads) qm[i / 256][i % 256] = 0.f;
-  __syncthreads();
-  for (int i = tid; i < group * a.tq * a.k; i += kThreads) {
-    const int t = i % a.k, row = i / a.k;   // row = local head * tq + r
-    const int hl = row / a.tq, r = row % a.tq;
-    const int h = g * group + hl;
-    const int f = a.idx ? a.idx[(size_t)h * a.k + t] : t;
-    const size_t off = (size_t)h * a.q_hs + (size_t)r * a.q_ts + f;
-    qm[row][f] = a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.Q)[off]) : ((const float*)a.Q)[off];
+  // ---- every feature of the group's query rows: qm[(h - g*group)*tq + r][f] ----
+  for (int i = tid; i < G * 256; i += kThreads) {
+    const int row = i / 256, f = i % 256;   // row = local head * tq + r
+    float v = 0.f;
+    if (row < group * a.tq && f < a.dh) {
+      const int hl = row / a.tq, r = row % a.tq;
+      const size_t off = (size_t)(g * group + hl) * a.q_hs + (size_t)r * a.q_ts + f;
+      v = a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.Q)[off]) : ((const float*)a.Q)[off];
+    }
+    qm[row][f] = v;
   }
   __syncthreads();
+  // ---- the kept features of each query head of the group, from the column
+  //      energies of its tq rows (row order; with bf16 Q every square is exact
+  //      in fp32, so these keys equal the scoring pass's).  Each feature gets
+  //      the composite key (energy bits, 0xFFFF - j): a larger composite
+  //      outranks (higher energy, or equal energy and lower index), so one
+  //      64-bit compare per pair ranks it, and feature j is kept when fewer
+  //      than k composites exceed its own.  With dh <= 128 two heads are
+  //      ranked at once.  Dropped features are zeroed in qm; the workgroups
+  //      of the first token block write the ascending lists ----
+  const int hp_n = a.dh <= 128 ? 2 : 1;                 // heads per pass
+  const int tph = kThreads / hp_n;                      // threads per head
+  const int hsub = tid / tph, jf = tid % tph;           // head within the pass, feature
+  const int lane_ = tid & 63, wave_ = tid >> 6;
+  for (int h0 = 0; h0 < group; h0 += hp_n) {
+    const int hl = h0 + hsub;
+    const bool live = hl < group && jf < a.dh;
+    int32_t* out = a.idx_out + (size_t)(g * group + (hl < group ? hl : 0)) * a.k;
+    if (!a.select) {
+      if (blockIdx.x == 0 && live) out[jf] = jf;
+      continue;
+    }
+    float key = 0.f;
+    if (live)
+      for (int r = 0; r < a.tq; ++r) key = fmaf(qm[hl * a.tq + r][jf], qm[hl * a.tq + r][jf], key);
+    const uint64_t ck = ((uint64_t)__float_as_uint(key) << 32) | (uint32_t)(0xFFFF - jf);
+    s_ck[tid] = ck;
+    __syncthreads();
+    // two composites per 16-byte LDS read, many reads in flight (dh % 8 == 0)
+    const uint64_t* row = s_ck + hsub * tph;
+    int rank = 0;
+#pragma unroll 8
+    for (int i2 = 0; i2 < a.dh / 2; ++i2) {
+      const u64x2 v = *(const u64x2*)(row + 2 * i2);
+      rank += (int)(v[0] > ck) + (int)(v[1] > ck);
+    }
+    const bool keep = live && rank < a.k;
+    const uint64_t kept = __ballot(keep);
+    if (lane_ == 0) s_cnt[wave_] = __popcll(kept);
+    __syncthreads();
+    int pos = __popcll(kept & ((1ull << lane_) - 1ull));
+    for (int w = hsub * (tph / 64); w < wave_; ++w) pos += s_cnt[w];
+    if (keep && blockIdx.x == 0) out[pos] = jf;
+    if (live && !keep)
+      for (int r = 0; r < a.tq; ++r) qm[hl * a.tq + r][jf] = 0.f;
+    __syncthreads();   // s_ck and s_cnt are reused by the next pass
+  }
   const int lane = tid & 63, wave = tid >> 6;
   const int sub = lane % LPT;                    // which 8 features
   const int tw = lane / LPT;                     // token within the wave step

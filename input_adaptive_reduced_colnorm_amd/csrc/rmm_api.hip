@@ -717,20 +717,16 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
   const Marks mk{stage_events, s};
   clear_error();
   RMM_LAUNCH(mk.mark(0));
-  if (p.use_sel) {
-    RMM_LAUNCH(run_select(p.sel, ws, Q, bf16, q_hs, q_ts, (int)hq, tq, dh, p.k, idx, p.k, nullptr, s, &mk));
-  } else {
-    RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, nullptr, 0, 0, s));
-    RMM_LAUNCH(mk.mark(1));
-  }
-  RMM_LAUNCH(mk.mark(2));
   if (p.mfma && tq <= kDecodeRows && qk_decode_fits(group, (int)tq, (int)dh) && aligned(K, 16) && k_ts % 8 == 0 &&
       k_hs % 8 == 0) {
-    // decode-shaped: one streaming pass over the key cache
+    // decode-shaped: one kernel selects the features (bf16 Q, so its keys
+    // equal the scoring pass's) and streams the key cache once
+    RMM_LAUNCH(mk.mark(1));
+    RMM_LAUNCH(mk.mark(2));
     QkDecodeArgs a{};
     a.Q = Q; a.q_bf16 = true; a.q_hs = q_hs; a.q_ts = q_ts;
     a.K = (const uint16_t*)K; a.k_hs = k_hs; a.k_ts = k_ts;
-    a.idx = p.all ? nullptr : idx; a.k = (int)p.k;
+    a.idx_out = idx; a.k = (int)p.k; a.select = !p.all;
     a.hq = (int)hq; a.hkv = (int)hkv; a.tq = (int)tq; a.tk = (int)tk; a.dh = (int)dh;
     a.S = S; a.s_bf16 = s_dtype == RMM_BF16;
     a.causal = causal;
@@ -739,6 +735,13 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
     RMM_LAUNCH(mk.mark(4));
     return RMM_OK;
   }
+  if (p.use_sel) {
+    RMM_LAUNCH(run_select(p.sel, ws, Q, bf16, q_hs, q_ts, (int)hq, tq, dh, p.k, idx, p.k, nullptr, s, &mk));
+  } else {
+    RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, nullptr, 0, 0, s));
+    RMM_LAUNCH(mk.mark(1));
+  }
+  RMM_LAUNCH(mk.mark(2));
   if (!p.mfma) {
     SimtArgs g{};
     g.A = Q; g.a_bf16 = false; g.a_bs = q_hs; g.a_rs = q_ts; g.a_cs = 1;

@@ -12,6 +12,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned long long)))) unsigned long long u64x2;
 
 // Fourth descriptor word of a raw buffer resource on gfx9-family parts
 // (32-bit data format, no swizzle): loads past num_records return zero.

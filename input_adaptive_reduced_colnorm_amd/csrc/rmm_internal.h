@@ -115,10 +115,12 @@ hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);
 // Decode-shaped QK^T (tq <= 16, group * tq <= 8, dh <= 256 and a multiple
 // of 8, bf16 K with 16-byte aligned rows): S[h][r][t] = sum over the k
 // features idx[h][0..k) (all dh when idx is null) of Q[h][r][f] K[g(h)][t][f].
+// The kernel also selects: idx_out[h][0..k) receives the kept features of
+// head h (ascending; all dh of them when select is false).
 struct QkDecodeArgs {
   const void* Q; bool q_bf16; int64_t q_hs, q_ts;
   const uint16_t* K; int64_t k_hs, k_ts;
-  const int32_t* idx; int k;
+  int32_t* idx_out; int k; bool select;
   int hq, hkv, tq, tk, dh;
   void* S; bool s_bf16;
   bool causal;          // S[h][r][t] = -inf where t > r + tk - tq

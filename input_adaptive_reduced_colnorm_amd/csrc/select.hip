@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __rest
                                                              float* __restrict__ scores, int64_t scores_hs,
                                                              int32_t* __restrict__ mask, int64_t mask_hs,
                                                              float* __restrict__ retained) {
-  __shared__ uint32_t s_keys[kSmallD];
+  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSmallD];
   __shared__ int s_wave[kSmallD / 64];
   __shared__ double s_energy[kSmallD / 64][2];
   const int head = blockIdx.x;
@@ -579,10 +579,19 @@ __global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __rest
   const uint32_t key = __float_as_uint(q);
   s_keys[j] = key;
   __syncthreads();
+  // four keys per 16-byte LDS read; bitwise, not short-circuit, so there is
+  // no branch per key
   int rank = 0;
-  for (int i = 0; i < d; ++i) {
-    const uint32_t v = s_keys[i];
-    rank += (v > key) || (v == key && i < j);
+  const uint4* sk4 = (const uint4*)s_keys;
+#pragma unroll 8
+  for (int i4 = 0; i4 < (d + 3) / 4; ++i4) {
+    const uint4 v = sk4[i4];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * i4 + e;
+      rank += (int)(i < d) & ((int)(w[e] > key) | ((int)(w[e] == key) & (int)(i < j)));
+    }
   }
   const bool keep = j < d && rank < k;
   const uint64_t ballot = __ballot(keep);

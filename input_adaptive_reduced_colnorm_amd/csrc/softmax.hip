@@ -13,7 +13,8 @@
 // registers, reduces the row maximum and the exponential sum over the
 // workgroup in a fixed order, writes P, and accumulates P^2 per column.
 // The per-workgroup column sums go to partial[h][row block][tk]; a second
-// kernel adds the row blocks in order.  Everything is deterministic.
+// kernel adds the row blocks in order (with a single row block per head the
+// sums are written as the energies directly).  Everything is deterministic.
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
@@ -130,6 +131,9 @@ hipError_t launch_softmax_energy(const float* L, int64_t l_hs, int64_t l_ts, flo
                                  hipStream_t s) {
   const int rpb = (tq + blocks - 1) / blocks;
   dim3 grid(blocks, heads);
+  // one row block per head (decode): its column sums are the energies, laid
+  // out [h][1][tk] = [h][tk], so they go straight to q
+  if (blocks == 1) partial = q;
   const int C = (tk + kThreads - 1) / kThreads;
   if (C <= 8)
     softmax_energy_kernel<8><<<grid, kThreads, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, rpb, scale, partial);
@@ -138,7 +142,7 @@ hipError_t launch_softmax_energy(const float* L, int64_t l_hs, int64_t l_ts, flo
   else
     softmax_energy_kernel<64><<<grid, kThreads, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, rpb, scale, partial);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || blocks == 1) return e;
   dim3 g2((tk + 255) / 256, heads);
   energy_reduce_kernel<<<g2, 256, 0, s>>>(partial, blocks, tk, q);
   return hipGetLastError();
