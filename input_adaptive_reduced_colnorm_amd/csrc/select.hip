@@ -565,7 +565,7 @@ __global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __rest
                                                              float* __restrict__ scores, int64_t scores_hs,
                                                              int32_t* __restrict__ mask, int64_t mask_hs,
                                                              float* __restrict__ retained) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSmallD];
+  __shared__ __attribute__((aligned(16))) uint64_t s_ck[kSmallD];
   __shared__ int s_wave[kSmallD / 64];
   __shared__ double s_energy[kSmallD / 64][2];
   const int head = blockIdx.x;
@@ -573,25 +573,29 @@ __global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __rest
   const float* P = partial + (size_t)head * splits * d;
   float q = 0.f;
   if (j < d) {
-    for (int s = 0; s < splits; ++s) q += P[(size_t)s * d + j];   // split order, as in topk_kernel
+    // the loads of up to 16 splits (the scoring pass makes at most 16) are
+    // issued together, then added in split order (the order topk_kernel uses)
+    for (int s0 = 0; s0 < splits; s0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = s0 + u < splits ? P[(size_t)(s0 + u) * d + j] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (s0 + u < splits) q += v[u];
+    }
     if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q);
   }
-  const uint32_t key = __float_as_uint(q);
-  s_keys[j] = key;
+  // composite key (energy bits, 0xFFFF - j): a larger composite outranks
+  // (higher energy, or equal energy and lower index), so one 64-bit compare
+  // per pair ranks it; two composites per 16-byte LDS read
+  const uint64_t ck = ((uint64_t)__float_as_uint(q) << 32) | (uint32_t)(0xFFFF - j);
+  s_ck[j] = ck;
   __syncthreads();
-  // four keys per 16-byte LDS read; bitwise, not short-circuit, so there is
-  // no branch per key
   int rank = 0;
-  const uint4* sk4 = (const uint4*)s_keys;
 #pragma unroll 8
-  for (int i4 = 0; i4 < (d + 3) / 4; ++i4) {
-    const uint4 v = sk4[i4];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * i4 + e;
-      rank += (int)(i < d) & ((int)(w[e] > key) | ((int)(w[e] == key) & (int)(i < j)));
-    }
+  for (int i2 = 0; i2 < (d + 1) / 2; ++i2) {
+    const u64x2 v = *(const u64x2*)(s_ck + 2 * i2);
+    rank += (int)(v[0] > ck) + ((int)(2 * i2 + 1 < d) & (int)(v[1] > ck));
   }
   const bool keep = j < d && rank < k;
   const uint64_t ballot = __ballot(keep);
