@@ -44,7 +44,7 @@ constexpr int kCols = 128;                    // output columns per workgroup (o
 constexpr int kChunk = 32;                    // kept rows per MFMA step
 constexpr int kChunksPerWave = 4;
 constexpr int kMaxSlice = kWaves * kChunksPerWave * kChunk;   // 512 kept rows per workgroup
-constexpr int kTargetGroups = 384;            // workgroups aimed for (256 CUs, two resident per CU)
+constexpr int kTargetGroups = 480;            // workgroups aimed for (256 CUs; measured best near 1.9 per CU)
 
 __device__ __forceinline__ int slice_rows(int k, int splits) {
   return ((k + splits - 1) / splits + kChunk - 1) / kChunk * kChunk;
@@ -202,8 +202,16 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const GemvArgs g) {
   const int bz = blockIdx.y;
   const int r = i / g.m, col = i % g.m;
   const float* part = g.partial + (size_t)bz * g.splits * g.n * g.m;
+  // the loads of 16 slices are issued before they are added (in order)
   float v = 0.f;
-  for (int s = 0; s < g.splits; ++s) v += part[(size_t)s * g.n * g.m + i];
+  for (int s0 = 0; s0 < g.splits; s0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) x[t] = s0 + t < g.splits ? part[(size_t)(s0 + t) * g.n * g.m + i] : 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (s0 + t < g.splits) v += x[t];
+  }
   if (g.col_scale) v *= g.col_scale[col];
   const size_t off = (size_t)bz * g.y_bs + (size_t)r * g.ldy + col;
   if (g.y_bf16)

@@ -135,6 +135,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 }
 
 constexpr int kHistBins = 2048;  // 11-bit radix digits
+constexpr uint32_t kFoldAbove = 2048;   // bucket size from which a radix pass folds equal digits
 constexpr int kChunk = (kKeyCap + kSelThreads - 1) / kSelThreads;  // most keys per thread held in registers
 
 // Keys per thread for a key count d held in LDS: the radix passes run one
@@ -145,6 +146,7 @@ struct SelShared {
   uint32_t hist[3 * kHistBins];   // one histogram per radix pass
   uint32_t misc[4];
   uint32_t wave_tot[kSelWaves][2];
+  uint32_t wave_nz[kSelWaves];
   double energy[kSelWaves][2];
 };
 
@@ -214,9 +216,16 @@ __device__ __forceinline__ void load_chunk(const uint32_t* keys, int d, KeyChunk
   for (int i = 0; i < CH; ++i) kc.key[i] = i < kc.cnt ? keys[kc.j0 + i] : 0u;
 }
 
-// Histogram increment with the lanes of a wave that share the first active
-// lane's digit folded into one atomic (ties and underflowed energies put
-// thousands of keys in one bin; one LDS atomic per lane would serialize).
+// Histogram increments.  hist_add_lane: one LDS atomic per active lane, the
+// cheapest form while the lanes' digits are spread over many bins.
+// hist_add: the lanes that share the first active lane's digit are folded
+// into one atomic, for buckets where ties are likely (a run of equal keys
+// sends every lane of a wave to one address, and per-lane atomics on one
+// address serialize); it costs about twice the instructions per key.
+__device__ __forceinline__ void hist_add_lane(uint32_t* hist, bool m, uint32_t dig) {
+  if (m) atomicAdd(&hist[dig], 1u);
+}
+
 __device__ __forceinline__ void hist_add(uint32_t* hist, bool m, uint32_t dig) {
   const uint64_t act = __ballot(m);
   if (act == 0) return;
@@ -235,48 +244,73 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool m, uint32_t dig) {
 // magnitude share sign and upper exponent bits), so the first histogram is
 // spread over many buckets instead of a few contended ones; all histograms
 // are cleared up front, and the passes stop as soon as the bucket holding
-// the k-th key is kept whole.
+// the k-th key is kept whole.  Zero keys (energies that are exactly zero or
+// underflowed, often thousands of ties) stay out of the histograms: when k
+// exceeds the nonzero count the answer is T = 0 at once, otherwise no zero
+// key can be kept.  The first pass adds one atomic per lane; a later pass
+// folds equal digits only when the bucket it refines holds more than
+// kFoldAbove keys (a bucket that large makes ties likely).
 template <int CH>
 __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t k_or = 0u, k_and = 0xffffffffu;
+  uint32_t k_or = 0u, k_and = 0xffffffffu, nz = 0u;
 #pragma unroll
   for (int i = 0; i < CH; ++i)
     if (i < kc.cnt) {
       k_or |= kc.key[i];
       k_and &= kc.key[i];
+      nz += kc.key[i] != 0u;
     }
   k_or = (uint32_t)__builtin_amdgcn_readlane(
       (int)wave_scan_dpp(k_or, 0u, [](uint32_t a, uint32_t b) { return a | b; }), 63);
   k_and = (uint32_t)__builtin_amdgcn_readlane(
       (int)wave_scan_dpp(k_and, ~0u, [](uint32_t a, uint32_t b) { return a & b; }), 63);
+  nz = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(nz), 63);
   for (int i = tid; i < 3 * kHistBins; i += kSelThreads) sh.hist[i] = 0;
   if (lane == 0) {
     sh.wave_tot[wave][0] = k_or;
     sh.wave_tot[wave][1] = k_and;
+    sh.wave_nz[wave] = nz;
   }
   __syncthreads();
   k_or = 0u;
   k_and = 0xffffffffu;
+  nz = 0u;
 #pragma unroll
   for (int w = 0; w < kSelWaves; ++w) {
     k_or |= sh.wave_tot[w][0];
     k_and &= sh.wave_tot[w][1];
+    nz += sh.wave_nz[w];
+  }
+  if ((uint32_t)k > nz) {
+    // every nonzero key is kept, and the lowest-indexed zeros fill up to k
+    *T = 0u;
+    *rem_out = (uint32_t)k - nz;
+    return;
   }
   const uint32_t diff = k_or ^ k_and;        // bits that differ between some keys
   int hi = diff ? 32 - __clz(diff) : 0;      // bits below hi still to resolve
   uint32_t mask = hi == 32 ? 0u : ~((1u << hi) - 1u);
   uint32_t prefix = k_and & mask;            // shared leading bits
   uint32_t rem = (uint32_t)k;
+  bool fold = false;
   for (int pass = 0; hi > 0; ++pass) {
     const int w = hi < 11 ? hi : 11;
     const int shift = hi - w;
     const uint32_t nb = 1u << w;
     uint32_t* hist = sh.hist + pass * kHistBins;
+    if (fold) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const uint32_t key = kc.key[i];
-      hist_add(hist, i < kc.cnt && (key & mask) == prefix, (key >> shift) & (nb - 1));
+      for (int i = 0; i < CH; ++i) {
+        const uint32_t key = kc.key[i];
+        hist_add(hist, i < kc.cnt && key != 0u && (key & mask) == prefix, (key >> shift) & (nb - 1));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const uint32_t key = kc.key[i];
+        hist_add_lane(hist, i < kc.cnt && key != 0u && (key & mask) == prefix, (key >> shift) & (nb - 1));
+      }
     }
     __syncthreads();
     // thread t owns the buckets nb-1-2t and nb-2-2t, counted from the top
@@ -302,9 +336,11 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
     prefix |= b << shift;
     mask |= (nb - 1) << shift;
     hi = shift;
+    fold = cnt > kFoldAbove;
     if (cnt == rem) {
       // every key of this bucket is kept: keep all keys >= its lowest value
-      *T = prefix;
+      // (a bucket starting at 0 holds no zero key here: start it at 1)
+      *T = prefix != 0u ? prefix : 1u;
       *rem_out = 0xffffffffu;
       return;
     }
@@ -441,30 +477,46 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   uint32_t* keys = LDS_KEYS ? s_keys : gkeys + (size_t)head * d;
   if constexpr (LDS_KEYS) {
     if (d % 4 == 0) {
-      // 4 columns per 16-byte load; the loads of up to 8 splits are issued
-      // together, then added in split order
+      // 4 columns per 16-byte load; a thread takes up to four 4-column
+      // groups at once and issues the loads of all of them for up to four
+      // splits before adding any (each column in split order)
+      constexpr int G = 4, S = 4;
       const int d4 = d / 4;
       const f32x4* P4 = (const f32x4*)P;
-      for (int j4 = threadIdx.x; j4 < d4; j4 += kSelThreads) {
-        f32x4 q = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < splits; s0 += 8) {
-          f32x4 v[8];
+      for (int jb = threadIdx.x; jb < d4; jb += G * kSelThreads) {
+        f32x4 q[G];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            v[u] = s0 + u < splits ? P4[(size_t)(s0 + u) * d4 + j4] : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < G; ++u) q[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < splits; s0 += S) {
+          f32x4 v[G][S];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (s0 + u < splits) {
-              q[0] += v[u][0];
-              q[1] += v[u][1];
-              q[2] += v[u][2];
-              q[3] += v[u][3];
+          for (int u = 0; u < G; ++u)
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+              const int j4 = jb + u * kSelThreads;
+              v[u][t] = (s0 + t < splits && j4 < d4) ? P4[(size_t)(s0 + t) * d4 + j4] : f32x4{0.f, 0.f, 0.f, 0.f};
             }
+#pragma unroll
+          for (int u = 0; u < G; ++u)
+#pragma unroll
+            for (int t = 0; t < S; ++t)
+              if (s0 + t < splits) {
+                q[u][0] += v[u][t][0];
+                q[u][1] += v[u][t][1];
+                q[u][2] += v[u][t][2];
+                q[u][3] += v[u][t][3];
+              }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          keys[4 * j4 + e] = __float_as_uint(q[e]);
-          if (scores) scores[(size_t)head * scores_hs + 4 * j4 + e] = sqrtf(q[e]);
+        for (int u = 0; u < G; ++u) {
+          const int j4 = jb + u * kSelThreads;
+          if (j4 < d4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              keys[4 * j4 + e] = __float_as_uint(q[u][e]);
+              if (scores) scores[(size_t)head * scores_hs + 4 * j4 + e] = sqrtf(q[u][e]);
+            }
+          }
         }
       }
     } else {
@@ -531,13 +583,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
     KeyChunk<CH> kc;
     load_chunk(keys, d, kc);
     radix_threshold(kc, k, sh, &T, &rem);
-    compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t key) {
-      if (take) s_out[pos] = j;
-      s_keys[j] = take;
-      const double q = (double)__uint_as_float(key);
-      e_all += q;
-      e_kept += take ? q : 0.0;
-    });
+    if (retained || mo) {
+      compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t key) {
+        if (take) s_out[pos] = j;
+        s_keys[j] = take;
+        const double q = (double)__uint_as_float(key);
+        e_all += q;
+        e_kept += take ? q : 0.0;
+      });
+    } else {
+      compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
+        if (take) s_out[pos] = j;
+      });
+    }
     __syncthreads();
     for (int t = threadIdx.x; t < k; t += kSelThreads) {
       const int j = s_out[t];

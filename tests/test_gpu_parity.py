@@ -151,6 +151,26 @@ def test_exact_ties_lowest_index(dev):
             np.testing.assert_array_equal(idx, idx_o)
 
 
+@pytest.mark.parametrize("n,d", [(32, 3000), (32, 9000), (8, 4096)])
+def test_radix_zero_and_tied_energies(dev, n, d):
+    # integer entries give exact energies on both sides, with many ties; 40%
+    # of the columns are zero, so large rho keeps every nonzero column plus
+    # the lowest-indexed zero columns, and small rho never reaches the zeros.
+    # d > 256 runs the radix selection (n = 8: the decode-shaped selection)
+    r = np.random.default_rng(n * 7 + d)
+    A = r.integers(-8, 9, size=(n, d)).astype(np.float32)
+    A[:, r.random(d) < 0.4] = 0.0
+    B = r.standard_normal((d, 16)).astype(np.float32)
+    for rho in (0.1, 0.3, 0.5, 0.62, 0.7, 0.9):
+        idx_o, _ = O.matmul(A, B, rho)
+        At = torch.from_numpy(A).to(torch.bfloat16)
+        idx = rmm.select(At.to(dev), rho)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+        idx_m, _ = run_matmul(At, torch.from_numpy(B).to(torch.bfloat16), rho, dev)
+        np.testing.assert_array_equal(idx_m, idx_o)
+
+
 @pytest.mark.parametrize("n", [1, 5, 8, 16])
 def test_decode_rows(dev, n):
     w = synth.decode_qkv(n=n, d=1024, m=776, rho=0.8)
