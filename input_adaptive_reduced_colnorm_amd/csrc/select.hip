@@ -23,21 +23,27 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kKeyCap = 15360;  // keys held in LDS (60 KiB); larger d uses global scratch
 
 // ---------------------------------------------------------------------------
-// Column energy sweep.  One workgroup covers a 128-byte column strip (64 bf16
-// or 32 fp32 columns) over one row split: 8 lanes span the strip with 16-byte
-// loads, 32 row lanes stride the rows, then the 32 row sums of each column
-// are added in a fixed order.
+// Column energy sweep.  One workgroup covers a 256-byte column strip (128
+// bf16 or 64 fp32 columns) over one row split: 16 lanes span the strip with
+// 16-byte loads, 16 row lanes stride the rows with 8 rows in flight each,
+// then the 16 row sums of each column are added in a fixed order.  (Strips
+// of 128 bytes streamed about 4.6 TB/s here, 256-byte strips about 5.2.)
 // ---------------------------------------------------------------------------
+constexpr int kCnLanes = 16;               // lanes across a strip
+constexpr int kCnRowLanes = 256 / kCnLanes;
+constexpr int kCnInFlight = 8;             // rows loaded per lane before use
+
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void colnorm_kernel(const void* __restrict__ A_, int64_t hs, int64_t lda,
                                                       int n, int d, int rows_per_split, int splits,
                                                       float* __restrict__ partial) {
   constexpr int VPT = BF16 ? 8 : 4;  // values per 16-byte load
-  constexpr int CB = 8 * VPT;        // columns per workgroup
-  __shared__ float red[32][CB + 1];
+  constexpr int CB = kCnLanes * VPT; // columns per workgroup
+  constexpr int RL = kCnRowLanes, U = kCnInFlight;
+  __shared__ float red[RL][CB + 1];
 
   const int tid = threadIdx.x;
-  const int tr = tid >> 3, tc = tid & 7;
+  const int tr = tid / kCnLanes, tc = tid % kCnLanes;
   const int head = blockIdx.z;
   const int col0 = blockIdx.x * CB + tc * VPT;
   const int r_begin = blockIdx.y * rows_per_split;
@@ -50,49 +56,34 @@ __global__ __launch_bounds__(256) void colnorm_kernel(const void* __restrict__ A
   if (VEC && col0 + VPT <= d) {
     const char* base = (const char*)A_ + (size_t)head * hs * (BF16 ? 2 : 4) + (size_t)col0 * (BF16 ? 2 : 4);
     const size_t row_bytes = (size_t)lda * (BF16 ? 2 : 4);
-    int r = r_begin + tr;
-    for (; r + 96 < r_end; r += 128) {
-      i32x4 x[4];
+    for (int r = r_begin + tr; r < r_end; r += RL * U) {
+      i32x4 x[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = *(const i32x4*)(base + (size_t)(r + 32 * u) * row_bytes);
+      for (int u = 0; u < U; ++u)
+        x[u] = r + RL * u < r_end ? *(const i32x4*)(base + (size_t)(r + RL * u) * row_bytes) : i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          uint32_t bits = (uint32_t)x[u][w];
+          const uint32_t bits = (uint32_t)x[u][w];
           if (BF16) {
-            float lo = __uint_as_float(bits << 16), hi = __uint_as_float(bits & 0xffff0000u);
+            const float lo = __uint_as_float(bits << 16), hi = __uint_as_float(bits & 0xffff0000u);
             acc[2 * w] = fmaf(lo, lo, acc[2 * w]);
             acc[2 * w + 1] = fmaf(hi, hi, acc[2 * w + 1]);
           } else {
-            float f = __uint_as_float(bits);
+            const float f = __uint_as_float(bits);
             acc[w] = fmaf(f, f, acc[w]);
           }
         }
       }
     }
-    for (; r < r_end; r += 32) {
-      i32x4 x = *(const i32x4*)(base + (size_t)r * row_bytes);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t bits = (uint32_t)x[w];
-        if (BF16) {
-          float lo = __uint_as_float(bits << 16), hi = __uint_as_float(bits & 0xffff0000u);
-          acc[2 * w] = fmaf(lo, lo, acc[2 * w]);
-          acc[2 * w + 1] = fmaf(hi, hi, acc[2 * w + 1]);
-        } else {
-          float f = __uint_as_float(bits);
-          acc[w] = fmaf(f, f, acc[w]);
-        }
-      }
-    }
   } else {
-    for (int r = r_begin + tr; r < r_end; r += 32) {
+    for (int r = r_begin + tr; r < r_end; r += RL) {
 #pragma unroll
       for (int v = 0; v < VPT; ++v) {
         if (col0 + v < d) {
-          size_t off = (size_t)head * hs + (size_t)r * lda + col0 + v;
-          float f = BF16 ? bf16_to_f32(((const uint16_t*)A_)[off]) : ((const float*)A_)[off];
+          const size_t off = (size_t)head * hs + (size_t)r * lda + col0 + v;
+          const float f = BF16 ? bf16_to_f32(((const uint16_t*)A_)[off]) : ((const float*)A_)[off];
           acc[v] = fmaf(f, f, acc[v]);
         }
       }
@@ -104,8 +95,8 @@ __global__ __launch_bounds__(256) void colnorm_kernel(const void* __restrict__ A
   __syncthreads();
   if (tid < CB) {
     float s = 0.f;
-#pragma unroll 8
-    for (int t = 0; t < 32; ++t) s += red[t][tid];
+#pragma unroll
+    for (int t = 0; t < RL; ++t) s += red[t][tid];
     const int col = blockIdx.x * CB + tid;
     if (col < d) partial[((size_t)head * splits + blockIdx.y) * d + col] = s;
   }
@@ -804,19 +795,24 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
 }  // namespace
 
 int colnorm_splits(int heads, int n, int d, bool elt_bf16) {
-  const int cb = elt_bf16 ? 64 : 32;
+  const int cb = kCnLanes * (elt_bf16 ? 8 : 4);
   const long col_blocks = (long)((d + cb - 1) / cb) * heads;
-  long s = (1024 + col_blocks - 1) / col_blocks;
+  // about 560 workgroups: more splits stream A a little faster (5.2 -> 5.4
+  // TB/s at 1800 groups) but cost the selection more than they save
+  long s = (560 + col_blocks - 1) / col_blocks;
   long max_by_rows = (n + 127) / 128;
   if (s > max_by_rows) s = max_by_rows;
-  if (s > 16) s = 16;
+  // the selection re-reads splits x d partials in one workgroup: few
+  // splits for wide rows, more for the short feature rows of attention heads
+  const long max_splits = d <= 256 ? 32 : 16;
+  if (s > max_splits) s = max_splits;
   if (s < 1) s = 1;
   return (int)s;
 }
 
 hipError_t launch_colnorm(const void* A, bool elt_bf16, int64_t head_stride, int64_t lda, int heads, int n, int d,
                           int splits, float* partial, hipStream_t s) {
-  const int cb = elt_bf16 ? 64 : 32;
+  const int cb = kCnLanes * (elt_bf16 ? 8 : 4);
   const int rows_per_split = (n + splits - 1) / splits;
   dim3 grid((d + cb - 1) / cb, splits, heads);
   const size_t elt = elt_bf16 ? 2 : 4;
