@@ -230,47 +230,49 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool m, uint32_t dig) {
 // Finds the k-th largest key: on return *T is its value and *rem the number
 // of keys equal to T that belong to the kept set (the lowest-indexed ones;
 // 0xffffffff means every key equal to T is kept).  MSB-first radix passes
-// with integer LDS histograms of up to 11-bit digits.  The digits start
-// below the leading bits that all keys share (fp32 energies of similar
-// magnitude share sign and upper exponent bits), so the first histogram is
-// spread over many buckets instead of a few contended ones; all histograms
-// are cleared up front, and the passes stop as soon as the bucket holding
-// the k-th key is kept whole.  Zero keys (energies that are exactly zero or
-// underflowed, often thousands of ties) stay out of the histograms: when k
-// exceeds the nonzero count the answer is T = 0 at once, otherwise no zero
-// key can be kept.  The first pass adds one atomic per lane; a later pass
-// folds equal digits only when the bucket it refines holds more than
-// kFoldAbove keys (a bucket that large makes ties likely).
+// with integer LDS histograms of up to 11-bit digits, over the offsets
+// key - kmin of the nonzero keys: the first digit starts at the top bit of
+// kmax - kmin, so the first histogram spreads over 1024-2048 buckets
+// whatever the keys' magnitude (fp32 energies of a few octaves would share
+// their sign and upper exponent bits and crowd a few dozen buckets).  All
+// histograms are cleared up front, and the passes stop as soon as the
+// bucket holding the k-th key is kept whole.  Zero keys (energies that are
+// exactly zero or underflowed, often thousands of ties) stay out of the
+// histograms: when k exceeds the nonzero count the answer is T = 0 at once,
+// otherwise no zero key can be kept.  The first pass adds one atomic per
+// lane; a later pass folds equal digits only when the bucket it refines
+// holds more than kFoldAbove keys (a bucket that large makes ties likely).
 template <int CH>
 __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t k_or = 0u, k_and = 0xffffffffu, nz = 0u;
+  uint32_t k_min = 0xffffffffu, k_max = 0u, nz = 0u;
 #pragma unroll
-  for (int i = 0; i < CH; ++i)
-    if (i < kc.cnt) {
-      k_or |= kc.key[i];
-      k_and &= kc.key[i];
-      nz += kc.key[i] != 0u;
-    }
-  k_or = (uint32_t)__builtin_amdgcn_readlane(
-      (int)wave_scan_dpp(k_or, 0u, [](uint32_t a, uint32_t b) { return a | b; }), 63);
-  k_and = (uint32_t)__builtin_amdgcn_readlane(
-      (int)wave_scan_dpp(k_and, ~0u, [](uint32_t a, uint32_t b) { return a & b; }), 63);
+  for (int i = 0; i < CH; ++i) {
+    const uint32_t key = kc.key[i];
+    const bool live = i < kc.cnt && key != 0u;
+    k_min = min(k_min, live ? key : 0xffffffffu);
+    k_max = max(k_max, live ? key : 0u);
+    nz += live;
+  }
+  k_min = (uint32_t)__builtin_amdgcn_readlane(
+      (int)wave_scan_dpp(k_min, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); }), 63);
+  k_max = (uint32_t)__builtin_amdgcn_readlane(
+      (int)wave_scan_dpp(k_max, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }), 63);
   nz = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(nz), 63);
   for (int i = tid; i < 3 * kHistBins; i += kSelThreads) sh.hist[i] = 0;
   if (lane == 0) {
-    sh.wave_tot[wave][0] = k_or;
-    sh.wave_tot[wave][1] = k_and;
+    sh.wave_tot[wave][0] = k_min;
+    sh.wave_tot[wave][1] = k_max;
     sh.wave_nz[wave] = nz;
   }
   __syncthreads();
-  k_or = 0u;
-  k_and = 0xffffffffu;
+  k_min = 0xffffffffu;
+  k_max = 0u;
   nz = 0u;
 #pragma unroll
   for (int w = 0; w < kSelWaves; ++w) {
-    k_or |= sh.wave_tot[w][0];
-    k_and &= sh.wave_tot[w][1];
+    k_min = min(k_min, sh.wave_tot[w][0]);
+    k_max = max(k_max, sh.wave_tot[w][1]);
     nz += sh.wave_nz[w];
   }
   if ((uint32_t)k > nz) {
@@ -279,10 +281,11 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
     *rem_out = (uint32_t)k - nz;
     return;
   }
-  const uint32_t diff = k_or ^ k_and;        // bits that differ between some keys
-  int hi = diff ? 32 - __clz(diff) : 0;      // bits below hi still to resolve
+  // from here k <= nz, so kmin <= kmax are keys; offsets lie in [0, span]
+  const uint32_t span = k_max - k_min;
+  int hi = span ? 32 - __clz(span) : 0;      // offset bits still to resolve
   uint32_t mask = hi == 32 ? 0u : ~((1u << hi) - 1u);
-  uint32_t prefix = k_and & mask;            // shared leading bits
+  uint32_t prefix = 0u;                      // resolved offset bits
   uint32_t rem = (uint32_t)k;
   bool fold = false;
   for (int pass = 0; hi > 0; ++pass) {
@@ -293,14 +296,14 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
     if (fold) {
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
-        const uint32_t key = kc.key[i];
-        hist_add(hist, i < kc.cnt && key != 0u && (key & mask) == prefix, (key >> shift) & (nb - 1));
+        const uint32_t key = kc.key[i], off = key - k_min;
+        hist_add(hist, i < kc.cnt && key != 0u && (off & mask) == prefix, (off >> shift) & (nb - 1));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
-        const uint32_t key = kc.key[i];
-        hist_add_lane(hist, i < kc.cnt && key != 0u && (key & mask) == prefix, (key >> shift) & (nb - 1));
+        const uint32_t key = kc.key[i], off = key - k_min;
+        hist_add_lane(hist, i < kc.cnt && key != 0u && (off & mask) == prefix, (off >> shift) & (nb - 1));
       }
     }
     __syncthreads();
@@ -330,13 +333,13 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
     fold = cnt > kFoldAbove;
     if (cnt == rem) {
       // every key of this bucket is kept: keep all keys >= its lowest value
-      // (a bucket starting at 0 holds no zero key here: start it at 1)
-      *T = prefix != 0u ? prefix : 1u;
+      // (at least kmin, so no zero key)
+      *T = k_min + prefix;
       *rem_out = 0xffffffffu;
       return;
     }
   }
-  *T = prefix;
+  *T = k_min + prefix;
   *rem_out = rem;
 }
 
