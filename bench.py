@@ -83,6 +83,22 @@ class Events:
             self.hip.hipEventDestroy(e)
 
 
+def _repeat_for(min_seconds, fn, max_reps=16):
+    """Runs fn until at least min_seconds of wall time have passed (at most
+    max_reps times); returns (repetitions, seconds)."""
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        fn()
+        reps += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_seconds or reps >= max_reps:
+            return reps, wall
+
+
+CPU_SAMPLE_SECONDS = 10.0
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -156,7 +172,7 @@ class MatmulOp:
 
     def roofline_kernel(self):
         if self.decode:
-            return "gemv_kernel (kept rows of B)"
+            return "gemv_kernel + gemv_reduce_kernel (kept rows of B, then the slices added in order)"
         return "gemm_bf16_kernel<256,256,kmajor,gather> (reduced GEMM)"
 
     def traffic_ref(self):
@@ -174,17 +190,14 @@ class MatmulOp:
         rows = None
         if self.n * self.d * self.m > 4096 * 14336 * 4096:
             rows = np.arange(1024)        # bound the sample for larger shapes
-        t0 = time.perf_counter()
-        for rho in self.rhos:
-            O.matmul(A, B, rho, rows=rows)
-        wall = time.perf_counter() - t0
+        reps, wall = _repeat_for(CPU_SAMPLE_SECONDS, lambda: [O.matmul(A, B, rho, rows=rows) for rho in self.rhos])
         scale = 1 if rows is None else self.n / len(rows)
-        ops = len(self.rhos) / (wall * scale)
+        ops = reps * len(self.rhos) / (wall * scale)
         what = "every row" if rows is None else f"rows 0..{len(rows) - 1} of {self.n} (product), scaled by {scale:g}x"
         return {"value": ops, "unit": "RMM ops/s", "cores": _blas_threads(), "host_cpus": os.cpu_count(),
                 "kind": "oracle",
                 "sample": (f"fp64 oracle (scoring, stable-sort TopK, gather, product) for one call per rho in "
-                           f"{list(self.rhos)} over {what}; {wall:.1f} s of CPU work")}
+                           f"{list(self.rhos)} over {what}, {reps} repetitions; {wall:.1f} s of CPU work")}
 
 
 class MatmulW8Op(MatmulOp):
@@ -234,7 +247,7 @@ class MatmulW8Op(MatmulOp):
 
     def roofline_kernel(self):
         if self.decode:
-            return "gemv_kernel<bf16 A, int8 B> (kept int8 rows of B)"
+            return "gemv_kernel<bf16 A, int8 B> + gemv_reduce_kernel (kept int8 rows of B, then the slices added in order)"
         return "gemm_bf16_kernel<256,256,kmajor,gather,int8 B> (reduced GEMM)"
 
     def traffic_ref(self):
@@ -280,16 +293,14 @@ class MatmulW8Op(MatmulOp):
         Bq = self.Bq_cpu.numpy()
         sc = self.scale_cpu.numpy()
         rows = None if self.n <= 1024 else np.arange(1024)
-        t0 = time.perf_counter()
-        for rho in self.rhos:
-            O.matmul_w8(A, Bq, sc, rho, rows=rows)
-        wall = time.perf_counter() - t0
+        reps, wall = _repeat_for(CPU_SAMPLE_SECONDS,
+                                 lambda: [O.matmul_w8(A, Bq, sc, rho, rows=rows) for rho in self.rhos])
         scale = 1 if rows is None else self.n / len(rows)
         what = "every row" if rows is None else f"rows 0..{len(rows) - 1} of {self.n} (product), scaled by {scale:g}x"
-        return {"value": len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
+        return {"value": reps * len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
                 "host_cpus": os.cpu_count(), "kind": "oracle",
-                "sample": (f"fp64 oracle with int8 weights for one call per rho in {list(self.rhos)} over {what}; "
-                           f"{wall:.1f} s of CPU work")}
+                "sample": (f"fp64 oracle with int8 weights for one call per rho in {list(self.rhos)} over {what}, "
+                           f"{reps} repetitions; {wall:.1f} s of CPU work")}
 
 
 class QkOp:
@@ -385,16 +396,13 @@ class QkOp:
         Q = self.Q_cpu.float().numpy()
         K = self.K_cpu.float().numpy()
         heads = list(range(0, self.hq, 4))          # 8 of 32 query heads
-        t0 = time.perf_counter()
-        for rho in self.rhos:
-            O.qk(Q, K, rho, heads=heads)
-        wall = time.perf_counter() - t0
+        reps, wall = _repeat_for(CPU_SAMPLE_SECONDS, lambda: [O.qk(Q, K, rho, heads=heads) for rho in self.rhos])
         scale = self.hq / len(heads)
-        return {"value": len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
+        return {"value": reps * len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
                 "host_cpus": os.cpu_count(), "kind": "oracle",
                 "sample": (f"fp64 oracle qk for query heads {heads[0]}, {heads[1]}, ... (every 4th, "
-                           f"{len(heads)} of {self.hq}) at each rho in {list(self.rhos)}, scaled by {scale:g}x; "
-                           f"{wall:.1f} s of CPU work")}
+                           f"{len(heads)} of {self.hq}) at each rho in {list(self.rhos)}, scaled by {scale:g}x, "
+                           f"{reps} repetitions; {wall:.1f} s of CPU work")}
 
 
 class PvOp:
@@ -524,16 +532,13 @@ class PvOp:
         P = self.P_cpu.numpy()
         V = self.V_cpu.float().numpy()
         heads = list(range(0, self.h, 4))           # 16 of 64 heads
-        t0 = time.perf_counter()
-        for rho in self.rhos:
-            O.pv(P, V, rho, heads=heads)
-        wall = time.perf_counter() - t0
+        reps, wall = _repeat_for(CPU_SAMPLE_SECONDS, lambda: [O.pv(P, V, rho, heads=heads) for rho in self.rhos])
         scale = self.h / len(heads)
-        return {"value": len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
+        return {"value": reps * len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
                 "host_cpus": os.cpu_count(), "kind": "oracle",
                 "sample": (f"fp64 oracle pv for heads {heads[0]}, {heads[1]}, ... (every 4th, {len(heads)} of "
-                           f"{self.h}) at each rho in {list(self.rhos)}, scaled by {scale:g}x; "
-                           f"{wall:.1f} s of CPU work")}
+                           f"{self.h}) at each rho in {list(self.rhos)}, scaled by {scale:g}x, "
+                           f"{reps} repetitions; {wall:.1f} s of CPU work")}
 
 
 # ---------------------------------------------------------------------------
@@ -810,7 +815,8 @@ class DecodeAttnOp:
 
     def roofline_kernel(self):
         return {"qk": "qk_decode_kernel (streaming pass over the key cache)",
-                "softmax": "softmax_energy_kernel", "pv": "gemv_kernel batched over heads (kept V rows)"}
+                "softmax": "softmax_energy_kernel", "pv": "the rmm_pv_energy call: topk_kernel over the key energies, gemv_kernel batched over heads "
+                      "(kept V rows) and gemv_reduce_kernel"}
 
     def traffic_ref(self):
         return None
@@ -833,7 +839,7 @@ class DecodeAttnOp:
                 E = np.stack([O.col_energy(P[h]) for h in range(self.hq)])
                 O.pv_given_energy(P, V, E, rho)
             reps += 1
-            if time.perf_counter() - t0 > 5.0:
+            if time.perf_counter() - t0 > CPU_SAMPLE_SECONDS:
                 break
         wall = time.perf_counter() - t0
         return {"value": reps * len(self.rhos) / wall, "unit": "decode attention steps/s", "cores": _blas_threads(),
