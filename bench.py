@@ -99,6 +99,17 @@ def _repeat_for(min_seconds, fn, max_reps=16):
 CPU_SAMPLE_SECONDS = 10.0
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover - informational only
+        pass
+    return None
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -160,7 +171,10 @@ class MatmulOp:
         n, d, m, k = self.n, self.d, self.m, self.ks[rho]
         if self.decode:
             # one workgroup scores and selects; the GEMV streams the kept rows of B
-            return {"score": ("B", n * d * 2), "gemm": ("B", k * m * 2)}
+            w = {"gemm": ("B", k * m * 2)}
+            if k < d:
+                w["score"] = ("B", n * d * 2)
+            return w
         w = {"gemm": ("F", 2.0 * n * k * m)}
         if k < d:
             w["score"] = ("B", n * d * 2)
@@ -194,7 +208,7 @@ class MatmulOp:
         scale = 1 if rows is None else self.n / len(rows)
         ops = reps * len(self.rhos) / (wall * scale)
         what = "every row" if rows is None else f"rows 0..{len(rows) - 1} of {self.n} (product), scaled by {scale:g}x"
-        return {"value": ops, "unit": "RMM ops/s", "cores": _blas_threads(), "host_cpus": os.cpu_count(),
+        return {"value": ops, "unit": "RMM ops/s", "cores": _blas_threads(), "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
                 "kind": "oracle",
                 "sample": (f"fp64 oracle (scoring, stable-sort TopK, gather, product) for one call per rho in "
                            f"{list(self.rhos)} over {what}, {reps} repetitions; {wall:.1f} s of CPU work")}
@@ -238,7 +252,10 @@ class MatmulW8Op(MatmulOp):
     def stage_work(self, rho):
         n, d, m, k = self.n, self.d, self.m, self.ks[rho]
         if self.decode:
-            return {"score": ("B", n * d * 2), "gemm": ("B", k * m * 1)}
+            w = {"gemm": ("B", k * m * 1)}
+            if k < d:
+                w["score"] = ("B", n * d * 2)
+            return w
         w = {"gemm": ("F", 2.0 * n * k * m)}
         if k < d:
             w["score"] = ("B", n * d * 2)
@@ -298,7 +315,7 @@ class MatmulW8Op(MatmulOp):
         scale = 1 if rows is None else self.n / len(rows)
         what = "every row" if rows is None else f"rows 0..{len(rows) - 1} of {self.n} (product), scaled by {scale:g}x"
         return {"value": reps * len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
-                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(), "kind": "oracle",
                 "sample": (f"fp64 oracle with int8 weights for one call per rho in {list(self.rhos)} over {what}, "
                            f"{reps} repetitions; {wall:.1f} s of CPU work")}
 
@@ -399,7 +416,7 @@ class QkOp:
         reps, wall = _repeat_for(CPU_SAMPLE_SECONDS, lambda: [O.qk(Q, K, rho, heads=heads) for rho in self.rhos])
         scale = self.hq / len(heads)
         return {"value": reps * len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
-                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(), "kind": "oracle",
                 "sample": (f"fp64 oracle qk for query heads {heads[0]}, {heads[1]}, ... (every 4th, "
                            f"{len(heads)} of {self.hq}) at each rho in {list(self.rhos)}, scaled by {scale:g}x, "
                            f"{reps} repetitions; {wall:.1f} s of CPU work")}
@@ -535,7 +552,7 @@ class PvOp:
         reps, wall = _repeat_for(CPU_SAMPLE_SECONDS, lambda: [O.pv(P, V, rho, heads=heads) for rho in self.rhos])
         scale = self.h / len(heads)
         return {"value": reps * len(self.rhos) / (wall * scale), "unit": "RMM ops/s", "cores": _blas_threads(),
-                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(), "kind": "oracle",
                 "sample": (f"fp64 oracle pv for heads {heads[0]}, {heads[1]}, ... (every 4th, {len(heads)} of "
                            f"{self.h}) at each rho in {list(self.rhos)}, scaled by {scale:g}x, "
                            f"{reps} repetitions; {wall:.1f} s of CPU work")}
@@ -660,6 +677,12 @@ def run(args, op):
                 if s in work:
                     for key, v in _rate(*work[s], mean[r][s]).items():
                         row[f"{s}_{key}"] = v
+        if "score" in work and work["score"][0] == "B" and "topk" in names:
+            # the whole selection (energies + TopK) against the bytes of A it reads
+            sel_us = mean[r]["score"] + mean[r]["topk"]
+            row["selection_us"] = round(sel_us, 2)
+            for key, v in _rate("B", work["score"][1], sel_us).items():
+                row[f"selection_{key}"] = v
         per_kernel[str(r)] = row
 
     # roofline of the dominant kernel of the reduced op (mean over its launches)
@@ -843,7 +866,7 @@ class DecodeAttnOp:
                 break
         wall = time.perf_counter() - t0
         return {"value": reps * len(self.rhos) / wall, "unit": "decode attention steps/s", "cores": _blas_threads(),
-                "host_cpus": os.cpu_count(), "kind": "oracle",
+                "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(), "kind": "oracle",
                 "sample": (f"fp64 oracle qk, row softmax, energies and pv on the whole step at each rho in "
                            f"{list(self.rhos)}, {reps} repetitions; {wall:.1f} s of CPU work")}
 

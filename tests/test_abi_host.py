@@ -91,6 +91,15 @@ def test_matmul_rejects_bad_arguments(L):
     assert _matmul(L, ws=FAKE + (3 << 30)) == ALIAS    # workspace overlaps Y
 
 
+def test_matmul_size_limits(L):
+    # dimensions reach 2^31 - 1 at most; a bf16 operand the matrix-core
+    # loaders address must stay below 2 GiB (32-bit byte offsets)
+    far = dict(B=FAKE + (1 << 40), idx=FAKE + (2 << 40), Y=FAKE + (3 << 40), ws=FAKE + (4 << 40), wsb=1 << 40)
+    assert _matmul(L, d=1 << 31, lda=1 << 31, **far) == SHAPE
+    assert _matmul(L, m=1 << 31, ldb=1 << 31, ldy=1 << 31, **far) == SHAPE
+    assert _matmul(L, d=32768, lda=32768, m=32768, ldb=32768, ldy=32768, **far) == SHAPE   # B is 2 GiB
+
+
 def test_matmul_dense_needs_no_workspace(L):
     assert L.rmm_matmul_workspace(64, 128, 64, 128, BF16, 1.0) == 0
     assert L.rmm_matmul_workspace(64, 128, 64, 128, BF16, 0.5) > 0
