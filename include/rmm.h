@@ -25,7 +25,9 @@
  *     is written in ascending index order.
  *   - One kept set per call over all rows of A; one per head for QK / PV.
  *   - GQA: query head h reads K/V head h / (hq / hkv).
- *   - Q K^T is the raw product (no 1/sqrt(dh) scale, no mask).
+ *   - Q K^T is the raw product with no 1/sqrt(dh) scale (the softmax
+ *     entry point takes the scale); rmm_qk applies no mask, rmm_qk_causal
+ *     the causal one.
  *
  * Conventions for every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -191,6 +193,11 @@ rmm_status_t rmm_matmul_idx(const void* A, const void* B, int dtype, int64_t n, 
  *       k_ts.  Q and K share `dtype` (fp32 or bf16).
  *   idx [hq][k] int32, each row ascending, k = rmm_k(rho, dh).
  *   S   [hq][tq][tk] contiguous, s_dtype fp32 or bf16.
+ * With bf16 Q and K, at most 8 query rows per kv head ((hq / hkv) * tq),
+ * dh a multiple of 8 up to 256 and 16-byte aligned K rows (decode), the
+ * selection and the product run in one streaming pass over K; otherwise
+ * the column energies, TopK, packs of Q and K and a batched matrix-core
+ * product.
  * Source: hackcv.com, Component mapping (QK^T over the head feature dim,
  * selection on Q, K gathers the matching dims under GQA).
  * ------------------------------------------------------------------- */
@@ -233,7 +240,8 @@ rmm_status_t rmm_qk_causal(const void* Q, const void* K, int dtype, int64_t hq, 
  *       the product reads P in place over all tk positions with the
  *       dropped rows of V read as zeros (the same sum over I_h; P is
  *       bandwidth-bound either way); otherwise the kept columns of P are
- *       packed first.
+ *       packed first.  tq <= 16 with bf16 V (decode) runs a GEMV per head
+ *       that reads only the kept rows of V.
  *   idx [h][k] int32, each row ascending, k = rmm_k(rho, tk).
  *   O   [h][tq][dv] contiguous, o_dtype fp32 or bf16.
  * Source: hackcv.com, Component mapping (PV optionally over token
