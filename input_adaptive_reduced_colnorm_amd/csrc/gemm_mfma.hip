@@ -60,6 +60,35 @@ __device__ __forceinline__ TileCoord tile_of(int bid, int tiles_m, int tiles_n, 
   return c;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes LDS bytes
+// [dst + 16 l, dst + 16 l + 16) (dst uniform across the wave); an offset past
+// the buffer end writes zeros.  Completion is counted by vmcnt.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier of the main loop with direct loads in flight: this
+// wave's LDS stores are complete (lgkmcnt(0); the direct loads that must
+// land are waited for by the caller), then s_barrier.  A release fence (as
+// in __syncthreads) would also wait for the direct loads of the tile after
+// next; the empty asm statements only keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
@@ -83,10 +112,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   constexpr int NBLK = BN;                          // (64 / 8) * (BN / 8)
   constexpr int BR = NT >= 2 * NBLK ? 4 : 8;
   constexpr int B_OWNERS = NBLK * (8 / BR);
-  constexpr int STAGE = (BM + BN) * 128;           // bytes per LDS stage
   constexpr int ES = A_F32 ? 4 : 2;                // A element size
   static_assert(B_OWNERS <= NT, "B blocks exceed the thread count");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  // With K-major B (the linear products) bf16 A goes from the buffer
+  // straight into LDS (no staging registers), two K tiles ahead through a
+  // ring of three A stages; fp32 A (converted on the way), the A of the
+  // N-major QK products (a K tile or two per output tile) and every B tile
+  // pass through registers into two stages
+  constexpr bool A_DIRECT = !A_F32 && KMAJOR;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  constexpr int A_STAGES = A_DIRECT ? 3 : 2;
+  static_assert(!A_DIRECT || !KMAJOR || B_OWNERS == NT, "every wave issues the same number of loads per tile");
+  __shared__ __attribute__((aligned(16))) char smem[A_STAGES * A_BYTES + 2 * B_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -115,6 +152,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     const int row = m0 + (tid >> 3) + ROWS_PER_PASS * i;
     a_off[i] = row < g.M ? (uint32_t)(row * g.lda + a_kc) * ES : kOobOffset;
   }
+  // direct A: instruction i of wave w fills LDS rows (w A_CH + i) 8 .. + 7 of
+  // a stage; lane l carries row + l / 8 and LDS chunk slot l % 8, which
+  // holds global chunk swz(row, slot) (the swizzle is an involution, so the
+  // layout is the one the fragment reads expect)
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t ad_off[A_DIRECT ? A_CH : 1];
+  if constexpr (A_DIRECT) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int r = (wave_u * A_CH + i) * 8 + (lane >> 3);
+      const int row = m0 + r;
+      ad_off[i] = row < g.M ? (uint32_t)(row * g.lda + swz(r, lane & 7) * 8) * 2u : kOobOffset;
+    }
+  }
   uint32_t b_off[KMAJOR ? 1 : B_CH];
   if constexpr (!KMAJOR) {
 #pragma unroll
@@ -133,7 +184,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   const int kb_col = n0 + kb_cg * 8;
   const int kb_row0 = kb_kg * 8 + kb_h * BR;
 
-  constexpr int A_REGS = A_F32 ? 2 * A_CH : A_CH;
+  constexpr int A_REGS = A_DIRECT ? 1 : (A_F32 ? 2 * A_CH : A_CH);
   i32x4 ra_regs[A_REGS];
   typename RowPiece<B_I8>::type rb_regs[KMAJOR ? BR : B_CH];
   i32x4 idx_lo, idx_hi;   // kept rows for the next tile to load
@@ -146,9 +197,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     }
   };
 
+  auto issue_a = [&](int kt, int stage) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      load_lds16(ra, (lds_void*)(smem + stage * A_BYTES + (wave_u * A_CH + i) * 1024),
+                 ad_off[i] + (uint32_t)(kt * BK * 2));
+  };
+
   auto load_tile = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
+    for (int i = 0; i < (A_DIRECT ? 0 : A_CH); ++i) {
       const uint32_t off = a_off[i] + (uint32_t)(kt * BK * ES);
       if constexpr (A_F32) {
         ra_regs[2 * i] = buf_load16(ra, off);
@@ -179,11 +237,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     }
   };
 
-  auto store_tile = [&](int buf) {
-    char* As = smem + buf * STAGE;
-    char* Bs = As + BM * 128;
+  // register-staged parts of K tile kt into LDS: B into stage kt & 1, and
+  // fp32 A (converted to bf16) into stage kt & 1 of the A stages
+  auto store_tile = [&](int kt) {
+    char* As = smem + (kt & 1) * A_BYTES;
+    char* Bs = smem + A_STAGES * A_BYTES + (kt & 1) * B_BYTES;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
+    for (int i = 0; i < (A_DIRECT ? 0 : A_CH); ++i) {
       const int row = (tid >> 3) + ROWS_PER_PASS * i, ch = tid & 7;
       i32x4 v;
       if constexpr (A_F32) {
@@ -252,9 +312,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
 #pragma unroll
   for (int j = 0; j < TN; ++j) b_row[j] = wn * WN + j * 32 + li;
 
-  auto read_frags = [&](int buf, int s, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
-    const char* As = smem + buf * STAGE;
-    const char* Bs = As + BM * 128;
+  auto read_frags = [&](int kt, int s, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
+    const char* As = smem + (A_DIRECT ? kt % 3 : kt & 1) * A_BYTES;
+    const char* Bs = smem + A_STAGES * A_BYTES + (kt & 1) * B_BYTES;
     const int ch = 2 * s + lk;
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8*)(As + a_row[i] * 128 + swz(a_row[i], ch) * 16);
@@ -287,39 +347,97 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       cs[j] = g.col_scale[col < g.N ? col : 0];
     }
   }
-  // prologue: tile 0 into LDS, tile 1 in flight in registers
+  // prologue: tile 0 into LDS, tile 1 in flight (direct A: already bound
+  // for its stage; the rest in registers)
   if (KT > 0) {
+    if constexpr (A_DIRECT) issue_a(0, 0);
     load_idx(0);
     load_tile(0);
     store_tile(0);
   }
   if (KT > 1) {
+    if constexpr (A_DIRECT) issue_a(1, 1);
     load_idx(1);
     load_tile(1);
   }
   if (KT > 2) load_idx(2);
+  if constexpr (A_DIRECT) wait_vmcnt<0>();
   __syncthreads();
 
+  // vector-memory operations one tile's issue adds per wave (direct A rows,
+  // B rows or chunks, the next index vector)
+  constexpr int VM_AB = A_CH + (KMAJOR ? BR : B_CH);
+  constexpr int VM_IDX = GATHER ? (BR == 8 ? 2 : 1) : 0;
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-    read_frags(cur, 0, a0, b0);
-    read_frags(cur, 1, a1, b1);
+    read_frags(kt, 0, a0, b0);
+    read_frags(kt, 1, a1, b1);
+    if constexpr (KMAJOR) __builtin_amdgcn_sched_barrier(0);
     mfma_all(a0, b0);
-    // the other buffer was released by the barrier that ended kt - 1
+    // the B stage of tile kt + 1 and the A stage of tile kt + 2 were last
+    // read in iteration kt - 1, released by the barrier that ended it
     if (kt + 1 < KT) {
-      store_tile(cur ^ 1);
+      store_tile(kt + 1);
       if (kt + 2 < KT) {
+        if constexpr (A_DIRECT) issue_a(kt + 2, (kt + 2) % 3);
         load_tile(kt + 2);
         if (kt + 3 < KT) load_idx(kt + 3);
       }
     }
-    read_frags(cur, 2, a0, b0);
+    if constexpr (KMAJOR) {
+      // K-major B (the linear products): an instruction order pinned by
+      // scheduling groups.  Step 0's products with the next tiles' LDS
+      // stores and loads between them; then step 1's products with step 2's
+      // fragment reads, and step 2's with step 3's, one LDS read after each
+      // MFMA (about 2% faster than the compiler's own order here; on the
+      // N-major QK products the pinned order was slower, so they keep it)
+#pragma unroll
+      for (int u = 0; u < TM * TN; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 2);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 2);   // LDS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);   // vector-memory read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(kt, 2, a0, b0);
+      mfma_all(a1, b1);
+#pragma unroll
+      for (int u = 0; u < TM + TN; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(kt, 3, a1, b1);
+      mfma_all(a0, b0);
+#pragma unroll
+      for (int u = 0; u < TM + TN; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 1);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      read_frags(kt, 2, a0, b0);
+      mfma_all(a1, b1);
+      read_frags(kt, 3, a1, b1);
+      mfma_all(a0, b0);
+    }
     mfma_all(a1, b1);
-    read_frags(cur, 3, a1, b1);
-    mfma_all(a0, b0);
-    mfma_all(a1, b1);
-    __syncthreads();
+    if constexpr (A_DIRECT) {
+      // the direct A rows of tile kt + 1 (issued an iteration ago) must be in
+      // LDS before the barrier; only this iteration's loads may stay in
+      // flight (vector-memory operations complete in issue order)
+      if (kt + 3 < KT)
+        wait_vmcnt<VM_AB + VM_IDX>();
+      else if (kt + 2 < KT)
+        wait_vmcnt<VM_AB>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+    } else {
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: lane (li, lk) of accumulator register v holds row
