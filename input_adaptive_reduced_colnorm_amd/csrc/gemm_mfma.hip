@@ -368,74 +368,98 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   // B rows or chunks, the next index vector)
   constexpr int VM_AB = A_CH + (KMAJOR ? BR : B_CH);
   constexpr int VM_IDX = GATHER ? (BR == 8 ? 2 : 1) : 0;
-  for (int kt = 0; kt < KT; ++kt) {
+  if constexpr (KMAJOR) {
+    // K-major B (the linear products): a software pipeline over the four k16
+    // steps of a tile, each group of MFMAs issued with the LDS reads of the
+    // next group's fragments between them (scheduling groups pin the order):
+    //   G1 step 0 products | step 1 reads, next tiles' LDS stores and loads
+    //   G2 step 1 products | step 2 reads
+    //   G3 step 2 products | step 3 reads, then the barrier
+    //   G4 step 3 products | step 0 reads of the next tile (after the barrier)
+    // so no MFMA group waits on an LDS read issued just before it and the
+    // barrier is followed by products whose operands are already loaded.
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-    read_frags(kt, 0, a0, b0);
-    read_frags(kt, 1, a1, b1);
-    if constexpr (KMAJOR) __builtin_amdgcn_sched_barrier(0);
-    mfma_all(a0, b0);
-    // the B stage of tile kt + 1 and the A stage of tile kt + 2 were last
-    // read in iteration kt - 1, released by the barrier that ended it
-    if (kt + 1 < KT) {
-      store_tile(kt + 1);
-      if (kt + 2 < KT) {
-        if constexpr (A_DIRECT) issue_a(kt + 2, (kt + 2) % 3);
-        load_tile(kt + 2);
-        if (kt + 3 < KT) load_idx(kt + 3);
+    if (KT > 0) read_frags(0, 0, a0, b0);
+    for (int kt = 0; kt < KT; ++kt) {
+      read_frags(kt, 1, a1, b1);
+      mfma_all(a0, b0);
+      // the B stage of tile kt + 1 and the A stage of tile kt + 2 were last
+      // read before the barrier of iteration kt - 1
+      if (kt + 1 < KT) {
+        store_tile(kt + 1);
+        if (kt + 2 < KT) {
+          if constexpr (A_DIRECT) issue_a(kt + 2, (kt + 2) % 3);
+          load_tile(kt + 2);
+          if (kt + 3 < KT) load_idx(kt + 3);
+        }
       }
-    }
-    if constexpr (KMAJOR) {
-      // K-major B (the linear products): an instruction order pinned by
-      // scheduling groups.  Step 0's products with the next tiles' LDS
-      // stores and loads between them; then step 1's products with step 2's
-      // fragment reads, and step 2's with step 3's, one LDS read after each
-      // MFMA (about 2% faster than the compiler's own order here; on the
-      // N-major QK products the pinned order was slower, so they keep it)
 #pragma unroll
       for (int u = 0; u < TM * TN; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 2);   // VALU
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 2);   // LDS write
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 2);   // vector-memory read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // vector-memory read
       }
       __builtin_amdgcn_sched_barrier(0);
       read_frags(kt, 2, a0, b0);
       mfma_all(a1, b1);
 #pragma unroll
-      for (int u = 0; u < TM + TN; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(kt, 3, a1, b1);
-      mfma_all(a0, b0);
-#pragma unroll
-      for (int u = 0; u < TM + TN; ++u) {
+      for (int u = 0; u < TM * TN; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 1);
       __builtin_amdgcn_sched_barrier(0);
-    } else {
+      read_frags(kt, 3, a1, b1);
+      mfma_all(a0, b0);
+#pragma unroll
+      for (int u = 0; u < TM * TN; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (A_DIRECT) {
+        // the direct A rows of tile kt + 1 (issued an iteration ago) must be
+        // in LDS before the barrier; only this iteration's loads may stay in
+        // flight (vector-memory operations complete in issue order)
+        if (kt + 3 < KT)
+          wait_vmcnt<VM_AB + VM_IDX>();
+        else if (kt + 2 < KT)
+          wait_vmcnt<VM_AB>();
+        else
+          wait_vmcnt<0>();
+        lds_barrier();
+      } else {
+        __syncthreads();
+      }
+      if (kt + 1 < KT) read_frags(kt + 1, 0, a0, b0);
+      mfma_all(a1, b1);
+#pragma unroll
+      for (int u = 0; u < TM * TN; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int kt = 0; kt < KT; ++kt) {
+      bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+      read_frags(kt, 0, a0, b0);
+      read_frags(kt, 1, a1, b1);
+      mfma_all(a0, b0);
+      // the other stages were released by the barrier that ended kt - 1
+      if (kt + 1 < KT) {
+        store_tile(kt + 1);
+        if (kt + 2 < KT) {
+          load_tile(kt + 2);
+          if (kt + 3 < KT) load_idx(kt + 3);
+        }
+      }
       read_frags(kt, 2, a0, b0);
       mfma_all(a1, b1);
       read_frags(kt, 3, a1, b1);
       mfma_all(a0, b0);
-    }
-    mfma_all(a1, b1);
-    if constexpr (A_DIRECT) {
-      // the direct A rows of tile kt + 1 (issued an iteration ago) must be in
-      // LDS before the barrier; only this iteration's loads may stay in
-      // flight (vector-memory operations complete in issue order)
-      if (kt + 3 < KT)
-        wait_vmcnt<VM_AB + VM_IDX>();
-      else if (kt + 2 < KT)
-        wait_vmcnt<VM_AB>();
-      else
-        wait_vmcnt<0>();
-      lds_barrier();
-    } else {
+      mfma_all(a1, b1);
       __syncthreads();
     }
   }
