@@ -12,6 +12,13 @@ library, and the copy kernel that calibrates the HBM byte counters.
         HBM bytes per launch of one kernel from two counter runs, each scaled by
         what the same counter reads for the calibration copy
 
+    python -m input_adaptive_reduced_colnorm_amd.profiling mfma --counters C.csv --kernel SUBSTR \
+            --title T --command CMD --out OUT.md
+        per launch of one kernel: shader clock (GRBM_GUI_ACTIVE of one XCD over
+        the launch time), matrix-core busy share (SQ_VALU_MFMA_BUSY_CYCLES over
+        the cycles of all 1024 SIMDs) and the bf16 MFMA rate from
+        SQ_INSTS_VALU_MFMA_MOPS_BF16 (512 FLOP per count)
+
 Nothing here is on the compute path; the JSON written by `traffic` records a
 hash of the kernel source so that a reader can tell when it is stale.
 """
@@ -97,6 +104,51 @@ def traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, kern
     return rec
 
 
+XCDS, SIMDS = 8, 1024           # MI355X: 8 accelerator complexes, 256 CUs x 4 SIMDs
+
+
+def _dispatch_rows(path: str, substr: str):
+    """{dispatch id: {"name", "ns", counter: summed value}} for kernels whose
+    name contains `substr`."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if substr not in r["Kernel_Name"]:
+            continue
+        d = out.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"],
+                                              "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def mfma(counters_csv: str, kernel: str, title: str, command: str, out_md: str) -> str:
+    rows = _dispatch_rows(counters_csv, kernel)
+    need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    rows = {k: v for k, v in rows.items() if all(c in v for c in need)}
+    if not rows:
+        raise SystemExit(f"no dispatches of {kernel!r} with {need}")
+    out = [f"# {title}", "", "Command (from the repository root on one MI355X, TMPDIR=/tmp):", "", "```", command,
+           "```", "", f"Kernel `{_short_name(next(iter(rows.values()))['name'])}`, one line per launch. Clock = "
+           "GRBM_GUI_ACTIVE / 8 XCDs / launch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 "
+           "x 1024 SIMDs); TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / launch time; the last column scales "
+           "the 2.5 PFLOP/s bf16 peak (quoted at 2.4 GHz) to the measured clock.", "",
+           "| launch | us | clock GHz | MFMA busy | TFLOP/s | peak at that clock |", "|---|---|---|---|---|---|"]
+    clocks, busy, tf = [], [], []
+    for i, (k, v) in enumerate(sorted(rows.items(), key=lambda kv: int(kv[0]))):
+        us = v["ns"] / 1e3
+        cyc = v["GRBM_GUI_ACTIVE"] / XCDS
+        ghz = cyc / (us * 1e3)
+        b = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS)
+        t = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / (us * 1e-6) / 1e12
+        clocks.append(ghz), busy.append(b), tf.append(t)
+        out.append(f"| {i} | {us:.1f} | {ghz:.2f} | {b:.1%} | {t:.0f} | {2500 * ghz / 2.4:.0f} |")
+    out += ["", f"Mean over {len(rows)} launches: clock {statistics.fmean(clocks):.2f} GHz, MFMA busy "
+            f"{statistics.fmean(busy):.1%}, {statistics.fmean(tf):.0f} TFLOP/s."]
+    text = "\n".join(out) + "\n"
+    with open(out_md, "w") as f:
+        f.write(text)
+    return text
+
+
 def copy(mib: int, iters: int):
     import torch
     n = mib * (1 << 20) // 4
@@ -124,11 +176,16 @@ def main(argv=None):
         t.add_argument("--" + name, required=True)
     t.add_argument("--copy-mib", type=int, default=256)
     t.add_argument("--copy-kernel", default="opy", help="name substring of the calibration copy kernel")
+    m = sub.add_parser("mfma")
+    for name in ("counters", "kernel", "title", "command", "out"):
+        m.add_argument("--" + name, required=True)
     a = ap.parse_args(argv)
     if a.cmd == "copy":
         copy(a.mib, a.iters)
     elif a.cmd == "summarize":
         sys.stdout.write(summarize(a.stats_csv, a.out_md, a.title, a.command))
+    elif a.cmd == "mfma":
+        sys.stdout.write(mfma(a.counters, a.kernel, a.title, a.command, a.out))
     else:
         print(json.dumps(traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.kernel, a.source,
                                  a.workload, a.out, a.copy_kernel), indent=1))
