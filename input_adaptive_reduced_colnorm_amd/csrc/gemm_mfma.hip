@@ -37,10 +37,15 @@ struct TileCoord {
 // XCD-aware tile order: consecutive workgroup ids land on different XCDs
 // (round robin over 8), so the ids are regrouped such that each XCD receives
 // a compact block of tiles that share A row panels and B column panels in its
-// own L2; inside that block tiles are rastered in groups of 4 tile rows.
+// own L2; inside that block tiles are rastered in groups of GM tile rows.
+// GM = 8 for the linear products (an XCD of the 4096 x 4096 MLP-down output
+// holds 8 x 4 tiles, so the gathered rows of B are fetched by half as many
+// XCDs as with 4 x 8: 2.5% faster); GM = 4 for the batched QK products,
+// where 8 was 1.5% slower.
 // Causal scores keep the plain order instead: a compact block of tile rows
 // per XCD would leave the XCDs holding the top rows (almost all masked) idle
 // while the others carry the whole product.
+template <int GM>
 __device__ __forceinline__ TileCoord tile_of(int bid, int tiles_m, int tiles_n, bool xcd_blocks) {
   const int total = tiles_m * tiles_n;
   int lin = bid;
@@ -48,7 +53,6 @@ __device__ __forceinline__ TileCoord tile_of(int bid, int tiles_m, int tiles_n, 
     const int per = total >> 3;
     lin = (bid & 7) * per + (bid >> 3);
   }
-  constexpr int GM = 4;
   const int group_size = GM * tiles_n;
   const int group = lin / group_size;
   const int first_m = group * GM;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   const int b = blockIdx.y;
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  const TileCoord tc = tile_of(blockIdx.x, tiles_m, tiles_n, !g.causal);
+  const TileCoord tc = tile_of<KMAJOR ? 8 : 4>(blockIdx.x, tiles_m, tiles_n, !g.causal);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
   const char* Ab = (const char*)g.A + (size_t)b * g.a_bs * ES;
