@@ -399,11 +399,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       }
 #pragma unroll
       for (int u = 0; u < TM * TN; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // vector-memory read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // vector-memory read
       }
       __builtin_amdgcn_sched_barrier(0);
       read_frags(kt, 2, a0, b0);
