@@ -439,10 +439,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       if (kt + 1 < KT) read_frags(kt + 1, 0, a0, b0);
       mfma_all(a1, b1);
 #pragma unroll
-      for (int u = 0; u < TM * TN; ++u) {
+      for (int u = 0; u < (TM + TN) / 2; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN) / 2, 3);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
