@@ -402,7 +402,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
         __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // vector-memory read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
       }
       __builtin_amdgcn_sched_barrier(0);
