@@ -151,6 +151,18 @@ def test_exact_ties_lowest_index(dev):
             np.testing.assert_array_equal(idx, idx_o)
 
 
+@pytest.mark.parametrize("d", [64, 128, 192, 256, 320])
+def test_linear_k_tile_counts(dev, d):
+    # 1 to 5 K tiles of 64 through the linear GEMM's prefetch ring (direct A
+    # rows two tiles ahead, per-iteration load counts), on the 256 x 256 tile
+    # variant (4096 x 3072 output) and on the 128 x 128 one (300 x 264)
+    for n, m in ((4096, 3072), (300, 264)):
+        w = synth.mlp_down(n=n, d=d, m=m, rhos=(0.5,))
+        A, B = w.tensors["A"], w.tensors["B"]
+        for rho in (1.0, 0.5):
+            check_matmul(A, B, rho, dev, TOL_BF16, rows=np.arange(0, n, 7) if n > 1000 else None)
+
+
 @pytest.mark.parametrize("n,d", [(32, 3000), (32, 9000), (8, 4096)])
 def test_radix_zero_and_tied_energies(dev, n, d):
     # integer entries give exact energies on both sides, with many ties; 40%
