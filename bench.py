@@ -720,6 +720,11 @@ def run(args, op):
     traffic, src = measured_traffic(op)
     roofline["traffic"] = traffic
     roofline["traffic_source"] = src
+    if roofline["bound"] == "hbm":
+        # the datasheet peak above; beside it the rate a plain copy reaches
+        measured = hbm_copy_gbs()
+        roofline["measured_copy_gbs"] = measured
+        roofline["frac_of_measured_copy"] = round(roofline["achieved"] / measured, 4)
 
     extra = op.extra(args, sh) if hasattr(op, "extra") else None
 
@@ -750,6 +755,28 @@ def run(args, op):
     if extra:
         line[getattr(op, "extra_key", "producer_side_scoring")] = extra
     return line
+
+
+def hbm_copy_gbs():
+    """Measured HBM rate of a plain 1 GiB device-to-device copy (bytes read
+    plus bytes written per second), as the practical ceiling beside the
+    datasheet 8 TB/s."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 5 * 1e3
+    del src, dst
+    return round(2 * (1 << 30) / (us * 1e-6) / 1e9, 1)
 
 
 def hipblaslt_context(op):
