@@ -409,18 +409,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       read_frags(kt, 2, a0, b0);
       mfma_all(a1, b1);
 #pragma unroll
-      for (int u = 0; u < TM * TN; ++u) {
+      for (int u = 0; u < (TM + TN) / 2; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN) / 2, 1);
       __builtin_amdgcn_sched_barrier(0);
       read_frags(kt, 3, a1, b1);
       mfma_all(a0, b0);
 #pragma unroll
-      for (int u = 0; u < TM * TN; ++u) {
+      for (int u = 0; u < (TM + TN) / 2; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN) / 2, 2);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (A_DIRECT) {
         // the direct A rows of tile kt + 1 (issued an iteration ago) must be
