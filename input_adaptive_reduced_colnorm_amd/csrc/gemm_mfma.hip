@@ -374,14 +374,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   constexpr int VM_IDX = GATHER ? (BR == 8 ? 2 : 1) : 0;
   if constexpr (KMAJOR) {
     // K-major B (the linear products): a software pipeline over the four k16
-    // steps of a tile, each group of MFMAs issued with the LDS reads of the
-    // next group's fragments between them (scheduling groups pin the order):
+    // steps of a tile, each group of MFMAs issued together with the LDS
+    // reads of the next group's fragments (scheduling groups pin the order):
     //   G1 step 0 products | step 1 reads, next tiles' LDS stores and loads
     //   G2 step 1 products | step 2 reads
     //   G3 step 2 products | step 3 reads, then the barrier
     //   G4 step 3 products | step 0 reads of the next tile (after the barrier)
     // so no MFMA group waits on an LDS read issued just before it and the
     // barrier is followed by products whose operands are already loaded.
+    // Measured orders (interleaved runs against each other): in G1 all the
+    // loads, transposes, LDS stores and reads go before the MFMAs (the other
+    // wave of the SIMD keeps the matrix core busy meanwhile); in G2-G4 two
+    // reads follow each of the first MFMAs; all reads first there was 2-3%
+    // slower.
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
     if (KT > 0) read_frags(0, 0, a0, b0);
     for (int kt = 0; kt < KT; ++kt) {
@@ -397,14 +402,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
           if (kt + 3 < KT) load_idx(kt + 3);
         }
       }
-#pragma unroll
-      for (int u = 0; u < TM * TN; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // vector-memory read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
-      }
+      __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);   // vector-memory read
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);   // LDS write
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);   // MFMA
       __builtin_amdgcn_sched_barrier(0);
       read_frags(kt, 2, a0, b0);
       mfma_all(a1, b1);
