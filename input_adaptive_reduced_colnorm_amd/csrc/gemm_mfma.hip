@@ -12,10 +12,13 @@
 // over 8 waves (2 x 4, two waves per SIMD so that one wave's MFMAs cover the
 // other's LDS traffic and barrier); small ones 128 x 128 over 4 waves (2 x 2).
 // Each wave owns a block of 32x32 accumulators fed by
-// v_mfma_f32_32x32x16_bf16.  Global -> register prefetch of the next K tile
-// overlaps the MFMAs of the current one; LDS is double buffered with one
-// barrier per K tile.  LDS rows are 128 bytes (64 bf16 along K) with an XOR
-// swizzle of the 16-byte chunks.
+// v_mfma_f32_32x32x16_bf16.  The loads of K tile kt + 2 are issued while
+// tile kt is multiplied; one barrier per K tile.  With K-major B (the linear
+// products) bf16 A goes straight from the buffer into a ring of three LDS
+// stages and the k16 steps run as a software pipeline with a pinned
+// instruction order (see the main loop); otherwise both operands pass
+// through registers into two LDS stages.  LDS rows are 128 bytes (64 bf16
+// along K) with an XOR swizzle of the 16-byte chunks.
 // B tiles that are K-major in memory (weights, V) are transposed in
 // registers in 8x8 blocks (v_perm) before they reach LDS; int8 weights are
 // loaded 8 bytes at a time and widened to bf16 just before that transpose,
