@@ -472,9 +472,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   if constexpr (LDS_KEYS) {
     if (d % 4 == 0) {
       // 4 columns per 16-byte load; a thread takes up to four 4-column
-      // groups at once and issues the loads of all of them for up to four
+      // groups at once and issues the loads of all of them for up to six
       // splits before adding any (each column in split order)
-      constexpr int G = 4, S = 4;
+      constexpr int G = 4, S = 6;
       const int d4 = d / 4;
       const f32x4* P4 = (const f32x4*)P;
       for (int jb = threadIdx.x; jb < d4; jb += G * kSelThreads) {
