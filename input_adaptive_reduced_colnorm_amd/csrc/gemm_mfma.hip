@@ -328,12 +328,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
 #pragma unroll
     for (int j = 0; j < TN; ++j) bfr[j] = *(const bf16x8*)(Bs + b_row[j] * 128 + swz(b_row[j], ch) * 16);
   };
+  // K-major products run through the A fragments under each B fragment
+  // (measured 0.5-1% faster than the A-outer order, interleaved runs); the
+  // QK products keep the A-outer order they were tuned with.
   auto mfma_all = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfr)[TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
+    if constexpr (KMAJOR) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
   };
 
   // causal scores: a tile whose every entry lies above the shifted diagonal
