@@ -26,92 +26,137 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTokSteps = 8;   // token rows in flight per lane
 
+// Workgroup barrier that waits for this wave's LDS operations only, not for
+// its global loads in flight (__syncthreads' release fence would wait for
+// those too).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int G, int LPT>
 __global__ __launch_bounds__(kThreads) void qk_decode_kernel(const QkDecodeArgs a) {
   constexpr int TPW = 64 / LPT;                 // tokens per wave step
   constexpr int TPB = TPW * (kThreads / 64);    // tokens per workgroup step
   __shared__ float qm[G][256];
-  __shared__ __attribute__((aligned(16))) uint64_t s_ck[kThreads];
-  __shared__ int s_cnt[kThreads / 64];
   const int g = blockIdx.y;
   const int group = a.hq / a.hkv;
   const int tid = threadIdx.x;
-  // ---- every feature of the group's query rows: qm[(h - g*group)*tq + r][f] ----
-  for (int i = tid; i < G * 256; i += kThreads) {
-    const int row = i / 256, f = i % 256;   // row = local head * tq + r
-    float v = 0.f;
-    if (row < group * a.tq && f < a.dh) {
-      const int hl = row / a.tq, r = row % a.tq;
-      const size_t off = (size_t)(g * group + hl) * a.q_hs + (size_t)r * a.q_ts + f;
-      v = a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.Q)[off]) : ((const float*)a.Q)[off];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % LPT;                    // which 8 features
+  const int tw = lane / LPT;                     // token within the wave step
+  // the first key rows are requested before the query loads and the ranking,
+  // so that their fetch overlaps the prologue
+  const uint16_t* Kg = (const uint16_t*)a.K + (size_t)g * a.k_hs;
+  const int t_begin = blockIdx.x * a.tok_per_block;
+  const int t_end = min(a.tk, t_begin + a.tok_per_block);
+  const int t_first = t_begin + wave * TPW + tw;
+  i32x4 kv[kTokSteps];
+  // loads outside any branch (out-of-range lanes read a clamped in-range
+  // row and drop the value), so that the waits before each use count exactly
+  // the loads issued after it
+  auto load_k = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < kTokSteps; ++u) {
+      const int t = t0 + u * TPB;
+      const bool ok = t < t_end && sub * 8 < a.dh;
+      const size_t off = ok ? (size_t)t * a.k_ts + sub * 8 : (size_t)t_begin * a.k_ts;
+      const i32x4 v = *(const i32x4*)(Kg + off);
+      kv[u] = ok ? v : i32x4{0, 0, 0, 0};
     }
-    qm[row][f] = v;
+  };
+  // ---- every feature of the group's query rows: qm[(h - g*group)*tq + r][f],
+  //      thread tid loading feature tid of each row.  The query loads go
+  //      out first and the first key rows right after them: loads complete in
+  //      issue order, so the query values can be waited for while the key
+  //      rows stay in flight through the ranking (the barriers wait for LDS
+  //      only) ----
+  uint16_t qv[G];
+#pragma unroll
+  for (int row = 0; row < G; ++row) {   // row = local head * tq + r
+    const bool ok = row < group * a.tq && tid < a.dh;
+    const int hl = ok ? row / a.tq : 0, r = ok ? row % a.tq : 0;
+    const size_t off = ok ? (size_t)(g * group + hl) * a.q_hs + (size_t)r * a.q_ts + tid : 0;
+    const uint16_t v = ((const uint16_t*)a.Q)[off];
+    qv[row] = ok ? v : (uint16_t)0;
   }
-  __syncthreads();
+  load_k(t_first);
+#pragma unroll
+  for (int row = 0; row < G; ++row) qm[row][tid] = bf16_to_f32(qv[row]);
+  lds_sync();
   // ---- the kept features of each query head of the group, from the column
   //      energies of its tq rows (row order; with bf16 Q every square is exact
   //      in fp32, so these keys equal the scoring pass's).  Each feature gets
   //      the composite key (energy bits, 0xFFFF - j): a larger composite
-  //      outranks (higher energy, or equal energy and lower index), so one
-  //      64-bit compare per pair ranks it, and feature j is kept when fewer
-  //      than k composites exceed its own.  With dh <= 128 two heads are
-  //      ranked at once.  Dropped features are zeroed in qm; the workgroups
-  //      of the first token block write the ascending lists ----
-  const int hp_n = a.dh <= 128 ? 2 : 1;                 // heads per pass
-  const int tph = kThreads / hp_n;                      // threads per head
-  const int hsub = tid / tph, jf = tid % tph;           // head within the pass, feature
-  const int lane_ = tid & 63, wave_ = tid >> 6;
-  for (int h0 = 0; h0 < group; h0 += hp_n) {
-    const int hl = h0 + hsub;
-    const bool live = hl < group && jf < a.dh;
-    int32_t* out = a.idx_out + (size_t)(g * group + (hl < group ? hl : 0)) * a.k;
+  //      outranks (higher energy, or equal energy and lower index).  One wave
+  //      per head finds the energy of the k-th largest composite with 32-bit
+  //      compares and ballot counts, keeps the features above it and, among
+  //      those equal to it, the lowest indices up to k places; it zeroes the
+  //      others in qm, and the workgroups of the first token block write the
+  //      ascending lists ----
+  for (int hl = wave; hl < group; hl += kThreads / 64) {
+    int32_t* out = a.idx_out + (size_t)(g * group + hl) * a.k;
     if (!a.select) {
-      if (blockIdx.x == 0 && live) out[jf] = jf;
+      if (blockIdx.x == 0)
+        for (int j = lane; j < a.dh; j += 64) out[j] = j;
       continue;
     }
-    float key = 0.f;
-    if (live)
-      for (int r = 0; r < a.tq; ++r) key = fmaf(qm[hl * a.tq + r][jf], qm[hl * a.tq + r][jf], key);
-    const uint64_t ck = ((uint64_t)__float_as_uint(key) << 32) | (uint32_t)(0xFFFF - jf);
-    s_ck[tid] = ck;
-    __syncthreads();
-    // two composites per 16-byte LDS read, many reads in flight (dh % 8 == 0)
-    const uint64_t* row = s_ck + hsub * tph;
-    int rank = 0;
-#pragma unroll 8
-    for (int i2 = 0; i2 < a.dh / 2; ++i2) {
-      const u64x2 v = *(const u64x2*)(row + 2 * i2);
-      rank += (int)(v[0] > ck) + (int)(v[1] > ck);
+    constexpr int NCH = LPT / 8;   // feature j = lane + 64 c, c < NCH (dh <= 8 LPT)
+    uint32_t e[NCH];               // energy bits; 0 on lanes past dh
+    uint64_t live[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int j = lane + 64 * c;
+      float key = 0.f;
+      if (j < a.dh)
+        for (int r = 0; r < a.tq; ++r) key = fmaf(qm[hl * a.tq + r][j], qm[hl * a.tq + r][j], key);
+      e[c] = j < a.dh ? __float_as_uint(key) : 0u;
+      live[c] = __ballot(j < a.dh);
     }
-    const bool keep = live && rank < a.k;
-    const uint64_t kept = __ballot(keep);
-    if (lane_ == 0) s_cnt[wave_] = __popcll(kept);
-    __syncthreads();
-    int pos = __popcll(kept & ((1ull << lane_) - 1ull));
-    for (int w = hsub * (tph / 64); w < wave_; ++w) pos += s_cnt[w];
-    if (keep && blockIdx.x == 0) out[pos] = jf;
-    if (live && !keep)
-      for (int r = 0; r < a.tq; ++r) qm[hl * a.tq + r][jf] = 0.f;
-    __syncthreads();   // s_ck and s_cnt are reused by the next pass
+    // Th: the energy bits of the k-th largest composite, built from the top
+    // bit down (a bit stays set while at least k features reach the
+    // candidate; the candidate is never 0, so lanes past dh never count)
+    uint32_t Th = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = Th | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) n += __popcll(__ballot(e[c] >= cand));
+      if (n >= a.k) Th = cand;
+    }
+    // every feature above Th is kept; the other places go to the lowest
+    // indices among the features equal to Th
+    int above = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) above += __popcll(__ballot(e[c] > Th));
+    const int eq_places = a.k - above;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int base = 0, eq_before = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int j = lane + 64 * c;
+      const bool lv = j < a.dh;
+      const uint64_t eqm = __ballot(e[c] == Th) & live[c];
+      const bool keep =
+          a.k > 0 && lv && (e[c] > Th || (e[c] == Th && eq_before + __popcll(eqm & lt) < eq_places));
+      const uint64_t kept = __ballot(keep);
+      if (keep && blockIdx.x == 0) out[base + __popcll(kept & lt)] = j;
+      base += __popcll(kept);
+      eq_before += __popcll(eqm);
+      if (lv && !keep)
+        for (int r = 0; r < a.tq; ++r) qm[hl * a.tq + r][j] = 0.f;
+    }
   }
-  const int lane = tid & 63, wave = tid >> 6;
-  const int sub = lane % LPT;                    // which 8 features
-  const int tw = lane / LPT;                     // token within the wave step
+  lds_sync();
   float q[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[j][e] = qm[j][sub * 8 + e];
-  const uint16_t* Kg = (const uint16_t*)a.K + (size_t)g * a.k_hs;
-  const int t_begin = blockIdx.x * a.tok_per_block;
-  const int t_end = min(a.tk, t_begin + a.tok_per_block);
-  for (int t0 = t_begin + wave * TPW + tw; t0 < t_end; t0 += TPB * kTokSteps) {
-    i32x4 kv[kTokSteps];
-#pragma unroll
-    for (int u = 0; u < kTokSteps; ++u) {
-      const int t = t0 + u * TPB;
-      kv[u] = (t < t_end && sub * 8 < a.dh) ? *(const i32x4*)(Kg + (size_t)t * a.k_ts + sub * 8) : i32x4{0, 0, 0, 0};
-    }
+  for (int t0 = t_first; t0 < t_end; t0 += TPB * kTokSteps) {
+    if (t0 != t_first) load_k(t0);
 #pragma unroll
     for (int u = 0; u < kTokSteps; ++u) {
       const int t = t0 + u * TPB;
@@ -160,6 +205,7 @@ hipError_t launch_g(const QkDecodeArgs& a, dim3 grid, hipStream_t s) {
 bool qk_decode_fits(int group, int tq, int dh) { return group * tq <= 8 && dh % 8 == 0 && dh <= 256; }
 
 hipError_t launch_qk_decode(QkDecodeArgs a, hipStream_t s) {
+  if (!a.q_bf16) return hipErrorInvalidValue;   // the kernel reads bf16 queries
   // about 512 workgroups in all, at least 64 tokens each
   int tpb = (int)(((long)a.tk * a.hkv + 511) / 512);
   tpb = tpb < 64 ? 64 : (tpb + 63) / 64 * 64;

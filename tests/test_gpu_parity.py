@@ -494,6 +494,18 @@ def test_qk_decode(dev, tq, dh, rho):
     check_qk(w.tensors["Q"], w.tensors["K"], rho, dev, TOL_BF16)
 
 
+@pytest.mark.parametrize("tq,dh,rho", [(1, 128, 0.5), (2, 64, 0.3), (1, 256, 0.7), (1, 128, 0.9)])
+def test_qk_decode_tied_energies(dev, tq, dh, rho):
+    # queries drawn from {0, +-1, +-2}: most feature energies tie and many are
+    # zero, so the kept set is decided by the lowest-index rule; the streaming
+    # kernel's in-kernel ranking must give the oracle's lists exactly
+    w = synth.decode_attn_qk(hq=8, hkv=2, tq=tq, tk=600, dh=dh)
+    g = torch.Generator().manual_seed(11)
+    vals = torch.tensor([0.0, 0.0, 1.0, -1.0, 2.0, -2.0])
+    Q = vals[torch.randint(0, len(vals), w.tensors["Q"].shape, generator=g)].to(torch.bfloat16)
+    check_qk(Q, w.tensors["K"], rho, dev, TOL_BF16)
+
+
 @pytest.mark.parametrize("tq,rho", [(1, 0.5), (1, 1.0), (4, 0.3)])
 def test_pv_decode(dev, tq, rho):
     # a GEMV per head over the kept rows of V
