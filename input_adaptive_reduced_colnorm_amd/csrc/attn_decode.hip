@@ -13,8 +13,9 @@
 // row is read once with 16-byte loads.  The partial dot products of the
 // lanes that span a row are folded with a fixed butterfly.  The kept
 // features of a head (at most 256, from at most 8 query rows) are ranked by
-// every workgroup in its prologue, so the decode step needs no separate
-// scoring and TopK launches.
+// every workgroup in its prologue (one wave per head, ballot counts, no LDS
+// traffic), while the workgroup's first key rows are already in flight, so
+// the decode step needs no separate scoring and TopK launches.
 
 #include "rmm_device.h"
 #include "rmm_internal.h"

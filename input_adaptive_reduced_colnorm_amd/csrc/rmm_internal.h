@@ -113,7 +113,8 @@ int gemv_splits(int k, int m, int batch = 1);
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);
 
 // Decode-shaped QK^T (tq <= 16, group * tq <= 8, dh <= 256 and a multiple
-// of 8, bf16 K with 16-byte aligned rows): S[h][r][t] = sum over the k
+// of 8, bf16 Q (q_bf16 must be set; the launch rejects fp32 queries), bf16 K
+// with 16-byte aligned rows): S[h][r][t] = sum over the k
 // features idx[h][0..k) (all dh when idx is null) of Q[h][r][f] K[g(h)][t][f].
 // The kernel also selects: idx_out[h][0..k) receives the kept features of
 // head h (ascending; all dh of them when select is false).
