@@ -398,11 +398,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     // barrier is followed by products whose operands are already loaded.
     // Measured orders (interleaved runs against each other): in G1 all the
     // loads, transposes, LDS stores and reads go before the MFMAs (the other
-    // wave of the SIMD keeps the matrix core busy meanwhile); in G2-G4 two
-    // reads follow each of the first MFMAs; all reads first there was 2-3%
-    // slower.  The wave runs G1 at raised priority so that its loads and LDS
-    // stores issue ahead of the other wave's products (0.2-2% faster; raising
-    // it for the MFMA groups instead was 3% slower).
+    // wave of the SIMD keeps the matrix core busy meanwhile); in G2-G4 one
+    // read follows each of the first TM + TN MFMAs (two reads after each of
+    // the first (TM + TN) / 2 was 1-1.6% slower, all reads first 2-3%).  The
+    // wave runs G1 at raised priority so that its loads and LDS stores issue
+    // ahead of the other wave's products (0.2-2% faster; raising it for the
+    // MFMA groups instead was 3% slower).
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
     if (KT > 0) read_frags(0, 0, a0, b0);
     for (int kt = 0; kt < KT; ++kt) {
@@ -429,20 +430,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       read_frags(kt, 2, a0, b0);
       mfma_all(a1, b1);
 #pragma unroll
-      for (int u = 0; u < (TM + TN) / 2; ++u) {
+      for (int u = 0; u < TM + TN; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN) / 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 1);
       __builtin_amdgcn_sched_barrier(0);
       read_frags(kt, 3, a1, b1);
       mfma_all(a0, b0);
 #pragma unroll
-      for (int u = 0; u < (TM + TN) / 2; ++u) {
+      for (int u = 0; u < TM + TN; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN) / 2, 2);
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 2);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (A_DIRECT) {
         // the direct A rows of tile kt + 1 (issued an iteration ago) must be
@@ -461,11 +462,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       if (kt + 1 < KT) read_frags(kt + 1, 0, a0, b0);
       mfma_all(a1, b1);
 #pragma unroll
-      for (int u = 0; u < (TM + TN) / 2; ++u) {
+      for (int u = 0; u < TM + TN; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN) / 2, 3);
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
