@@ -401,9 +401,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     // wave of the SIMD keeps the matrix core busy meanwhile); in G2-G4 one
     // read follows each of the first TM + TN MFMAs (two reads after each of
     // the first (TM + TN) / 2 was 1-1.6% slower, all reads first 2-3%).  The
-    // wave runs G1 at raised priority so that its loads and LDS stores issue
-    // ahead of the other wave's products (0.2-2% faster; raising it for the
-    // MFMA groups instead was 3% slower).
+    // wave runs G1 and G2 at raised priority so that its loads, LDS stores
+    // and first reads issue ahead of the other wave's products (G1 alone
+    // was about 1% slower, raising it for G2-G4 instead 3% slower).
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
     if (KT > 0) read_frags(0, 0, a0, b0);
     for (int kt = 0; kt < KT; ++kt) {
@@ -426,7 +426,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);   // MFMA
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
       read_frags(kt, 2, a0, b0);
       mfma_all(a1, b1);
 #pragma unroll
@@ -436,6 +435,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       }
       __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 1);
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       read_frags(kt, 3, a1, b1);
       mfma_all(a0, b0);
 #pragma unroll
