@@ -401,9 +401,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     // wave of the SIMD keeps the matrix core busy meanwhile); in G2-G4 one
     // read follows each of the first TM + TN MFMAs (two reads after each of
     // the first (TM + TN) / 2 was 1-1.6% slower, all reads first 2-3%).  The
-    // wave runs G1 and G2 at raised priority so that its loads, LDS stores
-    // and first reads issue ahead of the other wave's products (G1 alone
-    // was about 1% slower, raising it for G2-G4 instead 3% slower).
+    // wave runs G1-G3 at raised priority and drops it for G4, which follows
+    // the barrier, so that its loads, LDS stores and reads issue ahead of the
+    // other wave's products (each step from no change to G1 alone, G1-G2 and
+    // G1-G3 measured about 1% faster; raising it for G2-G4 instead was 3%
+    // slower).
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
     if (KT > 0) read_frags(0, 0, a0, b0);
     for (int kt = 0; kt < KT; ++kt) {
@@ -435,7 +437,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       }
       __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 1);
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
       read_frags(kt, 3, a1, b1);
       mfma_all(a0, b0);
 #pragma unroll
@@ -459,6 +460,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       } else {
         __syncthreads();
       }
+      __builtin_amdgcn_s_setprio(0);
       if (kt + 1 < KT) read_frags(kt + 1, 0, a0, b0);
       mfma_all(a1, b1);
 #pragma unroll
