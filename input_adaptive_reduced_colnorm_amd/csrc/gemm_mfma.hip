@@ -396,9 +396,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
     //   G4 step 3 products | step 0 reads of the next tile (after the barrier)
     // so no MFMA group waits on an LDS read issued just before it and the
     // barrier is followed by products whose operands are already loaded.
-    // Measured orders (interleaved runs against each other): in G1 all the
-    // loads, transposes, LDS stores and reads go before the MFMAs (the other
-    // wave of the SIMD keeps the matrix core busy meanwhile); in G2-G4 one
+    // Measured orders (interleaved runs against each other): in G1 the
+    // loads, the transposes, the LDS reads of step 1 and then the LDS stores
+    // of the next tiles all go before the MFMAs (the other wave of the SIMD
+    // keeps the matrix core busy meanwhile; stores before reads was 1.2%
+    // slower); in G2-G4 one
     // read follows each of the first TM + TN MFMAs (two reads after each of
     // the first (TM + TN) / 2 was 1-1.6% slower, all reads first 2-3%).  The
     // wave runs G1-G3 at raised priority and drops it for G4, which follows
@@ -424,8 +426,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       }
       __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);   // vector-memory read
       __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);   // VALU
-      __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);   // LDS write
       __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);   // LDS write
       __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);   // MFMA
       __builtin_amdgcn_sched_barrier(0);
       read_frags(kt, 2, a0, b0);
