@@ -212,7 +212,34 @@ class MatmulOp:
         return {"value": ops, "unit": "RMM ops/s", "cores": _blas_threads(), "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
                 "kind": "oracle",
                 "sample": (f"fp64 oracle (scoring, stable-sort TopK, gather, product) for one call per rho in "
-                           f"{list(self.rhos)} over {what}, {reps} repetitions; {wall:.1f} s of CPU work")}
+                           f"{list(self.rhos)} over {what}, {reps} repetitions; {wall:.1f} s of CPU work"),
+                "stages_ms": self._cpu_stages(O, A, B, rows)}
+
+    def _cpu_stages(self, O, A, B, rows):
+        """One pass per rho of the oracle's steps, each timed on its own (ms):
+        the column energies (O.col_energy), the stable-sort selection
+        (O.select minus its energies), the gather of A[:, I] and B[I, :]
+        and the fp64 product of the gathered slices (the two halves of the
+        oracle's product line)."""
+        import numpy as np
+        A64 = np.asarray(A, dtype=np.float64)
+        B64 = np.asarray(B, dtype=np.float64)
+        out = {}
+        for rho in self.rhos:
+            t0 = time.perf_counter()
+            O.col_energy(A64)
+            t1 = time.perf_counter()
+            idx, _ = O.select(A64, rho)
+            t2 = time.perf_counter()
+            Ar = A64 if rows is None else A64[rows]
+            Ag, Bg = Ar[:, idx], B64[idx, :]
+            t3 = time.perf_counter()
+            Ag @ Bg
+            t4 = time.perf_counter()
+            sc = 1 if rows is None else self.n / len(rows)
+            out[str(rho)] = {"norms": round(1e3 * (t1 - t0), 2), "stable_sort": round(1e3 * max(0.0, (t2 - t1) - (t1 - t0)), 2),
+                             "gather": round(1e3 * (t3 - t2) * sc, 2), "dgemm_fp64": round(1e3 * (t4 - t3) * sc, 2)}
+        return out
 
 
 class MatmulW8Op(MatmulOp):
@@ -742,7 +769,8 @@ def run(args, op):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": op.name, **op.shape(), "rhos": list(rhos),
-                   "k": {str(r): op.ks[r] for r in rhos}, "copies_rotated": copies},
+                   "k": {str(r): op.ks[r] for r in rhos}, "copies_rotated": copies,
+                   "score_separation": "every neighbouring pair" if args.strict_adjacent else "selection boundaries"},
         "latency_us": {str(r): round(op_us[r], 2) for r in rhos},
         "latency_note": "per-op mean of back-to-back calls; kernel times below come from stage events",
         "speedup_vs_dense": speed,
@@ -909,28 +937,28 @@ WORKLOADS = ("mlp_down_8b", "mlp_up_70b", "decode_qkv_8b", "gqa_qk_8b", "attn_pv
              "decode_qkv_8b_w8", "mlp_down_8b_w8")
 
 
-def make_op(name, copies):
+def make_op(name, copies, strict=False):
     import synth
     if name == "mlp_down_8b":
-        w = synth.mlp_down()
+        w = synth.mlp_down(strict_adjacent=strict)
         return MatmulOp(name, w.tensors["A"], w.tensors["B"], (0.9, 0.7, 0.5, 1.0),
                         "A 4096x14336 bf16 (log-normal channel scale, 1% outlier channels x20) @ "
                         "B 14336x4096 bf16 -> Y fp32", copies)
     if name == "mlp_up_70b":
-        w = synth.mlp_up()
+        w = synth.mlp_up(strict_adjacent=strict)
         return MatmulOp(name, w.tensors["A"], w.tensors["B"], (0.8, 1.0),
                         "A 2048x8192 bf16 @ B 8192x28672 bf16 -> Y fp32", copies)
     if name == "decode_qkv_8b":
-        w = synth.decode_qkv()
+        w = synth.decode_qkv(strict_adjacent=strict)
         return MatmulOp(name, w.tensors["A"], w.tensors["B"], (0.8, 1.0),
                         "A 8x4096 bf16 @ B 4096x6144 bf16 -> Y fp32 (decode GEMV over kept rows)", copies)
     if name == "decode_qkv_8b_w8":
-        w = synth.w8_projection()
+        w = synth.w8_projection(strict_adjacent=strict)
         return MatmulW8Op(name, w.tensors["A"], w.tensors["Bq"], w.tensors["scale"], (0.8, 1.0),
                           "A 8x4096 bf16 @ Bq 4096x6144 int8 (fp32 scale per column) -> Y fp32 "
                           "(decode GEMV over kept int8 rows)", copies)
     if name == "mlp_down_8b_w8":
-        w = synth.w8_projection(n=4096, d=14336, m=4096, rho=0.7, workload=1, name=name)
+        w = synth.w8_projection(n=4096, d=14336, m=4096, rho=0.7, workload=1, name=name, strict_adjacent=strict)
         return MatmulW8Op(name, w.tensors["A"], w.tensors["Bq"], w.tensors["scale"], (0.7, 1.0),
                           "A 4096x14336 bf16 @ Bq 14336x4096 int8 (fp32 scale per column) -> Y fp32", copies)
     if name == "gqa_qk_8b":
@@ -939,11 +967,11 @@ def make_op(name, copies):
                     "Q (32,4096,128) bf16, K (8,4096,128) bf16 (GQA group 4) -> S (32,4096,4096) fp32", copies)
     if name == "decode_attn_8b":
         wq = synth.decode_attn_qk(hq=32, hkv=8, tq=1, tk=8192, dh=128)
-        wp = synth.attn_pv(h=32, hkv=8, tq=1, tk=8192, dv=128)
+        wp = synth.attn_pv(h=32, hkv=8, tq=1, tk=8192, dv=128, strict_adjacent=strict)
         return DecodeAttnOp(name, wq.tensors["Q"], wq.tensors["K"], wp.tensors["V"], (0.5, 1.0),
                             "one query per head, Q (32,1,128) bf16, K and V caches (8,8192,128) bf16 (GQA group 4); "
                             "rho keeps features in QK^T and keys in PV", copies, _hip())
-    w = synth.attn_pv(with_logits=True)
+    w = synth.attn_pv(with_logits=True, strict_adjacent=strict)
     return PvOp(name, w.tensors["P"], w.tensors["V"], (0.5, 1.0),
                 "P (64,512,8192) fp32 row-softmax, V (8,8192,128) bf16 (GQA group 8) -> O (64,512,128) fp32",
                 copies, L_cpu=w.tensors["L"])
@@ -960,6 +988,9 @@ def main():
     ap.add_argument("--stage-iters", type=int, default=10, help="calls per rho with stage events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the hipBLASLt context timing")
+    ap.add_argument("--strict-adjacent", action="store_true",
+                    help="space every neighbouring pair of sorted scores (the literal separation reading) instead "
+                         "of the selection boundaries only; changes the values, not the work")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -969,7 +1000,7 @@ def main():
     copies = args.copies
     if copies <= 0:
         copies = {"gqa_qk_8b": 8, "attn_pv_70b": 2, "decode_attn_8b": 8}.get(args.workload, 4)
-    op = make_op(args.workload, copies)
+    op = make_op(args.workload, copies, strict=args.strict_adjacent)
     line = run(args, op)
     line["hipblaslt_dense_bf16out_us_context"] = None if args.no_context else hipblaslt_context(op)
     if not args.no_cpu_baseline:

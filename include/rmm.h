@@ -76,6 +76,18 @@ typedef enum {
 
 typedef enum { RMM_FP32 = 0, RMM_BF16 = 1 } rmm_dtype_t;
 
+/* Operations, for the generic workspace query rmm_workspace_bytes. */
+typedef enum {
+  RMM_OP_SELECT = 0,          /* rmm_select, rmm_select_retained */
+  RMM_OP_MATMUL = 1,          /* rmm_matmul (+ _timed) */
+  RMM_OP_QK = 2,              /* rmm_qk, rmm_qk_causal (+ _timed) */
+  RMM_OP_PV = 3,              /* rmm_pv (+ _timed) */
+  RMM_OP_MATMUL_W8 = 4,       /* rmm_matmul_w8 (+ _timed) */
+  RMM_OP_MATMUL_IDX = 5,      /* rmm_matmul_idx */
+  RMM_OP_SOFTMAX_ENERGY = 6,  /* rmm_softmax_energy */
+  RMM_OP_PV_ENERGY = 7        /* rmm_pv_energy */
+} rmm_op_t;
+
 /* Number of kept indices, ceil(rho * d) under the decimal reading above;
  * -1 when rho is not finite, rho <= 0, rho > 1 or d < 1.
  * hackcv.com "Algorithm Deep-Dive: RMM", Core Approach and the
@@ -84,6 +96,25 @@ int64_t rmm_k(double rho, int64_t d);
 
 /* Static, human-readable name of a status code. */
 const char* rmm_status_str(int status);
+
+/* Workspace bytes that suffice for every call of operation `op` (an
+ * rmm_op_t) of the given sizes, whatever rho in (0, 1], dtypes, strides and
+ * pointer alignment the call uses: an upper bound of the matching per-call
+ * query (rmm_*_workspace), which gives the exact need of one configuration.
+ * The pages define the operator (RMM_rho(A, B) with the retention ratio rho;
+ * hackcv.com, Core Approach and the retention-ratio section) and say it
+ * wraps the attention and FFN operators (hackcv.com, Engineering Notes);
+ * the sizes that bound an operation's scratch are:
+ *   RMM_OP_SELECT          n_or_heads = n rows, d = contraction length, m unused
+ *   RMM_OP_MATMUL, _W8     n_or_heads = n rows of A, d, m = columns of B
+ *   RMM_OP_MATMUL_IDX      n_or_heads = n, d = length of the index list, m
+ *   RMM_OP_QK              n_or_heads = hq, d = head dim, m >= max(tq, tk)
+ *   RMM_OP_PV, _PV_ENERGY  n_or_heads = h, d = tk (key positions), m >= max(tq, dv)
+ *   RMM_OP_SOFTMAX_ENERGY  n_or_heads = h, d = tk, m = tq
+ * Returns 0 for an unknown op or a size outside [1, 2^31) (and for
+ * softmax rows longer than the softmax pass takes).  Pure host arithmetic:
+ * no device call, no allocation. */
+size_t rmm_workspace_bytes(int op, int64_t n_or_heads, int64_t d, int64_t m);
 
 /* ---------------------------------------------------------------------
  * rmm_select: the kept index set of A alone.

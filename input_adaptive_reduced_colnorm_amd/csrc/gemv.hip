@@ -222,6 +222,18 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const GemvArgs g) {
 
 }  // namespace
 
+// Upper bound of gemv_splits(k, m, batch) over every k <= kmax: the split
+// count before whole-chunk slicing is at most the larger of the target
+// count and the minimum that keeps slices within kMaxSlice, and slicing only
+// lowers it.
+int gemv_splits_bound(int kmax, int m, int batch) {
+  const int strips = (m + kCols - 1) / kCols;
+  const int by_target = (kTargetGroups + strips * batch - 1) / (strips * batch);
+  const int by_slice = (kmax + kMaxSlice - 1) / kMaxSlice;
+  const int s = by_target > by_slice ? by_target : by_slice;
+  return s < 1 ? 1 : s;
+}
+
 int gemv_splits(int k, int m, int batch) {
   const int strips = (m + kCols - 1) / kCols;
   int splits = (kTargetGroups + strips * batch - 1) / (strips * batch);

@@ -256,10 +256,16 @@ rmm_status_t rmm_select_retained(const void* A, int dtype, int64_t n, int64_t d,
 
 size_t rmm_matmul_workspace(int64_t n, int64_t d, int64_t m, int64_t lda, int dtype, double rho) {
   if (!dim_ok(n) || !dim_ok(d) || !dim_ok(m) || lda < d || !dtype_ok(dtype) || !rho_ok(rho)) return 0;
-  // Upper bound over the paths the call may take (B layout is not known here).
-  MatPlan a = plan_matmul(n, d, m, lda, m, dtype, rho, true, true);
-  MatPlan b = plan_matmul(n, d, m, lda, m + 1, dtype, rho, true, false);
-  return a.total > b.total ? a.total : b.total;
+  // Upper bound over the paths the call may take: neither the alignment of
+  // A (rho = 1 reads a 16-byte aligned A in place, anything else is packed)
+  // nor the layout of B is known here.
+  size_t best = 0;
+  for (int a_ok = 0; a_ok < 2; ++a_ok)
+    for (int b_ok = 0; b_ok < 2; ++b_ok) {
+      const MatPlan p = plan_matmul(n, d, m, lda, b_ok ? m : m + 1, dtype, rho, a_ok != 0, b_ok != 0);
+      best = p.total > best ? p.total : best;
+    }
+  return best;
 }
 
 namespace {
@@ -1059,6 +1065,81 @@ rmm_status_t rmm_softmax_energy(const float* L, float scale, int64_t h, int64_t 
                                    softmax_row_blocks((int)h, (int)tq), scale, (float*)workspace, energy,
                                    (hipStream_t)stream));
   return RMM_OK;
+}
+
+// ------------------------- generic workspace query ---------------------------
+//
+// One bound per operation, over every rho in (0, 1], every dtype and
+// every alignment or layout the operation accepts: the sum of the largest
+// size each workspace region of the operation's paths can take (each
+// carved region is rounded up to 256 bytes).
+
+namespace {
+
+size_t region(size_t bytes) { return (bytes + 255) / 256 * 256; }
+
+// column-energy partials and the TopK key scratch of a selection over
+// `heads` matrices of n rows x d columns, either input dtype
+size_t select_bound(int64_t heads, int64_t n, int64_t d) {
+  const int s16 = colnorm_splits((int)heads, (int)n, (int)d, true);
+  const int s32 = colnorm_splits((int)heads, (int)n, (int)d, false);
+  const size_t splits = (size_t)(s16 > s32 ? s16 : s32);
+  return region((size_t)heads * splits * d * 4) + region((size_t)heads * d * 4);
+}
+
+// linear product (n x d) (d x m): selection, padded index list, packed A,
+// decode key scratch and slice partials
+size_t matmul_bound(int64_t n, int64_t d, int64_t m) {
+  const size_t k_pad = (size_t)round_up(d, kKTile);
+  size_t b = select_bound(1, n, d) + region(k_pad * 4) + region((size_t)n * k_pad * 2) + region((size_t)d * 4);
+  if (n <= kDecodeRows) b += region((size_t)gemv_splits_bound((int)d, (int)m) * n * m * 4);
+  return b;
+}
+
+}  // namespace
+
+size_t rmm_workspace_bytes(int op, int64_t n_or_heads, int64_t d, int64_t m) {
+  const int64_t h = n_or_heads;
+  switch (op) {
+    case RMM_OP_SELECT:
+      if (!dim_ok(h) || !dim_ok(d)) return 0;
+      return select_bound(1, h, d);
+    case RMM_OP_MATMUL:
+    case RMM_OP_MATMUL_W8:
+      if (!dim_ok(h) || !dim_ok(d) || !dim_ok(m)) return 0;
+      return matmul_bound(h, d, m);
+    case RMM_OP_MATMUL_IDX: {
+      // d is the length of the index list here
+      if (!dim_ok(h) || !dim_ok(d) || !dim_ok(m)) return 0;
+      const size_t k_pad = (size_t)round_up(d, kKTile);
+      size_t b = region(k_pad * 4) + region((size_t)h * k_pad * 2);
+      if (h <= kDecodeRows) b += region((size_t)gemv_splits_bound((int)d, (int)m) * h * m * 4);
+      return b;
+    }
+    case RMM_OP_QK: {
+      // d = head dim; m bounds both tq and tk
+      if (!dim_ok(h) || !dim_ok(d) || !dim_ok(m)) return 0;
+      const size_t k_pad = (size_t)round_up(d, kKTile);
+      return select_bound(h, m, d) + region((size_t)h * m * k_pad * 2) + region((size_t)h * m * k_pad * 2);
+    }
+    case RMM_OP_PV:
+    case RMM_OP_PV_ENERGY: {
+      // d = key positions tk (the contraction); m bounds both tq and dv
+      if (!dim_ok(h) || !dim_ok(d) || !dim_ok(m)) return 0;
+      const size_t k_pad = (size_t)round_up(d, kKTile);
+      const int64_t rows = m < kDecodeRows ? m : kDecodeRows;   // the GEMV path takes tq <= 16
+      return select_bound(h, m, d) + region((size_t)h * d * 4) + region((size_t)h * k_pad * 4) +
+             region((size_t)h * m * k_pad * 2) +
+             // dv <= m is not known: the slice count is largest for one strip
+             region((size_t)gemv_splits_bound((int)d, 1, (int)h) * h * rows * m * 4);
+    }
+    case RMM_OP_SOFTMAX_ENERGY:
+      // d = key positions tk, m = query rows tq
+      if (!dim_ok(h) || !dim_ok(d) || !dim_ok(m) || d > softmax_max_keys()) return 0;
+      return rmm_softmax_energy_workspace(h, m, d);
+    default:
+      return 0;
+  }
 }
 
 rmm_status_t rmm_pv_timed(const void* P, int p_dtype, const void* V, int v_dtype, int64_t h, int64_t hkv, int64_t tq,

@@ -110,6 +110,7 @@ struct GemvArgs {
   bool b_i8 = false; const float* col_scale = nullptr;
 };
 int gemv_splits(int k, int m, int batch = 1);
+int gemv_splits_bound(int kmax, int m, int batch = 1);   // >= gemv_splits(k, m, batch) for all k <= kmax
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);
 
 // Decode-shaped QK^T (tq <= 16, group * tq <= 8, dh <= 256 and a multiple

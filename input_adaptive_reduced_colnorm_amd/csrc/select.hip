@@ -275,6 +275,11 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
     k_max = max(k_max, sh.wave_tot[w][1]);
     nz += sh.wave_nz[w];
   }
+  // every wave has read wave_tot before any of them returns early: the
+  // compaction's block scan writes wave_tot next, and a wave that is still
+  // reading here would otherwise take a scan total for kmin (all nonzero
+  // keys equal, or k above the nonzero count, both skip the radix passes)
+  __syncthreads();
   if ((uint32_t)k > nz) {
     // every nonzero key is kept, and the lowest-indexed zeros fill up to k
     *T = 0u;

@@ -19,6 +19,10 @@ RMM_OK = 0
 RMM_FP32 = 0
 RMM_BF16 = 1
 
+# operation codes of rmm_workspace_bytes (rmm_op_t)
+OPS = {"select": 0, "matmul": 1, "qk": 2, "pv": 3, "matmul_w8": 4, "matmul_idx": 5, "softmax_energy": 6,
+       "pv_energy": 7}
+
 _c = ctypes
 _vp, _i64, _dbl, _sz, _int = _c.c_void_p, _c.c_int64, _c.c_double, _c.c_size_t, _c.c_int
 
@@ -26,6 +30,7 @@ _vp, _i64, _dbl, _sz, _int = _c.c_void_p, _c.c_int64, _c.c_double, _c.c_size_t, 
 SIGNATURES = {
     "rmm_k": (_i64, [_dbl, _i64]),
     "rmm_status_str": (_c.c_char_p, [_int]),
+    "rmm_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
     "rmm_select_workspace": (_sz, [_i64, _i64, _int]),
     "rmm_select": (_int, [_vp, _int, _i64, _i64, _i64, _dbl, _vp, _vp, _vp, _sz, _vp]),
     "rmm_select_retained": (_int, [_vp, _int, _i64, _i64, _i64, _dbl, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -241,6 +246,12 @@ def matmul_w8(A: torch.Tensor, Bq: torch.Tensor, scale: torch.Tensor, rho: float
                          workspace.numel(), _stream(dev))
     _raise(st, "rmm_matmul_w8")
     return idx, out
+
+
+def workspace_bytes(op: str, n_or_heads: int, d: int, m: int) -> int:
+    """rmm_workspace_bytes: a workspace size that serves every call of `op`
+    with these sizes (any rho, dtype, stride or alignment)."""
+    return int(lib().rmm_workspace_bytes(OPS[op], int(n_or_heads), int(d), int(m)))
 
 
 def matmul_workspace(n: int, d: int, m: int, lda: int, dtype, rho: float) -> int:

@@ -34,6 +34,12 @@ import torch
 
 GAP_REQUIRED = 1e-3   # acceptance: neighbouring sorted scores differ by more
 GAP_TARGET = 1.5e-3   # what the generator aims for at each boundary
+# With strict_adjacent every neighbouring pair of sorted scores is separated
+# (the literal reading of the acceptance rule), which needs a spread of
+# about (1 + gap)^d between the largest and smallest norm: for wide rows the
+# generator aims just above the required gap so the spread stays moderate
+# (1.00125^14336 is about 6e7 in norm, 4e15 in energy, far below fp32 range).
+GAP_STRICT = 1.25e-3
 
 
 def rng(workload: int, part: int = 0) -> np.random.Generator:
@@ -90,10 +96,10 @@ def _gaps(s: np.ndarray, ks) -> dict:
 
 
 def _space_columns(z: np.ndarray, mult: np.ndarray, store, ks, literal: bool,
-                   tries: int = 12):
+                   tries: int = 12, target: float = GAP_TARGET):
     """Rescale columns of draft z * mult until the required gaps hold.
 
-    ks: boundary positions (k values) whose gap must exceed GAP_TARGET.
+    ks: boundary positions (k values) whose gap must exceed `target`.
     literal: every neighbouring pair must exceed it (cumulative stretch).
     store: maps a float32 draft to the stored tensor (bf16 or fp32).
     Returns (stored tensor, min gap at the checked positions).
@@ -101,13 +107,13 @@ def _space_columns(z: np.ndarray, mult: np.ndarray, store, ks, literal: bool,
     mult = mult.astype(np.float64).copy()
     d = z.shape[1]
     check = list(range(1, d)) if literal else list(ks)
-    factor = 1.0 + 2 * GAP_TARGET
+    factor = 1.0 + 2 * target
     for _ in range(tries):
         t = store((z * mult.astype(np.float32)[None, :]).astype(np.float32))
         s = _draft_col_norms(t)
         gaps = _gaps(s, check)
         worst = min(gaps.values()) if gaps else 1.0
-        if worst > GAP_TARGET:
+        if worst > target:
             return t, worst
         order = np.argsort(-s, kind="stable")
         if literal:
@@ -122,10 +128,18 @@ def _space_columns(z: np.ndarray, mult: np.ndarray, store, ks, literal: bool,
                 t_prev = tj
         else:
             for k, g in sorted(gaps.items(), reverse=True):
-                if g <= GAP_TARGET:
+                if g <= target:
                     mult[order[k:]] /= factor
         factor = 1.0 + (factor - 1.0) * 1.5
     raise RuntimeError("could not space the selection boundaries")
+
+
+def _spacing(ks, strict: bool, d: int):
+    """(boundaries, literal, target) for _space_columns: the selection
+    boundaries of the workload, or every neighbouring pair when strict."""
+    if strict:
+        return (), True, (GAP_STRICT if d > 256 else GAP_TARGET)
+    return ks, False, GAP_TARGET
 
 
 @dataclass
@@ -146,7 +160,7 @@ def _activation(g: np.random.Generator, n: int, d: int, outlier_frac: float):
     return z, c
 
 
-def tiny_projection(n=16, d=256, m=256, rho=0.5) -> Workload:
+def tiny_projection(n=16, d=256, m=256, rho=0.5, strict_adjacent=True) -> Workload:
     """A n x d fp32, literal score separation; B d x m fp32 N(0, 1/sqrt(d))."""
     g = rng(0)
     z = g.standard_normal((n, d), dtype=np.float32)
@@ -158,33 +172,35 @@ def tiny_projection(n=16, d=256, m=256, rho=0.5) -> Workload:
                     {"n": n, "d": d, "m": m, "dtype": "fp32", "min_gap": gap})
 
 
-def mlp_down(n=4096, d=14336, m=4096, rhos=(0.9, 0.7, 0.5), workload=1) -> Workload:
+def mlp_down(n=4096, d=14336, m=4096, rhos=(0.9, 0.7, 0.5), workload=1, strict_adjacent=False) -> Workload:
     """Llama-3.1-8B MLP down projection, prefill: A n x d, B d x m, bf16."""
     g = rng(workload)
     z, c = _activation(g, n, d, 0.01)
     ks = sorted({ceil_keep(r, d) for r in rhos if r < 1.0}, reverse=True)
-    A, gap = _space_columns(z, c, to_bf16, ks, literal=False)
+    ks, literal, target = _spacing(ks, strict_adjacent, d)
+    A, gap = _space_columns(z, c, to_bf16, ks, literal=literal, target=target)
     del z
     B = to_bf16(g.standard_normal((d, m), dtype=np.float32) / np.float32(math.sqrt(d)))
     return Workload("mlp_down_8b", {"A": A, "B": B}, tuple(rhos),
-                    {"n": n, "d": d, "m": m, "dtype": "bf16", "min_gap": gap})
+                    {"n": n, "d": d, "m": m, "dtype": "bf16", "min_gap": gap, "strict_adjacent": strict_adjacent})
 
 
-def mlp_up(n=2048, d=8192, m=28672, rho=0.8) -> Workload:
+def mlp_up(n=2048, d=8192, m=28672, rho=0.8, strict_adjacent=False) -> Workload:
     """Llama-3.1-70B MLP up projection: A n x d (MLP-down recipe), B d x m."""
-    w = mlp_down(n=n, d=d, m=m, rhos=(rho,), workload=4)
+    w = mlp_down(n=n, d=d, m=m, rhos=(rho,), workload=4, strict_adjacent=strict_adjacent)
     w.name = "mlp_up_70b"
     return w
 
 
-def decode_qkv(n=8, d=4096, m=6144, rho=0.8) -> Workload:
+def decode_qkv(n=8, d=4096, m=6144, rho=0.8, strict_adjacent=False) -> Workload:
     """Decode-shaped fused QKV projection: A n x d, B d x m (std 1/sqrt(d))."""
     g = rng(3)
     z, c = _activation(g, n, d, 0.0)
-    A, gap = _space_columns(z, c, to_bf16, (ceil_keep(rho, d),), literal=False)
+    ks, literal, target = _spacing((ceil_keep(rho, d),), strict_adjacent, d)
+    A, gap = _space_columns(z, c, to_bf16, ks, literal=literal, target=target)
     B = to_bf16(g.standard_normal((d, m), dtype=np.float32) / np.float32(math.sqrt(d)))
     return Workload("decode_qkv_8b", {"A": A, "B": B}, (rho,),
-                    {"n": n, "d": d, "m": m, "dtype": "bf16", "min_gap": gap})
+                    {"n": n, "d": d, "m": m, "dtype": "bf16", "min_gap": gap, "strict_adjacent": strict_adjacent})
 
 
 def int8_weights(g: np.random.Generator, d: int, m: int):
@@ -202,19 +218,21 @@ def int8_weights(g: np.random.Generator, d: int, m: int):
     return torch.from_numpy(Bq), torch.from_numpy(scale)
 
 
-def w8_projection(n=8, d=4096, m=6144, rho=0.8, workload=5, name="decode_qkv_8b_w8") -> Workload:
+def w8_projection(n=8, d=4096, m=6144, rho=0.8, workload=5, name="decode_qkv_8b_w8",
+                  strict_adjacent=False) -> Workload:
     """A n x d bf16 (MLP-down activation recipe, boundary separation at rho)
     with int8 weights of d x m (int8_weights)."""
     g = rng(workload)
     z, c = _activation(g, n, d, 0.01 if n > 64 else 0.0)
-    A, gap = _space_columns(z, c, to_bf16, (ceil_keep(rho, d),) if rho < 1.0 else (), literal=False)
+    ks, literal, target = _spacing((ceil_keep(rho, d),) if rho < 1.0 else (), strict_adjacent, d)
+    A, gap = _space_columns(z, c, to_bf16, ks, literal=literal, target=target)
     del z
     Bq, scale = int8_weights(g, d, m)
     return Workload(name, {"A": A, "Bq": Bq, "scale": scale}, (rho,),
                     {"n": n, "d": d, "m": m, "dtype": "bf16 x int8", "min_gap": gap})
 
 
-def gqa_qk(hq=32, hkv=8, t=4096, dh=128, rho=0.5) -> Workload:
+def gqa_qk(hq=32, hkv=8, t=4096, dh=128, rho=0.5, strict_adjacent=True) -> Workload:
     """QK^T prefill: Q (hq, t, dh), K (hkv, t, dh) bf16, per-feature scales.
 
     Every query head gets literal separation of its dh column norms.
@@ -237,7 +255,7 @@ def gqa_qk(hq=32, hkv=8, t=4096, dh=128, rho=0.5) -> Workload:
                      "min_gap": float(min(gaps))})
 
 
-def decode_attn_qk(hq=32, hkv=8, tq=1, tk=8192, dh=128, rho=0.5) -> Workload:
+def decode_attn_qk(hq=32, hkv=8, tq=1, tk=8192, dh=128, rho=0.5, strict_adjacent=True) -> Workload:
     """Decode QK^T: Q (hq, tq, dh) with literal separation of each head's
     feature norms over its tq rows; a key cache K (hkv, tk, dh); bf16."""
     g = rng(6)
@@ -263,34 +281,49 @@ def _softmax_rows(L: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=1, keepdims=True)
 
 
-def attn_pv(h=64, hkv=8, tq=512, tk=8192, dv=128, rho=0.5, with_logits=False) -> Workload:
+def attn_pv(h=64, hkv=8, tq=512, tk=8192, dv=128, rho=0.5, with_logits=False, strict_adjacent=False) -> Workload:
     """PV: P (h, tq, tk) fp32 = row softmax of N(0, std 2) logits; V (hkv, tk, dv).
 
     The boundary gap of each head is widened by lowering the logits of the
     key positions ranked below the boundary (rows stay stochastic).  With
-    `with_logits` the shifted logits L (fp32) whose softmax P is are kept too.
+    `strict_adjacent` every neighbouring pair of sorted key norms is spaced
+    instead (cumulative logit shifts, walked from the smallest norm up).
+    With `with_logits` the shifted logits L (fp32) whose softmax P is are
+    kept too.
     """
     g = rng(4, part=1)
     k = ceil_keep(rho, tk)
     P = torch.empty((h, tq, tk), dtype=torch.float32)
     Ls = torch.empty((h, tq, tk), dtype=torch.float32) if with_logits else None
     gaps = []
+    check = list(range(1, tk)) if strict_adjacent else [k]
+    target = (GAP_STRICT if tk > 256 else GAP_TARGET) if strict_adjacent else GAP_TARGET
     for hh in range(h):
         L = 2.0 * g.standard_normal((tq, tk))
         shift = np.zeros(tk)
-        step = math.log(1.0 + 2 * GAP_TARGET)
-        for _ in range(12):
+        step = math.log(1.0 + 2 * target)
+        for _ in range(16):
             Ph = to_f32(_softmax_rows(L + shift[None, :]))
             s = _draft_col_norms(Ph)
-            gp = _gaps(s, (k,))
-            gap = gp.get(k, 1.0)
-            if gap > GAP_TARGET:
+            gp = _gaps(s, check)
+            gap = min(gp.values()) if gp else 1.0
+            if gap > target:
                 break
             order = np.argsort(-s, kind="stable")
-            shift[order[k:]] -= step
+            if strict_adjacent:
+                # each norm, walking up from the smallest, must exceed the one
+                # below it by the step: raise its logit by the missing factor
+                t_prev = None
+                for j in order[::-1]:
+                    tj = s[j] if t_prev is None else max(s[j], t_prev * math.exp(step))
+                    if s[j] > 0:
+                        shift[j] += math.log(tj / s[j])
+                    t_prev = tj
+            else:
+                shift[order[k:]] -= step
             step *= 1.5
         else:
-            raise RuntimeError("could not space the PV boundary")
+            raise RuntimeError("could not space the PV key norms")
         P[hh] = Ph
         if with_logits:
             Ls[hh] = to_f32(L + shift[None, :])
@@ -301,7 +334,7 @@ def attn_pv(h=64, hkv=8, tq=512, tk=8192, dv=128, rho=0.5, with_logits=False) ->
         tensors["L"] = Ls
     return Workload("attn_pv_70b", tensors, (rho,),
                     {"h": h, "hkv": hkv, "tq": tq, "tk": tk, "dv": dv,
-                     "dtype": "fp32/bf16", "min_gap": float(min(gaps))})
+                     "dtype": "fp32/bf16", "min_gap": float(min(gaps)), "strict_adjacent": strict_adjacent})
 
 
 # The workloads named by the benchmark configuration list, in its order.

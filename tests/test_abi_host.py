@@ -100,8 +100,11 @@ def test_matmul_size_limits(L):
     assert _matmul(L, d=32768, lda=32768, m=32768, ldb=32768, ldy=32768, **far) == SHAPE   # B is 2 GiB
 
 
-def test_matmul_dense_needs_no_workspace(L):
-    assert L.rmm_matmul_workspace(64, 128, 64, 128, BF16, 1.0) == 0
+def test_matmul_workspace_covers_an_element_aligned_dense_a(L):
+    # rho = 1 reads a 16-byte aligned A in place, but the query does not
+    # know the pointer: an A that is only 2-byte aligned (a column-offset
+    # view) is packed, n x d bf16 plus the padded index list
+    assert L.rmm_matmul_workspace(64, 128, 64, 128, BF16, 1.0) >= 64 * 128 * 2 + 128 * 4
     assert L.rmm_matmul_workspace(64, 128, 64, 128, BF16, 0.5) > 0
     assert L.rmm_matmul_workspace(0, 128, 64, 128, BF16, 0.5) == 0   # invalid shape
 
@@ -264,3 +267,44 @@ def test_softmax_energy_and_pv_energy_reject_bad_arguments(L):
     assert pe(rho=0.0) == RHO
     assert pe(h=6, hkv=4) == SHAPE
     assert pe(E=FAKE + (2 << 30)) == ALIAS   # energies on top of the index output
+
+
+def test_generic_workspace_bound_covers_every_per_call_query(L):
+    """rmm_workspace_bytes(op, ...) is at least the per-call query for every
+    rho, dtype and size within its arguments' bounds."""
+    rhos = [1e-3, 0.05, 0.3, 0.5, 0.7, 0.8, 0.9, 0.999, 1.0]
+    for n, d, m in [(8, 4096, 6144), (16, 1000, 264), (17, 100, 48), (4096, 14336, 4096), (300, 64, 8),
+                    (1, 20000, 8), (2048, 8192, 28672)]:
+        for dt in (FP32, BF16):
+            bs = L.rmm_workspace_bytes(0, n, d, 0)
+            bm = L.rmm_workspace_bytes(1, n, d, m)
+            bw = L.rmm_workspace_bytes(4, n, d, m)
+            for lda in (d, d + 1, d + 8):
+                for rho in rhos:
+                    assert bm >= L.rmm_matmul_workspace(n, d, m, lda, dt, rho), (n, d, m, lda, dt, rho)
+                    assert bw >= L.rmm_matmul_w8_workspace(n, d, m, lda, rho), (n, d, m, lda, rho)
+            assert bs >= L.rmm_select_workspace(n, d, dt)
+            for k in (1, d // 2, d, 3 * d):
+                bi = L.rmm_workspace_bytes(5, n, k, m)
+                assert bi >= L.rmm_matmul_idx_workspace(n, k, m, dt), (n, k, m, dt)
+    for hq, dh, tq, tk in [(32, 128, 4096, 4096), (8, 40, 45, 45), (4, 256, 130, 130), (8, 128, 1, 1000),
+                           (4, 64, 200, 520)]:
+        bq = L.rmm_workspace_bytes(2, hq, dh, max(tq, tk))
+        for dt in (FP32, BF16):
+            for rho in rhos:
+                assert bq >= L.rmm_qk_workspace(hq, tq, tk, dh, dt, rho), (hq, tq, tk, dh, dt, rho)
+    for h, tq, tk, dv in [(64, 512, 8192, 128), (32, 1, 8192, 128), (4, 16, 512, 64), (8, 4, 1000, 128),
+                          (2, 40, 300, 24), (4, 96, 1024, 64)]:
+        bp = L.rmm_workspace_bytes(3, h, tk, max(tq, dv))
+        be = L.rmm_workspace_bytes(7, h, tk, max(tq, dv))
+        for pdt in (FP32, BF16):
+            for vdt in (FP32, BF16):
+                for rho in rhos:
+                    assert bp >= L.rmm_pv_workspace(h, tq, tk, dv, pdt, vdt, rho), (h, tq, tk, dv, pdt, vdt, rho)
+                    assert be >= L.rmm_pv_energy_workspace(h, tq, tk, dv, pdt, vdt, rho)
+        if tk <= 8192:
+            assert L.rmm_workspace_bytes(6, h, tk, tq) == L.rmm_softmax_energy_workspace(h, tq, tk)
+    # unknown op and bad sizes
+    assert L.rmm_workspace_bytes(99, 8, 8, 8) == 0
+    assert L.rmm_workspace_bytes(1, 0, 8, 8) == 0
+    assert L.rmm_workspace_bytes(1, 8, -1, 8) == 0

@@ -79,6 +79,10 @@ def pin_worked_example(ns):
 
 
 def pin_dense_loop(ns):
+    """rho = 1 keeps every index and gives the unreduced product; `dense`
+    (the unreduced product on its own) equals the same exactly rounded
+    triple loop, on a non-square case so that a transposed or truncated
+    operand cannot pass."""
     r = np.random.default_rng(7)
     A = r.standard_normal((5, 7))
     B = r.standard_normal((7, 3))
@@ -88,6 +92,16 @@ def pin_dense_loop(ns):
     ref = np.array(_loop_matmul(A.tolist(), B.tolist()))
     if np.max(np.abs(np.asarray(Y) - ref)) > 1e-12 * np.max(np.abs(ref)):
         return "rho=1 product differs from the triple loop"
+    # dense on bf16-representable values (float32 storage), the way the
+    # tests feed it: entries k / 64 with |k| < 256 are exact in bf16
+    A2 = r.integers(-255, 256, size=(6, 11)).astype(np.float32) / np.float32(64)
+    B2 = (r.standard_normal((11, 4)) * 1e3).astype(np.float32)
+    D = np.asarray(ns.dense(A2, B2))
+    if D.shape != (6, 4):
+        return f"dense has shape {D.shape}, expected (6, 4)"
+    ref2 = np.array(_loop_matmul(A2.tolist(), B2.tolist()))
+    if np.max(np.abs(D - ref2)) > 1e-12 * np.max(np.abs(ref2)):
+        return "dense differs from the triple loop"
     return None
 
 
@@ -534,6 +548,8 @@ MUTANTS = {
     "gqa_modulo_mapping": dict(kv_head=lambda h, hq, hkv: h % hkv),
     "product_sign_flip": dict(_product=lambda A, B, idx: -(A[:, idx] @ B[idx, :])),
     "dense_instead_of_reduced": dict(_product=lambda A, B, idx: A @ B),
+    "dense_drops_last_term": dict(dense=lambda A, B: np.asarray(A, float)[:, :-1] @ np.asarray(B, float)[:-1, :]),
+    "dense_in_float32": dict(dense=lambda A, B: (np.asarray(A, np.float32) @ np.asarray(B, np.float32)).astype(float)),
     "given_list_repeats_counted_once": dict(matmul_given=lambda A, B, idx: np.asarray(A, float)[:, np.unique(
         [t for t in np.asarray(idx) if 0 <= t < np.asarray(A).shape[1]]).astype(int)] @ np.asarray(B, float)[np.unique(
         [t for t in np.asarray(idx) if 0 <= t < np.asarray(A).shape[1]]).astype(int), :]),
