@@ -155,6 +155,24 @@ rmm_status_t rmm_matmul(const void* A, const void* B, int dtype, int64_t n, int6
                         int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* rmm_matmul for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as rmm_matmul minus the workspace: the call's
+ * scratch lives in a fixed array of 32 MiB inside the library, one per GPU
+ * (reserved when the library's code is first loaded on that GPU and held
+ * until the process ends).  The call allocates nothing and calls no
+ * allocating routine.  The first call on a device looks up that device's
+ * array (the calling thread's current device must be the device of `stream`
+ * and of the operands).  A call whose rmm_matmul_workspace need exceeds 32
+ * MiB is refused with RMM_ERR_WORKSPACE before anything is queued (e.g. the
+ * packed prefill path needs about 2 n ceil(rho d) bytes; the decode path,
+ * n <= 16, needs under 4 MiB for d, m <= 16384).  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams, or
+ * host threads) race and must be serialised by the caller. */
+rmm_status_t rmm_matmul_noalloc(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m,
+                                int64_t lda, int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype,
+                                int64_t ldy, void* stream);
+
 /* Instrumented rmm_matmul: the same computation, and in addition records
  * five caller-created HIP events (hipEvent_t, timing enabled) on `stream`
  * at the stage boundaries: [0] before scoring, [1] before TopK, [2] before

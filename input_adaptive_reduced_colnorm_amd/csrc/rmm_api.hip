@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <string.h>
 
 #include "rmm.h"
@@ -270,9 +271,39 @@ size_t rmm_matmul_workspace(int64_t n, int64_t d, int64_t m, int64_t lda, int dt
 
 namespace {
 
+// ------------------------ scratch of the no-alloc call ----------------------
+// A file-scope device array, one copy per GPU the library runs on (held until
+// the process ends), stands in for the caller's workspace in
+// rmm_matmul_noalloc.  Its host-side name is not a device address: host code
+// only uses the per-device address hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+static rmm_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RMM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RMM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RMM_OK;
+}
+
+// use_scratch: the workspace is the current device's scratch array instead
+// of (workspace, workspace_bytes); a call that needs more than it holds is
+// refused with RMM_ERR_WORKSPACE before anything is queued.
 rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
                          int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy, void* workspace,
-                         size_t workspace_bytes, void* stream, void* const* stage_events) {
+                         size_t workspace_bytes, void* stream, void* const* stage_events, bool use_scratch = false) {
   if (!A || !B || !idx || !Y) return RMM_ERR_NULL;
   if (!rho_ok(rho)) return RMM_ERR_RHO;
   if (!dtype_ok(dtype) || !dtype_ok(y_dtype)) return RMM_ERR_DTYPE;
@@ -283,13 +314,16 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
   if (!aligned(A, elt) || !aligned(B, elt) || !aligned(idx, 4) || !aligned(Y, elt_size(y_dtype)))
     return RMM_ERR_ALIGN;
   const MatPlan p = plan_matmul(n, d, m, lda, ldb, dtype, rho, aligned(A, 16), aligned(B, 16));
-  if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
+  if (use_scratch) {
+    if (p.total > kScratchBytes) return RMM_ERR_WORKSPACE;
+  } else if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256))) {
     return RMM_ERR_WORKSPACE;
+  }
   const Span sa = span3(A, 1, 0, n, lda, d, elt), sb = span3(B, 1, 0, d, ldb, m, elt);
   const Span si = span3(idx, 1, 0, 1, p.k, p.k, 4), sy = span3(Y, 1, 0, n, ldy, m, elt_size(y_dtype));
   if (overlap(si, sa) || overlap(si, sb) || overlap(sy, sa) || overlap(sy, sb) || overlap(sy, si))
     return RMM_ERR_ALIAS;
-  if (p.total > 0) {
+  if (p.total > 0 && !use_scratch) {
     const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
     if (overlap(sw, sa) || overlap(sw, sb) || overlap(sw, si) || overlap(sw, sy)) return RMM_ERR_ALIAS;
   }
@@ -297,6 +331,12 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
     const int64_t b_bytes = ((d - 1) * ldb + m) * 2;
     const int64_t a_bytes = p.path == MatPath::kMfmaDirect ? ((n - 1) * lda + d) * 2 : n * p.k_pad * 2;
     if (b_bytes > kMaxOperandBytes || a_bytes > kMaxOperandBytes) return RMM_ERR_SHAPE;
+  }
+  if (use_scratch && p.total > 0) {
+    // every argument is valid: only now look up this device's scratch
+    const rmm_status_t st = scratch_of_current_device(&workspace);
+    if (st != RMM_OK) return st;
+    workspace_bytes = kScratchBytes;
   }
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -394,6 +434,11 @@ rmm_status_t rmm_matmul(const void* A, const void* B, int dtype, int64_t n, int6
                         size_t workspace_bytes, void* stream) {
   return matmul_impl(A, B, dtype, n, d, m, lda, ldb, rho, idx, Y, y_dtype, ldy, workspace, workspace_bytes, stream,
                      nullptr);
+}
+
+rmm_status_t rmm_matmul_noalloc(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
+                                int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy, void* stream) {
+  return matmul_impl(A, B, dtype, n, d, m, lda, ldb, rho, idx, Y, y_dtype, ldy, nullptr, 0, stream, nullptr, true);
 }
 
 rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,

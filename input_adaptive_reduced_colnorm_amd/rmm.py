@@ -36,6 +36,7 @@ SIGNATURES = {
     "rmm_select_retained": (_int, [_vp, _int, _i64, _i64, _i64, _dbl, _vp, _vp, _vp, _vp, _sz, _vp]),
     "rmm_matmul_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _dbl]),
     "rmm_matmul": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz, _vp]),
+    "rmm_matmul_noalloc": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp]),
     "rmm_matmul_timed": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp, _int, _i64, _vp, _sz,
                                 _vp, _vp]),
     "rmm_matmul_w8_workspace": (_sz, [_i64, _i64, _i64, _i64, _dbl]),

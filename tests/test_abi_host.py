@@ -308,3 +308,19 @@ def test_generic_workspace_bound_covers_every_per_call_query(L):
     assert L.rmm_workspace_bytes(99, 8, 8, 8) == 0
     assert L.rmm_workspace_bytes(1, 0, 8, 8) == 0
     assert L.rmm_workspace_bytes(1, 8, -1, 8) == 0
+
+
+def test_noalloc_matmul_rejects_bad_arguments_before_touching_the_device(L):
+    def call(A=FAKE, B=FAKE + (1 << 30), dt=BF16, n=64, d=128, m=64, lda=128, ldb=64, rho=0.5,
+             idx=FAKE + (2 << 30), Y=FAKE + (3 << 30), ydt=FP32, ldy=64):
+        return L.rmm_matmul_noalloc(A, B, dt, n, d, m, lda, ldb, rho, idx, Y, ydt, ldy, None)
+    assert call(A=None) == NULL
+    assert call(rho=0.0) == RHO
+    assert call(dt=7) == DTYPE
+    assert call(lda=100) == SHAPE
+    assert call(A=FAKE + 1) == ALIGN
+    assert call(Y=FAKE + 16) == ALIAS
+    # more scratch than the library's 32 MiB array: the packed A alone is
+    # 2 * 4096 * 12928 bytes at rho = 0.9
+    big = dict(B=FAKE + (1 << 40), idx=FAKE + (2 << 40), Y=FAKE + (3 << 40))
+    assert call(n=4096, d=14336, m=256, lda=14336, ldb=256, ldy=256, rho=0.9, **big) == WS
