@@ -33,6 +33,7 @@
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
+#include "select_block.h"
 
 namespace rmm {
 
@@ -50,11 +51,77 @@ __device__ __forceinline__ int slice_rows(int k, int splits) {
   return ((k + splits - 1) / splits + kChunk - 1) / kChunk * kChunk;
 }
 
-template <int NR, bool A_BF16, bool B_I8>
+// The kept set ranked inside the GEMV (CH > 0): every workgroup computes
+// the column energies of all of A (n <= 16 rows, read from L2 after the
+// first touch) with the same fixed-order fp32 sums as the selection kernel,
+// finds the k-th largest (energy, lowest index) key with the block radix
+// search, and compacts the kept indices that fall in its own slice of the
+// ascending list into LDS; the workgroups of the first column strip also
+// write their slice of the list to idx_out.  This replaces the selection
+// launch in front of the GEMV and the round trip of the list through memory.
+// Thread t ranks the columns [t c, t c + c), c = ceil(d / 256) <= CH.
+template <int CH, int NR, bool A_BF16>
+__device__ __forceinline__ void rank_columns(const GemvArgs& g, sel::KeyChunk<CH>& kc) {
+  const int tid = threadIdx.x;
+  const int chunk = (g.d + kThreads - 1) / kThreads;
+  kc.j0 = min(g.d, tid * chunk);
+  kc.cnt = min(chunk, g.d - kc.j0);
+  float q[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) q[i] = 0.f;
+  const bool vec = A_BF16 && ((uintptr_t)g.A % 16 == 0) && (g.lda % 8 == 0) && (chunk % 8 == 0);
+  if (vec) {
+    // 16-byte loads; the loads of 8 rows are issued before they are used,
+    // rows are added in ascending order
+    constexpr int V = CH / 8;
+    const char* base = (const char*)g.A + (size_t)kc.j0 * 2;
+    for (int r0 = 0; r0 < NR; r0 += 8) {
+      i32x4 x[8][V];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const bool ok = r0 + r < g.n && 8 * v < kc.cnt;
+          x[r][v] = ok ? *(const i32x4*)(base + ((size_t)(r0 + r) * g.lda + 8 * v) * 2) : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if (r0 + r < g.n) {
+#pragma unroll
+          for (int v = 0; v < V; ++v)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t w = (uint32_t)x[r][v][e >> 1];
+              const float f = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+              q[8 * v + e] = fmaf(f, f, q[8 * v + e]);
+            }
+        }
+      }
+    }
+  } else {
+    for (int r = 0; r < g.n; ++r) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        if (i < kc.cnt) {
+          const size_t off = (size_t)r * g.lda + kc.j0 + i;
+          const float f = A_BF16 ? bf16_to_f32(((const uint16_t*)g.A)[off]) : ((const float*)g.A)[off];
+          q[i] = fmaf(f, f, q[i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) kc.key[i] = __float_as_uint(q[i]);
+}
+
+template <int NR, bool A_BF16, bool B_I8, int CH = 0>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   constexpr int BE = B_I8 ? 1 : 2;   // bytes per B element
+  constexpr bool SEL = CH > 0;
   __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kMaxSlice + 8];   // bf16 activations, row r, kept row t
   __shared__ float red[kWaves][16][kCols];
+  __shared__ sel::Shared<SEL ? kWaves : 1> ssh;
+  __shared__ int32_t s_list[SEL ? kMaxSlice : 1];
   {
     // batch member (attention head): shift every operand to its slice
     const int bz = blockIdx.z;
@@ -72,6 +139,28 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   const int rb = lane >> 4, cg = lane & 15;
   const int c = blockIdx.x * kCols + cg * 8;
   const bool col_ok = c < g.m;   // m is a multiple of 8
+  const bool write_list = g.idx_out && blockIdx.x == 0;
+
+  if constexpr (SEL) {
+    // ---- rank every column of A and keep this slice of the ascending list ----
+    sel::KeyChunk<CH> kc;
+    rank_columns<CH, NR, A_BF16>(g, kc);
+    int32_t* out = g.idx_out;
+    sel::select_window<kThreads, CH>(kc, g.k, ssh, (uint32_t)t0, (uint32_t)(t0 + L), [&](uint32_t pos, int j) {
+      s_list[pos - t0] = j;
+      if (write_list) out[pos] = j;
+    });
+    __syncthreads();
+  } else if (write_list) {
+    // the identity list (rho = 1): the first strip's workgroups write it
+    for (int i = tid; i < L; i += kThreads) g.idx_out[t0 + i] = t0 + i;
+  }
+  auto kept = [&](int t) -> int {
+    if constexpr (SEL)
+      return s_list[t];
+    else
+      return g.idx ? g.idx[t0 + t] : t0 + t;
+  };
 
   // ---- load order matters: vector loads retire in order, so a wait for a
   //      load also waits for every load issued before it.  First every
@@ -84,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int t = (wave + kWaves * q) * kChunk + 8 * rb + e;
-      row[q][e] = t < L ? (g.idx ? g.idx[t0 + t] : t0 + t) : -1;
+      row[q][e] = t < L ? kept(t) : -1;
     }
   constexpr int PER = kMaxSlice / kThreads;
   const int L32 = (L + kChunk - 1) / kChunk * kChunk;
@@ -92,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int i = tid + u * kThreads;
-    srow[u] = i < L ? (g.idx ? g.idx[t0 + i] : t0 + i) : -1;
+    srow[u] = i < L ? kept(i) : -1;
   }
   // ---- then the activations to stage and every B row, all unconditional
   //      (an invalid row reads row 0 and is zeroed where it is used), so the
@@ -248,18 +337,31 @@ int gemv_splits(int k, int m, int batch) {
   return (k + slice - 1) / slice;
 }
 
+template <int NR, int CH>
+void launch_nr_ch(const GemvArgs& g, dim3 grid, hipStream_t s) {
+  if (g.b_i8)
+    gemv_kernel<NR, true, true, CH><<<grid, kThreads, 0, s>>>(g);   // int8 weights take bf16 activations
+  else if (g.a_bf16)
+    gemv_kernel<NR, true, false, CH><<<grid, kThreads, 0, s>>>(g);
+  else
+    gemv_kernel<NR, false, false, CH><<<grid, kThreads, 0, s>>>(g);
+}
+
 template <int NR>
 void launch_nr(const GemvArgs& g, dim3 grid, hipStream_t s) {
-  if (g.b_i8)
-    gemv_kernel<NR, true, true><<<grid, kThreads, 0, s>>>(g);   // int8 weights take bf16 activations
-  else if (g.a_bf16)
-    gemv_kernel<NR, true, false><<<grid, kThreads, 0, s>>>(g);
+  if (!g.select)
+    launch_nr_ch<NR, 0>(g, grid, s);
+  else if (g.d <= 16 * kThreads)
+    launch_nr_ch<NR, 16>(g, grid, s);
   else
-    gemv_kernel<NR, false, false><<<grid, kThreads, 0, s>>>(g);
+    launch_nr_ch<NR, 32>(g, grid, s);
 }
+
+int gemv_select_max_d() { return 32 * kThreads; }
 
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s) {
   if (g.n > 16 || (g.b_i8 && !g.a_bf16)) return hipErrorInvalidValue;
+  if (g.select && (g.batch != 1 || g.d > gemv_select_max_d() || g.d < g.k || g.idx)) return hipErrorInvalidValue;
   dim3 grid((g.m + kCols - 1) / kCols, g.splits, g.batch);
   if (g.n <= 4)
     launch_nr<4>(g, grid, s);

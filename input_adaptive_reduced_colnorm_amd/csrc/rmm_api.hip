@@ -364,19 +364,22 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
       break;
     }
     case MatPath::kDecode: {
-      // rho < 1: one selection kernel; rho = 1: the identity index
-      if (!p.all)
+      // rho < 1: the GEMV ranks the columns of A itself (up to
+      // gemv_select_max_d() columns; wider rows take one selection kernel
+      // first); rho = 1: the identity list, written by the GEMV
+      const bool fused = !p.all && d <= gemv_select_max_d();
+      if (!p.all && !fused)
         RMM_LAUNCH(launch_decode_select(A, bf16, lda, (int)n, (int)d, (int)p.k, idx, nullptr,
                                         d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, s));
-      else
-        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
       RMM_LAUNCH(mk.mark(1));
       RMM_LAUNCH(mk.mark(2));
       RMM_LAUNCH(mk.mark(3));
       GemvArgs g{};
       g.A = A; g.a_bf16 = bf16; g.lda = lda;
       g.B = (const uint16_t*)B; g.ldb = ldb;
-      g.idx = p.all ? nullptr : idx;
+      g.idx = p.all || fused ? nullptr : idx;
+      g.select = fused; g.d = (int)d;
+      g.idx_out = p.all || fused ? idx : nullptr;
       g.k = (int)p.k; g.n = (int)n; g.m = (int)m;
       g.partial = (float*)(ws + p.off_part); g.splits = p.gemv_splits;
       g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;
@@ -502,18 +505,19 @@ rmm_status_t matmul_w8_impl(const void* A, int a_dtype, const int8_t* Bq, const 
   clear_error();
   RMM_LAUNCH(mk.mark(0));
   if (p.path == MatPath::kDecode) {
-    if (!p.all)
+    const bool fused = !p.all && d <= gemv_select_max_d();
+    if (!p.all && !fused)
       RMM_LAUNCH(launch_decode_select(A, true, lda, (int)n, (int)d, (int)p.k, idx, nullptr,
                                       d > topk_lds_capacity() ? (uint32_t*)(ws + p.off_dkeys) : nullptr, s));
-    else
-      RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
     RMM_LAUNCH(mk.mark(1));
     RMM_LAUNCH(mk.mark(2));
     RMM_LAUNCH(mk.mark(3));
     GemvArgs g{};
     g.A = A; g.a_bf16 = true; g.lda = lda;
     g.B = Bq; g.ldb = ldb; g.b_i8 = true; g.col_scale = scale;
-    g.idx = p.all ? nullptr : idx;
+    g.idx = p.all || fused ? nullptr : idx;
+    g.select = fused; g.d = (int)d;
+    g.idx_out = p.all || fused ? idx : nullptr;
     g.k = (int)p.k; g.n = (int)n; g.m = (int)m;
     g.partial = (float*)(ws + p.off_part); g.splits = p.gemv_splits;
     g.Y = Y; g.y_bf16 = y_dtype == RMM_BF16; g.ldy = ldy;

@@ -99,6 +99,10 @@ hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, 
 // b_i8: B holds int8 weights (rows 8-byte aligned), widened to bf16 exactly;
 // col_scale (if not null) multiplies output column c by col_scale[c] once
 // the sum over the kept rows is complete.
+// select: the kernel ranks the d columns of A itself (batch 1, d <=
+// gemv_select_max_d(), idx must be null) and keeps the k largest column
+// energies; idx_out (optional, [k]) receives the ascending kept list (the
+// identity list when idx is null and select is false).
 struct GemvArgs {
   const void* A; bool a_bf16; int64_t lda;
   const void* B; int64_t ldb;
@@ -108,7 +112,9 @@ struct GemvArgs {
   void* Y; bool y_bf16; int64_t ldy;
   int batch = 1; int64_t a_bs = 0, b_bs = 0, idx_bs = 0, y_bs = 0; int b_group = 1;
   bool b_i8 = false; const float* col_scale = nullptr;
+  bool select = false; int d = 0; int32_t* idx_out = nullptr;
 };
+int gemv_select_max_d();
 int gemv_splits(int k, int m, int batch = 1);
 int gemv_splits_bound(int kmax, int m, int batch = 1);   // >= gemv_splits(k, m, batch) for all k <= kmax
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);

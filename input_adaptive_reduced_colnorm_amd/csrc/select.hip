@@ -13,6 +13,7 @@
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
+#include "select_block.h"
 
 namespace rmm {
 
@@ -103,43 +104,18 @@ __global__ __launch_bounds__(256) void colnorm_kernel(const void* __restrict__ A
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide helpers for 1024-thread selection workgroups.
+// Selection workgroups of 1024 threads (the block helpers: select_block.h).
 // ---------------------------------------------------------------------------
-// Wave-wide inclusive scans on the DPP cross-lane paths (no LDS round
-// trip): shifts by 1, 2, 4 and 8 lanes inside each row of 16, then the
-// totals of rows 0 and 2 broadcast into rows 1 and 3 (row_bcast:15) and the
-// total of rows 0-1 into rows 2-3 (row_bcast:31).  Lanes whose source is
-// outside the pattern take `id`, the identity of the operation.
-template <typename F>
-__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t x, uint32_t id, F op) {
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));   // row_shr:1
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));   // row_shr:2
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));   // row_shr:4
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));   // row_shr:8
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));   // row_bcast:15
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));   // row_bcast:31
-  return x;
-}
+using sel::hist_add;
+using sel::kHistBins;
+using sel::KeyChunk;
+using SelShared = sel::Shared<kSelWaves>;
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  return wave_scan_dpp(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
-}
-
-constexpr int kHistBins = 2048;  // 11-bit radix digits
-constexpr uint32_t kFoldAbove = 2048;   // bucket size from which a radix pass folds equal digits
 constexpr int kChunk = (kKeyCap + kSelThreads - 1) / kSelThreads;  // most keys per thread held in registers
 
 // Keys per thread for a key count d held in LDS: the radix passes run one
 // unrolled histogram step per register slot, so the slot count follows d.
 __host__ __device__ constexpr int chunk_for(int d) { return d <= 4096 ? 4 : (d <= 8192 ? 8 : kChunk); }
-
-struct SelShared {
-  uint32_t hist[3 * kHistBins];   // one histogram per radix pass
-  uint32_t misc[4];
-  uint32_t wave_tot[kSelWaves][2];
-  uint32_t wave_nz[kSelWaves];
-  double energy[kSelWaves][2];
-};
 
 // Retained fraction of the energy: sum of the kept keys over the sum of all
 // keys (each thread's keys in index order, then a butterfly inside each
@@ -167,36 +143,9 @@ __device__ void write_retained(double kept, double total, SelShared& sh, float* 
   }
 }
 
-// Block-wide inclusive scan of two counters (1024 threads, fixed order).
 __device__ __forceinline__ void block_incl_scan2(uint32_t& a, uint32_t& b, SelShared& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  a = wave_incl_scan(a);
-  b = wave_incl_scan(b);
-  if (lane == 63) {
-    sh.wave_tot[wave][0] = a;
-    sh.wave_tot[wave][1] = b;
-  }
-  __syncthreads();
-  uint32_t pa = 0, pb = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const uint32_t ta = sh.wave_tot[w][0], tb = sh.wave_tot[w][1];
-    if (w < wave) {
-      pa += ta;
-      pb += tb;
-    }
-  }
-  a += pa;
-  b += pb;
+  sel::block_incl_scan2<kSelThreads>(a, b, sh);
 }
-
-// The keys of one thread: a contiguous index chunk [j0, j0 + cnt), kept in
-// registers across all radix passes and the compaction.
-template <int CH>
-struct KeyChunk {
-  uint32_t key[CH];
-  int j0, cnt;
-};
 
 template <int CH>
 __device__ __forceinline__ void load_chunk(const uint32_t* keys, int d, KeyChunk<CH>& kc) {
@@ -207,178 +156,16 @@ __device__ __forceinline__ void load_chunk(const uint32_t* keys, int d, KeyChunk
   for (int i = 0; i < CH; ++i) kc.key[i] = i < kc.cnt ? keys[kc.j0 + i] : 0u;
 }
 
-// Histogram increments.  hist_add_lane: one LDS atomic per active lane, the
-// cheapest form while the lanes' digits are spread over many bins.
-// hist_add: the lanes that share the first active lane's digit are folded
-// into one atomic, for buckets where ties are likely (a run of equal keys
-// sends every lane of a wave to one address, and per-lane atomics on one
-// address serialize); it costs about twice the instructions per key.
-__device__ __forceinline__ void hist_add_lane(uint32_t* hist, bool m, uint32_t dig) {
-  if (m) atomicAdd(&hist[dig], 1u);
-}
-
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool m, uint32_t dig) {
-  const uint64_t act = __ballot(m);
-  if (act == 0) return;
-  const int first = __ffsll((unsigned long long)act) - 1;
-  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)dig, first);
-  const uint64_t same = __ballot(m && dig == d0);
-  if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
-  if (m && dig != d0) atomicAdd(&hist[dig], 1u);
-}
-
-// Finds the k-th largest key: on return *T is its value and *rem the number
-// of keys equal to T that belong to the kept set (the lowest-indexed ones;
-// 0xffffffff means every key equal to T is kept).  MSB-first radix passes
-// with integer LDS histograms of up to 11-bit digits, over the offsets
-// key - kmin of the nonzero keys: the first digit starts at the top bit of
-// kmax - kmin, so the first histogram spreads over 1024-2048 buckets
-// whatever the keys' magnitude (fp32 energies of a few octaves would share
-// their sign and upper exponent bits and crowd a few dozen buckets).  All
-// histograms are cleared up front, and the passes stop as soon as the
-// bucket holding the k-th key is kept whole.  Zero keys (energies that are
-// exactly zero or underflowed, often thousands of ties) stay out of the
-// histograms: when k exceeds the nonzero count the answer is T = 0 at once,
-// otherwise no zero key can be kept.  The first pass adds one atomic per
-// lane; a later pass folds equal digits only when the bucket it refines
-// holds more than kFoldAbove keys (a bucket that large makes ties likely).
 template <int CH>
-__device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, SelShared& sh, uint32_t* T, uint32_t* rem_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t k_min = 0xffffffffu, k_max = 0u, nz = 0u;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const uint32_t key = kc.key[i];
-    const bool live = i < kc.cnt && key != 0u;
-    k_min = min(k_min, live ? key : 0xffffffffu);
-    k_max = max(k_max, live ? key : 0u);
-    nz += live;
-  }
-  k_min = (uint32_t)__builtin_amdgcn_readlane(
-      (int)wave_scan_dpp(k_min, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); }), 63);
-  k_max = (uint32_t)__builtin_amdgcn_readlane(
-      (int)wave_scan_dpp(k_max, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }), 63);
-  nz = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(nz), 63);
-  for (int i = tid; i < 3 * kHistBins; i += kSelThreads) sh.hist[i] = 0;
-  if (lane == 0) {
-    sh.wave_tot[wave][0] = k_min;
-    sh.wave_tot[wave][1] = k_max;
-    sh.wave_nz[wave] = nz;
-  }
-  __syncthreads();
-  k_min = 0xffffffffu;
-  k_max = 0u;
-  nz = 0u;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    k_min = min(k_min, sh.wave_tot[w][0]);
-    k_max = max(k_max, sh.wave_tot[w][1]);
-    nz += sh.wave_nz[w];
-  }
-  // every wave has read wave_tot before any of them returns early: the
-  // compaction's block scan writes wave_tot next, and a wave that is still
-  // reading here would otherwise take a scan total for kmin (all nonzero
-  // keys equal, or k above the nonzero count, both skip the radix passes)
-  __syncthreads();
-  if ((uint32_t)k > nz) {
-    // every nonzero key is kept, and the lowest-indexed zeros fill up to k
-    *T = 0u;
-    *rem_out = (uint32_t)k - nz;
-    return;
-  }
-  // from here k <= nz, so kmin <= kmax are keys; offsets lie in [0, span]
-  const uint32_t span = k_max - k_min;
-  int hi = span ? 32 - __clz(span) : 0;      // offset bits still to resolve
-  uint32_t mask = hi == 32 ? 0u : ~((1u << hi) - 1u);
-  uint32_t prefix = 0u;                      // resolved offset bits
-  uint32_t rem = (uint32_t)k;
-  bool fold = false;
-  for (int pass = 0; hi > 0; ++pass) {
-    const int w = hi < 11 ? hi : 11;
-    const int shift = hi - w;
-    const uint32_t nb = 1u << w;
-    uint32_t* hist = sh.hist + pass * kHistBins;
-    if (fold) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const uint32_t key = kc.key[i], off = key - k_min;
-        hist_add(hist, i < kc.cnt && key != 0u && (off & mask) == prefix, (off >> shift) & (nb - 1));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const uint32_t key = kc.key[i], off = key - k_min;
-        hist_add_lane(hist, i < kc.cnt && key != 0u && (off & mask) == prefix, (off >> shift) & (nb - 1));
-      }
-    }
-    __syncthreads();
-    // thread t owns the buckets nb-1-2t and nb-2-2t, counted from the top
-    const int b0 = (int)nb - 1 - 2 * tid, b1 = b0 - 1;
-    const uint32_t c0 = b0 >= 0 ? hist[b0] : 0u, c1 = b1 >= 0 ? hist[b1] : 0u;
-    uint32_t incl = c0 + c1, dummy = 0;
-    block_incl_scan2(incl, dummy, sh);
-    const uint32_t excl = incl - (c0 + c1);
-    if (excl < rem && rem <= incl) {
-      if (excl + c0 >= rem) {
-        sh.misc[0] = (uint32_t)b0;
-        sh.misc[1] = rem - excl;
-        sh.misc[2] = c0;
-      } else {
-        sh.misc[0] = (uint32_t)b1;
-        sh.misc[1] = rem - excl - c0;
-        sh.misc[2] = c1;
-      }
-    }
-    __syncthreads();
-    const uint32_t b = sh.misc[0], cnt = sh.misc[2];
-    rem = sh.misc[1];
-    prefix |= b << shift;
-    mask |= (nb - 1) << shift;
-    hi = shift;
-    fold = cnt > kFoldAbove;
-    if (cnt == rem) {
-      // every key of this bucket is kept: keep all keys >= its lowest value
-      // (at least kmin, so no zero key)
-      *T = k_min + prefix;
-      *rem_out = 0xffffffffu;
-      return;
-    }
-  }
-  *T = k_min + prefix;
-  *rem_out = rem;
+__device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, SelShared& sh, uint32_t* T,
+                                                uint32_t* rem_out) {
+  sel::radix_threshold<kSelThreads, CH>(kc, k, sh, T, rem_out);
 }
 
-// Ordered compaction: every thread owns a contiguous index chunk; a block
-// scan of (#greater, #equal) fixes each thread's output position, so the kept
-// indices come out ascending.  emit(take, pos, j, key) is called once for
-// every index j of the chunk, in order; pos is the output position when take.
 template <int CH, typename Emit>
-__device__ __forceinline__ void compact_ascending(const KeyChunk<CH>& kc, uint32_t T, uint32_t rem, SelShared& sh, Emit emit) {
-  uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    if (i < kc.cnt) {
-      n_gt += kc.key[i] > T;
-      n_eq += kc.key[i] == T;
-    }
-  }
-  uint32_t i_gt = n_gt, i_eq = n_eq;
-  block_incl_scan2(i_gt, i_eq, sh);
-  uint32_t pos = (i_gt - n_gt) + min(i_eq - n_eq, rem);
-  uint32_t eq_seen = i_eq - n_eq;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    if (i < kc.cnt) {
-      const uint32_t key = kc.key[i];
-      bool take = key > T;
-      if (key == T) {
-        take = eq_seen < rem;
-        ++eq_seen;
-      }
-      emit(take, pos, kc.j0 + i, key);
-      pos += take;
-    }
-  }
+__device__ __forceinline__ void compact_ascending(const KeyChunk<CH>& kc, uint32_t T, uint32_t rem, SelShared& sh,
+                                                  Emit emit) {
+  sel::compact_ascending<kSelThreads, CH>(kc, T, rem, sh, emit);
 }
 
 // Same selection for key arrays too large for the register chunks (d above
@@ -581,9 +368,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
     // now live in registers, so s_keys takes the keep flags
     KeyChunk<CH> kc;
     load_chunk(keys, d, kc);
-    radix_threshold(kc, k, sh, &T, &rem);
+    // (the selection's first barrier orders these reads of s_keys before
+    // the compaction's writes of the keep flags)
     if (retained || mo) {
-      compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t key) {
+      sel::select_ascending<kSelThreads, CH>(kc, k, sh, [&](bool take, uint32_t pos, int j, uint32_t key) {
         if (take) s_out[pos] = j;
         s_keys[j] = take;
         const double q = (double)__uint_as_float(key);
@@ -591,7 +379,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
         e_kept += take ? q : 0.0;
       });
     } else {
-      compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
+      sel::select_ascending<kSelThreads, CH>(kc, k, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
         if (take) s_out[pos] = j;
       });
     }
@@ -786,8 +574,7 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
   if constexpr (LDS_KEYS) {
     KeyChunk<CH> kc;
     load_chunk(keys, d, kc);
-    radix_threshold(kc, k, sh, &T, &rem);
-    compact_ascending(kc, T, rem, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
+    sel::select_ascending<kSelThreads, CH>(kc, k, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
       if (take) s_out[pos] = j;
     });
     __syncthreads();

@@ -287,6 +287,16 @@ def test_decode_rows(dev, n):
     check_matmul(w.tensors["A"], w.tensors["B"], 1.0, dev, TOL_BF16)
 
 
+@pytest.mark.parametrize("n,d", [(8, 1001), (3, 4104), (16, 8192), (8, 9000)])
+def test_decode_row_widths(dev, n, d):
+    # the GEMV ranks the columns itself with 16 keys per thread (d <= 4096;
+    # d = 1001 takes the element loads), 32 keys (d <= 8192); wider rows run
+    # the selection kernel first
+    w = synth.decode_qkv(n=n, d=d, m=520, rho=0.7)
+    for rho in (0.7, 1.0):
+        check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16)
+
+
 def test_select_scores(dev):
     w = synth.mlp_down(n=200, d=700, m=8, rhos=(0.4,))
     A = w.tensors["A"]
