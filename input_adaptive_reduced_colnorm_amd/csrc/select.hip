@@ -111,7 +111,9 @@ using sel::kHistBins;
 using sel::KeyChunk;
 using SelShared = sel::Shared<kSelWaves>;
 
-constexpr int kChunk = (kKeyCap + kSelThreads - 1) / kSelThreads;  // most keys per thread held in registers
+// most keys per thread held in registers (a multiple of 4, so that a
+// thread's chunk is whole 16-byte groups of split partials)
+constexpr int kChunk = ((kKeyCap + kSelThreads - 1) / kSelThreads + 3) / 4 * 4;
 
 // Keys per thread for a key count d held in LDS: the radix passes run one
 // unrolled histogram step per register slot, so the slot count follows d.
@@ -244,6 +246,56 @@ __device__ __forceinline__ void compact_ascending_big(const uint32_t* keys, int 
   }
 }
 
+// The keys of one thread's contiguous chunk of columns, summed over the
+// split partials in split order straight into registers: the chunk is a
+// whole number of 16-byte groups when d % 4 == 0 (c = ceil(d / 1024)
+// rounded up to 4, at most CH), else single columns (c = ceil(d / 1024)).
+// Two splits' loads are issued before either is added.
+template <int CH>
+__device__ __forceinline__ void sum_chunk(const float* P, int splits, int d, KeyChunk<CH>& kc, float* scores) {
+  const bool vec = d % 4 == 0;
+  int c = (d + kSelThreads - 1) / kSelThreads;
+  if (vec) c = (c + 3) / 4 * 4;
+  kc.j0 = min(d, (int)threadIdx.x * c);
+  kc.cnt = min(c, d - kc.j0);
+  float q[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) q[i] = 0.f;
+  if (vec) {
+    constexpr int V = CH / 4;
+    for (int s0 = 0; s0 < splits; s0 += 2) {
+      f32x4 v[2][V];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < V; ++u)
+          v[t][u] = (s0 + t < splits && 4 * u < kc.cnt)
+                        ? *(const f32x4*)(P + (size_t)(s0 + t) * d + kc.j0 + 4 * u)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        if (s0 + t < splits)
+#pragma unroll
+          for (int u = 0; u < V; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[4 * u + e] += v[t][u][e];
+    }
+  } else {
+    for (int s0 = 0; s0 < splits; ++s0) {
+      float v[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) v[i] = i < kc.cnt ? P[(size_t)s0 * d + kc.j0 + i] : 0.f;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) q[i] += v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    kc.key[i] = i < kc.cnt ? __float_as_uint(q[i]) : 0u;
+    if (scores && i < kc.cnt) scores[kc.j0 + i] = sqrtf(q[i]);
+  }
+}
+
 // CH: keys per thread in registers (chunk_for(d)), or 0 for keys in global
 // scratch (d above the LDS key capacity).
 template <int CH>
@@ -256,86 +308,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
                                                            uint32_t* __restrict__ gkeys) {
   constexpr bool LDS_KEYS = CH > 0;
   __shared__ uint32_t s_keys[LDS_KEYS ? kKeyCap : 1];
-  __shared__ int32_t s_out[LDS_KEYS ? kKeyCap : 1];
+  __shared__ __attribute__((aligned(16))) int32_t s_out[LDS_KEYS ? kKeyCap : 1];
   __shared__ SelShared sh;
   const int head = blockIdx.x;
   const float* P = partial + (size_t)head * splits * d;
   uint32_t* keys = LDS_KEYS ? s_keys : gkeys + (size_t)head * d;
+  KeyChunk<LDS_KEYS ? CH : 1> kc;
   if constexpr (LDS_KEYS) {
-    if (d % 4 == 0) {
-      // 4 columns per 16-byte load; a thread takes up to four 4-column
-      // groups at once and issues the loads of all of them for up to six
-      // splits before adding any (each column in split order)
-      constexpr int G = 4, S = 6;
-      const int d4 = d / 4;
-      const f32x4* P4 = (const f32x4*)P;
-      for (int jb = threadIdx.x; jb < d4; jb += G * kSelThreads) {
-        f32x4 q[G];
-#pragma unroll
-        for (int u = 0; u < G; ++u) q[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < splits; s0 += S) {
-          f32x4 v[G][S];
-#pragma unroll
-          for (int u = 0; u < G; ++u)
-#pragma unroll
-            for (int t = 0; t < S; ++t) {
-              const int j4 = jb + u * kSelThreads;
-              v[u][t] = (s0 + t < splits && j4 < d4) ? P4[(size_t)(s0 + t) * d4 + j4] : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-          for (int u = 0; u < G; ++u)
-#pragma unroll
-            for (int t = 0; t < S; ++t)
-              if (s0 + t < splits) {
-                q[u][0] += v[u][t][0];
-                q[u][1] += v[u][t][1];
-                q[u][2] += v[u][t][2];
-                q[u][3] += v[u][t][3];
-              }
-        }
-#pragma unroll
-        for (int u = 0; u < G; ++u) {
-          const int j4 = jb + u * kSelThreads;
-          if (j4 < d4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              keys[4 * j4 + e] = __float_as_uint(q[u][e]);
-              if (scores) scores[(size_t)head * scores_hs + 4 * j4 + e] = sqrtf(q[u][e]);
-            }
-          }
-        }
-      }
-    } else {
-      // each thread owns columns tid + 1024 c; the loads of four splits are
-      // issued together before they are added (in split order)
-      constexpr int NC = CH > 0 ? CH : 1;
-      float q[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) q[c] = 0.f;
-      for (int s0 = 0; s0 < splits; s0 += 4) {
-        float v[4][NC];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int j = threadIdx.x + c * kSelThreads;
-            v[u][c] = (s0 + u < splits && j < d) ? P[(size_t)(s0 + u) * d + j] : 0.f;
-          }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (s0 + u < splits)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) q[c] += v[u][c];
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int j = threadIdx.x + c * kSelThreads;
-        if (j < d) {
-          keys[j] = __float_as_uint(q[c]);
-          if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q[c]);
-        }
-      }
-    }
+    sum_chunk(P, splits, d, kc, scores ? scores + (size_t)head * scores_hs : nullptr);
   } else {
     for (int j = threadIdx.x; j < d; j += kSelThreads) {
       float q = 0.f;
@@ -343,9 +323,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
       keys[j] = __float_as_uint(q);
       if (scores) scores[(size_t)head * scores_hs + j] = sqrtf(q);
     }
+    __threadfence_block();
+    __syncthreads();
   }
-  if (!LDS_KEYS) __threadfence_block();
-  __syncthreads();
   int32_t* out = idx + (size_t)head * idx_hs;
   int32_t* po = pad ? pad + (size_t)head * pad_hs : nullptr;
   if (po)
@@ -364,12 +344,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
   };
   uint32_t T, rem;
   if constexpr (LDS_KEYS) {
-    // the kept list is assembled in LDS and written out coalesced; the keys
-    // now live in registers, so s_keys takes the keep flags
-    KeyChunk<CH> kc;
-    load_chunk(keys, d, kc);
-    // (the selection's first barrier orders these reads of s_keys before
-    // the compaction's writes of the keep flags)
+    // the keys live in registers; the kept list is assembled in LDS and
+    // written out coalesced, and s_keys takes the keep flags
     if (retained || mo) {
       sel::select_ascending<kSelThreads, CH>(kc, k, sh, [&](bool take, uint32_t pos, int j, uint32_t key) {
         if (take) s_out[pos] = j;
@@ -384,7 +360,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
       });
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < k; t += kSelThreads) {
+    int t_done = 0;
+    if ((((uintptr_t)out | (uintptr_t)(po ? po : out)) & 15) == 0) {
+      // 16-byte pieces of the list, then the tail
+      const int k4 = k / 4;
+      for (int t4 = threadIdx.x; t4 < k4; t4 += kSelThreads) {
+        const i32x4 v = *(const i32x4*)(s_out + 4 * t4);
+        *(i32x4*)(out + 4 * t4) = v;
+        if (po) *(i32x4*)(po + 4 * t4) = v;
+      }
+      t_done = 4 * k4;
+    }
+    for (int t = t_done + threadIdx.x; t < k; t += kSelThreads) {
       const int j = s_out[t];
       out[t] = j;
       if (po) po[t] = j;
