@@ -128,6 +128,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
     g.A = (const char*)g.A + (size_t)bz * g.a_bs * (A_BF16 ? 2 : 4);
     g.B = (const char*)g.B + (size_t)(bz / g.b_group) * g.b_bs * BE;
     if (g.idx) g.idx += (size_t)bz * g.idx_bs;
+    if (g.idx_out) g.idx_out += (size_t)bz * g.idx_bs;
     g.Y = (char*)g.Y + (size_t)bz * g.y_bs * (g.y_bf16 ? 2 : 4);
     g.partial += (size_t)bz * g.splits * g.n * g.m;
   }

@@ -988,6 +988,8 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
   int32_t* ipad = packed ? (int32_t*)(ws + p.off_ipad) : nullptr;
   int32_t* kmask = p.masked ? (int32_t*)(ws + p.off_mask) : nullptr;
   uint16_t* pp = packed ? (uint16_t*)(ws + p.off_p) : nullptr;
+  // decode at rho = 1: the GEMV writes the identity lists (no iota launch)
+  const bool gemv_lists = p.decode && p.all;
   if (p.use_sel) {
     const float* partial = energy;
     if (!energy) {
@@ -999,8 +1001,10 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
     RMM_LAUNCH(launch_topk(partial, (int)h, p.sel.splits, (int)tk, (int)p.k, idx, p.k, ipad, p.k_pad,
                            ipad ? (int)p.k_pad : 0, nullptr, tk,
                            p.sel.gkeys ? (uint32_t*)(ws + p.sel.off_gkeys) : nullptr, s, kmask, tk));
-  } else {
+  } else if (!gemv_lists) {
     RMM_LAUNCH(launch_iota(idx, p.k, (int)h, (int)tk, ipad, ipad ? p.k_pad : 0, ipad ? (int)p.k_pad : 0, s));
+    RMM_LAUNCH(mk.mark(1));
+  } else {
     RMM_LAUNCH(mk.mark(1));
   }
   RMM_LAUNCH(mk.mark(2));
@@ -1024,6 +1028,7 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
     g.A = P; g.a_bf16 = !p_f32; g.lda = p_ts; g.a_bs = p_hs;
     g.B = (const uint16_t*)V; g.ldb = v_ts; g.b_bs = v_hs; g.b_group = group;
     g.idx = p.all ? nullptr : idx; g.idx_bs = p.k;
+    g.idx_out = gemv_lists ? idx : nullptr;
     g.k = (int)p.k; g.n = (int)tq; g.m = (int)dv;
     g.partial = (float*)(ws + p.off_gpart); g.splits = p.gemv_splits;
     g.Y = O; g.y_bf16 = o_dtype == RMM_BF16; g.ldy = dv; g.y_bs = tq * dv;

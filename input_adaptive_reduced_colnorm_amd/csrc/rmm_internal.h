@@ -101,8 +101,9 @@ hipError_t launch_decode_select(const void* A, bool a_bf16, int64_t lda, int n, 
 // the sum over the kept rows is complete.
 // select: the kernel ranks the d columns of A itself (batch 1, d <=
 // gemv_select_max_d(), idx must be null) and keeps the k largest column
-// energies; idx_out (optional, [k]) receives the ascending kept list (the
-// identity list when idx is null and select is false).
+// energies; idx_out (optional, [batch][k], stride idx_bs) receives the
+// ascending kept lists (the identity lists when idx is null and select is
+// false).
 struct GemvArgs {
   const void* A; bool a_bf16; int64_t lda;
   const void* B; int64_t ldb;
