@@ -179,8 +179,19 @@ class MatmulOp:
         w = {"gemm": ("F", 2.0 * n * k * m)}
         if k < d:
             w["score"] = ("B", n * d * 2)
-            w["pack"] = ("B", 2 * n * k * 2)
+            if self.fused(rho):
+                # one launch ranks the keys and gathers: whole rows of A in,
+                # the kept columns out (stage events 1 -> 2 bracket it)
+                w["topk"] = ("B", n * d * 2 + n * k * 2)
+            else:
+                w["pack"] = ("B", 2 * n * k * 2)
         return w
+
+    def fused(self, rho):
+        """Whether the prefill product at this rho ranks and gathers in one
+        launch (the library's rule for a contiguous bf16 A: at most 15360
+        columns, whole 16-byte row pieces)."""
+        return (not self.decode) and self.ks[rho] < self.d and self.d <= 15360 and self.d % 8 == 0
 
     def roofline_stage(self):
         return "gemm"
@@ -287,7 +298,12 @@ class MatmulW8Op(MatmulOp):
         w = {"gemm": ("F", 2.0 * n * k * m)}
         if k < d:
             w["score"] = ("B", n * d * 2)
-            w["pack"] = ("B", 2 * n * k * 2)
+            if self.fused(rho):
+                # one launch ranks the keys and gathers: whole rows of A in,
+                # the kept columns out (stage events 1 -> 2 bracket it)
+                w["topk"] = ("B", n * d * 2 + n * k * 2)
+            else:
+                w["pack"] = ("B", 2 * n * k * 2)
         return w
 
     def roofline_kernel(self):
@@ -711,7 +727,15 @@ def run(args, op):
                 if s in work:
                     for key, v in _rate(*work[s], mean[r][s]).items():
                         row[f"{s}_{key}"] = v
-        if "score" in work and work["score"][0] == "B" and "topk" in names:
+        fused = getattr(op, "fused", None) and op.fused(r)
+        if fused:
+            # the TopK stage is the fused ranking + gather launch
+            row = {(f"select_pack{k[4:]}" if k.startswith("topk") else k): v for k, v in row.items()}
+            sel_us = mean[r]["score"] + mean[r]["topk"]
+            row["selection_gather_us"] = round(sel_us, 2)
+            for key, v in _rate("B", work["score"][1] + work["topk"][1], sel_us).items():
+                row[f"selection_gather_{key}"] = v
+        elif "score" in work and work["score"][0] == "B" and "topk" in names:
             # the whole selection (energies + TopK) against the bytes of A it reads
             sel_us = mean[r]["score"] + mean[r]["topk"]
             row["selection_us"] = round(sel_us, 2)

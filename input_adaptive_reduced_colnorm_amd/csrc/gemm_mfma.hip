@@ -67,35 +67,6 @@ __device__ __forceinline__ TileCoord tile_of(int bid, int tiles_m, int tiles_n, 
   return c;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from a buffer straight into LDS: lane l writes LDS bytes
-// [dst + 16 l, dst + 16 l + 16) (dst uniform across the wave); an offset past
-// the buffer end writes zeros.  Completion is counted by vmcnt.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
-}
-
-// wait until at most N vector-memory operations of this wave are in flight
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier of the main loop with direct loads in flight: this
-// wave's LDS stores are complete (lgkmcnt(0); the direct loads that must
-// land are waited for by the caller), then s_barrier.  A release fence (as
-// in __syncthreads) would also wait for the direct loads of the tile after
-// next; the empty asm statements only keep the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt at their maxima
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }

@@ -105,6 +105,22 @@ hipError_t run_select(const SelPlan& sp, char* ws, const void* A, bool bf16, int
                      sp.gkeys ? (uint32_t*)(ws + sp.off_gkeys) : nullptr, s);
 }
 
+// Energies, then the selection and the gather of the kept columns in one
+// launch (single bf16 matrix, shapes that select_pack_fits accepts).  Stage
+// events 2 and 3 both close the fused launch.
+hipError_t run_select_pack(const SelPlan& sp, char* ws, const void* A, int64_t lda, int64_t n, int64_t d, int64_t k,
+                           int64_t k_pad, int32_t* idx, int32_t* ipad, uint16_t* pk, hipStream_t s, const Marks& mk) {
+  float* partial = (float*)(ws + sp.off_partial);
+  hipError_t e = launch_colnorm(A, true, 0, lda, 1, (int)n, (int)d, sp.splits, partial, s);
+  if (e == hipSuccess) e = mk.mark(1);
+  if (e == hipSuccess)
+    e = launch_select_pack(partial, sp.splits, (const uint16_t*)A, lda, (int)n, (int)d, (int)k, (int)k_pad, idx, ipad,
+                           pk, s);
+  if (e == hipSuccess) e = mk.mark(2);
+  if (e == hipSuccess) e = mk.mark(3);
+  return e;
+}
+
 // ---------------------------------------------------------------------------
 // matmul plan
 // ---------------------------------------------------------------------------
@@ -404,16 +420,20 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
     }
     case MatPath::kMfmaPacked: {
       int32_t* ipad = (int32_t*)(ws + p.off_ipad);
-      if (p.use_sel) {
-        RMM_LAUNCH(run_select(p.sel, ws, A, true, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk, ipad, p.k_pad));
-      } else {
-        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, ipad, 0, (int)p.k_pad, s));
-        RMM_LAUNCH(mk.mark(1));
-      }
-      RMM_LAUNCH(mk.mark(2));
       uint16_t* pk = (uint16_t*)(ws + p.off_pack);
-      RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, idx, p.k, (int)p.k, (int)p.k_pad, 1, (int)n, pk, 0, s));
-      RMM_LAUNCH(mk.mark(3));
+      if (p.use_sel && select_pack_fits(A, lda, d)) {
+        RMM_LAUNCH(run_select_pack(p.sel, ws, A, lda, n, d, p.k, p.k_pad, idx, ipad, pk, s, mk));
+      } else {
+        if (p.use_sel) {
+          RMM_LAUNCH(run_select(p.sel, ws, A, true, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk, ipad, p.k_pad));
+        } else {
+          RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, ipad, 0, (int)p.k_pad, s));
+          RMM_LAUNCH(mk.mark(1));
+        }
+        RMM_LAUNCH(mk.mark(2));
+        RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, idx, p.k, (int)p.k, (int)p.k_pad, 1, (int)n, pk, 0, s));
+        RMM_LAUNCH(mk.mark(3));
+      }
       GemmArgs g{};
       g.A = pk; g.a_bs = 0; g.lda = p.k_pad;
       g.B = (const uint16_t*)B; g.b_bs = 0; g.ldb = ldb; g.b_group = 1;
@@ -542,16 +562,20 @@ rmm_status_t matmul_w8_impl(const void* A, int a_dtype, const int8_t* Bq, const 
     g.a_bytes = (uint32_t)(((n - 1) * lda + d) * 2);
   } else {
     int32_t* ipad = (int32_t*)(ws + p.off_ipad);
-    if (p.use_sel) {
-      RMM_LAUNCH(run_select(p.sel, ws, A, true, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk, ipad, p.k_pad));
-    } else {
-      RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, ipad, 0, (int)p.k_pad, s));
-      RMM_LAUNCH(mk.mark(1));
-    }
-    RMM_LAUNCH(mk.mark(2));
     uint16_t* pk = (uint16_t*)(ws + p.off_pack);
-    RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, idx, p.k, (int)p.k, (int)p.k_pad, 1, (int)n, pk, 0, s));
-    RMM_LAUNCH(mk.mark(3));
+    if (p.use_sel && select_pack_fits(A, lda, d)) {
+      RMM_LAUNCH(run_select_pack(p.sel, ws, A, lda, n, d, p.k, p.k_pad, idx, ipad, pk, s, mk));
+    } else {
+      if (p.use_sel) {
+        RMM_LAUNCH(run_select(p.sel, ws, A, true, 0, lda, 1, n, d, p.k, idx, p.k, nullptr, s, &mk, ipad, p.k_pad));
+      } else {
+        RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, ipad, 0, (int)p.k_pad, s));
+        RMM_LAUNCH(mk.mark(1));
+      }
+      RMM_LAUNCH(mk.mark(2));
+      RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, idx, p.k, (int)p.k, (int)p.k_pad, 1, (int)n, pk, 0, s));
+      RMM_LAUNCH(mk.mark(3));
+    }
     g.A = pk; g.a_bs = 0; g.lda = p.k_pad;
     g.idx = ipad; g.idx_bs = 0;
     g.K = (int)p.k_pad;

@@ -33,6 +33,65 @@ __device__ __forceinline__ i32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes LDS bytes
+// [dst + 16 l, dst + 16 l + 16) (dst uniform across the wave); an offset past
+// the buffer end writes zeros.  Completion is counted by vmcnt.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+// The same direct load issued from inline asm, for loops whose LDS reads
+// must not wait for it: the compiler makes every LDS access wait for the
+// direct loads it knows of (it cannot tell which LDS bytes they write), so
+// a prefetch it sees would drain before each read.  The compiler neither
+// sees nor counts this load; that only makes its own vmcnt waits stricter
+// (the load lands in the in-order queue beside the ones it counts), and the
+// caller orders the load's LDS bytes with wait_vmcnt and a barrier.  rsrc:
+// buffer descriptor words (wave-uniform); lds: LDS byte address of lane 0
+// (wave-uniform).  The nops cover the M0 and SGPR-to-VMEM read hazards.
+__device__ __forceinline__ void load_lds16_async(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// Descriptor words of a raw buffer of `bytes` bytes at `base` (as make_rsrc).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, kBufferFlags};
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS
+// accesses are complete (lgkmcnt(0); direct loads that must land are waited
+// for by the caller), then s_barrier.  A release fence (as in
+// __syncthreads) would also wait for every vector-memory access still in
+// flight, prefetches included; the empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // A row piece of 8 B-matrix elements while in flight: 8 bf16 (16 bytes) or
 // 8 int8 weights (8 bytes).
 template <bool I8> struct RowPiece { typedef i32x4 type; };

@@ -27,6 +27,17 @@ hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k
                        int32_t* mask = nullptr, int64_t mask_hs = 0, float* retained = nullptr);
 int topk_lds_capacity();
 
+// Selection and gather in one launch for a single bf16 matrix A (n x d, row
+// stride lda): from the summed partials it writes the ascending kept list
+// idx[0..k), the same list padded with -1 to k_pad entries (pad), and the
+// panel out[r][t] = A[r][idx[t]] for t < k, 0 for k <= t < k_pad (out
+// 16-byte aligned, k_pad a multiple of 8).  select_pack_fits tells whether
+// the shape and alignment allow it (d within the LDS key capacity, rows
+// whole 16-byte pieces).
+bool select_pack_fits(const void* A, int64_t lda, int64_t d);
+hipError_t launch_select_pack(const float* partial, int splits, const uint16_t* A, int64_t lda, int n, int d, int k,
+                              int k_pad, int32_t* idx, int32_t* pad, uint16_t* out, hipStream_t s);
+
 // Writes idx[h][t] = t for t < d (the rho = 1 selection), and optionally
 // the padded copy pad[h][t] (t < k_pad, -1 past d).
 hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* pad, int64_t pad_hs, int k_pad,

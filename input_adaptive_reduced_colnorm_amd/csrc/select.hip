@@ -574,6 +574,130 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Selection fused with the gather of the kept columns (the prefill products).
+// One 1024-thread workgroup per compute unit: each sums the split partials
+// and ranks the keys as topk_kernel does, so that every workgroup holds the
+// same ascending kept list, as 16-bit column indices in LDS padded to k_pad
+// with the index z of a zero slot.  It then streams its block of rows of A:
+// each row goes whole from HBM into an LDS row buffer by direct 16-byte
+// loads (D rows in flight, the first D issued before the ranking so that
+// they land while it runs), and each lane gathers 8 consecutive kept
+// positions from LDS and writes them as one 16-byte piece of the
+// K-contiguous panel.  Whole-row loads avoid the address rate of 2-byte
+// global gathers, and the ranking repeated per workgroup (a few microseconds
+// of VALU work) replaces a single-workgroup launch that the whole chip
+// waited for.  Needs d <= kKeyCap, d % 8 == 0, lda % 8 == 0 and A 16-byte
+// aligned (select_pack_fits).
+//
+// Row buffers: NB = D + 1, row i in buffer i % NB, so the buffer refilled
+// for row i + D held row i - 1, which every thread finished reading before
+// the barrier of row i.  The ranking's scratch lies in buffer D (and past
+// it), which first receives a row after the ranking.  Rows past the block
+// are loaded through an empty buffer resource (no memory access, zeros),
+// so every wave issues the same loads per row and the waits count them.
+// ---------------------------------------------------------------------------
+constexpr int kSpGroups = 256;   // workgroups: one per compute unit
+
+__host__ __device__ constexpr int sp_row_cap(int pr) { return (pr == 1 ? 8192 : kKeyCap) + 8; }
+
+// CH: keys per thread; PR: 16-byte pieces of a row per thread (rows of up
+// to PR * 8192 columns); D: rows in flight.
+template <int CH, int PR, int D>
+__global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* __restrict__ partial, int splits,
+                                                                  const uint16_t* __restrict__ A, int64_t lda, int n,
+                                                                  int d, int k, int k_pad, int rows_per_wg,
+                                                                  int32_t* __restrict__ idx,
+                                                                  int32_t* __restrict__ pad,
+                                                                  uint16_t* __restrict__ out) {
+  constexpr int NB = D + 1;
+  constexpr int RC = sp_row_cap(PR);   // elements per row buffer (16-byte multiple)
+  constexpr int LC = RC - 8;           // kept list capacity
+  constexpr size_t kRowsBytes = (size_t)NB * RC * 2;
+  constexpr size_t kSelEnd = (size_t)D * RC * 2 + sizeof(SelShared);
+  constexpr size_t kStage = kRowsBytes > kSelEnd ? kRowsBytes : kSelEnd;
+  static_assert(RC % 8 == 0, "row buffers must stay 16-byte aligned");
+  __shared__ __attribute__((aligned(16))) uint16_t s_stage[kStage / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t s_list[LC];
+  SelShared& sh = *reinterpret_cast<SelShared*>(s_stage + (size_t)D * RC);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r0 = blockIdx.x * rows_per_wg;
+  const int nr = min(n - r0, rows_per_wg);
+  const int pieces = d >> 3;                    // 16-byte pieces of a row
+  const int z = (pieces + 63) / 64 * 512;       // zero slot: past every wave's load span
+  // this wave's loads per row: load p covers pieces [1024 p + 64 wave, + 64)
+  int nload = 0;
+#pragma unroll
+  for (int p = 0; p < PR; ++p) nload += 1024 * p + 64 * wave < pieces;
+
+  const uint32_t stage0 = lds_addr(s_stage);
+  auto fetch = [&](int i) {
+    const i32x4 r = rsrc_words(A + (size_t)(r0 + min(i, nr - 1)) * lda, i < nr ? (uint32_t)d * 2u : 0u);
+    const uint32_t row = stage0 + (uint32_t)((i % NB) * RC * 2);
+#pragma unroll
+    for (int p = 0; p < PR; ++p)
+      if (1024 * p + 64 * wave < pieces)
+        load_lds16_async(r, row + 16u * (uint32_t)(1024 * p + 64 * wave), 16u * (uint32_t)(1024 * p + tid));
+  };
+
+  KeyChunk<CH> kc;
+  sum_chunk(partial, splits, d, kc, nullptr);
+#pragma unroll
+  for (int i = 0; i < D; ++i) fetch(i);
+
+  sel::select_ascending<kSelThreads, CH>(kc, k, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
+    if (take) s_list[pos] = (uint16_t)j;
+  });
+  for (int t = k + tid; t < k_pad; t += kSelThreads) s_list[t] = (uint16_t)z;
+  lds_barrier();
+
+  // the kept list and its copy padded with -1, spread over the workgroups
+  for (int t = blockIdx.x * kSelThreads + tid; t < k_pad; t += gridDim.x * kSelThreads) {
+    const int j = s_list[t];
+    if (t < k) idx[t] = j;
+    pad[t] = t < k ? j : -1;
+  }
+  if (tid < 8 * NB) s_stage[(size_t)(tid >> 3) * RC + z + (tid & 7)] = 0;
+  // this thread's output pieces g = tid + 1024 p: kept positions [8g, 8g + 8)
+  uint32_t cw[PR][4];
+#pragma unroll
+  for (int p = 0; p < PR; ++p) {
+    const int g = tid + p * kSelThreads;
+    const i32x4 v = 8 * g < k_pad ? *(const i32x4*)(s_list + 8 * g) : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cw[p][e] = (uint32_t)v[e];
+  }
+
+  uint16_t* ob = out + (size_t)r0 * k_pad;
+  for (int i = 0; i < nr; ++i) {
+    // row i's loads are followed by those of rows i + 1 .. i + D - 1
+    if (nload == PR)
+      wait_vmcnt<(D - 1) * PR>();
+    else if (PR == 2 && nload == 1)
+      wait_vmcnt<D - 1>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    fetch(i + D);
+    const uint16_t* buf = s_stage + (size_t)(i % NB) * RC;
+#pragma unroll
+    for (int p = 0; p < PR; ++p) {
+      const int g = tid + p * kSelThreads;
+      if (8 * g < k_pad) {
+        i32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (int)((uint32_t)buf[cw[p][e] & 0xffffu] | ((uint32_t)buf[cw[p][e] >> 16] << 16));
+        *(i32x4*)(ob + (size_t)i * k_pad + 8 * g) = w;
+      }
+    }
+  }
+  // no direct load may still be writing LDS when the workgroup ends
+  wait_vmcnt<0>();
+}
+
 }  // namespace
 
 int colnorm_splits(int heads, int n, int d, bool elt_bf16) {
@@ -633,6 +757,26 @@ hipError_t launch_topk(const float* partial, int heads, int splits, int d, int k
   else
     topk_kernel<0><<<heads, kSelThreads, 0, s>>>(partial, splits, d, k, idx, idx_hs, pad, pad_hs, k_pad, scores,
                                                  scores_hs, mask, mask_hs, retained, gkeys);
+  return hipGetLastError();
+}
+
+bool select_pack_fits(const void* A, int64_t lda, int64_t d) {
+  return d <= kKeyCap && d % 8 == 0 && lda % 8 == 0 && (uintptr_t)A % 16 == 0;
+}
+
+hipError_t launch_select_pack(const float* partial, int splits, const uint16_t* A, int64_t lda, int n, int d, int k,
+                              int k_pad, int32_t* idx, int32_t* pad, uint16_t* out, hipStream_t s) {
+  const int rows_per_wg = (n + kSpGroups - 1) / kSpGroups;
+  const int grid = (n + rows_per_wg - 1) / rows_per_wg;
+  if (d <= 4096)
+    select_pack_kernel<chunk_for(4096), 1, 5>
+        <<<grid, kSelThreads, 0, s>>>(partial, splits, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+  else if (d <= 8192)
+    select_pack_kernel<chunk_for(8192), 1, 5>
+        <<<grid, kSelThreads, 0, s>>>(partial, splits, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+  else
+    select_pack_kernel<kChunk, 2, 3>
+        <<<grid, kSelThreads, 0, s>>>(partial, splits, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
   return hipGetLastError();
 }
 

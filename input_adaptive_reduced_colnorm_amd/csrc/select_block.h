@@ -8,7 +8,9 @@
 // order is their value order); the k largest are kept, equal keys going to
 // the lower index, and the kept indices come out ascending ("Algorithm
 // Deep-Dive: RMM" (hackcv.com), Core Approach: TopK by the column norm).
-// Only integer LDS atomics are used, so the result is reproducible.
+// Only integer LDS atomics are used, so the result is reproducible.  The
+// helpers exchange data through LDS alone, so their barriers are LDS-only
+// (lds_barrier): loads the caller has in flight (a prefetch) keep flying.
 #pragma once
 
 #include "rmm_device.h"
@@ -64,7 +66,7 @@ __device__ __forceinline__ void block_incl_scan2(uint32_t& a, uint32_t& b, Share
     sh.wave_tot[wave][0] = a;
     sh.wave_tot[wave][1] = b;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t pa = 0, pb = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -150,7 +152,7 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
     sh.wave_tot[wave][1] = k_max;
     sh.wave_nz[wave] = nz;
   }
-  __syncthreads();
+  lds_barrier();
   k_min = 0xffffffffu;
   k_max = 0u;
   nz = 0u;
@@ -164,7 +166,7 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
   // compaction's block scan writes wave_tot next, and a wave that is still
   // reading here would otherwise take a scan total for kmin (all nonzero
   // keys equal, or k above the nonzero count, both skip the radix passes)
-  __syncthreads();
+  lds_barrier();
   if ((uint32_t)k > nz) {
     // every nonzero key is kept, and the lowest-indexed zeros fill up to k
     *T = 0u;
@@ -196,7 +198,7 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
         hist_add_lane(hist, i < kc.cnt && key != 0u && (off & mask) == prefix, (off >> shift) & (nb - 1));
       }
     }
-    __syncthreads();
+    lds_barrier();
     // thread t owns the buckets nb-1-BPT t .. nb-BPT-BPT t, counted from the top
     const int top = (int)nb - 1 - BPT * tid;
     uint32_t c[BPT], sum = 0;
@@ -222,7 +224,7 @@ __device__ __forceinline__ void radix_threshold(const KeyChunk<CH>& kc, int k, S
         run += c[i];
       }
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t b = sh.misc[0], cnt = sh.misc[2];
     rem = sh.misc[1];
     prefix |= b << shift;
@@ -285,7 +287,7 @@ __device__ __forceinline__ bool bucket_threshold(const KeyChunk<CH>& kc, int k, 
     sh.wave_tot[wave][1] = k_max;
     sh.wave_nz[wave] = nz;
   }
-  __syncthreads();
+  lds_barrier();
   k_min = 0xffffffffu;
   k_max = 0u;
   nz = 0u;
@@ -295,7 +297,7 @@ __device__ __forceinline__ bool bucket_threshold(const KeyChunk<CH>& kc, int k, 
     k_max = max(k_max, sh.wave_tot[w][1]);
     nz += sh.wave_nz[w];
   }
-  __syncthreads();   // wave_tot is rewritten below
+  lds_barrier();   // wave_tot is rewritten below
   if ((uint32_t)k > nz) return false;   // zero keys are kept: the radix path handles them
   const uint32_t span = k_max - k_min;
   const int bits = span ? 32 - __clz(span) : 0;
@@ -305,7 +307,7 @@ __device__ __forceinline__ bool bucket_threshold(const KeyChunk<CH>& kc, int k, 
     const uint32_t key = kc.key[i];
     if (i < kc.cnt && key != 0u) atomicAdd(&sh.hist[(key - k_min) >> shift], 1u);
   }
-  __syncthreads();
+  lds_barrier();
   // thread t owns buckets 4095 - BPT t down to 4096 - BPT (t + 1), read as
   // 16-byte groups (ascending in memory, so the top bucket is the last word)
   const int lo = kBucketBins - BPT * (tid + 1);
@@ -337,7 +339,7 @@ __device__ __forceinline__ bool bucket_threshold(const KeyChunk<CH>& kc, int k, 
       run += c[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t b = sh.misc[0], rem = sh.misc[1], cnt = sh.misc[2];
   if (cnt == rem) {
     // the whole bucket is kept: every key at or above its lower edge
@@ -355,7 +357,7 @@ __device__ __forceinline__ bool bucket_threshold(const KeyChunk<CH>& kc, int k, 
       sh.cand[slot] = uint2{key, (uint32_t)(kc.j0 + i)};
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < (int)cnt) {
     const uint2 me = sh.cand[tid];
     uint32_t rank = 0;
@@ -368,7 +370,7 @@ __device__ __forceinline__ bool bucket_threshold(const KeyChunk<CH>& kc, int k, 
       sh.misc[1] = me.y;
     }
   }
-  __syncthreads();
+  lds_barrier();
   *T = sh.misc[0];
   *jT = (int)sh.misc[1];
   return true;

@@ -228,6 +228,19 @@ def test_linear_k_tile_counts(dev, d):
             check_matmul(A, B, rho, dev, TOL_BF16, rows=np.arange(0, n, 7) if n > 1000 else None)
 
 
+@pytest.mark.parametrize("n,d,rho", [(17, 8, 0.5), (257, 8200, 0.9), (300, 15360, 0.999), (64, 4096, 1e-6),
+                                     (1000, 2048, 0.5), (4100, 15360, 0.7)])
+def test_fused_selection_gather_shapes(dev, n, d, rho):
+    # the one-launch selection + gather of the prefill products: one row
+    # block per workgroup (a short last block when n is not a multiple of
+    # it), rows of one 16-byte piece up to the 15360-column key capacity,
+    # waves with one or two row loads (d = 8200), k = 1 and k = d - 15
+    w = synth.mlp_down(n=n, d=d, m=72, rhos=(rho,))
+    print(f"fused selection+gather n={n} d={d} rho={rho}", flush=True)
+    rows = tile_rows(n) if n > 1000 else None
+    check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16, rows=rows)
+
+
 @pytest.mark.parametrize("n,d", [(32, 3000), (32, 9000), (8, 4096)])
 def test_radix_zero_and_tied_energies(dev, n, d):
     # integer entries give exact energies on both sides, with many ties; 40%
