@@ -143,6 +143,10 @@ class MatmulOp:
         self.idx = {r: torch.empty(self.ks[r], dtype=torch.int32, device=dev) for r in rhos}
         wsb = max(int(self.L.rmm_matmul_workspace(self.n, self.d, self.m, self.d, rmm.RMM_BF16, r)) for r in rhos)
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+        # the given-index calls get their own workspace, allocated here so
+        # that no allocation falls inside a timed region
+        wsb = max(int(self.L.rmm_matmul_idx_workspace(self.n, self.ks[r], self.m, rmm.RMM_BF16)) for r in rhos)
+        self.ws_idx = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
         self.decode = self.n <= 16
 
     def call(self, c, rho, sh, events=None):
@@ -157,10 +161,6 @@ class MatmulOp:
         """The product over the index set the last call at this rho selected
         (rmm_matmul_idx: the reuse of one selection for another projection)."""
         n, d, m, L, rmm = self.n, self.d, self.m, self.L, self.rmm
-        if not hasattr(self, "ws_idx"):
-            import torch
-            wsb = max(int(L.rmm_matmul_idx_workspace(n, self.ks[r], m, rmm.RMM_BF16)) for r in self.rhos)
-            self.ws_idx = torch.empty(max(wsb, 256), dtype=torch.uint8, device=self.Y.device)
         st = L.rmm_matmul_idx(self.As[c].data_ptr(), self.Bs[c].data_ptr(), rmm.RMM_BF16, n, d, m, d, m,
                               self.idx[rho].data_ptr(), self.ks[rho], self.Y.data_ptr(), rmm.RMM_FP32, m,
                               self.ws_idx.data_ptr(), self.ws_idx.numel(), sh)
@@ -685,6 +685,7 @@ def run(args, op):
             if rho >= 1.0:
                 continue
             op.call(j % copies, rho, sh)   # the index set of this rho
+            op.call_idx(j % copies, rho, sh)   # untimed first call
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for it in range(args.steps):

@@ -674,7 +674,8 @@ rmm_status_t rmm_matmul_idx(const void* A, const void* B, int dtype, int64_t n, 
   const bool bf16 = dtype == RMM_BF16;
   int32_t* ipad = (int32_t*)(ws + p.off_ipad);
   clear_error();
-  RMM_LAUNCH(launch_pad_index(idx, (int)k, (int)d, ipad, (int)p.k_pad, s));
+  const bool gather = p.path == MatPath::kMfmaPacked && bf16 && gather_pack_fits(A, lda, d, p.k_pad);
+  if (!gather) RMM_LAUNCH(launch_pad_index(idx, (int)k, (int)d, ipad, (int)p.k_pad, s));
   switch (p.path) {
     case MatPath::kSimt: {
       SimtArgs g{};
@@ -699,7 +700,11 @@ rmm_status_t rmm_matmul_idx(const void* A, const void* B, int dtype, int64_t n, 
     }
     default: {
       uint16_t* pk = (uint16_t*)(ws + p.off_pack);
-      RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, ipad, 0, (int)p.k_pad, (int)p.k_pad, 1, (int)n, pk, 0, s));
+      if (gather)
+        RMM_LAUNCH(launch_gather_pack(idx, (int)k, (const uint16_t*)A, lda, (int)n, (int)d, (int)p.k_pad, ipad, pk,
+                                      s));
+      else
+        RMM_LAUNCH(launch_pack(A, true, 0, lda, 1, ipad, 0, (int)p.k_pad, (int)p.k_pad, 1, (int)n, pk, 0, s));
       GemmArgs g{};
       g.A = pk; g.a_bs = 0; g.lda = p.k_pad;
       g.B = (const uint16_t*)B; g.b_bs = 0; g.ldb = ldb; g.b_group = 1;

@@ -38,6 +38,14 @@ bool select_pack_fits(const void* A, int64_t lda, int64_t d);
 hipError_t launch_select_pack(const float* partial, int splits, const uint16_t* A, int64_t lda, int n, int d, int k,
                               int k_pad, int32_t* idx, int32_t* pad, uint16_t* out, hipStream_t s);
 
+// The same gather by a caller's list: given[0..k) in any order (entries
+// outside [0, d) read as zeros), out[r][t] = A[r][given[t]] for t < k and 0
+// up to k_pad, pad[t] = given[t] if in range else -1 (k_pad entries).
+// gather_pack_fits adds k_pad <= the LDS list capacity to select_pack_fits.
+bool gather_pack_fits(const void* A, int64_t lda, int64_t d, int64_t k_pad);
+hipError_t launch_gather_pack(const int32_t* given, int k, const uint16_t* A, int64_t lda, int n, int d, int k_pad,
+                              int32_t* pad, uint16_t* out, hipStream_t s);
+
 // Writes idx[h][t] = t for t < d (the rho = 1 selection), and optionally
 // the padded copy pad[h][t] (t < k_pad, -1 past d).
 hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* pad, int64_t pad_hs, int k_pad,

@@ -601,10 +601,14 @@ constexpr int kSpGroups = 256;   // workgroups: one per compute unit
 
 __host__ __device__ constexpr int sp_row_cap(int pr) { return (pr == 1 ? 8192 : kKeyCap) + 8; }
 
-// CH: keys per thread; PR: 16-byte pieces of a row per thread (rows of up
-// to PR * 8192 columns); D: rows in flight.
-template <int CH, int PR, int D>
+// CH: keys per thread; PR: 16-byte pieces of a row per thread (rows and
+// kept lists of up to PR * 8192 entries); D: rows in flight.  RANK = false
+// gathers by a caller's list instead (`given`, k entries in any order,
+// entries outside [0, d) read as zeros; k_pad may exceed d): no ranking, no
+// idx output, and pad[t] is the entry or -1.
+template <int CH, int PR, int D, bool RANK>
 __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* __restrict__ partial, int splits,
+                                                                  const int32_t* __restrict__ given,
                                                                   const uint16_t* __restrict__ A, int64_t lda, int n,
                                                                   int d, int k, int k_pad, int rows_per_wg,
                                                                   int32_t* __restrict__ idx,
@@ -642,22 +646,36 @@ __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* _
         load_lds16_async(r, row + 16u * (uint32_t)(1024 * p + 64 * wave), 16u * (uint32_t)(1024 * p + tid));
   };
 
-  KeyChunk<CH> kc;
-  sum_chunk(partial, splits, d, kc, nullptr);
+  if constexpr (RANK) {
+    KeyChunk<CH> kc;
+    sum_chunk(partial, splits, d, kc, nullptr);
 #pragma unroll
-  for (int i = 0; i < D; ++i) fetch(i);
-
-  sel::select_ascending<kSelThreads, CH>(kc, k, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
-    if (take) s_list[pos] = (uint16_t)j;
-  });
-  for (int t = k + tid; t < k_pad; t += kSelThreads) s_list[t] = (uint16_t)z;
+    for (int i = 0; i < D; ++i) fetch(i);
+    sel::select_ascending<kSelThreads, CH>(kc, k, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
+      if (take) s_list[pos] = (uint16_t)j;
+    });
+    for (int t = k + tid; t < k_pad; t += kSelThreads) s_list[t] = (uint16_t)z;
+  } else {
+    // the list first: a wait the compiler places for these loads after the
+    // untracked row loads would also wait for the rows
+    for (int t = tid; t < k_pad; t += kSelThreads) {
+      const int j = t < k ? given[t] : -1;
+      s_list[t] = (uint16_t)((unsigned)j < (unsigned)d ? j : z);
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) fetch(i);
+  }
   lds_barrier();
 
   // the kept list and its copy padded with -1, spread over the workgroups
   for (int t = blockIdx.x * kSelThreads + tid; t < k_pad; t += gridDim.x * kSelThreads) {
     const int j = s_list[t];
-    if (t < k) idx[t] = j;
-    pad[t] = t < k ? j : -1;
+    if constexpr (RANK) {
+      if (t < k) idx[t] = j;
+      pad[t] = t < k ? j : -1;
+    } else {
+      pad[t] = j == z ? -1 : j;
+    }
   }
   if (tid < 8 * NB) s_stage[(size_t)(tid >> 3) * RC + z + (tid & 7)] = 0;
   // this thread's output pieces g = tid + 1024 p: kept positions [8g, 8g + 8)
@@ -769,14 +787,31 @@ hipError_t launch_select_pack(const float* partial, int splits, const uint16_t* 
   const int rows_per_wg = (n + kSpGroups - 1) / kSpGroups;
   const int grid = (n + rows_per_wg - 1) / rows_per_wg;
   if (d <= 4096)
-    select_pack_kernel<chunk_for(4096), 1, 5>
-        <<<grid, kSelThreads, 0, s>>>(partial, splits, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+    select_pack_kernel<chunk_for(4096), 1, 5, true><<<grid, kSelThreads, 0, s>>>(
+        partial, splits, nullptr, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
   else if (d <= 8192)
-    select_pack_kernel<chunk_for(8192), 1, 5>
-        <<<grid, kSelThreads, 0, s>>>(partial, splits, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+    select_pack_kernel<chunk_for(8192), 1, 5, true><<<grid, kSelThreads, 0, s>>>(
+        partial, splits, nullptr, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
   else
-    select_pack_kernel<kChunk, 2, 3>
-        <<<grid, kSelThreads, 0, s>>>(partial, splits, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+    select_pack_kernel<kChunk, 2, 3, true><<<grid, kSelThreads, 0, s>>>(
+        partial, splits, nullptr, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+  return hipGetLastError();
+}
+
+bool gather_pack_fits(const void* A, int64_t lda, int64_t d, int64_t k_pad) {
+  return select_pack_fits(A, lda, d) && k_pad <= kKeyCap;
+}
+
+hipError_t launch_gather_pack(const int32_t* given, int k, const uint16_t* A, int64_t lda, int n, int d, int k_pad,
+                              int32_t* pad, uint16_t* out, hipStream_t s) {
+  const int rows_per_wg = (n + kSpGroups - 1) / kSpGroups;
+  const int grid = (n + rows_per_wg - 1) / rows_per_wg;
+  if (d <= 8192 && k_pad <= 8192)
+    select_pack_kernel<4, 1, 5, false><<<grid, kSelThreads, 0, s>>>(nullptr, 0, given, A, lda, n, d, k, k_pad,
+                                                                     rows_per_wg, nullptr, pad, out);
+  else
+    select_pack_kernel<4, 2, 3, false><<<grid, kSelThreads, 0, s>>>(nullptr, 0, given, A, lda, n, d, k, k_pad,
+                                                                     rows_per_wg, nullptr, pad, out);
   return hipGetLastError();
 }
 

@@ -383,6 +383,23 @@ def test_matmul_idx_arbitrary_list(dev, n, dtype):
     assert_close(f32(Y), ref, envelope(f32(A), f32(B), idx), TOL_FP32 if dtype == torch.float32 else TOL_BF16)
 
 
+@pytest.mark.parametrize("n,d,k", [(300, 1000, 450), (300, 1000, 1500), (257, 4096, 9000), (64, 2048, 16000)])
+def test_matmul_idx_whole_row_gather(dev, n, d, k):
+    # given lists on rows of whole 16-byte pieces (the one-launch gather
+    # through LDS): unsorted, repeated and out-of-range entries; lists longer
+    # than d, one with more entries than the 8192 a thread pair holds for
+    # rows of 4096 columns, and one past the LDS list capacity (the
+    # element-gather pack instead)
+    w = synth.mlp_down(n=n, d=d, m=136, rhos=(0.5,))
+    A, B = w.tensors["A"], w.tensors["B"]
+    idx = _given_idx(d, k, seed=k)
+    print(f"matmul_idx n={n} d={d} k={k}", flush=True)
+    Y = rmm.matmul_idx(A.to(dev), B.to(dev), torch.from_numpy(idx).to(dev))
+    torch.cuda.synchronize()
+    ref = O.matmul_given(f32(A), f32(B), idx)
+    assert_close(f32(Y), ref, envelope(f32(A), f32(B), idx), TOL_BF16)
+
+
 def test_select_once_reuse_for_qkv(dev):
     # one selection on X serves three projections; each equals the matching
     # columns of the reduced product with the concatenated weights
