@@ -435,9 +435,21 @@ class QkOp:
         s_bytes = hq * tq * tk * 4
         if k == dh:   # dense: Q and K read in place, S written
             return {"gemm": ("B", s_bytes + hq * tq * dh * 2 + hkv * tk * dh * 2)}
-        return {"score": ("B", hq * tq * dh * 2),
-                "pack": ("B", 2 * (hq * tq * k + hq * tk * k) * 2),
-                "gemm": ("B", s_bytes + (hq * tq * k + hq * tk * k) * 2)}
+        w = {"score": ("B", hq * tq * dh * 2),
+             "gemm": ("B", s_bytes + (hq * tq * k + hq * tk * k) * 2)}
+        if self.fused(rho):
+            # one launch ranks each head's features and gathers Q and K:
+            # whole rows of Q and of the kv heads' K in, both panels out
+            w["topk"] = ("B", hq * tq * dh * 2 + hkv * tk * dh * 2 + (hq * tq * k + hq * tk * k) * 2)
+        else:
+            w["pack"] = ("B", 2 * (hq * tq * k + hq * tk * k) * 2)
+        return w
+
+    def fused(self, rho):
+        """Whether the call ranks the features and gathers Q and K in one
+        launch (the library's rule for contiguous bf16 heads of at most 256
+        features in whole 16-byte pieces)."""
+        return self.ks[rho] < self.dh and self.dh <= 256 and self.dh % 8 == 0
 
     def roofline_stage(self):
         return "gemm"

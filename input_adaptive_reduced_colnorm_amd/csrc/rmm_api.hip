@@ -819,7 +819,17 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
     RMM_LAUNCH(mk.mark(4));
     return RMM_OK;
   }
-  if (p.use_sel) {
+  // bf16 heads of whole 16-byte pieces: the features are ranked and Q and
+  // K gathered in one launch after the energy sweep
+  const bool fused = p.mfma && p.use_sel && !p.direct && qk_select_pack_fits(Q, K, q_hs, q_ts, k_hs, k_ts, dh);
+  if (fused) {
+    float* partial = (float*)(ws + p.sel.off_partial);
+    RMM_LAUNCH(launch_colnorm(Q, true, q_hs, q_ts, (int)hq, (int)tq, (int)dh, p.sel.splits, partial, s));
+    RMM_LAUNCH(mk.mark(1));
+    RMM_LAUNCH(launch_qk_select_pack(partial, p.sel.splits, (const uint16_t*)Q, q_hs, q_ts, (const uint16_t*)K, k_hs,
+                                     k_ts, (int)hq, group, (int)tq, (int)tk, (int)dh, (int)p.k, (int)p.k_pad, idx,
+                                     (uint16_t*)(ws + p.off_q), (uint16_t*)(ws + p.off_k), s));
+  } else if (p.use_sel) {
     RMM_LAUNCH(run_select(p.sel, ws, Q, bf16, q_hs, q_ts, (int)hq, tq, dh, p.k, idx, p.k, nullptr, s, &mk));
   } else {
     RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, nullptr, 0, 0, s));
@@ -849,10 +859,12 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
   } else {
     uint16_t* qp = (uint16_t*)(ws + p.off_q);
     uint16_t* kp = (uint16_t*)(ws + p.off_k);
-    RMM_LAUNCH(launch_pack(Q, true, q_hs, q_ts, 1, idx, p.k, (int)p.k, (int)p.k_pad, (int)hq, (int)tq, qp,
-                           tq * p.k_pad, s));
-    RMM_LAUNCH(launch_pack(K, true, k_hs, k_ts, group, idx, p.k, (int)p.k, (int)p.k_pad, (int)hq, (int)tk, kp,
-                           tk * p.k_pad, s));
+    if (!fused) {
+      RMM_LAUNCH(launch_pack(Q, true, q_hs, q_ts, 1, idx, p.k, (int)p.k, (int)p.k_pad, (int)hq, (int)tq, qp,
+                             tq * p.k_pad, s));
+      RMM_LAUNCH(launch_pack(K, true, k_hs, k_ts, group, idx, p.k, (int)p.k, (int)p.k_pad, (int)hq, (int)tk, kp,
+                             tk * p.k_pad, s));
+    }
     g.A = qp; g.a_bs = tq * p.k_pad; g.lda = p.k_pad;
     g.B = kp; g.b_bs = tk * p.k_pad; g.ldb = p.k_pad; g.b_group = 1;
     g.K = (int)p.k_pad;

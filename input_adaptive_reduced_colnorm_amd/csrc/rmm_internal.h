@@ -54,6 +54,17 @@ hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* 
 // pad[t] = idx[t] for t < k when 0 <= idx[t] < d, else -1 (t < k_pad).
 hipError_t launch_pad_index(const int32_t* idx, int k, int d, int32_t* pad, int k_pad, hipStream_t s);
 
+// QK^T selection and gather in one launch (heads of dh <= 256 features,
+// 16-byte aligned rows): from the summed partials of each query head it
+// writes the ascending kept list idx[h][0..k), and the panels
+// qp[h][r][t] = Q[h][r][idx[h][t]], kp[h][r][t] = K[h / group][r][idx[h][t]]
+// for t < k, 0 up to k_pad.
+bool qk_select_pack_fits(const void* Q, const void* K, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts,
+                         int64_t dh);
+hipError_t launch_qk_select_pack(const float* partial, int splits, const uint16_t* Q, int64_t q_hs, int64_t q_ts,
+                                 const uint16_t* K, int64_t k_hs, int64_t k_ts, int hq, int group, int tq, int tk,
+                                 int dh, int k, int k_pad, int32_t* idx, uint16_t* qp, uint16_t* kp, hipStream_t s);
+
 // Gather-pack: out[b][r][t] = t < k && idx[b][t] >= 0 ? bf16(src[b / src_group][r][idx[b][t]]) : 0
 // for t < k_pad, rows r < rows.  src_bf16 selects bf16 (else fp32) input.
 // k_pad must be a multiple of 8 and out 16-byte aligned (16-byte stores).

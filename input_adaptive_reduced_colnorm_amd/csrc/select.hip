@@ -716,7 +716,131 @@ __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* _
   wait_vmcnt<0>();
 }
 
+// ---------------------------------------------------------------------------
+// Per-head feature selection fused with the gather of Q and K (QK^T with
+// heads of at most 256 features, rows of whole 16-byte pieces).  A
+// workgroup of 256 threads owns 32 KB of rows (16384 / dh rows) of one
+// query head's Q, or of its kv head's K: it sums the head's split partials,
+// sends its rows
+// from the buffer straight into LDS (untracked direct loads, issued before
+// the ranking so that they land while it runs), ranks the features as
+// topk_small_kernel does (each thread counts the composite keys that
+// outrank its own), and writes the kept features of each row as 16-byte
+// pieces of the K-contiguous panels.  The first Q workgroup of each head
+// writes its ascending kept list.  Four workgroups share a compute unit
+// (35 KB of LDS each), so one's ranking overlaps another's loads.
+// ---------------------------------------------------------------------------
+constexpr int kQkElems = 16384;   // row elements per workgroup (32 KB of bf16)
+
+__global__ __launch_bounds__(kSmallD) void qk_select_pack_kernel(
+    const float* __restrict__ partial, int splits, const uint16_t* __restrict__ Q, int64_t q_hs, int64_t q_ts,
+    const uint16_t* __restrict__ K, int64_t k_hs, int64_t k_ts, int group, int tq, int tk, int dh, int k, int k_pad,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ qp, uint16_t* __restrict__ kp) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_rows[kQkElems];   // row r at r * dh
+  __shared__ __attribute__((aligned(16))) uint16_t s_list[kSmallD];
+  __shared__ __attribute__((aligned(16))) uint64_t s_ck[kSmallD];
+  __shared__ int s_wave[kSmallD / 64];
+  const int h = blockIdx.y;
+  const int j = threadIdx.x;
+  const int lane = j & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(j >> 6);
+  const int rb_rows = kQkElems / dh;   // rows per workgroup
+  const int qblocks = (tq + rb_rows - 1) / rb_rows;
+  const bool is_q = (int)blockIdx.x < qblocks;
+  const int r0 = (is_q ? (int)blockIdx.x : (int)blockIdx.x - qblocks) * rb_rows;
+  const int nr = min(rb_rows, (is_q ? tq : tk) - r0);
+  const int64_t ts = is_q ? q_ts : k_ts;
+  const uint16_t* src = (is_q ? Q + (size_t)h * q_hs : K + (size_t)(h / group) * k_hs) + (size_t)r0 * ts;
+  const int pieces = dh >> 3;   // 16-byte pieces of a row
+
+  // the head's energies, summed over the splits in split order
+  float q = 0.f;
+  if (j < dh) {
+    const float* P = partial + (size_t)h * splits * dh;
+    for (int s0 = 0; s0 < splits; s0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = s0 + u < splits ? P[(size_t)(s0 + u) * dh + j] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (s0 + u < splits) q += v[u];
+    }
+  }
+
+  // the block's rows: piece i = row * pieces + c lands at LDS byte 16 i;
+  // wave w sends pieces [64 (w + 4 t), + 64) for t = 0, 1, ...
+  const int npieces = nr * pieces;
+  const i32x4 rs = rsrc_words(src, (uint32_t)(((size_t)(nr - 1) * ts + dh) * 2));
+  const uint32_t rows0 = lds_addr(s_rows);
+  for (int base = 64 * wave; base < npieces; base += 256) {
+    const int i = base + lane;
+    const int row = i / pieces, c = i - row * pieces;
+    const uint32_t off = i < npieces ? (uint32_t)(((size_t)row * ts + 8 * c) * 2) : kOobOffset;
+    load_lds16_async(rs, rows0 + 16u * (uint32_t)base, off);
+  }
+
+  // rank: composite key (energy bits, 0xFFFF - j), a larger one outranks
+  const uint64_t ck = ((uint64_t)__float_as_uint(q) << 32) | (uint32_t)(0xFFFF - j);
+  s_ck[j] = ck;
+  lds_barrier();
+  int rank = 0;
+  for (int i2 = 0; i2 < (dh + 1) / 2; ++i2) {
+    const u64x2 v = *(const u64x2*)(s_ck + 2 * i2);
+    rank += (int)(v[0] > ck) + ((int)(2 * i2 + 1 < dh) & (int)(v[1] > ck));
+  }
+  const bool keep = j < dh && rank < k;
+  const uint64_t ballot = __ballot(keep);
+  if (lane == 0) s_wave[wave] = __popcll(ballot);
+  lds_barrier();
+  int pos = __popcll(ballot & ((1ull << lane) - 1ull));
+  for (int w = 0; w < wave; ++w) pos += s_wave[w];
+  if (keep) s_list[pos] = (uint16_t)j;
+  if (j >= k && j < k_pad) s_list[j] = 0xFFFF;   // padding: reads as zero
+  if (keep && is_q && blockIdx.x == 0) idx[(size_t)h * k + pos] = j;
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  // gather: output piece g = row * (k_pad / 8) + p holds kept positions
+  // [8 p, 8 p + 8) of that row; the threads step through the pieces by a
+  // multiple of k_pad / 8, so each keeps one p (and its 8 column indices)
+  const int opr = k_pad >> 3;
+  const int gstride = kSmallD / opr * opr;
+  uint16_t* dst = (is_q ? qp + (size_t)h * tq * k_pad : kp + (size_t)h * tk * k_pad) + (size_t)r0 * k_pad;
+  const int p = j % opr;
+  uint32_t col[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) col[e] = s_list[8 * p + e];
+  for (int g = j < gstride ? j : nr * opr; g < nr * opr; g += gstride) {
+    const int row = g / opr;
+    const uint16_t* rb = s_rows + row * dh;
+    i32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t v0 = col[2 * e] == 0xFFFFu ? 0u : rb[col[2 * e]];
+      const uint32_t v1 = col[2 * e + 1] == 0xFFFFu ? 0u : rb[col[2 * e + 1]];
+      w[e] = (int)(v0 | (v1 << 16));
+    }
+    *(i32x4*)(dst + (size_t)row * k_pad + 8 * p) = w;
+  }
+}
+
 }  // namespace
+
+bool qk_select_pack_fits(const void* Q, const void* K, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts,
+                         int64_t dh) {
+  return dh <= kSmallD && dh % 8 == 0 && (uintptr_t)Q % 16 == 0 && (uintptr_t)K % 16 == 0 && q_hs % 8 == 0 &&
+         q_ts % 8 == 0 && k_hs % 8 == 0 && k_ts % 8 == 0;
+}
+
+hipError_t launch_qk_select_pack(const float* partial, int splits, const uint16_t* Q, int64_t q_hs, int64_t q_ts,
+                                 const uint16_t* K, int64_t k_hs, int64_t k_ts, int hq, int group, int tq, int tk,
+                                 int dh, int k, int k_pad, int32_t* idx, uint16_t* qp, uint16_t* kp, hipStream_t s) {
+  const int rb_rows = kQkElems / dh;
+  const int blocks = (tq + rb_rows - 1) / rb_rows + (tk + rb_rows - 1) / rb_rows;
+  qk_select_pack_kernel<<<dim3(blocks, hq), kSmallD, 0, s>>>(partial, splits, Q, q_hs, q_ts, K, k_hs, k_ts, group,
+                                                            tq, tk, dh, k, k_pad, idx, qp, kp);
+  return hipGetLastError();
+}
 
 int colnorm_splits(int heads, int n, int d, bool elt_bf16) {
   const int cb = kCnLanes * (elt_bf16 ? 8 : 4);

@@ -541,6 +541,33 @@ def test_qk_wide_head(dev):
     check_qk(w.tensors["Q"], w.tensors["K"], 0.7, dev, TOL_BF16)
 
 
+def test_qk_strided_heads(dev):
+    # Q and K as views of token-major [t][heads][dh] buffers (head stride dh,
+    # row stride heads * dh), then of rows padded to 152 elements, both
+    # through the one-launch feature selection and gather; rows padded to
+    # 131 elements (not whole 16-byte pieces) take the separate TopK and
+    # element-gather packs
+    w = synth.gqa_qk(hq=8, hkv=2, t=200, dh=128)
+    Q, K = w.tensors["Q"], w.tensors["K"]
+    Qf, Kf = f32(Q), f32(K)
+    idx_o, S_o = O.qk(Qf, Kf, 0.5)
+    env = qk_envelope(Qf, Kf, idx_o)
+    views = [(Q.permute(1, 0, 2).contiguous().to(dev).permute(1, 0, 2),
+              K.permute(1, 0, 2).contiguous().to(dev).permute(1, 0, 2))]
+    for width in (152, 131):
+        Qw = torch.zeros((8, 200, width), dtype=Q.dtype)
+        Kw = torch.zeros((2, 200, width), dtype=K.dtype)
+        Qw[:, :, :128] = Q
+        Kw[:, :, :128] = K
+        views.append((Qw.to(dev)[:, :, :128], Kw.to(dev)[:, :, :128]))
+    for Qd, Kd in views:
+        print(f"qk strides Q {Qd.stride()} K {Kd.stride()}", flush=True)
+        idx, S = rmm.qk(Qd, Kd, 0.5)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+        assert_close(f32(S), S_o, env, TOL_BF16, "scores")
+
+
 @pytest.mark.parametrize("d", [255, 256, 257])
 def test_selection_size_boundary(dev, d):
     # d <= 256 selects with the rank kernel, larger d with the radix kernel
