@@ -241,6 +241,40 @@ def test_fused_selection_gather_shapes(dev, n, d, rho):
     check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16, rows=rows)
 
 
+def test_fused_and_separate_selection_agree_bitwise(dev):
+    # the one-launch ranking + gather and the separate TopK + pack launches
+    # (taken when rows are not whole 16-byte pieces: a row stride of d + 3)
+    # feed the same GEMM, so their kept lists and products agree bit for bit;
+    # likewise for QK^T heads and for a given index list
+    w = synth.mlp_down(n=600, d=2048, m=264, rhos=(0.7,))
+    A, B = w.tensors["A"], w.tensors["B"]
+    X = torch.zeros((600, 2051), dtype=A.dtype)
+    X[:, :2048] = A
+    Ad, Xd, Bd = A.to(dev), X.to(dev)[:, :2048], B.to(dev)
+    for rho in (0.7, 0.3):
+        i1, Y1 = rmm.matmul(Ad, Bd, rho)
+        i2, Y2 = rmm.matmul(Xd, Bd, rho)
+        torch.cuda.synchronize()
+        assert torch.equal(i1, i2)
+        assert torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
+        g1 = rmm.matmul_idx(Ad, Bd, i1)
+        g2 = rmm.matmul_idx(Xd, Bd, i1)
+        torch.cuda.synchronize()
+        assert torch.equal(g1.view(torch.int32), Y1.view(torch.int32))
+        assert torch.equal(g2.view(torch.int32), Y1.view(torch.int32))
+    q = synth.gqa_qk(hq=8, hkv=2, t=260, dh=128)
+    Q, K = q.tensors["Q"], q.tensors["K"]
+    Qw = torch.zeros((8, 260, 131), dtype=Q.dtype)
+    Kw = torch.zeros((2, 260, 131), dtype=K.dtype)
+    Qw[:, :, :128] = Q
+    Kw[:, :, :128] = K
+    j1, S1 = rmm.qk(Q.to(dev), K.to(dev), 0.5)
+    j2, S2 = rmm.qk(Qw.to(dev)[:, :, :128], Kw.to(dev)[:, :, :128], 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(j1, j2)
+    assert torch.equal(S1.view(torch.int32), S2.view(torch.int32))
+
+
 @pytest.mark.parametrize("n,d", [(32, 3000), (32, 9000), (8, 4096)])
 def test_radix_zero_and_tied_energies(dev, n, d):
     # integer entries give exact energies on both sides, with many ties; 40%
