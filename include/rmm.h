@@ -177,8 +177,11 @@ rmm_status_t rmm_matmul_noalloc(const void* A, const void* B, int dtype, int64_t
  * five caller-created HIP events (hipEvent_t, timing enabled) on `stream`
  * at the stage boundaries: [0] before scoring, [1] before TopK, [2] before
  * the gather-pack, [3] before the product kernel, [4] after it.  A stage a
- * path does not run leaves its two events back to back.  For per-kernel
- * timing by benchmarks; stage_events and its five entries must be non-NULL. */
+ * path does not run leaves its two events back to back; where one launch
+ * ranks and gathers (prefill with bf16 rows of whole 16-byte pieces and
+ * d <= 15360), [1] to [2] brackets it and [2], [3] are back to back.  For
+ * per-kernel timing by benchmarks; stage_events and its five entries must be
+ * non-NULL. */
 rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n, int64_t d, int64_t m, int64_t lda,
                               int64_t ldb, double rho, int32_t* idx, void* Y, int y_dtype, int64_t ldy,
                               void* workspace, size_t workspace_bytes, void* stream, void* const* stage_events);
@@ -246,7 +249,8 @@ rmm_status_t rmm_matmul_idx(const void* A, const void* B, int dtype, int64_t n, 
  * dh a multiple of 8 up to 256 and 16-byte aligned K rows (decode), the
  * selection and the product run in one streaming pass over K; otherwise
  * the column energies, TopK, packs of Q and K and a batched matrix-core
- * product.
+ * product (with bf16 heads of at most 256 features and 16-byte aligned rows,
+ * TopK and both packs are one launch).
  * Source: hackcv.com, Component mapping (QK^T over the head feature dim,
  * selection on Q, K gathers the matching dims under GQA).
  * ------------------------------------------------------------------- */
@@ -257,7 +261,8 @@ rmm_status_t rmm_qk(const void* Q, const void* K, int dtype, int64_t hq, int64_t
 
 /* rmm_qk with the five stage events of rmm_matmul_timed recorded on `stream`
  * ([0] start, [1] after the column energies, [2] after TopK, [3] after the
- * packs of Q and K, [4] after the batched product).  Same arguments,
+ * packs of Q and K, [4] after the batched product; when TopK and the packs
+ * are one launch, [2] follows it and [3] follows [2]).  Same arguments,
  * results and errors as rmm_qk; stage_events and its entries non-NULL. */
 rmm_status_t rmm_qk_timed(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,
                           int64_t dh, int64_t q_hs, int64_t q_ts, int64_t k_hs, int64_t k_ts, double rho,
