@@ -865,9 +865,10 @@ def hipblaslt_context(op):
 class DecodeAttnOp:
     """One decode step of attention per layer (one query per head over a KV
     cache): rmm_qk (features of q kept, streaming pass over K), the softmax
-    of the scores scaled by 1/sqrt(head dim) that emits the key energies
-    (rmm_softmax_energy), and rmm_pv_energy
-    (keys kept by energy; a GEMV per head over the kept V rows)."""
+    of the scores scaled by 1/sqrt(head dim) that also ranks the key
+    energies and writes the kept lists (rmm_softmax_select), and rmm_pv_idx
+    (a GEMV per head over the kept V rows).  The dense step (rho = 1) runs
+    rmm_softmax_energy and rmm_pv_energy, which keep every key."""
 
     stage_names = ("qk", "softmax", "none", "pv")
 
@@ -896,6 +897,9 @@ class DecodeAttnOp:
         ws = max(int(L.rmm_softmax_energy_workspace(self.hq, self.tq, self.tk)), 1)
         wp = max(int(L.rmm_pv_energy_workspace(self.hq, self.tq, self.tk, self.dv, rmm.RMM_FP32, rmm.RMM_BF16, r))
                  for r in rhos)
+        ws = max(ws, max(int(L.rmm_softmax_select_workspace(self.hq, self.tq, self.tk)) for r in rhos))
+        wp = max(wp, max(int(L.rmm_pv_idx_workspace(self.hq, self.tq, self.ks[r], self.dv, rmm.RMM_BF16))
+                         for r in rhos))
         self.wsq = torch.empty(max(wq, 256), dtype=torch.uint8, device=dev)
         self.wss = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.wsp = torch.empty(max(wp, 256), dtype=torch.uint8, device=dev)
@@ -911,18 +915,33 @@ class DecodeAttnOp:
         if st != 0:
             raise RuntimeError(f"rmm_qk: {rmm.status_str(st)}")
         rec(1)
-        st = L.rmm_softmax_energy(self.S.data_ptr(), float(dh) ** -0.5, hq, tq, tk, tq * tk, tk, self.P.data_ptr(),
-                                  tq * tk, tk,
-                                  self.E.data_ptr(), self.wss.data_ptr(), self.wss.numel(), sh)
-        if st != 0:
-            raise RuntimeError(f"rmm_softmax_energy: {rmm.status_str(st)}")
-        rec(2)
-        rec(3)
-        st = L.rmm_pv_energy(self.P.data_ptr(), rmm.RMM_FP32, self.Vs[c].data_ptr(), rmm.RMM_BF16, self.E.data_ptr(),
-                             hq, hkv, tq, tk, dv, tq * tk, tk, tk * dv, dv, float(rho), self.ip[rho].data_ptr(),
-                             self.O.data_ptr(), rmm.RMM_FP32, self.wsp.data_ptr(), self.wsp.numel(), sh)
-        if st != 0:
-            raise RuntimeError(f"rmm_pv_energy: {rmm.status_str(st)}")
+        if rho < 1.0:
+            st = L.rmm_softmax_select(self.S.data_ptr(), float(dh) ** -0.5, hq, tq, tk, tq * tk, tk,
+                                      self.P.data_ptr(), tq * tk, tk, self.E.data_ptr(), float(rho),
+                                      self.ip[rho].data_ptr(), self.wss.data_ptr(), self.wss.numel(), sh)
+            if st != 0:
+                raise RuntimeError(f"rmm_softmax_select: {rmm.status_str(st)}")
+            rec(2)
+            rec(3)
+            st = L.rmm_pv_idx(self.P.data_ptr(), rmm.RMM_FP32, self.Vs[c].data_ptr(), rmm.RMM_BF16,
+                              self.ip[rho].data_ptr(), self.ks[rho], hq, hkv, tq, tk, dv, tq * tk, tk, tk * dv, dv,
+                              self.O.data_ptr(), rmm.RMM_FP32, self.wsp.data_ptr(), self.wsp.numel(), sh)
+            if st != 0:
+                raise RuntimeError(f"rmm_pv_idx: {rmm.status_str(st)}")
+        else:
+            st = L.rmm_softmax_energy(self.S.data_ptr(), float(dh) ** -0.5, hq, tq, tk, tq * tk, tk,
+                                      self.P.data_ptr(), tq * tk, tk, self.E.data_ptr(), self.wss.data_ptr(),
+                                      self.wss.numel(), sh)
+            if st != 0:
+                raise RuntimeError(f"rmm_softmax_energy: {rmm.status_str(st)}")
+            rec(2)
+            rec(3)
+            st = L.rmm_pv_energy(self.P.data_ptr(), rmm.RMM_FP32, self.Vs[c].data_ptr(), rmm.RMM_BF16,
+                                 self.E.data_ptr(), hq, hkv, tq, tk, dv, tq * tk, tk, tk * dv, dv, float(rho),
+                                 self.ip[rho].data_ptr(), self.O.data_ptr(), rmm.RMM_FP32, self.wsp.data_ptr(),
+                                 self.wsp.numel(), sh)
+            if st != 0:
+                raise RuntimeError(f"rmm_pv_energy: {rmm.status_str(st)}")
         rec(4)
 
     def stage_work(self, rho):
@@ -937,8 +956,10 @@ class DecodeAttnOp:
 
     def roofline_kernel(self):
         return {"qk": "qk_decode_kernel (streaming pass over the key cache)",
-                "softmax": "softmax_energy_kernel", "pv": "the rmm_pv_energy call: topk_kernel over the key energies, gemv_kernel batched over heads "
-                      "(kept V rows) and gemv_reduce_kernel"}
+                "softmax": "softmax_select_kernel (softmax, key energies and the kept lists; dense: "
+                           "softmax_energy_kernel)",
+                "pv": "the rmm_pv_idx call: pad_index_kernel, gemv_kernel batched over heads (kept V rows) and "
+                      "gemv_reduce_kernel (dense: rmm_pv_energy over every row)"}
 
     def traffic_ref(self):
         return None

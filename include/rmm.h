@@ -85,7 +85,9 @@ typedef enum {
   RMM_OP_MATMUL_W8 = 4,       /* rmm_matmul_w8 (+ _timed) */
   RMM_OP_MATMUL_IDX = 5,      /* rmm_matmul_idx */
   RMM_OP_SOFTMAX_ENERGY = 6,  /* rmm_softmax_energy */
-  RMM_OP_PV_ENERGY = 7        /* rmm_pv_energy */
+  RMM_OP_PV_ENERGY = 7,       /* rmm_pv_energy */
+  RMM_OP_SOFTMAX_SELECT = 8,  /* rmm_softmax_select */
+  RMM_OP_PV_IDX = 9           /* rmm_pv_idx */
 } rmm_op_t;
 
 /* Number of kept indices, ceil(rho * d) under the decimal reading above;
@@ -111,6 +113,8 @@ const char* rmm_status_str(int status);
  *   RMM_OP_QK              n_or_heads = hq, d = head dim, m >= max(tq, tk)
  *   RMM_OP_PV, _PV_ENERGY  n_or_heads = h, d = tk (key positions), m >= max(tq, dv)
  *   RMM_OP_SOFTMAX_ENERGY  n_or_heads = h, d = tk, m = tq
+ *   RMM_OP_SOFTMAX_SELECT  n_or_heads = h, d = tk, m = tq
+ *   RMM_OP_PV_IDX          n_or_heads = h, d = length of each list, m >= max(tq, dv)
  * Returns 0 for an unknown op or a size outside [1, 2^31) (and for
  * softmax rows longer than the softmax pass takes).  Pure host arithmetic:
  * no device call, no allocation. */
@@ -337,6 +341,41 @@ rmm_status_t rmm_pv_energy(const void* P, int p_dtype, const void* V, int v_dtyp
                            int64_t hkv, int64_t tq, int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts, int64_t v_hs,
                            int64_t v_ts, double rho, int32_t* idx, void* O, int o_dtype, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * rmm_softmax_select: rmm_softmax_energy, and in addition the kept key
+ * positions of every head, idx[h][0..k) ascending with k = rmm_k(rho, tk):
+ * the k largest energy[h][:], ties to the lowest index (the PV selection of
+ * rmm_pv_energy at the same rho).  kaelemshawn.blog, section on where RMM
+ * cuts inside the Transformer (PV contracts over key positions, scored by
+ * the column norms of P); hackcv.com, Core Approach (TopK of the scores).
+ * When one workgroup takes every query row of a head (decode-shaped calls,
+ * tk <= 8192) the ranking runs inside the softmax pass and needs no
+ * workspace; otherwise the softmax pass is followed by a TopK launch.
+ *   idx  [h][k] int32, written.  Other arguments and errors as
+ *        rmm_softmax_energy (RMM_ERR_RHO for rho outside (0, 1]).
+ *   Workspace: rmm_softmax_select_workspace(h, tq, tk) bytes (0: none).
+ *
+ * rmm_pv_idx: PV over given key lists, for every head h
+ *   O_h = sum over t < k of P_h[:, idx[h][t]] V_g(h)[idx[h][t], :],
+ * g(h) = h / (h / hkv); entries outside [0, tk) contribute nothing, repeats
+ * count once per occurrence (hackcv.com, Core Approach: the product over a
+ * kept index set; kaelemshawn.blog, the PV mapping).  For lists made once
+ * and used by the product that follows (rmm_softmax_select's).
+ *   idx  [h][k] int32 (row stride k), k >= 1, any order.
+ *   Other arguments, layouts and errors as rmm_pv (no rho).  tq <= 16
+ *   with bf16 V reads only the listed rows of V (a GEMV per head).
+ *   Workspace: rmm_pv_idx_workspace(h, tq, k, dv, v_dtype) bytes.
+ * ------------------------------------------------------------------- */
+size_t rmm_softmax_select_workspace(int64_t h, int64_t tq, int64_t tk);
+rmm_status_t rmm_softmax_select(const float* L, float scale, int64_t h, int64_t tq, int64_t tk, int64_t l_hs,
+                                int64_t l_ts, float* P, int64_t p_hs, int64_t p_ts, float* energy, double rho,
+                                int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
+size_t rmm_pv_idx_workspace(int64_t h, int64_t tq, int64_t k, int64_t dv, int v_dtype);
+rmm_status_t rmm_pv_idx(const void* P, int p_dtype, const void* V, int v_dtype, const int32_t* idx, int64_t k,
+                        int64_t h, int64_t hkv, int64_t tq, int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts,
+                        int64_t v_hs, int64_t v_ts, void* O, int o_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* rmm_pv with the five stage events of rmm_matmul_timed recorded on `stream`
  * ([0] start, [1] after the column energies of P, [2] after TopK, [3] after

@@ -156,11 +156,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
     // the identity list (rho = 1): the first strip's workgroups write it
     for (int i = tid; i < L; i += kThreads) g.idx_out[t0 + i] = t0 + i;
   }
+  // a caller's list entry outside [0, d) (d > 0: the row count of B) reads
+  // as a zero row
   auto kept = [&](int t) -> int {
-    if constexpr (SEL)
+    if constexpr (SEL) {
       return s_list[t];
-    else
-      return g.idx ? g.idx[t0 + t] : t0 + t;
+    } else {
+      if (!g.idx) return t0 + t;
+      const int j = g.idx[t0 + t];
+      return g.d > 0 && (unsigned)j >= (unsigned)g.d ? -1 : j;
+    }
   };
 
   // ---- load order matters: vector loads retire in order, so a wait for a

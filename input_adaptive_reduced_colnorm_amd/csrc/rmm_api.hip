@@ -1162,6 +1162,187 @@ rmm_status_t rmm_softmax_energy(const float* L, float scale, int64_t h, int64_t 
   return RMM_OK;
 }
 
+// ------------------------- softmax with selection ----------------------------
+
+namespace {
+
+// one workgroup per head (decode) ranks inside the softmax pass; otherwise
+// the softmax pass, then TopK over its energies
+bool softmax_select_fused(int64_t h, int64_t tq, int64_t tk) {
+  return softmax_row_blocks((int)h, (int)tq) == 1 && tk <= softmax_select_max_keys();
+}
+
+struct SmSelPlan {
+  size_t off_part = 0, off_gkeys = 0, total = 0;
+  bool fused = false, gkeys = false;
+};
+
+SmSelPlan plan_softmax_select(int64_t h, int64_t tq, int64_t tk) {
+  SmSelPlan p;
+  Carve cv;
+  p.fused = softmax_select_fused(h, tq, tk);
+  if (!p.fused) {
+    p.off_part = cv.take((size_t)h * softmax_row_blocks((int)h, (int)tq) * tk * 4);
+    p.gkeys = tk > topk_lds_capacity();
+    if (p.gkeys) p.off_gkeys = cv.take((size_t)h * tk * 4);
+  }
+  p.total = cv.used;
+  return p;
+}
+
+}  // namespace
+
+size_t rmm_softmax_select_workspace(int64_t h, int64_t tq, int64_t tk) {
+  if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(tk) || tk > softmax_max_keys()) return 0;
+  return plan_softmax_select(h, tq, tk).total;
+}
+
+rmm_status_t rmm_softmax_select(const float* L, float scale, int64_t h, int64_t tq, int64_t tk, int64_t l_hs,
+                                int64_t l_ts, float* P, int64_t p_hs, int64_t p_ts, float* energy, double rho,
+                                int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!L || !P || !energy || !idx) return RMM_ERR_NULL;
+  if (!rho_ok(rho)) return RMM_ERR_RHO;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return RMM_ERR_SHAPE;
+  if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(tk) || tk > softmax_max_keys() || l_ts < tk || p_ts < tk || l_hs < 0 ||
+      p_hs < 0 || (h > 1 && (l_hs < 1 || p_hs < 1)) || h * tq >= kMaxDim)
+    return RMM_ERR_SHAPE;
+  if (!aligned(L, 4) || !aligned(P, 4) || !aligned(energy, 4) || !aligned(idx, 4)) return RMM_ERR_ALIGN;
+  const SmSelPlan p = plan_softmax_select(h, tq, tk);
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)))
+    return RMM_ERR_WORKSPACE;
+  const int64_t k = k_of(rho, tk);
+  const Span sl = span3(L, h, l_hs, tq, l_ts, tk, 4), sp = span3(P, h, p_hs, tq, p_ts, tk, 4);
+  const Span se = span3(energy, 1, 0, h, tk, tk, 4), si = span3(idx, 1, 0, h, k, k, 4);
+  if (overlap(sp, sl) || overlap(se, sl) || overlap(se, sp) || overlap(si, sl) || overlap(si, sp) ||
+      overlap(si, se))
+    return RMM_ERR_ALIAS;
+  if (p.total > 0) {
+    const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
+    if (overlap(sw, sl) || overlap(sw, sp) || overlap(sw, se) || overlap(sw, si)) return RMM_ERR_ALIAS;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  clear_error();
+  if (p.fused) {
+    RMM_LAUNCH(launch_softmax_select(L, l_hs, l_ts, P, p_hs, p_ts, (int)h, (int)tq, (int)tk, scale, energy, (int)k,
+                                     idx, s));
+    return RMM_OK;
+  }
+  RMM_LAUNCH(launch_softmax_energy(L, l_hs, l_ts, P, p_hs, p_ts, (int)h, (int)tq, (int)tk,
+                                   softmax_row_blocks((int)h, (int)tq), scale, (float*)(ws + p.off_part), energy, s));
+  RMM_LAUNCH(launch_topk(energy, (int)h, 1, (int)tk, (int)k, idx, k, nullptr, 0, 0, nullptr, tk,
+                         p.gkeys ? (uint32_t*)(ws + p.off_gkeys) : nullptr, s));
+  return RMM_OK;
+}
+
+// ------------------------------ pv over given lists ------------------------------
+
+namespace {
+
+struct PvIdxPlan {
+  int64_t k_pad = 0;
+  bool mfma = false, decode = false;
+  int gemv_splits = 1;
+  size_t off_ipad = 0, off_p = 0, off_gpart = 0, total = 0;
+};
+
+PvIdxPlan plan_pv_idx(int64_t h, int64_t tq, int64_t k, int64_t dv, int v_dtype, bool v_ok) {
+  PvIdxPlan p;
+  Carve cv;
+  p.k_pad = round_up(k, kKTile);
+  p.off_ipad = cv.take((size_t)h * p.k_pad * 4);
+  p.mfma = v_dtype == RMM_BF16 && v_ok;
+  if (p.mfma && tq <= kDecodeRows) {
+    p.decode = true;
+    p.gemv_splits = gemv_splits((int)k, (int)dv, (int)h);
+    if (p.gemv_splits > 1) p.off_gpart = cv.take((size_t)p.gemv_splits * h * tq * dv * 4);
+  } else if (p.mfma) {
+    p.off_p = cv.take((size_t)h * tq * p.k_pad * 2);
+  }
+  p.total = cv.used;
+  return p;
+}
+
+}  // namespace
+
+size_t rmm_pv_idx_workspace(int64_t h, int64_t tq, int64_t k, int64_t dv, int v_dtype) {
+  if (!dim_ok(h) || !dim_ok(tq) || !dim_ok(k) || !dim_ok(dv) || !dtype_ok(v_dtype)) return 0;
+  const size_t a = plan_pv_idx(h, tq, k, dv, v_dtype, true).total;
+  const size_t b = plan_pv_idx(h, tq, k, dv, v_dtype, false).total;
+  return a > b ? a : b;
+}
+
+rmm_status_t rmm_pv_idx(const void* P, int p_dtype, const void* V, int v_dtype, const int32_t* idx, int64_t k,
+                        int64_t h, int64_t hkv, int64_t tq, int64_t tk, int64_t dv, int64_t p_hs, int64_t p_ts,
+                        int64_t v_hs, int64_t v_ts, void* O, int o_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!P || !V || !idx || !O) return RMM_ERR_NULL;
+  if (!dtype_ok(p_dtype) || !dtype_ok(v_dtype) || !dtype_ok(o_dtype)) return RMM_ERR_DTYPE;
+  if (!dim_ok(h) || !dim_ok(hkv) || !dim_ok(tq) || !dim_ok(tk) || !dim_ok(dv) || !dim_ok(k) || h % hkv != 0)
+    return RMM_ERR_SHAPE;
+  if (p_ts < tk || v_ts < dv || p_hs < 0 || v_hs < 0 || (h > 1 && p_hs < 1) || (hkv > 1 && v_hs < 1))
+    return RMM_ERR_SHAPE;
+  if (h * tq >= kMaxDim) return RMM_ERR_SHAPE;
+  const size_t pe = elt_size(p_dtype), ve = elt_size(v_dtype);
+  if (!aligned(P, pe) || !aligned(V, ve) || !aligned(idx, 4) || !aligned(O, elt_size(o_dtype))) return RMM_ERR_ALIGN;
+  const bool v_ok = v_dtype == RMM_BF16 && aligned(V, 16) && v_ts % 8 == 0 && v_hs % 8 == 0 && dv % 8 == 0 &&
+                    ((tk - 1) * v_ts + dv) * 2 <= kMaxOperandBytes;
+  const PvIdxPlan p = plan_pv_idx(h, tq, k, dv, v_dtype, v_ok);
+  if (!workspace || workspace_bytes < p.total || !aligned(workspace, 256)) return RMM_ERR_WORKSPACE;
+  if (p.mfma && !p.decode && tq * p.k_pad * 2 > kMaxOperandBytes) return RMM_ERR_SHAPE;
+  const Span sp = span3(P, h, p_hs, tq, p_ts, tk, pe), sv = span3(V, hkv, v_hs, tk, v_ts, dv, ve);
+  const Span si = span3(idx, 1, 0, h, k, k, 4);
+  const Span so = span3(O, h, tq * dv, tq, dv, dv, elt_size(o_dtype));
+  const Span sw = span3(workspace, 1, 0, 1, (int64_t)p.total, (int64_t)p.total, 1);
+  if (overlap(so, sp) || overlap(so, sv) || overlap(so, si) || overlap(sw, sp) || overlap(sw, sv) ||
+      overlap(sw, si) || overlap(sw, so))
+    return RMM_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int group = (int)(h / hkv);
+  int32_t* ipad = (int32_t*)(ws + p.off_ipad);
+  clear_error();
+  // entries outside [0, tk) become -1 (a zero row), the lists padded to
+  // k_pad; the GEMV (decode) takes the lists as they are and drops such
+  // entries itself
+  if (!p.decode) RMM_LAUNCH(launch_pad_index(idx, (int)k, (int)tk, ipad, (int)p.k_pad, s, (int)h, k, p.k_pad));
+  if (!p.mfma) {
+    SimtArgs g{};
+    g.A = P; g.a_bf16 = p_dtype == RMM_BF16; g.a_bs = p_hs; g.a_rs = p_ts; g.a_cs = 1;
+    g.B = V; g.b_bf16 = v_dtype == RMM_BF16; g.b_bs = v_hs; g.b_ts = v_ts; g.b_js = 1; g.b_group = group;
+    g.idx = ipad; g.idx_bs = p.k_pad;
+    g.C = O; g.c_bf16 = o_dtype == RMM_BF16; g.c_bs = tq * dv; g.ldc = dv;
+    g.M = (int)tq; g.N = (int)dv; g.k = (int)k; g.batch = (int)h;
+    RMM_LAUNCH(launch_gemm_simt(g, s));
+    return RMM_OK;
+  }
+  if (p.decode) {
+    GemvArgs g{};
+    g.A = P; g.a_bf16 = p_dtype == RMM_BF16; g.lda = p_ts; g.a_bs = p_hs;
+    g.B = (const uint16_t*)V; g.ldb = v_ts; g.b_bs = v_hs; g.b_group = group;
+    g.idx = idx; g.idx_bs = k; g.d = (int)tk;
+    g.k = (int)k; g.n = (int)tq; g.m = (int)dv;
+    g.partial = (float*)(ws + p.off_gpart); g.splits = p.gemv_splits;
+    g.Y = O; g.y_bf16 = o_dtype == RMM_BF16; g.ldy = dv; g.y_bs = tq * dv;
+    g.batch = (int)h;
+    RMM_LAUNCH(launch_gemv(g, s));
+    return RMM_OK;
+  }
+  uint16_t* pp = (uint16_t*)(ws + p.off_p);
+  RMM_LAUNCH(launch_pack(P, p_dtype == RMM_BF16, p_hs, p_ts, 1, ipad, p.k_pad, (int)p.k_pad, (int)p.k_pad, (int)h,
+                         (int)tq, pp, tq * p.k_pad, s));
+  GemmArgs g{};
+  g.A = pp; g.a_bs = tq * p.k_pad; g.lda = p.k_pad;
+  g.a_bytes = (uint32_t)(tq * p.k_pad * 2);
+  g.B = (const uint16_t*)V; g.b_bs = v_hs; g.ldb = v_ts; g.b_group = group;
+  g.b_bytes = (uint32_t)(((tk - 1) * v_ts + dv) * 2);
+  g.idx = ipad; g.idx_bs = p.k_pad;
+  g.C = O; g.c_bs = tq * dv; g.ldc = dv; g.c_bf16 = o_dtype == RMM_BF16;
+  g.M = (int)tq; g.N = (int)dv; g.K = (int)p.k_pad; g.batch = (int)h; g.b_kmajor = true;
+  RMM_LAUNCH(launch_gemm_bf16(g, s));
+  return RMM_OK;
+}
+
 // ------------------------- generic workspace query ---------------------------
 //
 // One bound per operation, over every rho in (0, 1], every dtype and
@@ -1232,6 +1413,18 @@ size_t rmm_workspace_bytes(int op, int64_t n_or_heads, int64_t d, int64_t m) {
       // d = key positions tk, m = query rows tq
       if (!dim_ok(h) || !dim_ok(d) || !dim_ok(m) || d > softmax_max_keys()) return 0;
       return rmm_softmax_energy_workspace(h, m, d);
+    case RMM_OP_SOFTMAX_SELECT:
+      // d = key positions tk, m = query rows tq (no rho dependence)
+      if (!dim_ok(h) || !dim_ok(d) || !dim_ok(m) || d > softmax_max_keys()) return 0;
+      return rmm_softmax_select_workspace(h, m, d);
+    case RMM_OP_PV_IDX: {
+      // d = length of each head's list, m bounds both tq and dv
+      if (!dim_ok(h) || !dim_ok(d) || !dim_ok(m)) return 0;
+      const size_t k_pad = (size_t)round_up(d, kKTile);
+      const int64_t rows = m < kDecodeRows ? m : kDecodeRows;
+      return region((size_t)h * k_pad * 4) + region((size_t)h * m * k_pad * 2) +
+             region((size_t)gemv_splits_bound((int)d, 1, (int)h) * h * rows * m * 4);
+    }
     default:
       return 0;
   }

@@ -51,8 +51,10 @@ hipError_t launch_gather_pack(const int32_t* given, int k, const uint16_t* A, in
 hipError_t launch_iota(int32_t* idx, int64_t idx_hs, int heads, int d, int32_t* pad, int64_t pad_hs, int k_pad,
                        hipStream_t s);
 
-// pad[t] = idx[t] for t < k when 0 <= idx[t] < d, else -1 (t < k_pad).
-hipError_t launch_pad_index(const int32_t* idx, int k, int d, int32_t* pad, int k_pad, hipStream_t s);
+// pad[b][t] = idx[b][t] for t < k when 0 <= idx[b][t] < d, else -1 (t < k_pad),
+// for each of `heads` lists (strides idx_hs, pad_hs).
+hipError_t launch_pad_index(const int32_t* idx, int k, int d, int32_t* pad, int k_pad, hipStream_t s,
+                            int heads = 1, int64_t idx_hs = 0, int64_t pad_hs = 0);
 
 // QK^T selection and gather in one launch (heads of dh <= 256 features,
 // 16-byte aligned rows): from the summed partials of each query head it
@@ -71,6 +73,15 @@ hipError_t launch_qk_select_pack(const float* partial, int splits, const uint16_
 hipError_t launch_pack(const void* src, bool src_bf16, int64_t src_hs, int64_t src_rs, int src_group,
                        const int32_t* idx, int64_t idx_hs, int k, int k_pad,
                        int batch, int rows, uint16_t* out, int64_t out_hs, hipStream_t s);
+
+// Softmax with the kept key lists (decode: every query row of a head in one
+// workgroup, tk <= softmax_select_max_keys()): writes P and the energies as
+// launch_softmax_energy does, and idx[h][0..k) ascending, the k largest
+// energies of head h (ties to the lower index).
+int softmax_select_max_keys();
+hipError_t launch_softmax_select(const float* L, int64_t l_hs, int64_t l_ts, float* P, int64_t p_hs, int64_t p_ts,
+                                 int heads, int tq, int tk, float scale, float* energy, int k, int32_t* idx,
+                                 hipStream_t s);
 
 // bf16 MFMA GEMM with fp32 accumulation.
 struct GemmArgs {
@@ -143,6 +154,8 @@ struct GemvArgs {
   void* Y; bool y_bf16; int64_t ldy;
   int batch = 1; int64_t a_bs = 0, b_bs = 0, idx_bs = 0, y_bs = 0; int b_group = 1;
   bool b_i8 = false; const float* col_scale = nullptr;
+  // select: rank the d columns of A in every workgroup (idx unused);
+  // otherwise d > 0 makes entries of idx outside [0, d) zero rows
   bool select = false; int d = 0; int32_t* idx_out = nullptr;
 };
 int gemv_select_max_d();

@@ -473,15 +473,17 @@ __global__ __launch_bounds__(kSmallD) void topk_small_kernel(const float* __rest
 // Caller-supplied index list -> the padded form the loaders read: entries
 // outside [0, d) and the tail past k become -1 (a column / row that
 // contributes nothing).
-__global__ void pad_index_kernel(const int32_t* __restrict__ idx, int k, int d, int32_t* __restrict__ pad, int k_pad) {
+__global__ void pad_index_kernel(const int32_t* __restrict__ idx, int64_t idx_hs, int k, int d,
+                                 int32_t* __restrict__ pad, int64_t pad_hs, int k_pad) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= k_pad) return;
+  const int b = blockIdx.y;
   int v = -1;
   if (t < k) {
-    const int j = idx[t];
+    const int j = idx[(size_t)b * idx_hs + t];
     v = (j >= 0 && j < d) ? j : -1;
   }
-  pad[t] = v;
+  pad[(size_t)b * pad_hs + t] = v;
 }
 
 __global__ void iota_kernel(int32_t* idx, int64_t idx_hs, int d, int32_t* pad, int64_t pad_hs, int k_pad) {
@@ -939,8 +941,9 @@ hipError_t launch_gather_pack(const int32_t* given, int k, const uint16_t* A, in
   return hipGetLastError();
 }
 
-hipError_t launch_pad_index(const int32_t* idx, int k, int d, int32_t* pad, int k_pad, hipStream_t s) {
-  pad_index_kernel<<<(k_pad + 255) / 256, 256, 0, s>>>(idx, k, d, pad, k_pad);
+hipError_t launch_pad_index(const int32_t* idx, int k, int d, int32_t* pad, int k_pad, hipStream_t s, int heads,
+                            int64_t idx_hs, int64_t pad_hs) {
+  pad_index_kernel<<<dim3((k_pad + 255) / 256, heads), 256, 0, s>>>(idx, idx_hs, k, d, pad, pad_hs, k_pad);
   return hipGetLastError();
 }
 

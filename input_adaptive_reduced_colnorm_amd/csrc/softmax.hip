@@ -18,6 +18,7 @@
 
 #include "rmm_device.h"
 #include "rmm_internal.h"
+#include "select_block.h"
 
 namespace rmm {
 
@@ -25,23 +26,76 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <int NT>
 __device__ __forceinline__ float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();   // red is reused row after row
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
 }
 
-// fixed-order sum: a butterfly inside each wave, then the 4 waves in order
+// fixed-order sum: a butterfly inside each wave, then the waves in order
+template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  return ((red[0] + red[1]) + red[2]) + red[3];
+  float t = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) t += red[w];
+  return t;
+}
+
+// Softmax of rows [r0, r1) of one head by NT threads, adding each key's
+// P^2 into e2[c] (key tid + NT c).
+template <int C, int NT = kThreads>
+__device__ __forceinline__ void softmax_rows(const float* __restrict__ Lh, int64_t l_ts, float* __restrict__ Ph,
+                                             int64_t p_ts, int r0, int r1, int tk, float scale, float* red,
+                                             float (&e2)[C]) {
+  for (int r = r0; r < r1; ++r) {
+    const float* lr = Lh + (size_t)r * l_ts;
+    float x[C];
+    float mx = -INFINITY;
+    // every load of the row is issued before any is used (a use inside the
+    // guarded load would wait for each load in turn); -inf stays -inf
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int j = threadIdx.x + NT * c;
+      x[c] = j < tk ? lr[j] : -INFINITY;
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      x[c] *= scale;
+      mx = fmaxf(mx, x[c]);
+    }
+    mx = block_max<NT>(mx, red);
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int j = threadIdx.x + NT * c;
+      x[c] = j < tk ? expf(x[c] - mx) : 0.f;
+      sum += x[c];
+    }
+    sum = block_sum<NT>(sum, red);
+    const float inv = 1.f / sum;
+    float* pr = Ph + (size_t)r * p_ts;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int j = threadIdx.x + NT * c;
+      if (j < tk) {
+        const float p = x[c] * inv;
+        pr[j] = p;
+        e2[c] = fmaf(p, p, e2[c]);
+      }
+    }
+  }
 }
 
 template <int C>
@@ -53,54 +107,63 @@ __global__ __launch_bounds__(kThreads) void softmax_energy_kernel(const float* _
   const int head = blockIdx.y;
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(tq, r0 + rows_per_block);
-  const float* Lh = L + (size_t)head * l_hs;
-  float* Ph = P + (size_t)head * p_hs;
   float e2[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) e2[c] = 0.f;
-  for (int r = r0; r < r1; ++r) {
-    const float* lr = Lh + (size_t)r * l_ts;
-    float x[C];
-    float mx = -INFINITY;
-    // every load of the row is issued before any is used (a use inside the
-    // guarded load would wait for each load in turn); -inf stays -inf
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int j = threadIdx.x + kThreads * c;
-      x[c] = j < tk ? lr[j] : -INFINITY;
-    }
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      x[c] *= scale;
-      mx = fmaxf(mx, x[c]);
-    }
-    mx = block_max(mx, red);
-    float sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int j = threadIdx.x + kThreads * c;
-      x[c] = j < tk ? expf(x[c] - mx) : 0.f;
-      sum += x[c];
-    }
-    sum = block_sum(sum, red);
-    const float inv = 1.f / sum;
-    float* pr = Ph + (size_t)r * p_ts;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int j = threadIdx.x + kThreads * c;
-      if (j < tk) {
-        const float p = x[c] * inv;
-        pr[j] = p;
-        e2[c] = fmaf(p, p, e2[c]);
-      }
-    }
-  }
+  softmax_rows<C>(L + (size_t)head * l_hs, l_ts, P + (size_t)head * p_hs, p_ts, r0, r1, tk, scale, red, e2);
   float* part = partial + ((size_t)head * gridDim.x + blockIdx.x) * tk;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int j = threadIdx.x + kThreads * c;
     if (j < tk) part[j] = e2[c];
   }
+}
+
+// Decode: one workgroup holds every query row of its head, so its column
+// sums are the head's final energies; it also ranks them (the block TopK of
+// select_block.h, the keys passing through LDS into a contiguous chunk per
+// thread so that the kept list comes out ascending) and writes the head's
+// kept list.  1024 threads, so that the ranking holds at most 8 keys per
+// thread (with 32 keys per thread on 256 threads it took longer than the
+// separate TopK launch it replaces).  The softmax sums run over 16 waves,
+// so P may differ from rmm_softmax_energy's in the last bit.
+constexpr int kSelNT = 1024;
+
+template <int C>
+__global__ __launch_bounds__(kSelNT) void softmax_select_kernel(const float* __restrict__ L, int64_t l_hs,
+                                                                int64_t l_ts, float* __restrict__ P, int64_t p_hs,
+                                                                int64_t p_ts, int tq, int tk, float scale,
+                                                                float* __restrict__ energy, int k,
+                                                                int32_t* __restrict__ idx) {
+  __shared__ float red[kSelNT / 64];
+  __shared__ uint32_t s_keys[kSelNT * C];
+  __shared__ sel::Shared<kSelNT / 64> sh;
+  const int head = blockIdx.x;
+  float e2[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) e2[c] = 0.f;
+  softmax_rows<C, kSelNT>(L + (size_t)head * l_hs, l_ts, P + (size_t)head * p_hs, p_ts, 0, tq, tk, scale, red,
+                          e2);
+  float* eh = energy + (size_t)head * tk;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int j = threadIdx.x + kSelNT * c;
+    if (j < tk) {
+      eh[j] = e2[c];
+      s_keys[j] = __float_as_uint(e2[c]);   // energies are >= 0: bit order is value order
+    }
+  }
+  lds_barrier();
+  sel::KeyChunk<C> kc;
+  const int chunk = (tk + kSelNT - 1) / kSelNT;   // <= C
+  kc.j0 = min(tk, (int)threadIdx.x * chunk);
+  kc.cnt = min(chunk, tk - kc.j0);
+#pragma unroll
+  for (int i = 0; i < C; ++i) kc.key[i] = i < kc.cnt ? s_keys[kc.j0 + i] : 0u;
+  int32_t* out = idx + (size_t)head * k;
+  sel::select_ascending<kSelNT, C>(kc, k, sh, [&](bool take, uint32_t pos, int j, uint32_t) {
+    if (take) out[pos] = j;
+  });
 }
 
 // q[h][j] = sum over row blocks b = 0, 1, ... of partial[h][b][j], in order.
@@ -145,6 +208,19 @@ hipError_t launch_softmax_energy(const float* L, int64_t l_hs, int64_t l_ts, flo
   if (e != hipSuccess || blocks == 1) return e;
   dim3 g2((tk + 255) / 256, heads);
   energy_reduce_kernel<<<g2, 256, 0, s>>>(partial, blocks, tk, q);
+  return hipGetLastError();
+}
+
+int softmax_select_max_keys() { return 8 * kSelNT; }
+
+hipError_t launch_softmax_select(const float* L, int64_t l_hs, int64_t l_ts, float* P, int64_t p_hs, int64_t p_ts,
+                                 int heads, int tq, int tk, float scale, float* energy, int k, int32_t* idx,
+                                 hipStream_t s) {
+  if (tk > softmax_select_max_keys() || k < 1 || k > tk) return hipErrorInvalidValue;
+  if (tk <= 4 * kSelNT)
+    softmax_select_kernel<4><<<heads, kSelNT, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, scale, energy, k, idx);
+  else
+    softmax_select_kernel<8><<<heads, kSelNT, 0, s>>>(L, l_hs, l_ts, P, p_hs, p_ts, tq, tk, scale, energy, k, idx);
   return hipGetLastError();
 }
 

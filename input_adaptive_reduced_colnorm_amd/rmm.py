@@ -21,7 +21,7 @@ RMM_BF16 = 1
 
 # operation codes of rmm_workspace_bytes (rmm_op_t)
 OPS = {"select": 0, "matmul": 1, "qk": 2, "pv": 3, "matmul_w8": 4, "matmul_idx": 5, "softmax_energy": 6,
-       "pv_energy": 7}
+       "pv_energy": 7, "softmax_select": 8, "pv_idx": 9}
 
 _c = ctypes
 _vp, _i64, _dbl, _sz, _int = _c.c_void_p, _c.c_int64, _c.c_double, _c.c_size_t, _c.c_int
@@ -58,6 +58,12 @@ SIGNATURES = {
     "rmm_pv": (_int, [_vp, _int, _vp, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl, _vp, _vp,
                       _int, _vp, _sz, _vp]),
     "rmm_softmax_energy_workspace": (_sz, [_i64, _i64, _i64]),
+    "rmm_softmax_select_workspace": (_sz, [_i64, _i64, _i64]),
+    "rmm_softmax_select": (_int, [_vp, _c.c_float, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _dbl, _vp,
+                                  _vp, _sz, _vp]),
+    "rmm_pv_idx_workspace": (_sz, [_i64, _i64, _i64, _i64, _int]),
+    "rmm_pv_idx": (_int, [_vp, _int, _vp, _int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                          _vp, _int, _vp, _sz, _vp]),
     "rmm_softmax_energy": (_int, [_vp, _c.c_float, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp]),
     "rmm_pv_energy_workspace": (_sz, [_i64, _i64, _i64, _i64, _int, _int, _dbl]),
     "rmm_pv_energy": (_int, [_vp, _int, _vp, _int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _dbl,
@@ -332,6 +338,53 @@ def softmax_energy(L_: torch.Tensor, scale: float = 1.0, P: torch.Tensor = None,
                               P.stride(1), energy.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _raise(st, "rmm_softmax_energy")
     return P, energy
+
+
+def softmax_select(L_: torch.Tensor, rho: float, scale: float = 1.0, P: torch.Tensor = None,
+                   energy: torch.Tensor = None, idx: torch.Tensor = None):
+    """rmm_softmax_select: softmax_energy and, for every head, the k = ceil(rho tk)
+    key positions of largest energy (ascending).  Returns (P, energy, idx (h, k))."""
+    dev = _check_dev(L_)
+    if L_.dtype != torch.float32 or L_.dim() != 3 or L_.stride(2) != 1:
+        raise TypeError("logits must be fp32 (h, tq, tk) with unit inner stride")
+    h, tq, tk = L_.shape
+    if P is None:
+        P = torch.empty((h, tq, tk), dtype=torch.float32, device=dev)
+    if energy is None:
+        energy = torch.empty((h, tk), dtype=torch.float32, device=dev)
+    L = lib()
+    if idx is None:
+        idx = torch.empty((h, k(rho, tk)), dtype=torch.int32, device=dev)
+    ws = _ws(L.rmm_softmax_select_workspace(h, tq, tk), dev)
+    st = L.rmm_softmax_select(L_.data_ptr(), float(scale), h, tq, tk, L_.stride(0), L_.stride(1), P.data_ptr(),
+                              P.stride(0), P.stride(1), energy.data_ptr(), float(rho), idx.data_ptr(), ws.data_ptr(),
+                              ws.numel(), _stream(dev))
+    _raise(st, "rmm_softmax_select")
+    return P, energy, idx
+
+
+def pv_idx(P: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, out_dtype=torch.float32,
+           workspace: torch.Tensor = None, out: torch.Tensor = None) -> torch.Tensor:
+    """rmm_pv_idx: per-head P V over given key lists idx (h, k) int32 (entries
+    outside [0, tk) contribute nothing).  Returns O (h, tq, dv)."""
+    dev = _check_dev(P, V, idx)
+    h, tq, tk = P.shape
+    hkv, tk2, dv = V.shape
+    if tk2 != tk or P.stride(2) != 1 or V.stride(2) != 1:
+        raise ValueError("P key axis must match V rows; unit inner strides")
+    if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != h or not idx.is_contiguous():
+        raise TypeError("idx must be a contiguous int32 (h, k) tensor")
+    L = lib()
+    kk = idx.shape[1]
+    if out is None:
+        out = torch.empty((h, tq, dv), dtype=out_dtype, device=dev)
+    if workspace is None:
+        workspace = _ws(L.rmm_pv_idx_workspace(h, tq, kk, dv, _dt(V)), dev)
+    st = L.rmm_pv_idx(P.data_ptr(), _dt(P), V.data_ptr(), _dt(V), idx.data_ptr(), kk, h, hkv, tq, tk, dv,
+                      P.stride(0), P.stride(1), V.stride(0), V.stride(1), out.data_ptr(), _dt(out),
+                      workspace.data_ptr(), workspace.numel(), _stream(dev))
+    _raise(st, "rmm_pv_idx")
+    return out
 
 
 def pv_energy(P: torch.Tensor, V: torch.Tensor, energy: torch.Tensor, rho: float, out_dtype=torch.float32,

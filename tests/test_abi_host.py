@@ -269,6 +269,36 @@ def test_softmax_energy_and_pv_energy_reject_bad_arguments(L):
     assert pe(E=FAKE + (2 << 30)) == ALIAS   # energies on top of the index output
 
 
+def test_softmax_select_and_pv_idx_reject_bad_arguments(L):
+    def ss(Lp=FAKE, scale=1.0, h=4, tq=16, tk=512, lhs=8192, lts=512, P=FAKE + (1 << 30), phs=8192, pts=512,
+           E=FAKE + (2 << 30), rho=0.5, idx=FAKE + (4 << 30), ws=FAKE + (3 << 30), wsb=1 << 30):
+        return L.rmm_softmax_select(Lp, scale, h, tq, tk, lhs, lts, P, phs, pts, E, rho, idx, ws, wsb, None)
+
+    assert ss(idx=None) == NULL
+    assert ss(rho=0.0) == RHO
+    assert ss(rho=1.5) == RHO
+    assert ss(scale=-1.0) == SHAPE
+    assert ss(tk=20000) == SHAPE
+    assert ss(idx=FAKE + (4 << 30) + 2) == ALIGN
+    assert ss(wsb=4) == WS                   # 16 rows of 4 heads: the separate TopK path needs scratch
+    assert ss(idx=FAKE + (2 << 30) + 64) == ALIAS   # the lists on top of the energies
+    # decode-shaped (one workgroup per head): no workspace at all
+    assert L.rmm_softmax_select_workspace(4, 1, 512) == 0
+
+    def pi(P=FAKE, pdt=FP32, V=FAKE + (1 << 30), vdt=BF16, idx=FAKE + (2 << 30), k=32, h=4, hkv=2, tq=8, tk=64,
+           dv=16, O=FAKE + (3 << 30), ws=FAKE + (4 << 30), wsb=1 << 30):
+        return L.rmm_pv_idx(P, pdt, V, vdt, idx, k, h, hkv, tq, tk, dv, 512, 64, 1024, 16, O, FP32, ws, wsb, None)
+
+    assert pi(idx=None) == NULL
+    assert pi(vdt=5) == DTYPE
+    assert pi(k=0) == SHAPE
+    assert pi(h=6, hkv=4) == SHAPE
+    assert pi(idx=FAKE + (2 << 30) + 1) == ALIGN
+    assert pi(ws=None) == WS                 # the padded lists always need workspace
+    assert pi(O=FAKE + (2 << 30)) == ALIAS   # output on top of the lists
+    assert L.rmm_pv_idx_workspace(4, 8, 32, 16, BF16) > 0
+
+
 def test_generic_workspace_bound_covers_every_per_call_query(L):
     """rmm_workspace_bytes(op, ...) is at least the per-call query for every
     rho, dtype and size within its arguments' bounds."""
@@ -304,6 +334,14 @@ def test_generic_workspace_bound_covers_every_per_call_query(L):
                     assert be >= L.rmm_pv_energy_workspace(h, tq, tk, dv, pdt, vdt, rho)
         if tk <= 8192:
             assert L.rmm_workspace_bytes(6, h, tk, tq) == L.rmm_softmax_energy_workspace(h, tq, tk)
+            assert L.rmm_workspace_bytes(8, h, tk, tq) == L.rmm_softmax_select_workspace(h, tq, tk)
+        for k in (1, tk // 2, tk, 2 * tk):
+            bi = L.rmm_workspace_bytes(9, h, k, max(tq, dv))
+            for vdt in (FP32, BF16):
+                assert bi >= L.rmm_pv_idx_workspace(h, tq, k, dv, vdt), (h, tq, k, dv, vdt)
+    # one workgroup per head (decode) ranks inside the softmax pass: no scratch
+    assert L.rmm_softmax_select_workspace(32, 1, 8192) == 0
+    assert L.rmm_softmax_select_workspace(64, 512, 8192) > 0
     # unknown op and bad sizes
     assert L.rmm_workspace_bytes(99, 8, 8, 8) == 0
     assert L.rmm_workspace_bytes(1, 0, 8, 8) == 0

@@ -751,6 +751,72 @@ def test_full_decode_attention(dev):
         assert_close(f32(Og), O_o, pv_envelope(Pc, Vc, idx_o), TOL_BF16, "PV")
 
 
+def check_softmax_select(L, rho, dev, scale=1.0):
+    P, E, idx = rmm.softmax_select(L.to(dev), rho, scale)
+    torch.cuda.synchronize()
+    Pg, Eg = f32(P), f32(E)
+    Po = O.softmax_rows(f32(L), scale)
+    assert rel_fro(Pg, Po) <= 1e-6
+    assert np.max(np.abs(Pg - Po)) <= 1e-6 * np.max(Po)
+    Eo = np.stack([O.col_energy(Pg[h]) for h in range(Pg.shape[0])])
+    assert rel_fro(Eg, Eo) <= 1e-5
+    # the lists are the selection on the energies the call wrote
+    zero_v = np.zeros((Pg.shape[0], Pg.shape[2], 1))
+    idx_o, _ = O.pv_given_energy(Pg, zero_v, Eg, rho)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    return P, E, idx
+
+
+@pytest.mark.parametrize("h,tq,tk,rho", [(32, 1, 8192, 0.5), (8, 1, 1000, 0.3), (8, 2, 3000, 0.7),
+                                         (16, 4, 2048, 1.0), (4, 96, 1024, 0.5), (2, 40, 300, 0.2)])
+def test_softmax_select(dev, h, tq, tk, rho):
+    # one workgroup per head ranks inside the softmax pass (8, 16 and 32 keys
+    # per thread, 1 to 4 query rows); longer query blocks run the softmax
+    # pass and then TopK over its energies
+    w = synth.attn_pv(h=h, hkv=1, tq=tq, tk=tk, dv=8, rho=min(rho, 0.9), with_logits=True)
+    print(f"softmax_select h={h} tq={tq} tk={tk} rho={rho}", flush=True)
+    check_softmax_select(w.tensors["L"], rho, dev, scale=0.5)
+
+
+@pytest.mark.parametrize("h,hkv,tq,tk,dv,vdt", [(32, 8, 1, 8192, 128, torch.bfloat16),
+                                                (8, 2, 4, 1000, 64, torch.bfloat16),
+                                                (4, 2, 96, 1024, 64, torch.bfloat16),
+                                                (4, 1, 20, 300, 24, torch.float32)])
+def test_pv_idx(dev, h, hkv, tq, tk, dv, vdt):
+    # PV over given per-head lists: the GEMV per head (tq <= 16), the packed
+    # product, and fp32 V (vector-ALU product); lists unsorted, with repeats
+    # and entries outside [0, tk)
+    w = synth.attn_pv(h=h, hkv=hkv, tq=tq, tk=tk, dv=dv, rho=0.5)
+    P, V = w.tensors["P"], w.tensors["V"].to(vdt)
+    k = tk // 2
+    idx = np.stack([_given_idx(tk, k, seed=100 + i) for i in range(h)])
+    print(f"pv_idx h={h} tq={tq} tk={tk} dv={dv} {vdt}", flush=True)
+    Og = rmm.pv_idx(P.to(dev), V.to(dev), torch.from_numpy(idx).to(dev))
+    torch.cuda.synchronize()
+    Pc, Vc = f32(P), f32(V)
+    g = h // hkv
+    ref = np.stack([O.matmul_given(Pc[i], Vc[i // g], idx[i]) for i in range(h)])
+    env = np.stack([envelope(Pc[i], Vc[i // g], idx[i]) for i in range(h)])
+    assert_close(f32(Og), ref, env, TOL_FP32 if vdt == torch.float32 else TOL_BF16, "PV over given lists")
+
+
+def test_decode_attention_softmax_select_then_pv_idx(dev):
+    # the ranking inside the softmax pass and the TopK launch of
+    # rmm_pv_energy, on the same P and energies, keep the same lists, and the
+    # PV over those lists is the same GEMV: bit for bit
+    w = synth.attn_pv(h=32, hkv=8, tq=1, tk=8192, dv=128, rho=0.5, with_logits=True)
+    Ld, Vd = w.tensors["L"].to(dev), w.tensors["V"].to(dev)
+    P1, E1, idx1 = check_softmax_select(w.tensors["L"], 0.5, dev, scale=128 ** -0.5)
+    O1 = rmm.pv_idx(P1, Vd, idx1)
+    idx2, O2 = rmm.pv_energy(P1, Vd, E1, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(O1.view(torch.int32), O2.view(torch.int32))
+    Pc, Vc = f32(P1), f32(w.tensors["V"])
+    idx_o, O_o = O.pv_given_energy(Pc, Vc, f32(E1), 0.5)
+    assert_close(f32(O1), O_o, pv_envelope(Pc, Vc, idx_o), TOL_BF16, "PV")
+
+
 # ----------------------------- full sizes -----------------------------------
 
 def test_full_mlp_down(dev):
