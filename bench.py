@@ -171,9 +171,11 @@ class MatmulOp:
         """Algorithmic work per stage: (kind, amount) with kind 'B' bytes or 'F' flops."""
         n, d, m, k = self.n, self.d, self.m, self.ks[rho]
         if self.decode:
-            # one workgroup scores and selects; the GEMV streams the kept rows of B
+            # rows of up to 8192 columns: every GEMV workgroup ranks the
+            # columns of A itself, so the GEMV stage holds the selection;
+            # wider rows select in one workgroup first
             w = {"gemm": ("B", k * m * 2)}
-            if k < d:
+            if k < d and d > 8192:
                 w["score"] = ("B", n * d * 2)
             return w
         w = {"gemm": ("F", 2.0 * n * k * m)}
@@ -198,7 +200,8 @@ class MatmulOp:
 
     def roofline_kernel(self):
         if self.decode:
-            return "gemv_kernel + gemv_reduce_kernel (kept rows of B, then the slices added in order)"
+            return ("gemv_kernel + gemv_reduce_kernel (each workgroup ranks the columns of A, then reads the kept "
+                    "rows of B; the slices added in order)")
         return "gemm_bf16_kernel<256,256,kmajor,gather> (reduced GEMM)"
 
     def traffic_ref(self):
@@ -292,7 +295,7 @@ class MatmulW8Op(MatmulOp):
         n, d, m, k = self.n, self.d, self.m, self.ks[rho]
         if self.decode:
             w = {"gemm": ("B", k * m * 1)}
-            if k < d:
+            if k < d and d > 8192:
                 w["score"] = ("B", n * d * 2)
             return w
         w = {"gemm": ("F", 2.0 * n * k * m)}
@@ -308,7 +311,8 @@ class MatmulW8Op(MatmulOp):
 
     def roofline_kernel(self):
         if self.decode:
-            return "gemv_kernel<bf16 A, int8 B> + gemv_reduce_kernel (kept int8 rows of B, then the slices added in order)"
+            return ("gemv_kernel<bf16 A, int8 B> + gemv_reduce_kernel (each workgroup ranks the columns of A, "
+                    "then reads the kept int8 rows of B; the slices added in order)")
         return "gemm_bf16_kernel<256,256,kmajor,gather,int8 B> (reduced GEMM)"
 
     def traffic_ref(self):
