@@ -587,9 +587,9 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
 // they land while it runs), and each lane gathers 8 consecutive kept
 // positions from LDS and writes them as one 16-byte piece of the
 // K-contiguous panel.  Whole-row loads avoid the address rate of 2-byte
-// global gathers, and the ranking repeated per workgroup (a few microseconds
-// of VALU work) replaces a single-workgroup launch that the whole chip
-// waited for.  Needs d <= kKeyCap, d % 8 == 0, lda % 8 == 0 and A 16-byte
+// global gathers, and the ranking repeated per workgroup (several
+// microseconds, while the first rows stream in) replaces a single-workgroup
+// launch that the whole chip waited for.  Needs d <= kKeyCap, d % 8 == 0, lda % 8 == 0 and A 16-byte
 // aligned (select_pack_fits).
 //
 // Row buffers: NB = D + 1, row i in buffer i % NB, so the buffer refilled
@@ -723,12 +723,11 @@ __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* _
 // heads of at most 256 features, rows of whole 16-byte pieces).  A
 // workgroup of 256 threads owns 32 KB of rows (16384 / dh rows) of one
 // query head's Q, or of its kv head's K: it sums the head's split partials,
-// sends its rows
-// from the buffer straight into LDS (untracked direct loads, issued before
-// the ranking so that they land while it runs), ranks the features as
-// topk_small_kernel does (each thread counts the composite keys that
-// outrank its own), and writes the kept features of each row as 16-byte
-// pieces of the K-contiguous panels.  The first Q workgroup of each head
+// sends its rows from the buffer straight into LDS (untracked direct loads,
+// issued before the ranking so that they land while it runs), ranks the
+// features as topk_small_kernel does (each thread counts the composite keys
+// that outrank its own), and writes the kept features of each row as
+// 16-byte pieces of the K-contiguous panels.  The first Q workgroup of each head
 // writes its ascending kept list.  Four workgroups share a compute unit
 // (35 KB of LDS each), so one's ranking overlaps another's loads.
 // ---------------------------------------------------------------------------
