@@ -150,7 +150,9 @@ rmm_status_t rmm_select_retained(const void* A, int dtype, int64_t n, int64_t d,
  *   idx [k] int32 ascending (always written; 0..d-1 when rho = 1).
  *   Y   [n x m] (ldy >= m), y_dtype fp32 or bf16.
  * rho = 1 computes the dense product with no scoring pass.
- * n <= 16 with bf16 takes the decode path (GEMV over the kept rows of B).
+ * n <= 16 with bf16 takes the decode path (GEMV over the kept rows of B;
+ * with rho < 1 and d <= 8192 it ranks A itself, and the first rows of each
+ * of its slices of B are requested while it ranks, dropped ones included).
  * Source: hackcv.com, Core Approach: RMM_rho(A, B) = A[:, I] B[I, :];
  * linear / MLP mapping from the Component mapping paragraph.
  * ------------------------------------------------------------------- */
@@ -204,8 +206,8 @@ rmm_status_t rmm_matmul_timed(const void* A, const void* B, int dtype, int64_t n
  *          ldb multiples of 8.  Values in [-128, 127], widened to bf16
  *          exactly on the device.
  *   scale  fp32 [m], device.
- *   idx, Y, y_dtype, ldy, rho as in rmm_matmul (n <= 16 runs the GEMV that
- *   reads only the kept rows of Bq: half the bytes of bf16 weights).
+ *   idx, Y, y_dtype, ldy, rho as in rmm_matmul (n <= 16 runs the GEMV over
+ *   the kept rows of Bq: half the bytes of bf16 weights).
  *   Workspace: rmm_matmul_w8_workspace(n, d, m, lda, rho) bytes, 256-byte
  *   aligned (0 means none needed).
  * Errors as rmm_matmul; RMM_ERR_DTYPE for an A that is not bf16,

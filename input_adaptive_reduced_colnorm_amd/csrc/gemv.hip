@@ -17,8 +17,10 @@
 // sit in LDS as bf16 and are the other operand.  Roofline: HBM; the matrix
 // cores only take the arithmetic off the vector ALUs.
 //
-// Work split: the kept rows are cut into `splits` slices of at most 512
-// (a multiple of 32) and the columns into 128-column strips; a 256-thread
+// Work split: the rows are cut into `splits` slices of at most 512 (a
+// multiple of 32; slices of a given or the identity list, or of the source
+// rows of B where the kernel ranks A itself, see gemv_rank_kernel) and the
+// columns into 128-column strips; a 256-thread
 // workgroup owns a (strip, slice) pair and its 4 waves take the slice's
 // 32-row chunks round robin.  Vector loads retire in order, so a wave first
 // loads every kept-row index it needs, then the activations it stages, and
@@ -46,82 +48,82 @@ constexpr int kChunk = 32;                    // kept rows per MFMA step
 constexpr int kChunksPerWave = 4;
 constexpr int kMaxSlice = kWaves * kChunksPerWave * kChunk;   // 512 kept rows per workgroup
 constexpr int kTargetGroups = 480;            // workgroups aimed for (256 CUs; measured best near 1.9 per CU)
+constexpr int kSliceStride = kMaxSlice + 8;   // LDS row of staged activations
+constexpr int kHeadChunks = 1;                // ranking GEMV: chunks per wave requested before the ranking
 
-__device__ __forceinline__ int slice_rows(int k, int splits) {
+__host__ __device__ __forceinline__ int slice_rows(int k, int splits) {
   return ((k + splits - 1) / splits + kChunk - 1) / kChunk * kChunk;
 }
 
-// The kept set ranked inside the GEMV (CH > 0): every workgroup computes
-// the column energies of all of A (n <= 16 rows, read from L2 after the
-// first touch) with the same fixed-order fp32 sums as the selection kernel,
-// finds the k-th largest (energy, lowest index) key with the block radix
-// search, and compacts the kept indices that fall in its own slice of the
-// ascending list into LDS; the workgroups of the first column strip also
-// write their slice of the list to idx_out.  This replaces the selection
-// launch in front of the GEMV and the round trip of the list through memory.
-// Thread t ranks the columns [t c, t c + c), c = ceil(d / 256) <= CH.
-template <int CH, int NR, bool A_BF16>
-__device__ __forceinline__ void rank_columns(const GemvArgs& g, sel::KeyChunk<CH>& kc) {
-  const int tid = threadIdx.x;
-  const int chunk = (g.d + kThreads - 1) / kThreads;
-  kc.j0 = min(g.d, tid * chunk);
-  kc.cnt = min(chunk, g.d - kc.j0);
-  float q[CH];
+// One 32-row MFMA step of a wave: the A operand (row l % 16 of the slice's
+// activations, kept rows 8 (l / 16) ..) from LDS, the lane's 8 B row pieces
+// (zeroed where `valid` is clear or the columns lie past m) transposed into
+// the eight column operands.
+template <bool B_I8>
+__device__ __forceinline__ void mfma_step(const bf16x8 af, const typename RowPiece<B_I8>::type (&bv)[8],
+                                          uint32_t valid, f32x4 (&acc)[8]) {
+  i32x4 rows8[8], tr[8];
 #pragma unroll
-  for (int i = 0; i < CH; ++i) q[i] = 0.f;
-  const bool vec = A_BF16 && ((uintptr_t)g.A % 16 == 0) && (g.lda % 8 == 0) && (chunk % 8 == 0);
-  if (vec) {
-    // 16-byte loads; the loads of 8 rows are issued before they are used,
-    // rows are added in ascending order
-    constexpr int V = CH / 8;
-    const char* base = (const char*)g.A + (size_t)kc.j0 * 2;
-    for (int r0 = 0; r0 < NR; r0 += 8) {
-      i32x4 x[8][V];
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const bool ok = r0 + r < g.n && 8 * v < kc.cnt;
-          x[r][v] = ok ? *(const i32x4*)(base + ((size_t)(r0 + r) * g.lda + 8 * v) * 2) : i32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        if (r0 + r < g.n) {
-#pragma unroll
-          for (int v = 0; v < V; ++v)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t w = (uint32_t)x[r][v][e >> 1];
-              const float f = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-              q[8 * v + e] = fmaf(f, f, q[8 * v + e]);
-            }
-        }
-      }
-    }
-  } else {
-    for (int r = 0; r < g.n; ++r) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        if (i < kc.cnt) {
-          const size_t off = (size_t)r * g.lda + kc.j0 + i;
-          const float f = A_BF16 ? bf16_to_f32(((const uint16_t*)g.A)[off]) : ((const float*)g.A)[off];
-          q[i] = fmaf(f, f, q[i]);
-        }
-      }
-    }
+  for (int e = 0; e < 8; ++e) {
+    if (!((valid >> e) & 1u))
+      rows8[e] = i32x4{0, 0, 0, 0};
+    else if constexpr (B_I8)
+      rows8[e] = i8x8_to_bf16x8(bv[e]);
+    else
+      rows8[e] = bv[e];
   }
+  transpose8x8(rows8, tr);
 #pragma unroll
-  for (int i = 0; i < CH; ++i) kc.key[i] = __float_as_uint(q[i]);
+  for (int j = 0; j < 8; ++j)
+    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, tr[j]), acc[j], 0, 0, 0);
 }
 
-template <int NR, bool A_BF16, bool B_I8, int CH = 0>
+// The workgroup's result: lane l, register v of acc[j] holds row 4 (l / 16)
+// + v, column 8 (l % 16) + j of the strip.  The waves are added in order in
+// LDS; one slice writes Y directly, several write their partial sums.
+__device__ __forceinline__ void store_strip(const GemvArgs& g, const f32x4 (&acc)[8], float (&red)[kWaves][16][kCols]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = lane >> 4, cg = lane & 15;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int r = 4 * rb + v;
+    if (r < g.n) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[wave][r][cg * 8 + j] = acc[j][v];
+    }
+  }
+  __syncthreads();
+  const bool direct = g.splits == 1;
+  float* part = g.partial + (size_t)blockIdx.y * g.n * g.m;
+  for (int i = tid; i < g.n * kCols; i += kThreads) {
+    const int r = i / kCols, cc = i % kCols;
+    const int col = blockIdx.x * kCols + cc;
+    if (col >= g.m) continue;
+    float v = red[0][r][cc];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[w][r][cc];
+    if (direct) {
+      const size_t off = (size_t)r * g.ldy + col;
+      if (g.col_scale) v *= g.col_scale[col];
+      if (g.y_bf16)
+        ((uint16_t*)g.Y)[off] = f32_to_bf16(v);
+      else
+        ((float*)g.Y)[off] = v;
+    } else {
+      part[(size_t)r * g.m + col] = v;
+    }
+  }
+}
+
+// Product over a given list (idx; entries outside [0, d) read as zero rows
+// when d > 0) or over the identity list (idx null: rows t0 .. of B, the
+// list also written to idx_out by the first strip's workgroups).  The
+// kept rows are cut into `splits` slices of the list.
+template <int NR, bool A_BF16, bool B_I8>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   constexpr int BE = B_I8 ? 1 : 2;   // bytes per B element
-  constexpr bool SEL = CH > 0;
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kMaxSlice + 8];   // bf16 activations, row r, kept row t
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kSliceStride];   // bf16 activations, row r, kept row t
   __shared__ float red[kWaves][16][kCols];
-  __shared__ sel::Shared<SEL ? kWaves : 1> ssh;
-  __shared__ int32_t s_list[SEL ? kMaxSlice : 1];
   {
     // batch member (attention head): shift every operand to its slice
     const int bz = blockIdx.z;
@@ -140,32 +142,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   const int rb = lane >> 4, cg = lane & 15;
   const int c = blockIdx.x * kCols + cg * 8;
   const bool col_ok = c < g.m;   // m is a multiple of 8
-  const bool write_list = g.idx_out && blockIdx.x == 0;
 
-  if constexpr (SEL) {
-    // ---- rank every column of A and keep this slice of the ascending list ----
-    sel::KeyChunk<CH> kc;
-    rank_columns<CH, NR, A_BF16>(g, kc);
-    int32_t* out = g.idx_out;
-    sel::select_window<kThreads, CH>(kc, g.k, ssh, (uint32_t)t0, (uint32_t)(t0 + L), [&](uint32_t pos, int j) {
-      s_list[pos - t0] = j;
-      if (write_list) out[pos] = j;
-    });
-    __syncthreads();
-  } else if (write_list) {
+  if (g.idx_out && blockIdx.x == 0) {
     // the identity list (rho = 1): the first strip's workgroups write it
     for (int i = tid; i < L; i += kThreads) g.idx_out[t0 + i] = t0 + i;
   }
-  // a caller's list entry outside [0, d) (d > 0: the row count of B) reads
-  // as a zero row
   auto kept = [&](int t) -> int {
-    if constexpr (SEL) {
-      return s_list[t];
-    } else {
-      if (!g.idx) return t0 + t;
-      const int j = g.idx[t0 + t];
-      return g.d > 0 && (unsigned)j >= (unsigned)g.d ? -1 : j;
-    }
+    if (!g.idx) return t0 + t;
+    const int j = g.idx[t0 + t];
+    return g.d > 0 && (unsigned)j >= (unsigned)g.d ? -1 : j;
   };
 
   // ---- load order matters: vector loads retire in order, so a wait for a
@@ -239,54 +224,288 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
   for (int q = 0; q < kChunksPerWave; ++q) {
     const int tb = (wave + kWaves * q) * kChunk;
     if (tb >= L) break;   // uniform across the wave
-    // A operand: row l % 16 of A, kept rows tb + 8 (l / 16) ..
-    const bf16x8 af = *(const bf16x8*)&s_a[cg][tb + 8 * rb];
-    i32x4 rows8[8], tr[8];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) valid |= (uint32_t)(row[q][e] >= 0 && col_ok) << e;
+    mfma_step<B_I8>(*(const bf16x8*)&s_a[cg][tb + 8 * rb], bv[q], valid, acc);
+  }
+  store_strip(g, acc, red);
+}
+
+// ---------------------------------------------------------------------------
+// The kept set ranked inside the GEMV (rho < 1, d <= 8192 columns, one
+// product per launch).  Every workgroup computes the column energies of all
+// of A (n <= 16 rows, read from L2 after the first touch) with the same
+// fixed-order fp32 sums as the selection kernel and finds the k-th largest
+// (energy, lowest index) key with the block search.  The slices here are
+// ranges of source rows of B, not of the kept list: workgroup (strip,
+// slice) owns rows [r0, r0 + S).  Ranking takes several microseconds, and a
+// workgroup that waited for it before requesting B would leave HBM idle
+// meanwhile; so the first kHeadChunks 32-row chunks of each wave (the
+// slice's first 128 source rows) are requested before the ranking,
+// whatever their fate, and a dropped row among them is zeroed on both
+// operands; after the ranking only the kept rows of the rest of the slice
+// are requested.  The loads of A for the energies go out first, the head's
+// B rows right after them, so the energies wait for A alone.  The
+// workgroup stages the activations of its own source rows from those same
+// A loads.  The first strip's workgroups write their rows' positions of the
+// ascending list to idx_out at the end.
+// Thread t ranks the columns [t c, t c + c), c = ceil(d / 256) <= CH.
+// `issue` is called once the last batch of A's loads is in flight (on the
+// element-load path, after all of A); `src[r][o]` receives the bf16 value
+// A[r][r0 + o] for the slice's columns.
+template <int CH, int NR, bool A_BF16, typename Issue>
+__device__ __forceinline__ void rank_columns(const GemvArgs& g, sel::KeyChunk<CH>& kc,
+                                             uint16_t (&src)[16][kSliceStride], int r0, int Ls, Issue issue) {
+  const int tid = threadIdx.x;
+  const int chunk = (g.d + kThreads - 1) / kThreads;
+  kc.j0 = min(g.d, tid * chunk);
+  kc.cnt = min(chunk, g.d - kc.j0);
+  // does this thread's chunk hold columns of the slice?
+  const bool mine = kc.j0 < r0 + Ls && kc.j0 + kc.cnt > r0;
+  float q[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) q[i] = 0.f;
+  const bool vec = A_BF16 && ((uintptr_t)g.A % 16 == 0) && (g.lda % 8 == 0) && (chunk % 8 == 0);
+  if (vec) {
+    // 16-byte loads in batches of RB rows (16 loads per lane in flight),
+    // each batch issued before it is used; rows are added in ascending order
+    constexpr int V = CH / 8;
+    constexpr int RB = 16 / V < NR ? 16 / V : NR;
+    const char* base = (const char*)g.A + (size_t)kc.j0 * 2;
+    auto load_batch = [&](int rb0, i32x4 (&x)[RB][V]) {
+      // unconditional (a masked lane reads the start of A), so that the
+      // energies can wait for these loads alone
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const bool ok = rb0 + r < g.n && 8 * v < kc.cnt;
+          const char* pa = ok ? base + ((size_t)(rb0 + r) * g.lda + 8 * v) * 2 : (const char*)g.A;
+          const i32x4 t = *(const i32x4*)pa;
+          x[r][v] = ok ? t : i32x4{0, 0, 0, 0};
+        }
+    };
+    auto fold_batch = [&](int rb0, const i32x4 (&x)[RB][V]) {
+      // the slice's columns go to LDS as whole 16-byte groups (o is a
+      // multiple of 8; past Ls they are never read)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const int o = kc.j0 + 8 * v - r0;
+          if (mine && rb0 + r < g.n && 8 * v < kc.cnt && (unsigned)o < (unsigned)Ls)
+            *(i32x4*)&src[rb0 + r][o] = x[r][v];
+        }
+      // every row is folded (a row past n is zero and adds +0 exactly): a
+      // fold under a branch would let the compiler sink its loads below the
+      // head's, and the energies would wait for B
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t w = (uint32_t)x[r][v][e >> 1];
+            const float f = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+            q[8 * v + e] = fmaf(f, f, q[8 * v + e]);
+          }
+    };
+    // batches of RB rows (16 loads of 16 bytes per lane in flight), rows
+    // added in ascending order; the head goes out after the last batch's
+    // loads, so that its energies wait for A alone
+#pragma unroll 1
+    for (int rb0 = 0; rb0 + RB < NR; rb0 += RB) {
+      i32x4 x[RB][V];
+      load_batch(rb0, x);
+      fold_batch(rb0, x);
+    }
+    {
+      i32x4 x[RB][V];
+      load_batch(NR - RB, x);
+      __builtin_amdgcn_sched_barrier(0);
+      issue();
+      __builtin_amdgcn_sched_barrier(0);
+      fold_batch(NR - RB, x);
+    }
+  } else {
+    // element loads, a row's CH loads in flight together (unconditional: a
+    // masked lane reads the start of A); the head goes out after them
+    for (int r = 0; r < g.n; ++r) {
+      float f[CH];
+      uint16_t h[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const size_t off = i < kc.cnt ? (size_t)r * g.lda + kc.j0 + i : 0;
+        if constexpr (A_BF16) {
+          h[i] = ((const uint16_t*)g.A)[off];
+          f[i] = bf16_to_f32(h[i]);
+        } else {
+          f[i] = ((const float*)g.A)[off];
+          h[i] = 0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        if (i < kc.cnt) {
+          q[i] = fmaf(f[i], f[i], q[i]);
+          const int o = kc.j0 + i - r0;
+          if (mine && (unsigned)o < (unsigned)Ls) src[r][o] = A_BF16 ? h[i] : f32_to_bf16(f[i]);
+        }
+      }
+    }
+    issue();
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) kc.key[i] = __float_as_uint(q[i]);
+}
+
+// LDS of the ranking GEMV: the block search's scratch and the slice's
+// activations are dead once the slice's rows are listed, so the wave sums
+// at the end reuse their space.
+struct RankStage {
+  sel::Shared<kWaves> ssh;
+  alignas(16) uint16_t src[16][kSliceStride];   // bf16 A[r][r0 + o] for the slice's source rows
+};
+union RankLds {
+  RankStage st;
+  float red[kWaves][16][kCols];
+};
+
+template <int NR, bool A_BF16, bool B_I8, int CH>
+__global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
+  constexpr int BE = B_I8 ? 1 : 2;
+  constexpr int HC = kHeadChunks;           // head chunks per wave
+  constexpr int HR = HC * kWaves * kChunk;  // head rows of the slice (128)
+  constexpr uint16_t kNone = 0xffff;   // s_pos of a dropped row (list positions are < k <= 8192)
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kSliceStride];   // activations by MFMA position
+  __shared__ __attribute__((aligned(16))) RankLds u;
+  __shared__ __attribute__((aligned(16))) uint16_t s_pos[kMaxSlice];   // list position of source row r0 + o
+  __shared__ uint16_t s_kept[kMaxSlice];                                 // kept offsets o, ascending
+  __shared__ uint32_t s_cnt[2];                                          // kept rows: all, in the head
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = slice_rows(g.d, g.splits);
+  const int r0 = blockIdx.y * S;
+  const int Ls = max(0, min(g.d, r0 + S) - r0);
+  const int rb = lane >> 4, cg = lane & 15;
+  const int c = blockIdx.x * kCols + cg * 8;
+  const bool col_ok = c < g.m;   // m is a multiple of 8
+  const int cc0 = col_ok ? c : 0;
+  typedef typename RowPiece<B_I8>::type R;
+  R bv[kChunksPerWave][8];
+
+  // head: chunk q < HC of this wave holds the source offsets
+  // (wave + 4 q) * 32 + 8 rb + e; offsets past the slice read row 0 and are
+  // zeroed below
+  auto issue_head = [&]() {
+#pragma unroll
+    for (int q = 0; q < HC; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int o = (wave + kWaves * q) * kChunk + 8 * rb + e;
+        const int rw = o < Ls ? r0 + o : 0;
+        bv[q][e] = __builtin_nontemporal_load((const R*)((const char*)g.B + ((size_t)rw * g.ldb + cc0) * BE));
+      }
+  };
+  for (int i = tid; i < kMaxSlice; i += kThreads) s_pos[i] = kNone;
+  sel::KeyChunk<CH> kc;
+  rank_columns<CH, NR, A_BF16>(g, kc, u.st.src, r0, Ls, issue_head);
+  // the ranking's barriers order the s_pos clear and the src stores before
+  // anything below reads them
+  sel::select_ascending<kThreads, CH>(kc, g.k, u.st.ssh, [&](bool take, uint32_t pos, int j, uint32_t) {
+    const int o = j - r0;
+    if (take && (unsigned)o < (unsigned)Ls) s_pos[o] = (uint16_t)pos;
+  });
+  lds_barrier();
+
+  // ---- the slice's kept offsets in order (two per thread), and how many
+  //      of them lie in the head ----
+  {
+    const int o0 = 2 * tid;
+    const bool k0 = o0 < Ls && s_pos[o0] != kNone;
+    const bool k1 = o0 + 1 < Ls && s_pos[o0 + 1] != kNone;
+    const uint32_t n_k = (uint32_t)k0 + (uint32_t)k1;
+    const uint32_t n_h = (uint32_t)(k0 && o0 < HR) + (uint32_t)(k1 && o0 + 1 < HR);
+    uint32_t inc = n_k, inc_h = n_h;
+    sel::block_incl_scan2<kThreads>(inc, inc_h, u.st.ssh);
+    uint32_t p = inc - n_k;
+    if (k0) s_kept[p++] = (uint16_t)o0;
+    if (k1) s_kept[p] = (uint16_t)(o0 + 1);
+    if (tid == kThreads - 1) {
+      s_cnt[0] = inc;
+      s_cnt[1] = inc_h;
+    }
+  }
+  lds_barrier();
+  const int nh = (int)s_cnt[1];
+  const int Lr = (int)s_cnt[0] - nh;   // kept rows after the head
+
+  // ---- rest: rest chunk i = wave + 4 (q - HC) takes the kept rows
+  //      nh + 32 i .. of the slice; loads unconditional as in gemv_kernel ----
+  int rrow[kChunksPerWave][8];
+#pragma unroll
+  for (int q = HC; q < kChunksPerWave; ++q)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (row[q][e] < 0 || !col_ok)
-        rows8[e] = i32x4{0, 0, 0, 0};
-      else if constexpr (B_I8)
-        rows8[e] = i8x8_to_bf16x8(bv[q][e]);
-      else
-        rows8[e] = bv[q][e];
+      const int i = (wave + kWaves * (q - HC)) * kChunk + 8 * rb + e;
+      rrow[q][e] = i < Lr ? r0 + (int)s_kept[nh + i] : -1;
     }
-    transpose8x8(rows8, tr);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, tr[j]), acc[j], 0, 0, 0);
-  }
+  for (int q = HC; q < kChunksPerWave; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int rw = rrow[q][e] >= 0 ? rrow[q][e] : 0;
+      bv[q][e] = __builtin_nontemporal_load((const R*)((const char*)g.B + ((size_t)rw * g.ldb + cc0) * BE));
+    }
 
-  // ---- lane l, register v of acc[j]: row 4 (l / 16) + v, column
-  //      8 (l % 16) + j of the strip.  Waves are added in order ----
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int r = 4 * rb + v;
-    if (r < g.n) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) red[wave][r][cg * 8 + j] = acc[j][v];
+  // ---- activations by MFMA position: the head's source offsets (dropped
+  //      rows zero), then the rest's kept rows, zero padded to a chunk ----
+  const int npos = HR + (Lr + kChunk - 1) / kChunk * kChunk;
+  for (int t = tid; t < npos; t += kThreads) {
+    int o = -1;
+    if (t < HR) {
+      if (t < Ls && s_pos[t] != kNone) o = t;
+    } else if (t - HR < Lr) {
+      o = s_kept[nh + t - HR];
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_a[r][t] = o >= 0 && r < g.n ? u.st.src[r][o] : (uint16_t)0;
   }
-  __syncthreads();
-  const bool direct = g.splits == 1;
-  float* part = g.partial + (size_t)blockIdx.y * g.n * g.m;
-  for (int i = tid; i < g.n * kCols; i += kThreads) {
-    const int r = i / kCols, cc = i % kCols;
-    const int col = blockIdx.x * kCols + cc;
-    if (col >= g.m) continue;
-    float v = red[0][r][cc];
+  lds_barrier();
+
+  f32x4 acc[8];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) v += red[w][r][cc];
-    if (direct) {
-      const size_t off = (size_t)r * g.ldy + col;
-      if (g.col_scale) v *= g.col_scale[col];
-      if (g.y_bf16)
-        ((uint16_t*)g.Y)[off] = f32_to_bf16(v);
-      else
-        ((float*)g.Y)[off] = v;
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < kChunksPerWave; ++q) {
+    uint32_t valid = 0;
+    int tb;
+    if (q < HC) {
+      tb = (wave + kWaves * q) * kChunk;
+      if (tb >= Ls) continue;   // uniform across the wave
+      const i32x4 pw = *(const i32x4*)&s_pos[tb + 8 * rb];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t pe = ((uint32_t)pw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        valid |= (uint32_t)(tb + 8 * rb + e < Ls && pe != kNone && col_ok) << e;
+      }
     } else {
-      part[(size_t)r * g.m + col] = v;
+      const int ti = (wave + kWaves * (q - HC)) * kChunk;
+      if (ti >= Lr) continue;   // uniform across the wave
+      tb = HR + ti;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) valid |= (uint32_t)(rrow[q][e] >= 0 && col_ok) << e;
     }
+    mfma_step<B_I8>(*(const bf16x8*)&s_a[cg][tb + 8 * rb], bv[q], valid, acc);
+  }
+  // the sums overwrite the ranking's LDS: its last readers (the staging
+  // above) are behind the barrier before the products
+  store_strip(g, acc, u.red);
+
+  if (g.idx_out && blockIdx.x == 0) {
+    for (int o = tid; o < Ls; o += kThreads)
+      if (s_pos[o] != kNone) g.idx_out[s_pos[o]] = r0 + o;
   }
 }
 
@@ -344,23 +563,29 @@ int gemv_splits(int k, int m, int batch) {
 }
 
 template <int NR, int CH>
-void launch_nr_ch(const GemvArgs& g, dim3 grid, hipStream_t s) {
+void launch_rank(const GemvArgs& g, dim3 grid, hipStream_t s) {
   if (g.b_i8)
-    gemv_kernel<NR, true, true, CH><<<grid, kThreads, 0, s>>>(g);   // int8 weights take bf16 activations
+    gemv_rank_kernel<NR, true, true, CH><<<grid, kThreads, 0, s>>>(g);   // int8 weights take bf16 activations
   else if (g.a_bf16)
-    gemv_kernel<NR, true, false, CH><<<grid, kThreads, 0, s>>>(g);
+    gemv_rank_kernel<NR, true, false, CH><<<grid, kThreads, 0, s>>>(g);
   else
-    gemv_kernel<NR, false, false, CH><<<grid, kThreads, 0, s>>>(g);
+    gemv_rank_kernel<NR, false, false, CH><<<grid, kThreads, 0, s>>>(g);
 }
 
 template <int NR>
 void launch_nr(const GemvArgs& g, dim3 grid, hipStream_t s) {
-  if (!g.select)
-    launch_nr_ch<NR, 0>(g, grid, s);
-  else if (g.d <= 16 * kThreads)
-    launch_nr_ch<NR, 16>(g, grid, s);
-  else
-    launch_nr_ch<NR, 32>(g, grid, s);
+  if (!g.select) {
+    if (g.b_i8)
+      gemv_kernel<NR, true, true><<<grid, kThreads, 0, s>>>(g);
+    else if (g.a_bf16)
+      gemv_kernel<NR, true, false><<<grid, kThreads, 0, s>>>(g);
+    else
+      gemv_kernel<NR, false, false><<<grid, kThreads, 0, s>>>(g);
+  } else if (g.d <= 16 * kThreads) {
+    launch_rank<NR, 16>(g, grid, s);
+  } else {
+    launch_rank<NR, 32>(g, grid, s);
+  }
 }
 
 int gemv_select_max_d() { return 32 * kThreads; }
@@ -368,6 +593,11 @@ int gemv_select_max_d() { return 32 * kThreads; }
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s) {
   if (g.n > 16 || (g.b_i8 && !g.a_bf16)) return hipErrorInvalidValue;
   if (g.select && (g.batch != 1 || g.d > gemv_select_max_d() || g.d < g.k || g.idx)) return hipErrorInvalidValue;
+  // slices: of the source rows (select) or of the list, at most kMaxSlice
+  // rows each, and the grid must cover them
+  const int rows = g.select ? g.d : g.k;
+  const int slice = slice_rows(rows, g.splits);
+  if (g.splits < 1 || slice > kMaxSlice || (int64_t)slice * g.splits < rows) return hipErrorInvalidValue;
   dim3 grid((g.m + kCols - 1) / kCols, g.splits, g.batch);
   if (g.n <= 4)
     launch_nr<4>(g, grid, s);

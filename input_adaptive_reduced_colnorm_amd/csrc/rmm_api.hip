@@ -155,7 +155,10 @@ MatPlan plan_matmul(int64_t n, int64_t d, int64_t m, int64_t lda, int64_t ldb, i
   } else if (n <= kDecodeRows) {
     p.path = MatPath::kDecode;
     if (!p.all && d > topk_lds_capacity()) p.off_dkeys = cv.take((size_t)d * 4);
-    p.gemv_splits = gemv_splits((int)p.k, (int)m);
+    // a GEMV that ranks A itself slices the d source rows of B, otherwise
+    // the k rows of the list
+    const bool rank = !p.all && d <= gemv_select_max_d();
+    p.gemv_splits = gemv_splits((int)(rank ? d : p.k), (int)m);
     if (p.gemv_splits > 1) p.off_part = cv.take((size_t)p.gemv_splits * n * m * 4);
   } else {
     const bool a_direct = p.all && a_ptr_ok && lda % 8 == 0 && d % kKTile == 0;

@@ -159,6 +159,7 @@ struct GemvArgs {
   bool select = false; int d = 0; int32_t* idx_out = nullptr;
 };
 int gemv_select_max_d();
+// slices for a list of k rows (with select: k = d, the source rows of B)
 int gemv_splits(int k, int m, int batch = 1);
 int gemv_splits_bound(int kmax, int m, int batch = 1);   // >= gemv_splits(k, m, batch) for all k <= kmax
 hipError_t launch_gemv(const GemvArgs& g, hipStream_t s);
