@@ -200,8 +200,8 @@ class MatmulOp:
 
     def roofline_kernel(self):
         if self.decode:
-            return ("gemv_kernel + gemv_reduce_kernel (each workgroup ranks the columns of A, then reads the kept "
-                    "rows of B; the slices added in order)")
+            return ("gemv_rank_kernel + gemv_reduce_kernel (each workgroup ranks the columns of A while the first "
+                    "rows of its slice of B stream in, then reads the kept rows; the slices added in order)")
         return "gemm_bf16_kernel<256,256,kmajor,gather> (reduced GEMM)"
 
     def traffic_ref(self):
@@ -311,8 +311,9 @@ class MatmulW8Op(MatmulOp):
 
     def roofline_kernel(self):
         if self.decode:
-            return ("gemv_kernel<bf16 A, int8 B> + gemv_reduce_kernel (each workgroup ranks the columns of A, "
-                    "then reads the kept int8 rows of B; the slices added in order)")
+            return ("gemv_rank_kernel<bf16 A, int8 B> + gemv_reduce_kernel (each workgroup ranks the columns of A "
+                    "while the first rows of its slice stream in, then reads the kept int8 rows of B; the slices "
+                    "added in order)")
         return "gemm_bf16_kernel<256,256,kmajor,gather,int8 B> (reduced GEMM)"
 
     def traffic_ref(self):
@@ -962,7 +963,7 @@ class DecodeAttnOp:
         return {"qk": "qk_decode_kernel (streaming pass over the key cache)",
                 "softmax": "softmax_select_kernel (softmax, key energies and the kept lists; dense: "
                            "softmax_energy_kernel)",
-                "pv": "the rmm_pv_idx call: pad_index_kernel, gemv_kernel batched over heads (kept V rows) and "
+                "pv": "the rmm_pv_idx call: gemv_kernel batched over heads (the listed V rows) and "
                       "gemv_reduce_kernel (dense: rmm_pv_energy over every row)"}
 
     def traffic_ref(self):
