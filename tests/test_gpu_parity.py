@@ -358,6 +358,27 @@ def test_decode_source_slices(dev, n, d, m, rho):
     check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16)
 
 
+@pytest.mark.parametrize("n,d,m", [(8, 4096, 520), (300, 2048, 264), (16, 8192, 264)])
+def test_dropped_rows_of_b_never_reach_the_product(dev, n, d, m):
+    # the decode GEMV requests each slice's first rows before it knows which
+    # are kept and zeroes the dropped ones on both operands; the prefill
+    # GEMM gathers only kept rows: NaN in every dropped row of B must leave
+    # Y and idx exactly as with zeros there
+    w = synth.decode_qkv(n=n, d=d, m=m, rho=0.6)
+    A, B = w.tensors["A"], w.tensors["B"]
+    idx_o, _ = O.select(f32(A), 0.6)
+    drop = np.setdiff1d(np.arange(d), idx_o)
+    Bz, Bn = B.clone(), B.clone()
+    Bz[drop] = 0
+    Bn[drop] = float("nan")
+    i1, y1 = rmm.matmul(A.to(dev), Bz.to(dev), 0.6)
+    i2, y2 = rmm.matmul(A.to(dev), Bn.to(dev), 0.6)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(i1.cpu().numpy(), idx_o)
+    assert torch.equal(i1, i2)
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
 def test_decode_ranked_unaligned_view(dev):
     # a column-offset view of A (rows not 16-byte aligned) takes the element
     # loads of the in-GEMV ranking and stages the slice's activations from them
