@@ -473,6 +473,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   char* Cb = (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
   const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
 
+  if (full && !some_masked && !g.c_bf16) {
+    // the common case without a test per element: a whole fp32 tile
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float* c = (float*)Cb + (size_t)(m0 + wm * WM + i * 32 + 4 * lk) * g.ldc + (n0 + wn * WN + j * 32 + li);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          __builtin_nontemporal_store(B_I8 ? acc[i][j][v] * cs[j] : acc[i][j][v],
+                                      c + (size_t)(8 * (v >> 2) + (v & 3)) * g.ldc);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -496,6 +510,199 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form of the N-major product (the batched QK^T scores, no
+// causal mask, many 256 x 256 tiles).  That product is bound by storing S:
+// a tile of 64 or 128 products per output ends in a 256 KB store.  With one
+// workgroup per tile (one per CU at a time) every tile pays its operand
+// loads again after the previous tile's store, and they queue behind it.
+// Here a workgroup per CU walks its tiles t = blockIdx.x + i gridDim.x as
+// one stream of K steps (tile, kt): the operands of step s + 2 are requested
+// while step s is multiplied, so the next tile's operands are already in
+// flight when a tile's stores go out; and the next step's operands are
+// moved into LDS before those stores are issued.  That move waits for every
+// earlier memory operation (a store and a load cannot be told apart by the
+// counter), i.e. for the previous tile's stores, which drain meanwhile: the
+// stores of consecutive tiles follow each other with only that move between
+// them.  Barriers wait for LDS only, never for the stores.
+// ---------------------------------------------------------------------------
+constexpr int kPersistGroups = 256;   // one workgroup per compute unit
+
+__global__ __launch_bounds__(512, 1) void gemm_nmajor_persistent_kernel(const GemmArgs g, int total_tiles) {
+  constexpr int BM = 256, BN = 256, NT = 512, WGN = 4;
+  constexpr int WM = BM / 2, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;
+  constexpr int ROWS_PER_PASS = NT / 8;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  __shared__ __attribute__((aligned(16))) char smem[2 * A_BYTES + 2 * B_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int li = lane & 31, lk = lane >> 5;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int per_batch = tiles_m * tiles_n;
+  const int KT = g.K / BK;
+  const int my_tiles = (total_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int S = my_tiles * KT;   // K steps of this workgroup
+
+  // tile i of this workgroup: batch and corner.  The grid is a multiple of
+  // 8 and so is a batch's tile count where the XCD order applies, so the
+  // tile keeps the XCD of its workgroup id and tile_of's blocks hold.
+  auto tile_at = [&](int i, int& b, int& m0, int& n0) {
+    const int t = (int)blockIdx.x + i * (int)gridDim.x;
+    b = t / per_batch;
+    const TileCoord c = tile_of<4>(t - b * per_batch, tiles_m, tiles_n, true);
+    m0 = c.tm * BM;
+    n0 = c.tn * BN;
+  };
+
+  const int a_kc = (tid & 7) * 8;
+  i32x4 ra_regs[A_CH], rb_regs[B_CH];
+  auto load_step = [&](int s) {
+    const int i = s / KT, kt = s - (s / KT) * KT;
+    int b, m0, n0;
+    tile_at(i, b, m0, n0);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc((const char*)g.A + (size_t)b * g.a_bs * 2, g.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc((const char*)g.B + (size_t)(b / g.b_group) * g.b_bs * 2, g.b_bytes);
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int row = m0 + (tid >> 3) + ROWS_PER_PASS * c;
+      const uint32_t off = row < g.M ? (uint32_t)(row * g.lda + a_kc + kt * BK) * 2u : kOobOffset;
+      ra_regs[c] = buf_load16(ra, off);
+    }
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c) {
+      const int row = n0 + (tid >> 3) + ROWS_PER_PASS * c;
+      const uint32_t off = row < g.N ? (uint32_t)(row * g.ldb + a_kc + kt * BK) * 2u : kOobOffset;
+      rb_regs[c] = buf_load16(rb, off);
+    }
+  };
+  auto store_step = [&](int s) {
+    char* As = smem + (s & 1) * A_BYTES;
+    char* Bs = smem + 2 * A_BYTES + (s & 1) * B_BYTES;
+    const int ch = tid & 7;
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int row = (tid >> 3) + ROWS_PER_PASS * c;
+      *(i32x4*)(As + row * 128 + swz(row, ch) * 16) = ra_regs[c];
+    }
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c) {
+      const int row = (tid >> 3) + ROWS_PER_PASS * c;
+      *(i32x4*)(Bs + row * 128 + swz(row, ch) * 16) = rb_regs[c];
+    }
+  };
+
+  int a_row[TM], b_row[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row[i] = wm * WM + i * 32 + li;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_row[j] = wn * WN + j * 32 + li;
+  auto read_frags = [&](int s, int k16, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
+    const char* As = smem + (s & 1) * A_BYTES;
+    const char* Bs = smem + 2 * A_BYTES + (s & 1) * B_BYTES;
+    const int ch = 2 * k16 + lk;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8*)(As + a_row[i] * 128 + swz(a_row[i], ch) * 16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[j] = *(const bf16x8*)(Bs + b_row[j] * 128 + swz(b_row[j], ch) * 16);
+  };
+
+  f32x16 acc[TM][TN];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  };
+  auto mfma_all = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfr)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  // lane (li, lk) of accumulator register v holds row 8 (v / 4) + 4 lk + v % 4
+  // and column li of its 32 x 32 block
+  auto store_c = [&](int i_tile) {
+    int b, m0, n0;
+    tile_at(i_tile, b, m0, n0);
+    char* Cb = (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
+    const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
+    if (full && !g.c_bf16) {
+      // the common case without a test per element: a whole fp32 tile
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          float* c = (float*)Cb + (size_t)(m0 + wm * WM + i * 32 + 4 * lk) * g.ldc + (n0 + wn * WN + j * 32 + li);
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            __builtin_nontemporal_store(acc[i][j][v], c + (size_t)(8 * (v >> 2) + (v & 3)) * g.ldc);
+        }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * WN + j * 32 + li;
+        const int row0 = m0 + wm * WM + i * 32 + 4 * lk;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = row0 + 8 * (v >> 2) + (v & 3);
+          if (full || (row < g.M && col < g.N)) {
+            const size_t off = (size_t)row * g.ldc + col;
+            if (g.c_bf16)
+              __builtin_nontemporal_store(f32_to_bf16(acc[i][j][v]), (uint16_t*)Cb + off);
+            else
+              __builtin_nontemporal_store(acc[i][j][v], (float*)Cb + off);
+          }
+        }
+      }
+    }
+  };
+
+  zero_acc();
+  if (S > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  if (S > 1) load_step(1);
+  lds_barrier();
+  for (int s = 0; s < S; ++s) {
+    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+    read_frags(s, 0, a0, b0);
+    read_frags(s, 1, a1, b1);
+    mfma_all(a0, b0);
+    read_frags(s, 2, a0, b0);
+    mfma_all(a1, b1);
+    read_frags(s, 3, a1, b1);
+    mfma_all(a0, b0);
+    mfma_all(a1, b1);
+    // stage (s + 1) & 1 was last read in step s - 1, before the barrier
+    if (s + 1 < S) store_step(s + 1);
+    if (s + 2 < S) load_step(s + 2);
+    if (s % KT == KT - 1) {
+      store_c(s / KT);
+      zero_acc();
+    }
+    lds_barrier();
+  }
+}
+
+hipError_t launch_gemm_nmajor_persistent(const GemmArgs& g, hipStream_t s) {
+  const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+  int groups = tiles < kPersistGroups ? tiles : kPersistGroups;
+  if (groups >= 8) groups &= ~7;
+  gemm_nmajor_persistent_kernel<<<groups, 512, 0, s>>>(g, tiles);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WAVES>
 hipError_t dispatch(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
@@ -516,8 +723,12 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   // Small-N / small-M products (per-head PV) use 128x128 tiles so that the
-  // grid still covers the chip; large products use 256x256.
+  // grid still covers the chip; large products use 256x256, and the
+  // store-bound N-major ones (QK^T scores over many tiles, no mask) the
+  // persistent kernel.
   const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+  if (!g.b_kmajor && !g.causal && t256 >= 2 * kPersistGroups && g.N >= 256 && g.M >= 256)
+    return launch_gemm_nmajor_persistent(g, s);
   if (t256 >= 192 && g.N >= 256 && g.M >= 256) return dispatch<256, 256, 8>(g, s);
   return dispatch<128, 128, 4>(g, s);
 }

@@ -899,6 +899,17 @@ def test_full_mlp_up(dev):
         check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16, rows=rows)
 
 
+@pytest.mark.parametrize("rho,out_dtype", [(0.5, torch.float32), (0.9, torch.float32), (0.5, torch.bfloat16)])
+def test_qk_many_tiles_ragged(dev, rho, out_dtype):
+    # 32 heads x 1100 x 1100: 800 score tiles of 256 x 256, so the persistent
+    # product walks 3 or 4 tiles per workgroup across heads, with ragged
+    # last tile rows and columns (1100 = 4 x 256 + 76); one K step (rho 0.5:
+    # 64 kept features) or two (rho 0.9: 116 kept, padded to 128); fp32
+    # output (whole tiles stored without a per-element test) and bf16
+    w = synth.gqa_qk(hq=32, hkv=8, t=1100, dh=128)
+    check_qk(w.tensors["Q"], w.tensors["K"], rho, dev, TOL_BF16, out_dtype=out_dtype)
+
+
 def test_full_gqa_qk(dev):
     w = synth.gqa_qk()
     Q, K = w.tensors["Q"], w.tensors["K"]
