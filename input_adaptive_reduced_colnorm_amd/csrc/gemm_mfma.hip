@@ -473,18 +473,37 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   char* Cb = (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
   const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
 
-  if (full && !some_masked && !g.c_bf16) {
-    // the common case without a test per element: a whole fp32 tile
+  if (full && !g.c_bf16) {
+    // whole fp32 tiles without a branch per element: unmasked, or with the
+    // causal mask applied by a select
+    if (!some_masked) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        float* c = (float*)Cb + (size_t)(m0 + wm * WM + i * 32 + 4 * lk) * g.ldc + (n0 + wn * WN + j * 32 + li);
+        for (int j = 0; j < TN; ++j) {
+          float* c = (float*)Cb + (size_t)(m0 + wm * WM + i * 32 + 4 * lk) * g.ldc + (n0 + wn * WN + j * 32 + li);
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          __builtin_nontemporal_store(B_I8 ? acc[i][j][v] * cs[j] : acc[i][j][v],
-                                      c + (size_t)(8 * (v >> 2) + (v & 3)) * g.ldc);
-      }
+          for (int v = 0; v < 16; ++v)
+            __builtin_nontemporal_store(B_I8 ? acc[i][j][v] * cs[j] : acc[i][j][v],
+                                        c + (size_t)(8 * (v >> 2) + (v & 3)) * g.ldc);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row0 = m0 + wm * WM + i * 32 + 4 * lk;
+          const int col = n0 + wn * WN + j * 32 + li;
+          float* c = (float*)Cb + (size_t)row0 * g.ldc + col;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = 8 * (v >> 2) + (v & 3);
+            const float a = B_I8 ? acc[i][j][v] * cs[j] : acc[i][j][v];
+            __builtin_nontemporal_store((int64_t)col > (int64_t)(row0 + r) + g.causal_off ? -INFINITY : a,
+                                        c + (size_t)r * g.ldc);
+          }
+        }
+    }
     return;
   }
 #pragma unroll
@@ -511,8 +530,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
 }
 
 // ---------------------------------------------------------------------------
-// Persistent form of the N-major product (the batched QK^T scores, no
-// causal mask, many 256 x 256 tiles).  That product is bound by storing S:
+// Persistent form of the N-major product (the batched QK^T scores over
+// many 256 x 256 tiles).  That product is bound by storing S:
 // a tile of 64 or 128 products per output ends in a 256 KB store.  With one
 // workgroup per tile (one per CU at a time) every tile pays its operand
 // loads again after the previous tile's store, and they queue behind it.
@@ -524,7 +543,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
 // earlier memory operation (a store and a load cannot be told apart by the
 // counter), i.e. for the previous tile's stores, which drain meanwhile: the
 // stores of consecutive tiles follow each other with only that move between
-// them.  Barriers wait for LDS only, never for the stores.
+// them.  Barriers wait for LDS only, never for the stores.  Causal scores
+// run through the same stream: a tile wholly above the diagonal is still
+// multiplied (its store, not its product, is the cost) and stored as -inf,
+// so every tile costs the same and the XCD-blocked order stays balanced.
 // ---------------------------------------------------------------------------
 constexpr int kPersistGroups = 256;   // one workgroup per compute unit
 
@@ -633,17 +655,39 @@ __global__ __launch_bounds__(512, 1) void gemm_nmajor_persistent_kernel(const Ge
     tile_at(i_tile, b, m0, n0);
     char* Cb = (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
     const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
+    // causal scores: every entry of the tile above the shifted diagonal, or some
+    const bool all_masked = g.causal && (int64_t)n0 > (int64_t)(m0 + BM - 1) + g.causal_off;
+    const bool some_masked = g.causal && (int64_t)(n0 + BN - 1) > (int64_t)m0 + g.causal_off;
     if (full && !g.c_bf16) {
-      // the common case without a test per element: a whole fp32 tile
+      // whole fp32 tiles without a branch per element: unmasked, or with
+      // the mask applied by a select (a branch per element around the
+      // stores of the diagonal tiles made causal launches a third slower)
+      if (!some_masked) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          float* c = (float*)Cb + (size_t)(m0 + wm * WM + i * 32 + 4 * lk) * g.ldc + (n0 + wn * WN + j * 32 + li);
+          for (int j = 0; j < TN; ++j) {
+            float* c = (float*)Cb + (size_t)(m0 + wm * WM + i * 32 + 4 * lk) * g.ldc + (n0 + wn * WN + j * 32 + li);
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            __builtin_nontemporal_store(acc[i][j][v], c + (size_t)(8 * (v >> 2) + (v & 3)) * g.ldc);
-        }
+            for (int v = 0; v < 16; ++v)
+              __builtin_nontemporal_store(acc[i][j][v], c + (size_t)(8 * (v >> 2) + (v & 3)) * g.ldc);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int row0 = m0 + wm * WM + i * 32 + 4 * lk;
+            const int col = n0 + wn * WN + j * 32 + li;
+            float* c = (float*)Cb + (size_t)row0 * g.ldc + col;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = 8 * (v >> 2) + (v & 3);
+              const bool mk = all_masked || (int64_t)col > (int64_t)(row0 + r) + g.causal_off;
+              __builtin_nontemporal_store(mk ? -INFINITY : acc[i][j][v], c + (size_t)r * g.ldc);
+            }
+          }
+      }
       return;
     }
 #pragma unroll
@@ -657,10 +701,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nmajor_persistent_kernel(const Ge
           const int row = row0 + 8 * (v >> 2) + (v & 3);
           if (full || (row < g.M && col < g.N)) {
             const size_t off = (size_t)row * g.ldc + col;
+            const float y = some_masked && (int64_t)col > (int64_t)row + g.causal_off ? -INFINITY : acc[i][j][v];
             if (g.c_bf16)
-              __builtin_nontemporal_store(f32_to_bf16(acc[i][j][v]), (uint16_t*)Cb + off);
+              __builtin_nontemporal_store(f32_to_bf16(y), (uint16_t*)Cb + off);
             else
-              __builtin_nontemporal_store(acc[i][j][v], (float*)Cb + off);
+              __builtin_nontemporal_store(y, (float*)Cb + off);
           }
         }
       }
@@ -724,10 +769,10 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   // Small-N / small-M products (per-head PV) use 128x128 tiles so that the
   // grid still covers the chip; large products use 256x256, and the
-  // store-bound N-major ones (QK^T scores over many tiles, no mask) the
-  // persistent kernel.
+  // store-bound N-major ones (QK^T scores over many tiles) the persistent
+  // kernel.
   const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-  if (!g.b_kmajor && !g.causal && t256 >= 2 * kPersistGroups && g.N >= 256 && g.M >= 256)
+  if (!g.b_kmajor && t256 >= 2 * kPersistGroups && g.N >= 256 && g.M >= 256)
     return launch_gemm_nmajor_persistent(g, s);
   if (t256 >= 192 && g.N >= 256 && g.M >= 256) return dispatch<256, 256, 8>(g, s);
   return dispatch<128, 128, 4>(g, s);

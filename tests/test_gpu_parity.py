@@ -910,6 +910,17 @@ def test_qk_many_tiles_ragged(dev, rho, out_dtype):
     check_qk(w.tensors["Q"], w.tensors["K"], rho, dev, TOL_BF16, out_dtype=out_dtype)
 
 
+@pytest.mark.parametrize("rho,out_dtype", [(0.5, torch.float32), (1.0, torch.bfloat16)])
+def test_qk_causal_many_tiles_ragged(dev, rho, out_dtype):
+    # the same 800 tiles with the causal mask: tiles wholly above the
+    # diagonal stored as -inf without a test per element, diagonal and
+    # ragged tiles element by element; then 900 queries at the end of 1100
+    # keys (the diagonal shifted by 200; 640 tiles)
+    w = synth.gqa_qk(hq=32, hkv=8, t=1100, dh=128)
+    check_qk_causal(w.tensors["Q"], w.tensors["K"], rho, dev, TOL_BF16, out_dtype=out_dtype)
+    check_qk_causal(w.tensors["Q"][:, -900:, :].contiguous(), w.tensors["K"], rho, dev, TOL_BF16)
+
+
 def test_full_gqa_qk(dev):
     w = synth.gqa_qk()
     Q, K = w.tensors["Q"], w.tensors["K"]
