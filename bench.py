@@ -460,7 +460,8 @@ class QkOp:
         return "gemm"
 
     def roofline_kernel(self):
-        return "gemm_bf16_kernel<256,256,nmajor> (batched per-head QK^T, fp32 S store)"
+        return ("gemm_nmajor_persistent_kernel (batched per-head QK^T, one workgroup per CU walking the "
+                "256x256 score tiles, fp32 S store)")
 
     def traffic_ref(self):
         return None
