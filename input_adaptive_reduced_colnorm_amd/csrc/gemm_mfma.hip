@@ -108,16 +108,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   const int wm = wave / WGN, wn = wave % WGN;
   const int li = lane & 31, lk = lane >> 5;
   const int b = blockIdx.y;
+  // split K (k_split > 1): this workgroup multiplies over the contraction
+  // range [k0, k0 + Kc) and writes a partial sum of its tile
+  const int Kc = g.K / g.k_split;
+  const int k0 = (int)blockIdx.z * Kc;
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const TileCoord tc = tile_of<KMAJOR ? 8 : 4>(blockIdx.x, tiles_m, tiles_n, !g.causal);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
-  const char* Ab = (const char*)g.A + (size_t)b * g.a_bs * ES;
+  const char* Ab = (const char*)g.A + (size_t)b * g.a_bs * ES + (size_t)k0 * ES;
   const char* Bb = (const char*)g.B + (size_t)(b / g.b_group) * g.b_bs * BE;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, g.a_bytes - (uint32_t)((size_t)k0 * ES));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, g.b_bytes);
-  const int32_t* idxb = GATHER ? g.idx + (size_t)b * g.idx_bs : nullptr;
+  const int32_t* idxb = GATHER ? g.idx + (size_t)b * g.idx_bs + k0 : nullptr;
 
   // ---- per-thread load geometry (K is a multiple of 64 on every path) -----
   // A chunk i of this thread: row (tid >> 3) + ROWS_PER_PASS * i, 8 elements
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
           if constexpr (GATHER)
             row = e < 4 ? idx_lo[e] : idx_hi[e - 4];
           else
-            row = kt * BK + kb_row0 + e;
+            row = k0 + kt * BK + kb_row0 + e;
           const uint32_t off = ((uint32_t)(row * g.ldb + kb_col) * BE) | kb_colmask;
           if constexpr (B_I8)
             rb_regs[e] = buf_load8(rb, off);
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) rb_regs[i] = buf_load16(rb, b_off[i] + (uint32_t)(kt * BK * 2));
+      for (int i = 0; i < B_CH; ++i) rb_regs[i] = buf_load16(rb, b_off[i] + (uint32_t)((k0 + kt * BK) * 2));
     }
   };
 
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   // only writes -inf
   const bool masked_tile = g.causal && (int64_t)n0 > (int64_t)(m0 + BM - 1) + g.causal_off;
   const bool some_masked = g.causal && (int64_t)(n0 + BN - 1) > (int64_t)m0 + g.causal_off;
-  const int KT = masked_tile ? 0 : g.K / BK;
+  const int KT = masked_tile ? 0 : Kc / BK;
   // per-column scales of int8 weights, loaded before the main loop: on this
   // chip the vector memory counter covers stores too, so a load among the
   // epilogue's stores would make its wait drain every store issued so far
@@ -470,10 +474,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
 
   // ---- epilogue: lane (li, lk) of accumulator register v holds row
   //      8*(v/4) + 4*lk + v%4 and column li of its 32x32 block.
-  char* Cb = (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
+  //      Split K: the fp32 partial of range blockIdx.z goes to
+  //      partial[blockIdx.z][b] (M x N, row stride N) instead of C.
+  const bool split = g.k_split > 1;
+  char* Cb = split ? (char*)(g.partial + ((size_t)blockIdx.z * g.batch + b) * g.M * g.N)
+                   : (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
+  const int64_t ldc = split ? g.N : g.ldc;
+  const bool c_bf16 = !split && g.c_bf16;
   const bool full = m0 + BM <= g.M && n0 + BN <= g.N;
 
-  if (full && !g.c_bf16) {
+  if (full && !c_bf16) {
     // whole fp32 tiles without a branch per element: unmasked, or with the
     // causal mask applied by a select
     if (!some_masked) {
@@ -481,11 +491,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          float* c = (float*)Cb + (size_t)(m0 + wm * WM + i * 32 + 4 * lk) * g.ldc + (n0 + wn * WN + j * 32 + li);
+          float* c = (float*)Cb + (size_t)(m0 + wm * WM + i * 32 + 4 * lk) * ldc + (n0 + wn * WN + j * 32 + li);
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             __builtin_nontemporal_store(B_I8 ? acc[i][j][v] * cs[j] : acc[i][j][v],
-                                        c + (size_t)(8 * (v >> 2) + (v & 3)) * g.ldc);
+                                        c + (size_t)(8 * (v >> 2) + (v & 3)) * ldc);
         }
     } else {
 #pragma unroll
@@ -494,13 +504,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
         for (int j = 0; j < TN; ++j) {
           const int row0 = m0 + wm * WM + i * 32 + 4 * lk;
           const int col = n0 + wn * WN + j * 32 + li;
-          float* c = (float*)Cb + (size_t)row0 * g.ldc + col;
+          float* c = (float*)Cb + (size_t)row0 * ldc + col;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int r = 8 * (v >> 2) + (v & 3);
             const float a = B_I8 ? acc[i][j][v] * cs[j] : acc[i][j][v];
             __builtin_nontemporal_store((int64_t)col > (int64_t)(row0 + r) + g.causal_off ? -INFINITY : a,
-                                        c + (size_t)r * g.ldc);
+                                        c + (size_t)r * ldc);
           }
         }
     }
@@ -516,10 +526,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
       for (int v = 0; v < 16; ++v) {
         const int row = row0 + 8 * (v >> 2) + (v & 3);
         if (full || (row < g.M && col < g.N)) {
-          const size_t off = (size_t)row * g.ldc + col;
+          const size_t off = (size_t)row * ldc + col;
           const float a = B_I8 ? acc[i][j][v] * cs[j] : acc[i][j][v];
           const float y = some_masked && (int64_t)col > (int64_t)row + g.causal_off ? -INFINITY : a;
-          if (g.c_bf16)
+          if (c_bf16)
             __builtin_nontemporal_store(f32_to_bf16(y), (uint16_t*)Cb + off);
           else
             __builtin_nontemporal_store(y, (float*)Cb + off);
@@ -751,7 +761,7 @@ hipError_t launch_gemm_nmajor_persistent(const GemmArgs& g, hipStream_t s) {
 template <int BM, int BN, int WAVES>
 hipError_t dispatch(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  dim3 grid(tiles, g.batch);
+  dim3 grid(tiles, g.batch, g.k_split);
   const bool gather = g.idx != nullptr;
   if (g.b_kmajor) {
     if (gather)
@@ -772,6 +782,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   // store-bound N-major ones (QK^T scores over many tiles) the persistent
   // kernel.
   const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
+  if (g.k_split != 1) return hipErrorInvalidValue;   // split K: fp32 A products only
   if (!g.b_kmajor && t256 >= 2 * kPersistGroups && g.N >= 256 && g.M >= 256)
     return launch_gemm_nmajor_persistent(g, s);
   if (t256 >= 192 && g.N >= 256 && g.M >= 256) return dispatch<256, 256, 8>(g, s);
@@ -785,7 +796,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
 template <int BM, int BN, int WAVES>
 void dispatch_af32(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  dim3 grid(tiles, g.batch);
+  dim3 grid(tiles, g.batch, g.k_split);
   if (g.b_kmajor) {
     if (g.idx)
       gemm_bf16_kernel<BM, BN, true, true, true, WAVES><<<grid, 64 * WAVES, 0, s>>>(g);
@@ -801,7 +812,7 @@ void dispatch_af32(const GemmArgs& g, hipStream_t s) {
 template <int BM, int BN, int WAVES>
 void dispatch_w8(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  dim3 grid(tiles, g.batch);
+  dim3 grid(tiles, g.batch, g.k_split);
   if (g.idx)
     gemm_bf16_kernel<BM, BN, true, true, false, WAVES, true><<<grid, 64 * WAVES, 0, s>>>(g);
   else
@@ -809,7 +820,7 @@ void dispatch_w8(const GemmArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_gemm_w8(const GemmArgs& g, hipStream_t s) {
-  if (!g.b_kmajor || !g.b_i8 || !g.col_scale) return hipErrorInvalidValue;
+  if (!g.b_kmajor || !g.b_i8 || !g.col_scale || g.k_split != 1) return hipErrorInvalidValue;
   const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
   if (t256 >= 192 && g.N >= 256 && g.M >= 256)
     dispatch_w8<256, 256, 8>(g, s);
@@ -818,10 +829,54 @@ hipError_t launch_gemm_w8(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// C[b][i][j] = sum over ranges z = 0, 1, ... of partial[z][b][i][j], in
+// range order; four consecutive elements per thread where N % 4 == 0.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs g) {
+  const size_t per = (size_t)g.M * g.N;
+  const int b = blockIdx.y;
+  const bool v4 = (g.N & 3) == 0;
+  const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * (v4 ? 4 : 1);
+  if (e0 >= per) return;
+  const int row = (int)(e0 / g.N), col = (int)(e0 % g.N);
+  char* Cb = (char*)g.C + (size_t)b * g.c_bs * (g.c_bf16 ? 2 : 4);
+  const size_t off = (size_t)row * g.ldc + col;
+  if (v4) {
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < g.k_split; ++z) {
+      const f32x4 p = *(const f32x4*)(g.partial + ((size_t)z * g.batch + b) * per + e0);
+      v[0] += p[0];
+      v[1] += p[1];
+      v[2] += p[2];
+      v[3] += p[3];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (g.c_bf16)
+        ((uint16_t*)Cb)[off + t] = f32_to_bf16(v[t]);
+      else
+        ((float*)Cb)[off + t] = v[t];
+    }
+  } else {
+    float v = 0.f;
+    for (int z = 0; z < g.k_split; ++z) v += g.partial[((size_t)z * g.batch + b) * per + e0];
+    if (g.c_bf16)
+      ((uint16_t*)Cb)[off] = f32_to_bf16(v);
+    else
+      ((float*)Cb)[off] = v;
+  }
+}
+
 hipError_t launch_gemm_bf16_af32(const GemmArgs& g, hipStream_t s) {
+  if (g.k_split < 1 || g.K % (BK * g.k_split) != 0 || (g.k_split > 1 && (!g.partial || g.causal)))
+    return hipErrorInvalidValue;
   // 128 x 128 tiles only: with fp32 A staged in registers the 256 x 256
   // tile needs more than the 256 registers two waves per SIMD allow
   dispatch_af32<128, 128, 4>(g, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.k_split == 1) return e;
+  const size_t per = (size_t)g.M * g.N;
+  const size_t threads = (g.N & 3) == 0 ? (per + 3) / 4 : per;
+  splitk_reduce_kernel<<<dim3((unsigned)((threads + 255) / 256), g.batch), 256, 0, s>>>(g);
   return hipGetLastError();
 }
 

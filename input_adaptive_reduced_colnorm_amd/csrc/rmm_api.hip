@@ -925,8 +925,9 @@ struct PvPlan {
   bool all = false, mfma = false, direct = false, masked = false, use_sel = false;
   bool decode = false;   // tq <= 16: per-head GEMV over the kept rows of V
   int gemv_splits = 1;
+  int k_split = 1;       // fp32 P read in place: contraction ranges of the product
   SelPlan sel;
-  size_t off_p = 0, off_ipad = 0, off_mask = 0, off_gpart = 0, total = 0;
+  size_t off_p = 0, off_ipad = 0, off_mask = 0, off_gpart = 0, off_kpart = 0, total = 0;
 };
 
 // PV reads P once for the column energies whatever the path; the product
@@ -968,6 +969,20 @@ PvPlan plan_pv(int64_t h, int64_t tq, int64_t tk, int64_t dv, int p_dtype, int v
     } else if (!p.direct) {
       p.off_ipad = cv.take((size_t)h * p.k_pad * 4);
       p.off_p = cv.take((size_t)h * tq * p.k_pad * 2);
+    }
+    if ((p.direct || p.masked) && p_dtype == RMM_FP32) {
+      // reading fp32 P in place is the whole cost: with fewer than two
+      // 128 x 128 tiles per CU the contraction is split into ranges (at
+      // least two K tiles each) so that twice the loads are in flight; the
+      // partial sums (at most the size of the packed P the other path uses)
+      // are added in range order
+      const int64_t tiles = ((tq + 127) / 128) * ((dv + 127) / 128) * h;
+      int ks = 1;
+      while (ks < 4 && tiles * ks < 2 * 256 && tk % (kKTile * 2 * ks) == 0 && tk / (2 * ks) >= 2 * kKTile &&
+             2 * ks * dv * 2 <= tk)
+        ks *= 2;
+      p.k_split = ks;
+      if (ks > 1) p.off_kpart = cv.take((size_t)ks * h * tq * dv * 4);
     }
   }
   p.total = cv.used;
@@ -1093,6 +1108,8 @@ rmm_status_t pv_impl(const void* P, int p_dtype, const void* V, int v_dtype, int
     g.idx = kmask; g.idx_bs = p.masked ? tk : 0; g.K = (int)tk;
     RMM_LAUNCH(mk.mark(3));
     if (p_f32) {
+      g.k_split = p.k_split;
+      g.partial = (float*)(ws + p.off_kpart);
       RMM_LAUNCH(launch_gemm_bf16_af32(g, s));
     } else {
       RMM_LAUNCH(launch_gemm_bf16(g, s));

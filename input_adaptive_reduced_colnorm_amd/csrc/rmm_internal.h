@@ -102,6 +102,11 @@ struct GemmArgs {
   const float* col_scale;     // int8 B only (required there): C[i][j] *= col_scale[j]
   bool causal;          // C[i][j] = -inf where j > i + causal_off (tiles wholly above skip the product)
   int64_t causal_off;
+  // split K: k_split contraction ranges of K / k_split (a multiple of 64)
+  // multiplied by separate workgroups into partial[k_split][batch][M][N]
+  // (fp32), then added in range order into C; 1 = no split
+  int k_split = 1;
+  float* partial = nullptr;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Same product with A given as fp32 (rounded to bf16 while staged); a gather
