@@ -402,8 +402,8 @@ class QkOp:
 
     def extra(self, args, sh):
         """Causal scores (rmm_qk_causal: keys after the query position get
-        -inf, tiles wholly above the diagonal skip the product) beside the
-        unmasked call, at each rho, back to back outside the stepped loop."""
+        -inf) beside the unmasked call, at each rho, back to back outside the
+        stepped loop."""
         import torch
         if self.tq > self.tk:
             return None
@@ -431,8 +431,9 @@ class QkOp:
                 us[name] = e0.elapsed_time(e1) / args.steps * 1e3
             out[str(rho)] = {"causal_latency_us": round(us["causal"], 2),
                              "unmasked_latency_us": round(us["unmasked"], 2)}
-        out["note"] = ("the causal call writes the same S bytes (-inf above the diagonal) and skips the product on "
-                       "tiles wholly above it")
+        out["note"] = ("the causal call writes the same S bytes (-inf above the diagonal); with this many tiles "
+                       "both run the persistent score kernel, which multiplies every tile since the store is the "
+                       "cost")
         return out
 
     def stage_work(self, rho):
