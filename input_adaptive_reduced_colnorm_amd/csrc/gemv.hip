@@ -380,9 +380,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
   constexpr uint16_t kNone = 0xffff;   // s_pos of a dropped row (list positions are < k <= 8192)
   __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kSliceStride];   // activations by MFMA position
   __shared__ __attribute__((aligned(16))) RankLds u;
-  __shared__ __attribute__((aligned(16))) uint16_t s_pos[kMaxSlice];   // list position of source row r0 + o
-  __shared__ uint16_t s_kept[kMaxSlice];                                 // kept offsets o, ascending
-  __shared__ uint32_t s_cnt[2];                                          // kept rows: all, in the head
+  __shared__ __attribute__((aligned(16))) uint16_t s_pos[kMaxSlice];    // list position of source row r0 + o
+  __shared__ __attribute__((aligned(16))) uint16_t s_rest[kMaxSlice];   // kept offsets o >= HR, ascending
+  __shared__ uint32_t s_cnt;                                              // kept rows past the head
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = slice_rows(g.d, g.splits);
@@ -408,7 +408,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
         bv[q][e] = __builtin_nontemporal_load((const R*)((const char*)g.B + ((size_t)rw * g.ldb + cc0) * BE));
       }
   };
-  for (int i = tid; i < kMaxSlice; i += kThreads) s_pos[i] = kNone;
+  for (int i = tid; i < kMaxSlice; i += kThreads) {
+    s_pos[i] = kNone;
+    s_rest[i] = kNone;   // past the kept rows the list reads as "none"
+  }
   sel::KeyChunk<CH> kc;
   rank_columns<CH, NR, A_BF16>(g, kc, u.st.src, r0, Ls, issue_head);
   // the ranking's barriers order the s_pos clear and the src stores before
@@ -419,38 +422,36 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
   });
   lds_barrier();
 
-  // ---- the slice's kept offsets in order (two per thread), and how many
-  //      of them lie in the head ----
+  // ---- the kept offsets past the head, in order (two per thread), from
+  //      index 0 of their own list so that 8 of them are one 16-byte read ----
   {
-    const int o0 = 2 * tid;
+    const int o0 = HR + 2 * tid;
     const bool k0 = o0 < Ls && s_pos[o0] != kNone;
     const bool k1 = o0 + 1 < Ls && s_pos[o0 + 1] != kNone;
-    const uint32_t n_k = (uint32_t)k0 + (uint32_t)k1;
-    const uint32_t n_h = (uint32_t)(k0 && o0 < HR) + (uint32_t)(k1 && o0 + 1 < HR);
-    uint32_t inc = n_k, inc_h = n_h;
-    sel::block_incl_scan2<kThreads>(inc, inc_h, u.st.ssh);
-    uint32_t p = inc - n_k;
-    if (k0) s_kept[p++] = (uint16_t)o0;
-    if (k1) s_kept[p] = (uint16_t)(o0 + 1);
-    if (tid == kThreads - 1) {
-      s_cnt[0] = inc;
-      s_cnt[1] = inc_h;
-    }
+    const uint32_t n_r = (uint32_t)k0 + (uint32_t)k1;
+    uint32_t inc = n_r, unused = 0;
+    sel::block_incl_scan2<kThreads>(inc, unused, u.st.ssh);
+    uint32_t p = inc - n_r;
+    if (k0) s_rest[p++] = (uint16_t)o0;
+    if (k1) s_rest[p] = (uint16_t)(o0 + 1);
+    if (tid == kThreads - 1) s_cnt = inc;
   }
   lds_barrier();
-  const int nh = (int)s_cnt[1];
-  const int Lr = (int)s_cnt[0] - nh;   // kept rows after the head
+  const int Lr = (int)s_cnt;   // kept rows after the head
 
-  // ---- rest: rest chunk i = wave + 4 (q - HC) takes the kept rows
-  //      nh + 32 i .. of the slice; loads unconditional as in gemv_kernel ----
+  // ---- rest: rest chunk i = wave + 4 (q - HC) takes rest entries 32 i ..;
+  //      the lane's 8 entries in one read, loads unconditional as in
+  //      gemv_kernel ----
   int rrow[kChunksPerWave][8];
 #pragma unroll
-  for (int q = HC; q < kChunksPerWave; ++q)
+  for (int q = HC; q < kChunksPerWave; ++q) {
+    const i32x4 w = *(const i32x4*)&s_rest[(wave + kWaves * (q - HC)) * kChunk + 8 * rb];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int i = (wave + kWaves * (q - HC)) * kChunk + 8 * rb + e;
-      rrow[q][e] = i < Lr ? r0 + (int)s_kept[nh + i] : -1;
+      const uint32_t o = ((uint32_t)w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      rrow[q][e] = o != kNone ? r0 + (int)o : -1;
     }
+  }
 #pragma unroll
   for (int q = HC; q < kChunksPerWave; ++q)
 #pragma unroll
@@ -459,18 +460,36 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
       bv[q][e] = __builtin_nontemporal_load((const R*)((const char*)g.B + ((size_t)rw * g.ldb + cc0) * BE));
     }
 
-  // ---- activations by MFMA position: the head's source offsets (dropped
-  //      rows zero), then the rest's kept rows, zero padded to a chunk ----
-  const int npos = HR + (Lr + kChunk - 1) / kChunk * kChunk;
-  for (int t = tid; t < npos; t += kThreads) {
-    int o = -1;
-    if (t < HR) {
-      if (t < Ls && s_pos[t] != kNone) o = t;
-    } else if (t - HR < Lr) {
-      o = s_kept[nh + t - HR];
-    }
+  // ---- activations by MFMA position, 8 positions of one row per item: the
+  //      head's source offsets (dropped rows and offsets past the slice
+  //      zero), then the rest's kept rows, zero padded to a chunk; rows past
+  //      n zero ----
+  const int groups = (HR + (Lr + kChunk - 1) / kChunk * kChunk) / 8;
+  for (int w = tid; w < 16 * groups; w += kThreads) {
+    const int r = w / groups, t0 = 8 * (w - r * groups);
+    i32x4 v = i32x4{0, 0, 0, 0};
+    if (r < g.n) {
+      if (t0 < HR) {
+        const i32x4 a = *(const i32x4*)&u.st.src[r][t0];
+        const i32x4 pw = *(const i32x4*)&s_pos[t0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_a[r][t] = o >= 0 && r < g.n ? u.st.src[r][o] : (uint16_t)0;
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t m = (((uint32_t)pw[h] & 0xffffu) != kNone ? 0x0000ffffu : 0u) |
+                             (((uint32_t)pw[h] >> 16) != kNone ? 0xffff0000u : 0u);
+          v[h] = (int)((uint32_t)a[h] & m);
+        }
+      } else {
+        const i32x4 ow = *(const i32x4*)&s_rest[t0 - HR];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t o_lo = (uint32_t)ow[h] & 0xffffu, o_hi = (uint32_t)ow[h] >> 16;
+          const uint32_t lo = o_lo != kNone ? u.st.src[r][o_lo] : 0u;
+          const uint32_t hi = o_hi != kNone ? u.st.src[r][o_hi] : 0u;
+          v[h] = (int)(lo | (hi << 16));
+        }
+      }
+    }
+    *(i32x4*)&s_a[r][t0] = v;
   }
   lds_barrier();
 
