@@ -846,17 +846,31 @@ hipError_t launch_qk_select_pack(const float* partial, int splits, const uint16_
 int colnorm_splits(int heads, int n, int d, bool elt_bf16) {
   const int cb = kCnLanes * (elt_bf16 ? 8 : 4);
   const long col_blocks = (long)((d + cb - 1) / cb) * heads;
-  // about 560 workgroups: more splits stream A a little faster (5.2 -> 5.4
-  // TB/s at 1800 groups) but cost the selection more than they save
-  long s = (560 + col_blocks - 1) / col_blocks;
-  long max_by_rows = (n + 127) / 128;
-  if (s > max_by_rows) s = max_by_rows;
-  // the selection re-reads splits x d partials in one workgroup: few
-  // splits for wide rows, more for the short feature rows of attention heads
-  const long max_splits = d <= 256 ? 32 : 16;
-  if (s > max_splits) s = max_splits;
-  if (s < 1) s = 1;
-  return (int)s;
+  // The sweep lasts as long as its busiest CU: the split count is the one
+  // that spreads the workgroups most evenly over the 256 CUs (average over
+  // maximum per CU), among those giving at least 1.5 workgroups per CU (so
+  // that enough loads are in flight), the fewest on a tie.  Every split adds
+  // d partials that the selection reads back, so wide rows take at most 8
+  // (mlp_down: 4 splits, 448 workgroups, sweep 24.5 against 27.9 us with 5,
+  // and the fused selection also faster); the short feature rows of
+  // attention heads up to 32.
+  const long max_by_rows = (n + 127) / 128;
+  long smax = d <= 256 ? 32 : 8;
+  if (smax > max_by_rows) smax = max_by_rows;
+  if (smax < 1) smax = 1;
+  long best = smax;
+  double best_eff = -1.0;
+  for (long sp = 1; sp <= smax; ++sp) {
+    const long groups = col_blocks * sp;
+    if (groups * 2 < 3L * 256 && sp < smax) continue;
+    const long per_cu = (groups + 255) / 256;
+    const double eff = (double)groups / (256.0 * (double)per_cu);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = sp;
+    }
+  }
+  return (int)best;
 }
 
 hipError_t launch_colnorm(const void* A, bool elt_bf16, int64_t head_stride, int64_t lda, int heads, int n, int d,
