@@ -281,7 +281,8 @@ rmm_status_t rmm_qk_timed(const void* Q, const void* K, int dtype, int64_t hq, i
  * "Algorithm Deep-Dive: RMM" (hackcv.com), Component mapping: the kept
  * features I_h still come from the column norms of Q[h] over all tq rows;
  * the mask acts on the scores only.  Tiles of S that lie wholly above the
- * shifted diagonal skip the product and only store -inf.  Arguments, idx,
+ * shifted diagonal store -inf (small launches skip their product; large
+ * ones, bound by the store of S, multiply every tile alike).  Arguments, idx,
  * workspace (rmm_qk_workspace) and errors as rmm_qk, and RMM_ERR_SHAPE when
  * tq > tk.  The scores go straight to rmm_softmax_energy. */
 rmm_status_t rmm_qk_causal(const void* Q, const void* K, int dtype, int64_t hq, int64_t hkv, int64_t tq, int64_t tk,

@@ -100,7 +100,8 @@ struct GemmArgs {
   uint32_t a_bytes, b_bytes;  // per-batch extents (bytes) for the buffer descriptors
   bool b_i8;                  // K-major B holds int8 weights (widened to bf16 exactly)
   const float* col_scale;     // int8 B only (required there): C[i][j] *= col_scale[j]
-  bool causal;          // C[i][j] = -inf where j > i + causal_off (tiles wholly above skip the product)
+  bool causal;          // C[i][j] = -inf where j > i + causal_off (the non-persistent kernel skips the
+                        // product of tiles wholly above)
   int64_t causal_off;
   // split K: k_split contraction ranges of K / k_split (a multiple of 64)
   // multiplied by separate workgroups into partial[k_split][batch][M][N]
