@@ -676,8 +676,8 @@ def pv_envelope(P, V, idx, heads=None) -> np.ndarray:
     return np.stack([envelope(P[h], V[h // (h_ // hkv)], idx[i]) for i, h in enumerate(hs)])
 
 
-def check_pv(P, V, rho, dev, tol, heads=None):
-    idx, Og = rmm.pv(P.to(dev), V.to(dev), rho)
+def check_pv(P, V, rho, dev, tol, heads=None, out_dtype=torch.float32):
+    idx, Og = rmm.pv(P.to(dev), V.to(dev), rho, out_dtype=out_dtype)
     torch.cuda.synchronize()
     hs = list(range(P.shape[0])) if heads is None else list(heads)
     Pf, Vf = f32(P), f32(V)
@@ -702,6 +702,9 @@ def test_pv_masked_and_packed(dev, rho):
     w = synth.attn_pv(h=4, hkv=2, tq=96, tk=1024, dv=64, rho=rho)
     check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16)
     check_pv(w.tensors["P"].to(torch.bfloat16), w.tensors["V"], rho, dev, TOL_BF16)
+    # where fp32 P is read in place (rho 0.5, 0.2) the contraction of its 4
+    # tiles runs in 4 ranges: their ordered sum also rounds to a bf16 output
+    check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16, out_dtype=torch.bfloat16)
 
 
 # ------------------- producer-side PV scoring (softmax) ----------------------
