@@ -26,6 +26,9 @@ pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 5e-3
 TOL_FP32 = 1e-5
+# two roundings to bf16 (nearest even, each at most 2**-8 of the element's
+# envelope): fp32 P staged as bf16 for the matrix cores, then a bf16 output
+TOL_BF16_TWICE = 8e-3
 
 
 @pytest.fixture(scope="module")
@@ -703,8 +706,9 @@ def test_pv_masked_and_packed(dev, rho):
     check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16)
     check_pv(w.tensors["P"].to(torch.bfloat16), w.tensors["V"], rho, dev, TOL_BF16)
     # where fp32 P is read in place (rho 0.5, 0.2) the contraction of its 4
-    # tiles runs in 4 ranges: their ordered sum also rounds to a bf16 output
-    check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16, out_dtype=torch.bfloat16)
+    # tiles runs in 4 ranges: their ordered sum also rounds to a bf16 output,
+    # a second rounding after that of P
+    check_pv(w.tensors["P"], w.tensors["V"], rho, dev, TOL_BF16_TWICE, out_dtype=torch.bfloat16)
 
 
 # ------------------- producer-side PV scoring (softmax) ----------------------
