@@ -774,6 +774,39 @@ hipError_t dispatch(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// A grid of 256 x 256 tiles whose last wave leaves at least half the CUs
+// idle (mlp_up 2048 x 28672: 896 tiles, 3.5 waves) is split by columns: the
+// tiles that fill whole waves keep 256 x 256, and the output columns after
+// them go to a second launch of 128 x 128 tiles, which run two to a CU (80
+// KB of LDS and at most 256 registers per lane each), so that last round
+// costs about half a 256 x 256 tile per CU instead of a whole one.  The
+// column band is a pointer offset into B, C and the column scale; B's
+// buffer extent shrinks by the same bytes, so reads past its end still
+// return zero.  Linear products only (K-major B, one batch, no mask, no
+// split contraction).
+bool split_last_wave(const GemmArgs& g, uint32_t b_esize, GemmArgs& head, GemmArgs& tail) {
+  if (!g.b_kmajor || g.causal || g.k_split != 1 || g.batch != 1 || g.M < 256 || g.N < 512) return false;
+  const long tm = (g.M + 255) / 256, tn = (g.N + 255) / 256;
+  if (tm * tn <= kPersistGroups || (tm * tn) % kPersistGroups > kPersistGroups / 2 ||
+      (tm * tn) % kPersistGroups == 0)
+    return false;
+  long n1 = tn - 1;                      // column tiles that fill whole waves
+  while (n1 > 0 && (tm * n1) % kPersistGroups != 0) --n1;
+  if (n1 == 0) return false;
+  const int cols = (int)(n1 * 256);
+  const long t128 = (long)((g.M + 127) / 128) * ((g.N - cols + 127) / 128);
+  if (t128 > 2 * kPersistGroups) return false;
+  head = g;
+  head.N = cols;
+  tail = g;
+  tail.N = g.N - cols;
+  tail.B = (const uint16_t*)((const char*)g.B + (size_t)cols * b_esize);
+  tail.b_bytes = g.b_bytes - (uint32_t)cols * b_esize;
+  tail.C = (char*)g.C + (size_t)cols * (g.c_bf16 ? 2 : 4);
+  if (g.col_scale) tail.col_scale = g.col_scale + cols;
+  return true;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
@@ -785,6 +818,11 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.k_split != 1) return hipErrorInvalidValue;   // split K: fp32 A products only
   if (!g.b_kmajor && t256 >= 2 * kPersistGroups && g.N >= 256 && g.M >= 256)
     return launch_gemm_nmajor_persistent(g, s);
+  GemmArgs head, tail;
+  if (split_last_wave(g, 2, head, tail)) {
+    const hipError_t e = dispatch<256, 256, 8>(head, s);
+    return e != hipSuccess ? e : dispatch<128, 128, 4>(tail, s);
+  }
   if (t256 >= 192 && g.N >= 256 && g.M >= 256) return dispatch<256, 256, 8>(g, s);
   return dispatch<128, 128, 4>(g, s);
 }
@@ -822,10 +860,17 @@ void dispatch_w8(const GemmArgs& g, hipStream_t s) {
 hipError_t launch_gemm_w8(const GemmArgs& g, hipStream_t s) {
   if (!g.b_kmajor || !g.b_i8 || !g.col_scale || g.k_split != 1) return hipErrorInvalidValue;
   const long t256 = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.batch;
-  if (t256 >= 192 && g.N >= 256 && g.M >= 256)
+  GemmArgs head, tail;
+  if (split_last_wave(g, 1, head, tail)) {
+    dispatch_w8<256, 256, 8>(head, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dispatch_w8<128, 128, 4>(tail, s);
+  } else if (t256 >= 192 && g.N >= 256 && g.M >= 256) {
     dispatch_w8<256, 256, 8>(g, s);
-  else
+  } else {
     dispatch_w8<128, 128, 4>(g, s);
+  }
   return hipGetLastError();
 }
 

@@ -898,6 +898,20 @@ def test_full_decode_qkv(dev):
         check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16)
 
 
+@pytest.mark.parametrize("rho", [0.5, 1.0])
+def test_linear_last_wave_split(dev, rho):
+    # 500 x 34776 output: 2 x 136 tiles of 256 x 256 would leave a last wave
+    # of 16 tiles, so the first 32768 columns run as two whole waves of
+    # 256 x 256 tiles and the last 2008 (a ragged band) as 128 x 128 tiles in
+    # a second launch; every row and column compared, fp32 and bf16 output,
+    # bf16 and int8 weights
+    w = synth.mlp_down(n=500, d=448, m=34776, rhos=(0.5,))
+    check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16)
+    check_matmul(w.tensors["A"], w.tensors["B"], rho, dev, TOL_BF16, out_dtype=torch.bfloat16)
+    w8 = synth.w8_projection(n=500, d=448, m=34776, rho=rho, name="w8_last_wave")
+    check_matmul_w8(w8, rho, dev, TOL_BF16)
+
+
 def test_full_mlp_up(dev):
     w = synth.mlp_up()
     rows = tile_rows(2048)[::2]
