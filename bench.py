@@ -123,6 +123,21 @@ def _blas_threads():
 # workloads: each provides the call, its stage work and its oracle sample
 # ---------------------------------------------------------------------------
 
+def splits_last_wave(M: int, N: int, cus: int = 256) -> bool:
+    """Whether the linear GEMM runs as two launches: 256 x 256 tiles over the
+    columns that fill whole waves, then 128 x 128 tiles over the rest (the
+    launcher's rule for a last wave that would fill at most half the CUs);
+    used to name the kernels in the bench line."""
+    tm, tn = -(-M // 256), -(-N // 256)
+    t = tm * tn
+    if M < 256 or N < 512 or t <= cus or t % cus == 0 or t % cus > cus // 2:
+        return False
+    n1 = tn - 1
+    while n1 > 0 and (tm * n1) % cus:
+        n1 -= 1
+    return n1 > 0 and -(-M // 128) * -(-(N - 256 * n1) // 128) <= 2 * cus
+
+
 class MatmulOp:
     """Linear / MLP product Y = A[:, I] B[I, :] (rmm_matmul)."""
 
@@ -202,6 +217,9 @@ class MatmulOp:
         if self.decode:
             return ("gemv_rank_kernel + gemv_reduce_kernel (each workgroup ranks the columns of A while the first "
                     "rows of its slice of B stream in, then reads the kept rows; the slices added in order)")
+        if splits_last_wave(self.n, self.m):
+            return ("gemm_bf16_kernel<256,256,kmajor,gather> over the columns that fill whole waves + "
+                    "gemm_bf16_kernel<128,128,kmajor,gather> over the rest (reduced GEMM, two launches)")
         return "gemm_bf16_kernel<256,256,kmajor,gather> (reduced GEMM)"
 
     def traffic_ref(self):
@@ -314,6 +332,9 @@ class MatmulW8Op(MatmulOp):
             return ("gemv_rank_kernel<bf16 A, int8 B> + gemv_reduce_kernel (each workgroup ranks the columns of A "
                     "while the first rows of its slice stream in, then reads the kept int8 rows of B; the slices "
                     "added in order)")
+        if splits_last_wave(self.n, self.m):
+            return ("gemm_bf16_kernel<256,256,kmajor,gather,int8 B> over the columns that fill whole waves + "
+                    "gemm_bf16_kernel<128,128,kmajor,gather,int8 B> over the rest (reduced GEMM, two launches)")
         return "gemm_bf16_kernel<256,256,kmajor,gather,int8 B> (reduced GEMM)"
 
     def traffic_ref(self):
