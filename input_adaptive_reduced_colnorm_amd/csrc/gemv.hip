@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
   constexpr uint16_t kNone = 0xffff;   // s_pos of a dropped row (list positions are < k <= 8192)
   __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kSliceStride];   // activations by MFMA position
   __shared__ __attribute__((aligned(16))) RankLds u;
-  __shared__ __attribute__((aligned(16))) uint16_t s_pos[kMaxSlice];    // list position of source row r0 + o
+  __shared__ __attribute__((aligned(16))) uint16_t s_pos[kMaxSlice];    // list position of source row r0 + o (first strip; 0 marks a kept row elsewhere)
   __shared__ __attribute__((aligned(16))) uint16_t s_rest[kMaxSlice];   // kept offsets o >= HR, ascending
   __shared__ uint32_t s_cnt;                                              // kept rows past the head
 
@@ -415,11 +415,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
   sel::KeyChunk<CH> kc;
   rank_columns<CH, NR, A_BF16>(g, kc, u.st.src, r0, Ls, issue_head);
   // the ranking's barriers order the s_pos clear and the src stores before
-  // anything below reads them
-  sel::select_ascending<kThreads, CH>(kc, g.k, u.st.ssh, [&](bool take, uint32_t pos, int j, uint32_t) {
-    const int o = j - r0;
-    if (take && (unsigned)o < (unsigned)Ls) s_pos[o] = (uint16_t)pos;
-  });
+  // anything below reads them.  Only the workgroups that write idx (the
+  // first strip) need list positions; the others mark their kept rows
+  // (position 0) and skip the ordered compaction's block scan
+  if (g.idx_out && blockIdx.x == 0) {
+    sel::select_ascending<kThreads, CH>(kc, g.k, u.st.ssh, [&](bool take, uint32_t pos, int j, uint32_t) {
+      const int o = j - r0;
+      if (take && (unsigned)o < (unsigned)Ls) s_pos[o] = (uint16_t)pos;
+    });
+  } else {
+    sel::select_kept<kThreads, CH>(kc, g.k, u.st.ssh, [&](int j) {
+      const int o = j - r0;
+      if ((unsigned)o < (unsigned)Ls) s_pos[o] = 0;
+    });
+  }
   lds_barrier();
 
   // ---- the kept offsets past the head, in order (two per thread), from

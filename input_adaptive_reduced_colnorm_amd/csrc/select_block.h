@@ -444,6 +444,30 @@ __device__ __forceinline__ void select_ascending(const KeyChunk<CH>& kc, int k, 
   }
 }
 
+// Which indices are kept, without their list positions: fn(j) for every
+// kept index j of the chunk.  Where the bucket search decides, each thread
+// tests its own keys against the composite threshold and no block scan
+// runs; otherwise the radix search and the ordered compaction run as in
+// select_ascending.
+template <int NT, int CH, typename Fn>
+__device__ __forceinline__ void select_kept(const KeyChunk<CH>& kc, int k, Shared<NT / 64>& sh, Fn fn) {
+  uint32_t T;
+  int jT;
+  if (bucket_threshold<NT, CH>(kc, k, sh, &T, &jT)) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t key = kc.key[i];
+      if (i < kc.cnt && (key > T || (key == T && kc.j0 + i <= jT))) fn(kc.j0 + i);
+    }
+  } else {
+    uint32_t rem;
+    radix_threshold<NT, CH>(kc, k, sh, &T, &rem);
+    compact_ascending<NT, CH>(kc, T, rem, sh, [&](bool take, uint32_t, int j, uint32_t) {
+      if (take) fn(j);
+    });
+  }
+}
+
 // One window [lo, hi) of the ascending kept list (see compact_window).
 template <int NT, int CH, typename Fn>
 __device__ __forceinline__ void select_window(const KeyChunk<CH>& kc, int k, Shared<NT / 64>& sh, uint32_t lo,
