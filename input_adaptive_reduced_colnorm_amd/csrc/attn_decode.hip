@@ -11,7 +11,8 @@
 // holds, for its 8 consecutive features, the query values of every (head,
 // row) of the group with the unselected features set to zero, and every K
 // row is read once with 16-byte loads.  The partial dot products of the
-// lanes that span a row are folded with a fixed butterfly.  The kept
+// lanes that span a row are folded in a fixed order on the DPP cross-lane
+// paths, all of a pass's tokens at once.  The kept
 // features of a head (at most 256, from at most 8 query rows) are ranked by
 // every workgroup in its prologue (one wave per head, ballot counts, no LDS
 // traffic), while the workgroup's first key rows are already in flight, so
@@ -35,6 +36,28 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt untouched
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Sum of a token's partial dot products over its LPT lanes, on the DPP
+// cross-lane paths (no LDS round trip): xor 1 and xor 2 inside each quad,
+// then each lane with its mirror in the half-row (lane i with 7 - i) and in
+// the row (i with 15 - i).  Every lane of a quad holds the same quad sum
+// after the first two steps, so lane 0 adds the same pairs in the same order
+// as a butterfly over xor 1, 2, 4 and 8; LPT = 32 adds the other row of 16
+// through a cross-lane permute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+template <int LPT>
+__device__ __forceinline__ float fold_lanes(float v) {
+  v += dpp_move<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);   // row_half_mirror
+  if constexpr (LPT >= 16) v += dpp_move<0x140>(v);   // row_mirror
+  if constexpr (LPT >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
 }
 
 template <int G, int LPT>
@@ -156,11 +179,23 @@ __global__ __launch_bounds__(kThreads) void qk_decode_kernel(const QkDecodeArgs 
   for (int j = 0; j < G; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[j][e] = qm[j][sub * 8 + e];
+  // the S row of each (head, query row) of the group, and the last key
+  // position it sees under the causal mask
+  size_t srow[G];
+  int tmax[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const int hl = j / a.tq, r = j % a.tq;
+    srow[j] = ((size_t)(g * group + hl) * a.tq + r) * a.tk;
+    tmax[j] = a.causal ? r + a.tk - a.tq : a.tk;
+  }
+  // all dot products of the token steps first, then their lane folds, then
+  // the stores, so that no product waits on another's fold or store
   for (int t0 = t_first; t0 < t_end; t0 += TPB * kTokSteps) {
     if (t0 != t_first) load_k(t0);
+    float sv[kTokSteps][G];
 #pragma unroll
     for (int u = 0; u < kTokSteps; ++u) {
-      const int t = t0 + u * TPB;
       float kf[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -173,16 +208,26 @@ __global__ __launch_bounds__(kThreads) void qk_decode_kernel(const QkDecodeArgs 
         float v = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) v = fmaf(q[j][e], kf[e], v);
+        sv[u][j] = v;
+      }
+    }
 #pragma unroll
-        for (int o = 1; o < LPT; o <<= 1) v += __shfl_xor(v, o, 64);
-        if (sub == 0 && t < t_end && j < group * a.tq) {
-          const int hl = j / a.tq, r = j % a.tq;
-          const size_t off = ((size_t)(g * group + hl) * a.tq + r) * a.tk + t;
-          if (a.causal && t > r + a.tk - a.tq) v = -INFINITY;
-          if (a.s_bf16)
-            ((uint16_t*)a.S)[off] = f32_to_bf16(v);
-          else
-            ((float*)a.S)[off] = v;
+    for (int u = 0; u < kTokSteps; ++u)
+#pragma unroll
+      for (int j = 0; j < G; ++j) sv[u][j] = fold_lanes<LPT>(sv[u][j]);
+    if (sub == 0) {
+#pragma unroll
+      for (int u = 0; u < kTokSteps; ++u) {
+        const int t = t0 + u * TPB;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          if (t < t_end && j < group * a.tq) {
+            const float v = t > tmax[j] ? -INFINITY : sv[u][j];
+            if (a.s_bf16)
+              ((uint16_t*)a.S)[srow[j] + t] = f32_to_bf16(v);
+            else
+              ((float*)a.S)[srow[j] + t] = v;
+          }
         }
       }
     }
