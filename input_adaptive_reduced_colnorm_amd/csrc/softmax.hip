@@ -26,9 +26,31 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Wave reduction in a fixed order on the DPP cross-lane paths (no LDS round
+// trip): xor 1 and xor 2 inside each quad, then each lane with its mirror in
+// the half-row and in the row, so every lane of a row of 16 holds the row's
+// result; the four rows are then combined as (r0 op r1) op (r2 op r3).
+template <typename F>
+__device__ __forceinline__ float wave_reduce(float v, F op) {
+  v = op(v, dpp_move<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));   // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* red) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();   // red is reused row after row
   if (lane == 0) red[wave] = v;
@@ -39,10 +61,10 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return m;
 }
 
-// fixed-order sum: a butterfly inside each wave, then the waves in order
+// fixed-order sum: wave_reduce inside each wave, then the waves in order
 template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_reduce(v, [](float a, float b) { return a + b; });
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
