@@ -71,6 +71,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
+// The identity lists a dense product reports as its idx output (see
+// GemmArgs::iota_out), written by the threads of the first workgroup.
+__device__ __forceinline__ void write_iota(const GemmArgs& g, int tid, int nt) {
+  const int total = g.iota_heads * g.iota_n;
+  for (int i = tid; i < total; i += nt) {
+    const int h = i / g.iota_n, t = i - h * g.iota_n;
+    g.iota_out[(size_t)h * g.iota_hs + t] = t;
+  }
+}
+
 // WAVES = 4: waves in a 2x2 grid, each (BM/2) x (BN/2).
 // WAVES = 8: waves in a 2x4 grid, each (BM/2) x (BN/4); two waves share a
 // SIMD so one wave's MFMAs cover the other's barrier and LDS latency.
@@ -104,6 +114,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(const GemmArgs
   __shared__ __attribute__((aligned(16))) char smem[A_STAGES * A_BYTES + 2 * B_BYTES];
 
   const int tid = threadIdx.x;
+  if (g.iota_out && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) write_iota(g, tid, NT);
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int li = lane & 31, lk = lane >> 5;
@@ -570,6 +581,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nmajor_persistent_kernel(const Ge
   __shared__ __attribute__((aligned(16))) char smem[2 * A_BYTES + 2 * B_BYTES];
 
   const int tid = threadIdx.x;
+  if (g.iota_out && blockIdx.x == 0) write_iota(g, tid, 512);
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int li = lane & 31, lk = lane >> 5;
@@ -799,6 +811,7 @@ bool split_last_wave(const GemmArgs& g, uint32_t b_esize, GemmArgs& head, GemmAr
   head = g;
   head.N = cols;
   tail = g;
+  tail.iota_out = nullptr;   // the head launch writes them
   tail.N = g.N - cols;
   tail.B = (const uint16_t*)((const char*)g.B + (size_t)cols * b_esize);
   tail.b_bytes = g.b_bytes - (uint32_t)cols * b_esize;

@@ -406,7 +406,7 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
       break;
     }
     case MatPath::kMfmaDirect: {
-      RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
+      // every column kept: the GEMM's first workgroup writes the identity list
       RMM_LAUNCH(mk.mark(1));
       RMM_LAUNCH(mk.mark(2));
       RMM_LAUNCH(mk.mark(3));
@@ -418,6 +418,7 @@ rmm_status_t matmul_impl(const void* A, const void* B, int dtype, int64_t n, int
       g.M = (int)n; g.N = (int)m; g.K = (int)d; g.batch = 1; g.b_kmajor = true;
       g.a_bytes = (uint32_t)(((n - 1) * lda + d) * 2);
       g.b_bytes = (uint32_t)(((d - 1) * ldb + m) * 2);
+      g.iota_out = idx; g.iota_heads = 1; g.iota_n = (int)d; g.iota_hs = 0;
       RMM_LAUNCH(launch_gemm_bf16(g, s));
       break;
     }
@@ -555,7 +556,7 @@ rmm_status_t matmul_w8_impl(const void* A, int a_dtype, const int8_t* Bq, const 
   g.C = Y; g.c_bs = 0; g.ldc = ldy; g.c_bf16 = y_dtype == RMM_BF16;
   g.M = (int)n; g.N = (int)m; g.batch = 1; g.b_kmajor = true;
   if (p.path == MatPath::kMfmaDirect) {
-    RMM_LAUNCH(launch_iota(idx, p.k, 1, (int)d, nullptr, 0, 0, s));
+    // every column kept: the GEMM's first workgroup writes the identity list
     RMM_LAUNCH(mk.mark(1));
     RMM_LAUNCH(mk.mark(2));
     RMM_LAUNCH(mk.mark(3));
@@ -563,6 +564,7 @@ rmm_status_t matmul_w8_impl(const void* A, int a_dtype, const int8_t* Bq, const 
     g.idx = nullptr; g.idx_bs = 0;
     g.K = (int)d;
     g.a_bytes = (uint32_t)(((n - 1) * lda + d) * 2);
+    g.iota_out = idx; g.iota_heads = 1; g.iota_n = (int)d; g.iota_hs = 0;
   } else {
     int32_t* ipad = (int32_t*)(ws + p.off_ipad);
     uint16_t* pk = (uint16_t*)(ws + p.off_pack);
@@ -835,7 +837,9 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
   } else if (p.use_sel) {
     RMM_LAUNCH(run_select(p.sel, ws, Q, bf16, q_hs, q_ts, (int)hq, tq, dh, p.k, idx, p.k, nullptr, s, &mk));
   } else {
-    RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, nullptr, 0, 0, s));
+    // every feature kept: the matrix-core product on Q and K in place writes
+    // the identity lists itself; the other paths read them (pack, SIMT)
+    if (!p.mfma || !p.direct) RMM_LAUNCH(launch_iota(idx, p.k, (int)hq, (int)dh, nullptr, 0, 0, s));
     RMM_LAUNCH(mk.mark(1));
   }
   RMM_LAUNCH(mk.mark(2));
@@ -857,6 +861,9 @@ rmm_status_t qk_impl(const void* Q, const void* K, int dtype, int64_t hq, int64_
     g.A = (const uint16_t*)Q; g.a_bs = q_hs; g.lda = q_ts;
     g.B = (const uint16_t*)K; g.b_bs = k_hs; g.ldb = k_ts; g.b_group = group;
     g.K = (int)dh;
+    if (!p.use_sel) {
+      g.iota_out = idx; g.iota_heads = (int)hq; g.iota_n = (int)dh; g.iota_hs = p.k;
+    }
     g.a_bytes = (uint32_t)(((tq - 1) * q_ts + dh) * 2);
     g.b_bytes = (uint32_t)(((tk - 1) * k_ts + dh) * 2);
   } else {

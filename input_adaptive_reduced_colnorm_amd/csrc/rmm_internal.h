@@ -108,6 +108,12 @@ struct GemmArgs {
   // (fp32), then added in range order into C; 1 = no split
   int k_split = 1;
   float* partial = nullptr;
+  // optional identity index lists, written by the first workgroup (the
+  // dense products' idx output, so that no separate launch writes it):
+  // iota_out[h * iota_hs + t] = t for h < iota_heads, t < iota_n
+  int32_t* iota_out = nullptr;
+  int iota_heads = 0, iota_n = 0;
+  int64_t iota_hs = 0;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
 // Same product with A given as fp32 (rounded to bf16 while staged); a gather
