@@ -784,10 +784,14 @@ __global__ __launch_bounds__(kSmallD) void qk_select_pack_kernel(
   const uint64_t ck = ((uint64_t)__float_as_uint(q) << 32) | (uint32_t)(0xFFFF - j);
   s_ck[j] = ck;
   lds_barrier();
+  // dh is a multiple of 8 here (whole 16-byte pieces), so the pairs cover
+  // exactly the dh keys and the count needs no bound test (a uniform test
+  // in the loop would put a scalar step between every compare and its add)
   int rank = 0;
-  for (int i2 = 0; i2 < (dh + 1) / 2; ++i2) {
+#pragma unroll 8
+  for (int i2 = 0; i2 < dh / 2; ++i2) {
     const u64x2 v = *(const u64x2*)(s_ck + 2 * i2);
-    rank += (int)(v[0] > ck) + ((int)(2 * i2 + 1 < dh) & (int)(v[1] > ck));
+    rank += (int)(v[0] > ck) + (int)(v[1] > ck);
   }
   const bool keep = j < dh && rank < k;
   const uint64_t ballot = __ballot(keep);
@@ -808,19 +812,24 @@ __global__ __launch_bounds__(kSmallD) void qk_select_pack_kernel(
   const int gstride = kSmallD / opr * opr;
   uint16_t* dst = (is_q ? qp + (size_t)h * tq * k_pad : kp + (size_t)h * tk * k_pad) + (size_t)r0 * k_pad;
   const int p = j % opr;
-  uint32_t col[8];
+  // padding positions read column 0 and are masked to zero afterwards, so
+  // every LDS read is unconditional and a row's 8 reads issue together
+  uint32_t col[8], keep_mask[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) col[e] = s_list[8 * p + e];
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t c = s_list[8 * p + e];
+    col[e] = c == 0xFFFFu ? 0u : c;
+    keep_mask[e] = c == 0xFFFFu ? 0u : 0xFFFFu;
+  }
   for (int g = j < gstride ? j : nr * opr; g < nr * opr; g += gstride) {
     const int row = g / opr;
     const uint16_t* rb = s_rows + row * dh;
+    uint32_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (uint32_t)rb[col[e]] & keep_mask[e];
     i32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t v0 = col[2 * e] == 0xFFFFu ? 0u : rb[col[2 * e]];
-      const uint32_t v1 = col[2 * e + 1] == 0xFFFFu ? 0u : rb[col[2 * e + 1]];
-      w[e] = (int)(v0 | (v1 << 16));
-    }
+    for (int e = 0; e < 4; ++e) w[e] = (int)(v[2 * e] | (v[2 * e + 1] << 16));
     *(i32x4*)(dst + (size_t)row * k_pad + 8 * p) = w;
   }
 }
