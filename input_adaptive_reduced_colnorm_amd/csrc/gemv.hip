@@ -434,9 +434,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
   // ---- the kept offsets past the head, in order (two per thread), from
   //      index 0 of their own list so that 8 of them are one 16-byte read ----
   {
+    // both entries in one aligned read (o0 is even; past the array the
+    // offsets are past Ls too and the read is masked)
     const int o0 = HR + 2 * tid;
-    const bool k0 = o0 < Ls && s_pos[o0] != kNone;
-    const bool k1 = o0 + 1 < Ls && s_pos[o0 + 1] != kNone;
+    const uint32_t pp = *(const uint32_t*)&s_pos[o0 < kMaxSlice ? o0 : 0];
+    const bool k0 = o0 < Ls && (pp & 0xffffu) != kNone;
+    const bool k1 = o0 + 1 < Ls && (pp >> 16) != kNone;
     const uint32_t n_r = (uint32_t)k0 + (uint32_t)k1;
     uint32_t inc = n_r, unused = 0;
     sel::block_incl_scan2<kThreads>(inc, unused, u.st.ssh);
@@ -488,14 +491,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemv_rank_kernel(GemvArgs g) {
           v[h] = (int)((uint32_t)a[h] & m);
         }
       } else {
+        // past the kept rows the list holds kNone: those positions read
+        // offset 0 and are masked, so the 8 reads issue unconditionally
         const i32x4 ow = *(const i32x4*)&s_rest[t0 - HR];
+        uint32_t e[8];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t o_lo = (uint32_t)ow[h] & 0xffffu, o_hi = (uint32_t)ow[h] >> 16;
-          const uint32_t lo = o_lo != kNone ? u.st.src[r][o_lo] : 0u;
-          const uint32_t hi = o_hi != kNone ? u.st.src[r][o_hi] : 0u;
-          v[h] = (int)(lo | (hi << 16));
+        for (int h = 0; h < 8; ++h) {
+          const uint32_t o = ((uint32_t)ow[h >> 1] >> (16 * (h & 1))) & 0xffffu;
+          e[h] = (uint32_t)u.st.src[r][o != kNone ? o : 0u] & (o != kNone ? 0xffffu : 0u);
         }
+#pragma unroll
+        for (int h = 0; h < 4; ++h) v[h] = (int)(e[2 * h] | (e[2 * h + 1] << 16));
       }
     }
     *(i32x4*)&s_a[r][t0] = v;
