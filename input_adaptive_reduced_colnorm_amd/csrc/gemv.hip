@@ -147,32 +147,54 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
     // the identity list (rho = 1): the first strip's workgroups write it
     for (int i = tid; i < L; i += kThreads) g.idx_out[t0 + i] = t0 + i;
   }
-  auto kept = [&](int t) -> int {
-    if (!g.idx) return t0 + t;
-    const int j = g.idx[t0 + t];
-    return g.d > 0 && (unsigned)j >= (unsigned)g.d ? -1 : j;
-  };
-
   // ---- load order matters: vector loads retire in order, so a wait for a
   //      load also waits for every load issued before it.  First every
   //      kept-row index this thread needs: its B rows (chunk q covers slice
   //      rows (wave + 4 q) * 32 .., the lane its 8 rows 8 rb ..) and the up
-  //      to two rows it stages.  A row of -1, or past the slice, is invalid ----
-  int row[kChunksPerWave][8];
-#pragma unroll
-  for (int q = 0; q < kChunksPerWave; ++q)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = (wave + kWaves * q) * kChunk + 8 * rb + e;
-      row[q][e] = t < L ? kept(t) : -1;
-    }
+  //      to two rows it stages.  The list loads are unconditional (positions
+  //      past the slice read its last entry) and issued together, so one
+  //      wait covers them all; then positions past the slice and entries
+  //      outside [0, d) become -1 (invalid) ----
   constexpr int PER = kMaxSlice / kThreads;
   const int L32 = (L + kChunk - 1) / kChunk * kChunk;
+  int row[kChunksPerWave][8];
   int srow[PER];
+  if (g.idx && L > 0) {
+    const int32_t* ip = g.idx + t0;
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int i = tid + u * kThreads;
-    srow[u] = i < L ? kept(i) : -1;
+    for (int q = 0; q < kChunksPerWave; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = (wave + kWaves * q) * kChunk + 8 * rb + e;
+        row[q][e] = ip[t < L ? t : L - 1];
+      }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kThreads;
+      srow[u] = ip[i < L ? i : L - 1];
+    }
+    auto check = [&](int t, int j) {
+      return t < L && !(g.d > 0 && (unsigned)j >= (unsigned)g.d) ? j : -1;
+    };
+#pragma unroll
+    for (int q = 0; q < kChunksPerWave; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) row[q][e] = check((wave + kWaves * q) * kChunk + 8 * rb + e, row[q][e]);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) srow[u] = check(tid + u * kThreads, srow[u]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < kChunksPerWave; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = (wave + kWaves * q) * kChunk + 8 * rb + e;
+        row[q][e] = t < L ? t0 + t : -1;
+      }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kThreads;
+      srow[u] = i < L ? t0 + i : -1;
+    }
   }
   // ---- then the activations to stage and every B row, all unconditional
   //      (an invalid row reads row 0 and is zeroed where it is used), so the
