@@ -581,8 +581,12 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
 // One 1024-thread workgroup per compute unit: each sums the split partials
 // and ranks the keys as topk_kernel does, so that every workgroup holds the
 // same ascending kept list, as 16-bit column indices in LDS padded to k_pad
-// with the index z of a zero slot.  It then streams its block of rows of A:
-// each row goes whole from HBM into an LDS row buffer by direct 16-byte
+// with the index z of a zero slot.  It then streams its rows of A, every
+// G-th row from its own index (G workgroups), so that each workgroup's rows
+// were swept by the column-energy pass at all stages of that pass (the rows
+// it read first are the likeliest to have left the Infinity Cache, and a
+// contiguous block of them made a few workgroups 1.5-2x slower than the
+// rest, since they all have the same number of rows): each row goes whole from HBM into an LDS row buffer by direct 16-byte
 // loads (D rows in flight, the first D issued before the ranking so that
 // they land while it runs), and each lane gathers 8 consecutive kept
 // positions from LDS and writes them as one 16-byte piece of the
@@ -595,8 +599,8 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(const void* 
 // Row buffers: NB = D + 1, row i in buffer i % NB, so the buffer refilled
 // for row i + D held row i - 1, which every thread finished reading before
 // the barrier of row i.  The ranking's scratch lies in buffer D (and past
-// it), which first receives a row after the ranking.  Rows past the block
-// are loaded through an empty buffer resource (no memory access, zeros),
+// it), which first receives a row after the ranking.  Rows past the last
+// one are loaded through an empty buffer resource (no memory access, zeros),
 // so every wave issues the same loads per row and the waits count them.
 // ---------------------------------------------------------------------------
 constexpr int kSpGroups = 256;   // workgroups: one per compute unit
@@ -612,7 +616,7 @@ template <int CH, int PR, int D, bool RANK>
 __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* __restrict__ partial, int splits,
                                                                   const int32_t* __restrict__ given,
                                                                   const uint16_t* __restrict__ A, int64_t lda, int n,
-                                                                  int d, int k, int k_pad, int rows_per_wg,
+                                                                  int d, int k, int k_pad,
                                                                   int32_t* __restrict__ idx,
                                                                   int32_t* __restrict__ pad,
                                                                   uint16_t* __restrict__ out) {
@@ -629,8 +633,8 @@ __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* _
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r0 = blockIdx.x * rows_per_wg;
-  const int nr = min(n - r0, rows_per_wg);
+  const int G = gridDim.x, w0 = blockIdx.x;
+  const int nr = (n - w0 + G - 1) / G;          // rows w0, w0 + G, ... below n (at least one)
   const int pieces = d >> 3;                    // 16-byte pieces of a row
   const int z = (pieces + 63) / 64 * 512;       // zero slot: past every wave's load span
   // this wave's loads per row: load p covers pieces [1024 p + 64 wave, + 64)
@@ -640,7 +644,7 @@ __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* _
 
   const uint32_t stage0 = lds_addr(s_stage);
   auto fetch = [&](int i) {
-    const i32x4 r = rsrc_words(A + (size_t)(r0 + min(i, nr - 1)) * lda, i < nr ? (uint32_t)d * 2u : 0u);
+    const i32x4 r = rsrc_words(A + ((size_t)w0 + (size_t)min(i, nr - 1) * G) * lda, i < nr ? (uint32_t)d * 2u : 0u);
     const uint32_t row = stage0 + (uint32_t)((i % NB) * RC * 2);
 #pragma unroll
     for (int p = 0; p < PR; ++p)
@@ -690,7 +694,6 @@ __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* _
     for (int e = 0; e < 4; ++e) cw[p][e] = (uint32_t)v[e];
   }
 
-  uint16_t* ob = out + (size_t)r0 * k_pad;
   for (int i = 0; i < nr; ++i) {
     // row i's loads are followed by those of rows i + 1 .. i + D - 1
     if (nload == PR)
@@ -710,7 +713,7 @@ __global__ __launch_bounds__(kSelThreads) void select_pack_kernel(const float* _
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           w[e] = (int)((uint32_t)buf[cw[p][e] & 0xffffu] | ((uint32_t)buf[cw[p][e] >> 16] << 16));
-        *(i32x4*)(ob + (size_t)i * k_pad + 8 * g) = w;
+        *(i32x4*)(out + ((size_t)w0 + (size_t)i * G) * k_pad + 8 * g) = w;
       }
     }
   }
@@ -932,17 +935,16 @@ bool select_pack_fits(const void* A, int64_t lda, int64_t d) {
 
 hipError_t launch_select_pack(const float* partial, int splits, const uint16_t* A, int64_t lda, int n, int d, int k,
                               int k_pad, int32_t* idx, int32_t* pad, uint16_t* out, hipStream_t s) {
-  const int rows_per_wg = (n + kSpGroups - 1) / kSpGroups;
-  const int grid = (n + rows_per_wg - 1) / rows_per_wg;
+  const int grid = n < kSpGroups ? n : kSpGroups;
   if (d <= 4096)
     select_pack_kernel<chunk_for(4096), 1, 5, true><<<grid, kSelThreads, 0, s>>>(
-        partial, splits, nullptr, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+        partial, splits, nullptr, A, lda, n, d, k, k_pad, idx, pad, out);
   else if (d <= 8192)
     select_pack_kernel<chunk_for(8192), 1, 5, true><<<grid, kSelThreads, 0, s>>>(
-        partial, splits, nullptr, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+        partial, splits, nullptr, A, lda, n, d, k, k_pad, idx, pad, out);
   else
     select_pack_kernel<kChunk, 2, 3, true><<<grid, kSelThreads, 0, s>>>(
-        partial, splits, nullptr, A, lda, n, d, k, k_pad, rows_per_wg, idx, pad, out);
+        partial, splits, nullptr, A, lda, n, d, k, k_pad, idx, pad, out);
   return hipGetLastError();
 }
 
@@ -952,14 +954,13 @@ bool gather_pack_fits(const void* A, int64_t lda, int64_t d, int64_t k_pad) {
 
 hipError_t launch_gather_pack(const int32_t* given, int k, const uint16_t* A, int64_t lda, int n, int d, int k_pad,
                               int32_t* pad, uint16_t* out, hipStream_t s) {
-  const int rows_per_wg = (n + kSpGroups - 1) / kSpGroups;
-  const int grid = (n + rows_per_wg - 1) / rows_per_wg;
+  const int grid = n < kSpGroups ? n : kSpGroups;
   if (d <= 8192 && k_pad <= 8192)
     select_pack_kernel<4, 1, 5, false><<<grid, kSelThreads, 0, s>>>(nullptr, 0, given, A, lda, n, d, k, k_pad,
-                                                                     rows_per_wg, nullptr, pad, out);
+                                                                     nullptr, pad, out);
   else
     select_pack_kernel<4, 2, 3, false><<<grid, kSelThreads, 0, s>>>(nullptr, 0, given, A, lda, n, d, k, k_pad,
-                                                                     rows_per_wg, nullptr, pad, out);
+                                                                     nullptr, pad, out);
   return hipGetLastError();
 }
 
