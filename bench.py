@@ -784,6 +784,14 @@ def run(args, op):
                 row[f"selection_{key}"] = v
         per_kernel[str(r)] = row
 
+    # bandwidth-bound stages also against the rate a plain copy reaches (the
+    # practical ceiling beside the datasheet 8 TB/s)
+    measured = hbm_copy_gbs() if any(k.endswith("_gbs") for row in per_kernel.values() for k in row) else None
+    if measured:
+        for row in per_kernel.values():
+            for key in [k for k in row if k.endswith("_gbs")]:
+                row[key[:-4] + "_frac_of_measured_copy"] = round(row[key] / measured, 4)
+
     # roofline of the dominant kernel of the reduced op (mean over its launches)
     red = [r for r in rhos if r != dense_r]
     stage = op.roofline_stage()
@@ -814,7 +822,7 @@ def run(args, op):
     roofline["traffic_source"] = src
     if roofline["bound"] == "hbm":
         # the datasheet peak above; beside it the rate a plain copy reaches
-        measured = hbm_copy_gbs()
+        measured = measured or hbm_copy_gbs()
         roofline["measured_copy_gbs"] = measured
         roofline["frac_of_measured_copy"] = round(roofline["achieved"] / measured, 4)
 
@@ -843,6 +851,7 @@ def run(args, op):
         "given_index_note": ("rmm_matmul_idx over the set each rho selected (pack + GEMM, no scoring or TopK): "
                              "the cost of a projection that reuses another's selection") if reuse_us else None,
         "kernels": per_kernel,
+        "measured_copy_gbs": measured,
         "roofline": roofline,
     }
     if extra:
